@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of split-KV decode attention on MI355X.
+
+A step is one decode-attention call: the split kernel and the combine kernel
+over one synthetic batch whose inputs are already resident in HBM. The
+headline workload is a 9B-like full-attention layer (16 query / 4 KV heads,
+head_dim 256, f32 KV, q f32) at 131,072 positions; other context lengths,
+storage types and workloads are reported in ``rungs``.
+
+Output: one JSON line with the metric, throughput (algorithmic HBM GB/s of the
+whole call), the split kernel's roofline (HIP-event time per launch on the
+launch stream) and the float64 CPU oracle's throughput on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
+MALL_FLUSH_BYTES = 512 << 20  # twice the 256 MB Infinity Cache
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--seq-len", type=int, default=131072)
+    ap.add_argument("--kv", default="f32", choices=["f32", "f16"])
+    ap.add_argument("--n-splits", type=int, default=0, help="0 = the library's heuristic")
+    ap.add_argument("--no-rungs", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rung-steps", type=int, default=20)
+    return ap.parse_args()
+
+
+def decode_call(case, tensors, n_splits=0):
+    from split_kv_flash_amd import DecodeCall
+
+    return DecodeCall(
+        tensors["q"], tensors["k"], tensors["v"], tensors["seq_lens"], case.seq_lens,
+        scale=case.scale, block_table=tensors["block_table"], page_size=case.page_size,
+        v_cols=case.head_dim_v if case.kv_shared else None, n_splits=n_splits)
+
+
+def algorithmic_bytes(case, plan):
+    """(whole call, split kernel) algorithmic bytes.
+
+    Whole call: K and V rows read once (positions < L_b), q read once, out and
+    lse written once. Split kernel: K, V, q read once plus the partials it
+    writes (B*Hq*S*(Dv+2) floats)."""
+    qb = case.q.nbytes
+    kv = case.kv_bytes()
+    out = case.batch * case.num_q_heads * (case.head_dim_v + 1) * 4
+    part = case.batch * case.num_q_heads * plan.n_splits * (case.head_dim_v + 2) * 4
+    table = 0 if case.block_table is None else sum(-(-int(L) // case.page_size) for L in case.seq_lens) * 4
+    return kv + qb + out + table, kv + qb + part + table
+
+
+def time_steps(call, steps, warmup, flush=None):
+    """Per-launch HIP-event times (ms) of split and combine, and wall ms per step.
+
+    Events are recorded on torch's current stream, which is the stream the
+    library launches on. With ``flush`` (a device buffer) a fill that evicts the
+    Infinity Cache runs before every step, outside the event pairs and the wall
+    clock is then not reported (None)."""
+    import torch
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        if flush is not None:
+            flush.fill_(1)
+        e0.record()
+        call.splitk()
+        e1.record()
+        call.combine()
+        e2.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    split = [a.elapsed_time(b) for a, b, _ in ev]
+    comb = [b.elapsed_time(c) for _, b, c in ev]
+    total = [a.elapsed_time(c) for a, _, c in ev]
+    return split, comb, total, (None if flush is not None else wall)
+
+
+def median(x):
+    return statistics.median(x)
+
+
+def pct(x, q):
+    s = sorted(x)
+    return s[min(len(s) - 1, max(0, int(round(q * (len(s) - 1)))))]
+
+
+def measure(case, steps, warmup, n_splits=0, flush=None):
+    import torch
+    from synthetic.torch_io import to_device
+
+    t = to_device(case)
+    call = decode_call(case, t, n_splits)
+    split, comb, total, wall = time_steps(call, steps, warmup, flush)
+    whole_b, split_b = algorithmic_bytes(case, call.plan)
+    us = median(total) * 1e3
+    res = {
+        "workload": case.name, "n_splits": call.plan.n_splits, "chunk": call.plan.chunk,
+        "us_per_call": round(us, 2), "us_p10": round(pct(total, 0.1) * 1e3, 2),
+        "us_p90": round(pct(total, 0.9) * 1e3, 2),
+        "split_us": round(statistics.mean(split) * 1e3, 2),
+        "combine_us": round(statistics.mean(comb) * 1e3, 2),
+        "GBps": round(whole_b / (us * 1e-6) / 1e9, 1),
+        "frac_of_peak": round(whole_b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "split_GBps": round(split_b / (statistics.mean(split) * 1e-3) / 1e9, 1),
+        "bytes_call": whole_b, "bytes_split": split_b,
+        "tokens_per_s_per_layer": round(case.batch * 1e6 / us, 1),
+        "mall_flushed": flush is not None,
+    }
+    del call, t
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, split, wall
+
+
+def cpu_baseline(case, heads, reps=3):
+    """Time the float64 oracle on a bounded sample (the given query heads)."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = None
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.attend_f64(case.q, case.k_rows(), case.v_rows(), case.seq_lens, case.scale,
+                          q_dtype=case.q_dtype, kv_dtype=case.kv_dtype, heads=heads)
+        times.append(time.perf_counter() - t0)
+    groups = sorted(set(h // case.group for _, h in heads))
+    kv_per_group = case.kv_bytes() / case.num_kv_heads
+    byts = kv_per_group * len(groups)
+    sec = median(times)
+    return {
+        "value": round(byts / sec / 1e9, 3), "unit": "GB/s", "cores": threads,
+        "kind": "oracle",
+        "sample": f"{case.name}: query heads {[h for _, h in heads]} (KV groups {groups}), "
+                  f"median of {reps} float64 two-pass oracle calls, {sec:.2f} s each; "
+                  f"bytes = K+V rows of the sampled KV groups",
+        "seconds_per_call": round(sec, 3),
+        "cpu": _cpu_model(),
+        "host_cores_visible": len(os.sched_getaffinity(0)),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU; every box here has one GPU and "
+                                   "the multi-GPU path is a design note only (run with --gpus 1)"}))
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    import synthetic
+
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name} CUs={props.multi_processor_count} "
+        f"mem={props.total_memory / 2**30:.0f} GiB")
+
+    # Headline: A and B runs of the same workload give the A/A noise floor.
+    case = synthetic.qwen9b_like(args.seq_len, args.kv, seed=2000 + args.seq_len)
+    log(f"headline workload {case.name}: K+V {case.kv_bytes() / 1e9:.3f} GB")
+    head_a, split_a, wall_a = measure(case, args.steps, args.warmup, args.n_splits)
+    log(f"run A: {head_a}")
+    head_b, split_b, _ = measure(case, args.steps, args.warmup, args.n_splits)
+    log(f"run B: {head_b}")
+    aa_spread = abs(head_a["us_per_call"] - head_b["us_per_call"]) / head_a["us_per_call"]
+
+    split_ms = statistics.mean(split_a)
+    achieved = head_a["bytes_split"] / (split_ms * 1e-3) / 1e9
+    roofline = {
+        "kernel": "gqa_split_kernel",
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+        "avg_launch_us": round(split_ms * 1e3, 2),
+        "algorithmic_bytes_per_launch": head_a["bytes_split"],
+    }
+
+    rungs = []
+    if not args.no_rungs:
+        flush = torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        specs = []
+        for kv in ("f32", "f16"):
+            for L in (4096, 20480, 61440, 151552, 262144):
+                specs.append(lambda kv=kv, L=L: synthetic.qwen9b_like(L, kv, seed=2000 + L))
+        specs.append(lambda: synthetic.wide_group_peaky(262144))
+        specs.append(lambda: synthetic.ragged_paged())
+        for mk in specs:
+            c = mk()
+            small = c.kv_bytes() < 2 * MALL_FLUSH_BYTES
+            r, _, _ = measure(c, args.rung_steps, 5, 0, flush if small else None)
+            log(f"rung {r}")
+            rungs.append(r)
+            del c
+        del flush
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(case, [(0, h) for h in range(case.num_q_heads)])
+        log(f"cpu baseline {cpu}")
+
+    line = {
+        "metric": "decode-attention µs/call and achieved HBM GB/s (% of peak) at 128k context",
+        "value": head_a["GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_a, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) q/K/V, no dataset)",
+        "config": {
+            "workload": f"9B-like full-attention decode layer: batch 1, 16 query / 4 KV heads, "
+                        f"head_dim 256, q f32, KV {args.kv}, context {args.seq_len}",
+            "global_batch": 1, "seq_len": args.seq_len, "kv_dtype": args.kv,
+            "n_splits": head_a["n_splits"], "chunk": head_a["chunk"],
+            "parallelism": "single GPU",
+        },
+        "us_per_call": head_a["us_per_call"],
+        "frac_of_peak": head_a["frac_of_peak"],
+        "split_us": head_a["split_us"],
+        "combine_us": head_a["combine_us"],
+        "tokens_per_s_per_layer": head_a["tokens_per_s_per_layer"],
+        "aa_noise_floor": round(aa_spread, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rungs": rungs,
+        "device": props.name,
+        "cu_count": props.multi_processor_count,
+    }
+    if cpu:
+        line["cpu_baseline_ratio"] = round(head_a["GBps"] / cpu["value"], 1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,210 @@
+/*
+ * splitkv.h — C ABI of a split-KV ("flash-decoding") decode-attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * One decode call computes, for every sequence b and query head h (reading
+ * KV head g = h / (num_q_heads / num_kv_heads)), single-token attention over
+ * the L_b cached positions:
+ *
+ *     s_j = scale * <q[b,h,:], K[b,g,j,:]>          j = 0 .. L_b - 1
+ *     out[b,h,:] = sum_j exp(s_j - m) V[b,g,j,:] / sum_j exp(s_j - m),
+ *     m = max_j s_j,   lse[b,h] = m + ln sum_j exp(s_j - m)
+ *
+ * in two launches, as the pages describe the method:
+ *
+ *   attn_decode_splitk   One workgroup per (sequence, KV head or shared
+ *                        latent, context split) runs the online-softmax
+ *                        recurrence over one contiguous slice of positions
+ *                        and writes the partial triple (m, l, acc) of every
+ *                        query head it serves ("Part 4 · Lecture 06 —
+ *                        Attention at 128k", section 2 "Split over context";
+ *                        aprender issue #3725 design note, section 2, kernel
+ *                        A; "The Kernel Level: Attention and MoE", section
+ *                        "Decode Starves the SMs: Split-KV, the LSE Merge, and
+ *                        One Latent for 128 Heads").
+ *   attn_decode_combine  Rescales the partials of each (sequence, query head)
+ *                        to their common maximum and sums them (Lecture 06
+ *                        section 2: M = max m_i, l = sum l_i exp(m_i - M),
+ *                        acc = sum acc_i exp(m_i - M); issue #3725 design
+ *                        note section 2, kernel B).
+ *
+ * Conventions shared by every call
+ *   - Pointers named "device" are device memory on the device that owns
+ *     `stream`; the library never dereferences them on the host.
+ *   - The caller owns every buffer, including the workspace. The library
+ *     allocates nothing and keeps no global or per-device state, so calls are
+ *     re-entrant and safe from several host threads and devices (Lecture 06
+ *     section 2 explains why scratch must be per device, never one static
+ *     pointer shared by several devices).
+ *   - Arguments are validated before any HIP call. A failed validation
+ *     returns SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED or
+ *     SK_ERR_WORKSPACE_TOO_SMALL and launches nothing.
+ *   - Every launch is followed by hipGetLastError(); a failure returns
+ *     SK_ERR_LAUNCH, so a bad launch is reported by the call that made it
+ *     and not by some later call (Lecture 06 section 5.3, "The launch guard").
+ *     attn_decode_last_error() returns the detail text for the calling thread.
+ *   - Launches are asynchronous on `stream`; results are valid once the stream
+ *     has completed them. Nothing synchronises inside the library.
+ *   - Plan-time inputs are two host integers; lengths are read on the device,
+ *     so pointers and shapes stay fixed across decode steps.
+ */
+#ifndef SPLITKV_H
+#define SPLITKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SK_OK = 0,
+  SK_ERR_INVALID_ARG = 1,         /* null pointer, bad size, inconsistent descriptor or plan */
+  SK_ERR_UNSUPPORTED = 2,         /* valid request with no kernel for it; nothing runs       */
+  SK_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < attn_decode_workspace_bytes(...)       */
+  SK_ERR_LAUNCH = 4,              /* hipGetLastError() failed right after a launch            */
+  SK_ERR_HIP = 5                  /* another HIP runtime call failed                           */
+} sk_status_t;
+
+/* Element types. q and KV may be any of them; out, lse and the workspace are f32. */
+typedef enum { SK_F32 = 0, SK_F16 = 1, SK_BF16 = 2 } sk_dtype_t;
+
+/* KV cache layouts. */
+typedef enum {
+  /* K and V are separate buffers addressed as
+   *   base + b*stride_seq + j*stride_pos + g*stride_head + d      (elements),
+   * d contiguous. The usual token-major cache [batch][capacity][Hkv][D] has
+   * stride_seq = capacity*Hkv*D, stride_pos = Hkv*D, stride_head = D
+   * (issue #3725 design note section 1 reads this layout).                    */
+  SK_KV_CONTIGUOUS = 0,
+  /* K and V are pools [num_pages][page_size][Hkv][D]; position j of sequence b
+   * lives in page block_table[b*max_pages_per_seq + j/page_size], slot
+   * j % page_size ("The Kernel Level: Attention and MoE": the kernel indexes
+   * KV through the block table; the table pointer stays fixed across steps). */
+  SK_KV_PAGED = 1
+} sk_kv_layout_t;
+
+/* Shape and layout of one decode call. Plain data; the caller fills it. */
+typedef struct {
+  int32_t batch;            /* B >= 1                                                   */
+  int32_t num_q_heads;      /* Hq >= 1, a multiple of num_kv_heads                       */
+  int32_t num_kv_heads;     /* Hkv >= 1; 1 when kv_shared                                */
+  int32_t head_dim_qk;      /* Dk: key width (GQA: 64, 128, 256; latent: 576)            */
+  int32_t head_dim_v;       /* Dv: value width (GQA: equal to Dk; latent: <= Dk, e.g. 512) */
+  int32_t kv_shared;        /* 1: values are columns [0, Dv) of the key rows (multi-head
+                               latent attention in absorbed form, "The Kernel Level:
+                               Attention and MoE": a 512-column latent followed by 64
+                               rotary columns); `v` must then be NULL                    */
+  float scale;              /* multiplies q.k (usually 1/sqrt(Dk))                       */
+  int32_t q_dtype;          /* sk_dtype_t of q                                          */
+  int32_t kv_dtype;         /* sk_dtype_t of K and V                                     */
+  int32_t layout;           /* sk_kv_layout_t                                           */
+  int32_t max_seq_len;      /* capacity per sequence in positions: contiguous rows
+                               readable per sequence; paged: <= max_pages_per_seq*page_size */
+  int32_t page_size;        /* paged: positions per page, a power of two                 */
+  int32_t max_pages_per_seq;/* paged: row length of block_table                          */
+  int64_t num_pages;        /* paged: pages in each pool                                 */
+  int64_t stride_seq;       /* contiguous: elements between sequences                    */
+  int64_t stride_pos;       /* contiguous: elements between consecutive positions       */
+  int64_t stride_head;      /* contiguous: elements between KV heads                     */
+} sk_desc_t;
+
+/* How the context axis is cut. Split i of sequence b covers positions
+ * [i*chunk, min(L_b, (i+1)*chunk)); sequence b uses splits 0 .. ceil(L_b/chunk)-1
+ * and splits past those are empty (their workgroups write the neutral partial
+ * m = -inf, l = 0, acc = 0 and read nothing). */
+typedef struct {
+  int32_t n_splits; /* S: split slots per (sequence, KV head); workspace is sized by it */
+  int32_t chunk;    /* positions per split                                                */
+} sk_plan_t;
+
+/* Choose S and chunk (host only; no HIP call).
+ *   max_seq_len         longest L_b of this call (>= 1)
+ *   total_tokens        sum of L_b over the batch (>= max_seq_len)
+ *   cu_count            compute units of the device (hipDeviceProp_t.multiProcessorCount)
+ *   n_splits_requested  > 0: honoured exactly, chunk = ceil(max_seq_len / S) (trailing
+ *                       splits may be empty); 0: heuristic.
+ * Heuristic (issue #3725 design note section 2: chunk = max(64, ceil(L/S_target)) and
+ * S = ceil(L/chunk) so that no split is empty, S_target about 4 blocks per
+ * multiprocessor; budgeted on the product of KV heads and splits summed over the
+ * batch, as Lecture 06 section 5.1 asks):
+ *   GQA:    chunk = max(64, ceil(Hkv * total_tokens / (4 * cu_count)))
+ *   latent: chunk = max(64, ceil(total_tokens / cu_count))  (one workgroup serves all
+ *           query heads, and each split costs a partial of every head)
+ *   chunk is rounded up to a multiple of 64 and S = ceil(max_seq_len / chunk).
+ * Below SK_MIN_SPLIT_CONTEXT positions the heuristic returns S = 1 (Lecture 06
+ * section 2 gates the split below a minimum context).
+ * Errors: SK_ERR_INVALID_ARG for null pointers or non-positive sizes. */
+#define SK_MIN_SPLIT_CONTEXT 0
+sk_status_t attn_decode_plan(const sk_desc_t* desc, int32_t max_seq_len, int64_t total_tokens,
+                             int32_t cu_count, int32_t n_splits_requested, sk_plan_t* plan);
+
+/* Bytes of workspace a call with (desc, plan) needs; 0 if the pair is invalid.
+ * Layout (f32, each section starting at a multiple of 256 bytes):
+ *   acc [batch][num_q_heads][n_splits][head_dim_v]   un-normalised accumulators
+ *   m   [batch][num_q_heads][n_splits]               slice maximum of s_j (natural-log units)
+ *   l   [batch][num_q_heads][n_splits]               sum over the slice of exp(s_j - m)
+ * (issue #3725 design note section 2: partials of (m, s, acc[D]) per query head and split,
+ * acc left un-normalised.) */
+size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan);
+
+/* Split kernel: writes the partial triple of every (b, h, split) into `workspace`.
+ *   q            device, [batch][num_q_heads][head_dim_qk] of q_dtype, contiguous
+ *   k, v         device, KV cache of kv_dtype in `layout`; v is NULL iff kv_shared
+ *   block_table  device int32 [batch][max_pages_per_seq] when paged, else NULL
+ *   seq_lens     device int32 [batch]; 1 <= L_b <= min(max_seq_len, n_splits*chunk)
+ *   workspace    device, >= attn_decode_workspace_bytes(desc, plan) bytes, 256-byte aligned
+ *   stream       HIP stream of the device holding every buffer
+ * A length outside its range is a caller error: the kernels never read outside
+ * [0, max_seq_len) nor outside the pools, and the combine then writes NaN for that
+ * sequence. A block-table entry outside [0, num_pages) is likewise never followed;
+ * the rows it names poison that head's output with NaN.
+ * Supported: GQA with head_dim_qk == head_dim_v in {64, 128, 256}, group size
+ * num_q_heads/num_kv_heads in {1, 2, 4, 6, 8}, any q/KV dtype, both layouts; latent
+ * (kv_shared) with num_kv_heads == 1, head_dim_qk == 576, head_dim_v == 512, num_q_heads
+ * a multiple of 32 up to 128, KV f32 or f16, contiguous. Anything else returns
+ * SK_ERR_UNSUPPORTED without launching. */
+sk_status_t attn_decode_splitk(const sk_desc_t* desc, const sk_plan_t* plan,
+                               const void* q, const void* k, const void* v,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Combine kernel: merges the first ceil(L_b/chunk) partials of each (b, h) — the only
+ * non-empty ones — into
+ *   out  device f32 [batch][num_q_heads][head_dim_v]
+ *   lse  device f32 [batch][num_q_heads], or NULL to skip (natural log of sum_j exp(s_j))
+ * reading `workspace` as written by attn_decode_splitk with the same desc and plan,
+ * earlier on the same stream. */
+sk_status_t attn_decode_combine(const sk_desc_t* desc, const sk_plan_t* plan,
+                                const int32_t* seq_lens, const void* workspace,
+                                size_t workspace_bytes, float* out, float* lse,
+                                hipStream_t stream);
+
+/* Static text for a status code. */
+const char* attn_decode_status_string(sk_status_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* attn_decode_last_error(void);
+
+/* Properties of the split kernel a (desc, plan) pair selects (needs a GPU: it asks
+ * the HIP runtime for the kernel's attributes).
+ *   lds_bytes    static LDS per workgroup (independent of the context length: Lecture 06
+ *                section 2 requires shared memory of O(key width + tile), never O(n_ctx))
+ *   vgprs        vector registers per lane (arch + accumulation), as the runtime reports
+ *   block        threads per workgroup; grid_x/y/z the launch grid */
+typedef struct {
+  int32_t lds_bytes;
+  int32_t vgprs;
+  int32_t block;
+  int32_t grid_x, grid_y, grid_z;
+} sk_kernel_info_t;
+sk_status_t attn_decode_kernel_info(const sk_desc_t* desc, const sk_plan_t* plan,
+                                    sk_kernel_info_t* info);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLITKV_H */

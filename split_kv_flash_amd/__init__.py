@@ -1,0 +1,162 @@
+"""Split-KV (flash-decoding) decode attention for AMD Instinct MI355X (gfx950).
+
+The compute path is the HIP library ``libsplitkv.so`` (C ABI in
+``include/splitkv.h``): a split kernel in which one workgroup serves every
+query head of a KV group (or of a shared latent) over one contiguous slice of
+the context, and a combine kernel that rescales the partials to their common
+maximum and sums them. This package is the thin Python side: ``binding``
+mirrors the C entry points one to one, and :class:`DecodeCall` fills the
+descriptor from torch tensors and owns the workspace. PyTorch is used only for
+device memory and streams.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+from . import binding
+from .binding import (  # noqa: F401
+    SK_BF16, SK_F16, SK_F32, SK_KV_CONTIGUOUS, SK_KV_PAGED, SkDesc, SkKernelInfo, SkPlan,
+    SplitKVError, attn_decode_combine, attn_decode_kernel_info, attn_decode_last_error,
+    attn_decode_plan, attn_decode_splitk, attn_decode_status_string,
+    attn_decode_workspace_bytes,
+)
+
+__all__ = [
+    "DecodeCall", "make_desc", "SkDesc", "SkPlan", "SplitKVError", "attn_decode_plan",
+    "attn_decode_workspace_bytes", "attn_decode_splitk", "attn_decode_combine",
+    "attn_decode_status_string", "attn_decode_last_error", "attn_decode_kernel_info",
+]
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    codes = {torch.float32: SK_F32, torch.float16: SK_F16, torch.bfloat16: SK_BF16}
+    if t.dtype not in codes:
+        raise SplitKVError(binding.SK_ERR_UNSUPPORTED, f"dtype {t.dtype} is not f32/f16/bf16")
+    return codes[t.dtype]
+
+
+def make_desc(q, k, v=None, *, scale: float, block_table=None, page_size: int = 0,
+              v_cols: Optional[int] = None, max_seq_len: Optional[int] = None) -> SkDesc:
+    """Descriptor for tensors laid out as the C header describes.
+
+    q            [B][Hq][Dk], contiguous
+    k, v         contiguous cache [B][capacity][Hkv][D] (any strides with unit
+                 last stride), or pools [pages][page_size][Hkv][D] when
+                 ``block_table`` ([B][max_pages] int32) is given
+    v = None     shared latent: values are the first ``v_cols`` key columns
+    """
+    d = SkDesc()
+    if q.dim() != 3 or not q.is_contiguous():
+        raise SplitKVError(binding.SK_ERR_INVALID_ARG, "q must be a contiguous [B][Hq][Dk] tensor")
+    B, Hq, Dk = q.shape
+    if k.dim() != 4 or k.stride(3) != 1:
+        raise SplitKVError(binding.SK_ERR_INVALID_ARG, "k must be 4-D with unit last stride")
+    d.batch, d.num_q_heads, d.head_dim_qk = B, Hq, Dk
+    d.num_kv_heads = k.shape[2]
+    if k.shape[3] != Dk:
+        raise SplitKVError(binding.SK_ERR_INVALID_ARG, "k's last dimension must equal q's")
+    d.kv_shared = 1 if v is None else 0
+    if v is None:
+        if v_cols is None:
+            raise SplitKVError(binding.SK_ERR_INVALID_ARG, "v_cols is required without v")
+        d.head_dim_v = int(v_cols)
+    else:
+        if v.shape != k.shape or v.stride() != k.stride() or v.dtype != k.dtype:
+            raise SplitKVError(binding.SK_ERR_INVALID_ARG, "v must match k's shape, strides and dtype")
+        d.head_dim_v = v.shape[3]
+    d.scale = float(scale)
+    d.q_dtype = _dtype_code(q)
+    d.kv_dtype = _dtype_code(k)
+    if block_table is None:
+        d.layout = SK_KV_CONTIGUOUS
+        d.max_seq_len = int(k.shape[1] if max_seq_len is None else max_seq_len)
+        d.stride_seq, d.stride_pos, d.stride_head = k.stride(0), k.stride(1), k.stride(2)
+    else:
+        if not k.is_contiguous():
+            raise SplitKVError(binding.SK_ERR_INVALID_ARG, "paged pools must be contiguous")
+        d.layout = SK_KV_PAGED
+        d.page_size = int(page_size or k.shape[1])
+        if k.shape[1] != d.page_size:
+            raise SplitKVError(binding.SK_ERR_INVALID_ARG, "pool dim 1 must equal page_size")
+        d.max_pages_per_seq = block_table.shape[1]
+        d.num_pages = k.shape[0]
+        d.max_seq_len = int(d.max_pages_per_seq * d.page_size if max_seq_len is None else max_seq_len)
+    return d
+
+
+def _stream_handle(stream) -> int:
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+class DecodeCall:
+    """One decode-attention call shape: descriptor, plan, workspace, outputs.
+
+    ``host_seq_lens`` gives the lengths on the host (for the plan and for the
+    contract check 1 <= L_b <= min(capacity, n_splits*chunk)); ``seq_lens`` is
+    the same int32 data on the device. Calls launch on the current torch
+    stream unless one is given.
+    """
+
+    def __init__(self, q, k, v, seq_lens, host_seq_lens, *, scale: float, block_table=None,
+                 page_size: int = 0, v_cols: Optional[int] = None, n_splits: int = 0,
+                 cu_count: Optional[int] = None, max_seq_len: Optional[int] = None):
+        import torch
+
+        self.desc = make_desc(q, k, v, scale=scale, block_table=block_table, page_size=page_size,
+                              v_cols=v_cols, max_seq_len=max_seq_len)
+        lens = [int(x) for x in host_seq_lens]
+        if len(lens) != self.desc.batch:
+            raise SplitKVError(binding.SK_ERR_INVALID_ARG, "host_seq_lens has the wrong length")
+        if cu_count is None:
+            cu_count = torch.cuda.get_device_properties(q.device).multi_processor_count
+        self.cu_count = int(cu_count)
+        self.plan = attn_decode_plan(self.desc, max(lens), sum(lens), self.cu_count, n_splits)
+        limit = min(self.desc.max_seq_len, self.plan.n_splits * self.plan.chunk)
+        if min(lens) < 1 or max(lens) > limit:
+            raise SplitKVError(binding.SK_ERR_INVALID_ARG,
+                               f"sequence lengths must lie in [1, {limit}]")
+        self.ws_bytes = attn_decode_workspace_bytes(self.desc, self.plan)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=q.device)
+        self.out = torch.empty(self.desc.batch, self.desc.num_q_heads, self.desc.head_dim_v,
+                               dtype=torch.float32, device=q.device)
+        self.lse = torch.empty(self.desc.batch, self.desc.num_q_heads, dtype=torch.float32,
+                               device=q.device)
+        self.q, self.k, self.v, self.seq_lens, self.block_table = q, k, v, seq_lens, block_table
+
+    def splitk(self, stream=None):
+        attn_decode_splitk(self.desc, self.plan, self.q, self.k, self.v, self.block_table,
+                           self.seq_lens, self.workspace, self.ws_bytes, _stream_handle(stream))
+
+    def combine(self, stream=None, with_lse: bool = True):
+        attn_decode_combine(self.desc, self.plan, self.seq_lens, self.workspace, self.ws_bytes,
+                            self.out, self.lse if with_lse else None, _stream_handle(stream))
+
+    def __call__(self, stream=None):
+        self.splitk(stream)
+        self.combine(stream)
+        return self.out, self.lse
+
+    def partials(self):
+        """Views of the workspace: acc [B][Hq][S][Dv], m and l [B][Hq][S] (f32)."""
+        import torch
+
+        d, p = self.desc, self.plan
+        rows = d.batch * d.num_q_heads * p.n_splits
+
+        def a256(x):
+            return (x + 255) // 256 * 256
+
+        acc_b = rows * d.head_dim_v * 4
+        m_off = a256(acc_b)
+        l_off = m_off + a256(rows * 4)
+        ws = self.workspace
+        acc = ws[:acc_b].view(torch.float32).view(d.batch, d.num_q_heads, p.n_splits, d.head_dim_v)
+        m = ws[m_off:m_off + rows * 4].view(torch.float32).view(d.batch, d.num_q_heads, p.n_splits)
+        l = ws[l_off:l_off + rows * 4].view(torch.float32).view(d.batch, d.num_q_heads, p.n_splits)
+        return acc, m, l

@@ -1,0 +1,324 @@
+// C ABI entry points: validation, split planning, workspace layout, launches.
+//
+// Everything before the first HIP call is plain host logic, so argument errors
+// are reported (and testable) on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "sk_internal.h"
+#include "splitkv.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sk_status_t fail(sk_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sk_status_t fail(sk_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+sk_status_t ok() {
+  g_last_error.clear();
+  return SK_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+constexpr int32_t kMinChunk = 64;
+constexpr int32_t kChunkGranule = 64;
+constexpr int32_t kGqaBlocksPerCu = 4;
+constexpr int32_t kMaxGridYZ = 65535;
+
+// Shape checks shared by every entry point (no pointer checks).
+sk_status_t check_desc(const sk_desc_t* d) {
+  if (!d) return fail(SK_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 1) return fail(SK_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", d->batch);
+  if (d->batch > kMaxGridYZ) return fail(SK_ERR_INVALID_ARG, "batch %d exceeds %d", d->batch, kMaxGridYZ);
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1)
+    return fail(SK_ERR_INVALID_ARG, "head counts must be >= 1 (q %d, kv %d)", d->num_q_heads,
+                d->num_kv_heads);
+  if (d->num_q_heads % d->num_kv_heads)
+    return fail(SK_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                d->num_q_heads, d->num_kv_heads);
+  if (d->head_dim_qk < 1 || d->head_dim_v < 1)
+    return fail(SK_ERR_INVALID_ARG, "head dims must be >= 1 (qk %d, v %d)", d->head_dim_qk,
+                d->head_dim_v);
+  if (d->head_dim_v % 4)
+    return fail(SK_ERR_INVALID_ARG, "head_dim_v %d is not a multiple of 4", d->head_dim_v);
+  if (d->kv_shared != 0 && d->kv_shared != 1)
+    return fail(SK_ERR_INVALID_ARG, "kv_shared must be 0 or 1");
+  if (d->kv_shared && d->head_dim_v > d->head_dim_qk)
+    return fail(SK_ERR_INVALID_ARG, "shared latent: head_dim_v %d exceeds head_dim_qk %d",
+                d->head_dim_v, d->head_dim_qk);
+  if (d->kv_shared && d->num_kv_heads != 1)
+    return fail(SK_ERR_INVALID_ARG, "shared latent needs num_kv_heads == 1");
+  if (!d->kv_shared && d->head_dim_v != d->head_dim_qk)
+    return fail(SK_ERR_UNSUPPORTED, "separate K and V need head_dim_qk == head_dim_v");
+  if (!(d->scale == d->scale) || d->scale == __builtin_inff() || d->scale == -__builtin_inff())
+    return fail(SK_ERR_INVALID_ARG, "scale must be finite");
+  if (d->q_dtype < SK_F32 || d->q_dtype > SK_BF16 || d->kv_dtype < SK_F32 || d->kv_dtype > SK_BF16)
+    return fail(SK_ERR_INVALID_ARG, "unknown dtype (q %d, kv %d)", d->q_dtype, d->kv_dtype);
+  if (d->max_seq_len < 1) return fail(SK_ERR_INVALID_ARG, "max_seq_len must be >= 1");
+  if (d->layout == SK_KV_CONTIGUOUS) {
+    if (d->stride_pos < 1 || d->stride_head < 0 || d->stride_seq < 0)
+      return fail(SK_ERR_INVALID_ARG, "contiguous strides must be non-negative (stride_pos >= 1)");
+    if (d->num_kv_heads > 1 && d->stride_head < d->head_dim_qk)
+      return fail(SK_ERR_INVALID_ARG, "stride_head %lld overlaps KV heads of width %d",
+                  (long long)d->stride_head, d->head_dim_qk);
+    const int64_t vec = d->kv_dtype == SK_F32 ? 4 : 8;  // elements per 16-byte load
+    if (d->stride_pos % vec || d->stride_head % vec || d->stride_seq % vec)
+      return fail(SK_ERR_UNSUPPORTED, "strides must be multiples of 16 bytes (vector loads)");
+  } else if (d->layout == SK_KV_PAGED) {
+    if (d->kv_shared) return fail(SK_ERR_UNSUPPORTED, "paged shared latent is not supported");
+    if (!is_pow2(d->page_size))
+      return fail(SK_ERR_INVALID_ARG, "page_size %d is not a power of two", d->page_size);
+    if (d->max_pages_per_seq < 1 || d->num_pages < 1)
+      return fail(SK_ERR_INVALID_ARG, "paged: max_pages_per_seq and num_pages must be >= 1");
+    if ((int64_t)d->max_seq_len > (int64_t)d->max_pages_per_seq * d->page_size)
+      return fail(SK_ERR_INVALID_ARG, "max_seq_len %d exceeds max_pages_per_seq*page_size",
+                  d->max_seq_len);
+  } else {
+    return fail(SK_ERR_INVALID_ARG, "unknown layout %d", d->layout);
+  }
+  return SK_OK;
+}
+
+sk_status_t check_plan(const sk_desc_t* d, const sk_plan_t* p) {
+  if (!p) return fail(SK_ERR_INVALID_ARG, "plan is NULL");
+  if (p->n_splits < 1 || p->chunk < 1)
+    return fail(SK_ERR_INVALID_ARG, "plan needs n_splits >= 1 and chunk >= 1 (got %d, %d)",
+                p->n_splits, p->chunk);
+  if (p->n_splits > kMaxGridYZ)
+    return fail(SK_ERR_INVALID_ARG, "n_splits %d exceeds %d", p->n_splits, kMaxGridYZ);
+  return SK_OK;
+}
+
+sk_status_t check_support(const sk_desc_t* d) {
+  if (d->kv_shared) {
+    if (!sk::latent_supported(*d))
+      return fail(SK_ERR_UNSUPPORTED,
+                  "shared latent supports Hkv 1, Dk 576, Dv 512, Hq a multiple of 32 up to 128, "
+                  "KV f32/f16, contiguous");
+  } else if (!sk::gqa_supported(*d)) {
+    return fail(SK_ERR_UNSUPPORTED,
+                "GQA supports head_dim 64/128/256 (qk == v) and group size 1/2/4/6/8");
+  }
+  return SK_OK;
+}
+
+}  // namespace
+
+namespace sk {
+
+WsLayout ws_layout(const sk_desc_t& d, const sk_plan_t& p) {
+  WsLayout w;
+  const size_t rows = (size_t)d.batch * d.num_q_heads * p.n_splits;
+  w.acc_off = 0;
+  w.m_off = align256(rows * d.head_dim_v * sizeof(float));
+  w.l_off = w.m_off + align256(rows * sizeof(float));
+  w.total = w.l_off + align256(rows * sizeof(float));
+  return w;
+}
+
+}  // namespace sk
+
+extern "C" {
+
+sk_status_t attn_decode_plan(const sk_desc_t* desc, int32_t max_seq_len, int64_t total_tokens,
+                             int32_t cu_count, int32_t n_splits_requested, sk_plan_t* plan) {
+  sk_status_t s = check_desc(desc);
+  if (s != SK_OK) return s;
+  if (!plan) return fail(SK_ERR_INVALID_ARG, "plan is NULL");
+  if (max_seq_len < 1) return fail(SK_ERR_INVALID_ARG, "max_seq_len must be >= 1");
+  if (max_seq_len > desc->max_seq_len)
+    return fail(SK_ERR_INVALID_ARG, "max_seq_len %d exceeds the capacity %d", max_seq_len,
+                desc->max_seq_len);
+  if (total_tokens < max_seq_len || total_tokens > (int64_t)max_seq_len * desc->batch)
+    return fail(SK_ERR_INVALID_ARG, "total_tokens %lld is inconsistent with max_seq_len and batch",
+                (long long)total_tokens);
+  if (cu_count < 1) return fail(SK_ERR_INVALID_ARG, "cu_count must be >= 1");
+  if (n_splits_requested < 0) return fail(SK_ERR_INVALID_ARG, "n_splits_requested must be >= 0");
+  if (n_splits_requested > kMaxGridYZ)
+    return fail(SK_ERR_INVALID_ARG, "n_splits_requested %d exceeds %d", n_splits_requested,
+                kMaxGridYZ);
+  if (n_splits_requested > 0) {
+    plan->n_splits = n_splits_requested;
+    plan->chunk = (int32_t)ceil_div(max_seq_len, n_splits_requested);
+    return ok();
+  }
+  if (max_seq_len < SK_MIN_SPLIT_CONTEXT) {
+    plan->n_splits = 1;
+    plan->chunk = max_seq_len;
+    return ok();
+  }
+  int64_t chunk;
+  if (desc->kv_shared) {
+    chunk = ceil_div(total_tokens, cu_count);
+  } else {
+    chunk = ceil_div((int64_t)desc->num_kv_heads * total_tokens, (int64_t)kGqaBlocksPerCu * cu_count);
+  }
+  if (chunk < kMinChunk) chunk = kMinChunk;
+  chunk = ceil_div(chunk, kChunkGranule) * kChunkGranule;
+  int64_t n = ceil_div(max_seq_len, chunk);
+  if (n > kMaxGridYZ) {  // unreachable for 32-bit lengths and chunk >= 64; kept as a guard
+    n = kMaxGridYZ;
+    chunk = ceil_div(max_seq_len, n);
+  }
+  plan->n_splits = (int32_t)n;
+  plan->chunk = (int32_t)chunk;
+  return ok();
+}
+
+size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan) {
+  if (check_desc(desc) != SK_OK) return 0;
+  if (check_plan(desc, plan) != SK_OK) return 0;
+  return sk::ws_layout(*desc, *plan).total;
+}
+
+static sk_status_t prepare_split(const sk_desc_t* desc, const sk_plan_t* plan, const void* q,
+                                 const void* k, const void* v, const int32_t* block_table,
+                                 const int32_t* seq_lens, void* workspace, size_t workspace_bytes,
+                                 bool need_pointers, sk::SplitLaunch* out) {
+  sk_status_t s = check_desc(desc);
+  if (s != SK_OK) return s;
+  if ((s = check_plan(desc, plan)) != SK_OK) return s;
+  if (need_pointers) {
+    if (!q || !k || !seq_lens || !workspace)
+      return fail(SK_ERR_INVALID_ARG, "q, k, seq_lens and workspace must be non-NULL");
+    if (desc->kv_shared && v)
+      return fail(SK_ERR_INVALID_ARG, "v must be NULL when keys and values share the latent");
+    if (!desc->kv_shared && !v) return fail(SK_ERR_INVALID_ARG, "v is NULL");
+    if (desc->layout == SK_KV_PAGED && !block_table)
+      return fail(SK_ERR_INVALID_ARG, "paged layout needs block_table");
+    if (desc->layout == SK_KV_CONTIGUOUS && block_table)
+      return fail(SK_ERR_INVALID_ARG, "contiguous layout takes no block_table");
+    if ((uintptr_t)workspace % 256) return fail(SK_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    if ((uintptr_t)k % 16 || (v && (uintptr_t)v % 16))
+      return fail(SK_ERR_INVALID_ARG, "K and V must be 16-byte aligned");
+    const size_t need = sk::ws_layout(*desc, *plan).total;
+    if (workspace_bytes < need)
+      return fail(SK_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                  need);
+  }
+  if ((s = check_support(desc)) != SK_OK) return s;
+  const sk::WsLayout w = sk::ws_layout(*desc, *plan);
+  char* ws = static_cast<char*>(workspace);
+  out->d = desc;
+  out->p = plan;
+  out->q = q;
+  out->k = k;
+  out->v = v;
+  out->block_table = block_table;
+  out->seq_lens = seq_lens;
+  out->ws_acc = reinterpret_cast<float*>(ws + w.acc_off);
+  out->ws_m = reinterpret_cast<float*>(ws + w.m_off);
+  out->ws_l = reinterpret_cast<float*>(ws + w.l_off);
+  out->stream = nullptr;
+  return SK_OK;
+}
+
+sk_status_t attn_decode_splitk(const sk_desc_t* desc, const sk_plan_t* plan, const void* q,
+                               const void* k, const void* v, const int32_t* block_table,
+                               const int32_t* seq_lens, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  sk::SplitLaunch a;
+  sk_status_t s = prepare_split(desc, plan, q, k, v, block_table, seq_lens, workspace,
+                                workspace_bytes, true, &a);
+  if (s != SK_OK) return s;
+  a.stream = stream;
+  int grid[3], block;
+  s = desc->kv_shared ? sk::latent_split_launch(a, true, nullptr, grid, &block)
+                      : sk::gqa_split_launch(a, true, nullptr, grid, &block);
+  if (s != SK_OK) return fail(s, "no split kernel for this descriptor");
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(SK_ERR_LAUNCH, "split kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sk_status_t attn_decode_combine(const sk_desc_t* desc, const sk_plan_t* plan,
+                                const int32_t* seq_lens, const void* workspace,
+                                size_t workspace_bytes, float* out, float* lse,
+                                hipStream_t stream) {
+  sk_status_t s = check_desc(desc);
+  if (s != SK_OK) return s;
+  if ((s = check_plan(desc, plan)) != SK_OK) return s;
+  if (!seq_lens || !workspace || !out)
+    return fail(SK_ERR_INVALID_ARG, "seq_lens, workspace and out must be non-NULL");
+  if ((uintptr_t)workspace % 256) return fail(SK_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if ((uintptr_t)out % 16) return fail(SK_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  const sk::WsLayout w = sk::ws_layout(*desc, *plan);
+  if (workspace_bytes < w.total)
+    return fail(SK_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                w.total);
+  const char* ws = static_cast<const char*>(workspace);
+  sk::CombineLaunch c;
+  c.d = desc;
+  c.p = plan;
+  c.seq_lens = seq_lens;
+  c.ws_acc = reinterpret_cast<const float*>(ws + w.acc_off);
+  c.ws_m = reinterpret_cast<const float*>(ws + w.m_off);
+  c.ws_l = reinterpret_cast<const float*>(ws + w.l_off);
+  c.out = out;
+  c.lse = lse;
+  c.stream = stream;
+  s = sk::combine_launch(c);
+  if (s != SK_OK) return fail(s, "combine launch rejected");
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(SK_ERR_LAUNCH, "combine kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* attn_decode_status_string(sk_status_t status) {
+  switch (status) {
+    case SK_OK: return "ok";
+    case SK_ERR_INVALID_ARG: return "invalid argument";
+    case SK_ERR_UNSUPPORTED: return "unsupported combination";
+    case SK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case SK_ERR_LAUNCH: return "kernel launch failed";
+    case SK_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* attn_decode_last_error(void) { return g_last_error.c_str(); }
+
+sk_status_t attn_decode_kernel_info(const sk_desc_t* desc, const sk_plan_t* plan,
+                                    sk_kernel_info_t* info) {
+  if (!info) return fail(SK_ERR_INVALID_ARG, "info is NULL");
+  sk::SplitLaunch a;
+  sk_status_t s = prepare_split(desc, plan, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                0, false, &a);
+  if (s != SK_OK) return s;
+  const void* fn = nullptr;
+  int grid[3], block;
+  s = desc->kv_shared ? sk::latent_split_launch(a, false, &fn, grid, &block)
+                      : sk::gqa_split_launch(a, false, &fn, grid, &block);
+  if (s != SK_OK) return fail(s, "no split kernel for this descriptor");
+  hipFuncAttributes attr;
+  hipError_t e = hipFuncGetAttributes(&attr, fn);
+  if (e != hipSuccess) return fail(SK_ERR_HIP, "hipFuncGetAttributes: %s", hipGetErrorString(e));
+  info->lds_bytes = (int32_t)attr.sharedSizeBytes;
+  info->vgprs = attr.numRegs;
+  info->block = block;
+  info->grid_x = grid[0];
+  info->grid_y = grid[1];
+  info->grid_z = grid[2];
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Device-side helpers shared by the split and combine kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sk {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Storage types. bf16 is carried as its 16-bit pattern: the upper half of an
+// IEEE binary32 word, so widening is a shift.
+// ---------------------------------------------------------------------------
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+  return __uint_as_float(((uint32_t)x.bits) << 16);
+}
+
+// Reads element i of a q vector whose type is known only at run time (q is
+// read once per workgroup, so the switch costs nothing measurable).
+__device__ __forceinline__ float load_q(const void* q, int dtype, int64_t i) {
+  if (dtype == 0) return reinterpret_cast<const float*>(q)[i];
+  if (dtype == 1) return (float)reinterpret_cast<const _Float16*>(q)[i];
+  return __uint_as_float(((uint32_t)reinterpret_cast<const uint16_t*>(q)[i]) << 16);
+}
+
+// A vector of N storage elements loaded with one instruction (4, 8 or 16 bytes).
+template <typename T, int N>
+struct alignas(sizeof(T) * N) Vec {
+  T v[N];
+};
+
+template <typename T, int N>
+__device__ __forceinline__ Vec<T, N> load_vec(const T* p) {
+  return *reinterpret_cast<const Vec<T, N>*>(p);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions. A row of 16 lanes is the unit DPP works in on gfx9:
+// row_ror:8, row_ror:4 and two quad permutations give every lane the sum of
+// its 16-lane row in four VALU operations.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<kDppRowRor8>(x);
+  x += dpp<kDppRowRor4>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppQuadXor1>(x);
+  return x;
+}
+
+// Exchange with lane ^ 16 (within each 32-lane half): ds_swizzle in bit mode,
+// and_mask 0x1F, xor_mask 0x10. Uses the LDS crossbar, no LDS memory.
+__device__ __forceinline__ float xor16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+// Exchange with lane ^ 32 through ds_bpermute (byte address of the source lane).
+__device__ __forceinline__ float xor32(float x) {
+  const int src = ((int)(threadIdx.x & 63) ^ 32) << 2;
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(x)));
+}
+
+// Sum over the RL consecutive lanes that hold one KV row (RL in {16, 32, 64});
+// every lane of the group receives the total.
+template <int RL>
+__device__ __forceinline__ float row_sum(float x) {
+  x = row16_sum(x);
+  if constexpr (RL >= 32) x += xor16(x);
+  if constexpr (RL >= 64) x += xor32(x);
+  return x;
+}
+
+// Combine values across the row groups of a wave (lanes l, l+RL, l+2RL, ...).
+template <int RL>
+__device__ __forceinline__ float groups_max(float x) {
+  if constexpr (RL <= 16) x = fmaxf(x, xor16(x));
+  if constexpr (RL <= 32) x = fmaxf(x, xor32(x));
+  return x;
+}
+template <int RL>
+__device__ __forceinline__ float groups_sum(float x) {
+  if constexpr (RL <= 16) x += xor16(x);
+  if constexpr (RL <= 32) x += xor32(x);
+  return x;
+}
+
+// exp2 on the hardware transcendental unit through HIP's own math library.
+__device__ __forceinline__ float fast_exp2(float x) { return exp2f(x); }
+
+}  // namespace sk

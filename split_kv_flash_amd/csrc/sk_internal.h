@@ -1,0 +1,57 @@
+// Host-side interface between the C ABI (api.cpp) and the kernel launchers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "splitkv.h"
+
+namespace sk {
+
+// Workspace section offsets (bytes), each a multiple of 256.
+struct WsLayout {
+  size_t acc_off, m_off, l_off, total;
+};
+WsLayout ws_layout(const sk_desc_t& d, const sk_plan_t& p);
+
+// Everything a launcher needs; validated by the caller.
+struct SplitLaunch {
+  const sk_desc_t* d;
+  const sk_plan_t* p;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* ws_acc;
+  float* ws_m;
+  float* ws_l;
+  hipStream_t stream;
+};
+
+struct CombineLaunch {
+  const sk_desc_t* d;
+  const sk_plan_t* p;
+  const int32_t* seq_lens;
+  const float* ws_acc;
+  const float* ws_m;
+  const float* ws_l;
+  float* out;
+  float* lse;
+  hipStream_t stream;
+};
+
+// Host-only capability checks (no HIP calls).
+bool gqa_supported(const sk_desc_t& d);
+bool latent_supported(const sk_desc_t& d);
+
+// Launchers: return the kernel function pointer they use through `fn` when
+// non-null (for attribute queries) and launch only when `launch` is true.
+// Grid dimensions are written to grid[3].
+sk_status_t gqa_split_launch(const SplitLaunch& a, bool launch, const void** fn, int grid[3],
+                             int* block);
+sk_status_t latent_split_launch(const SplitLaunch& a, bool launch, const void** fn, int grid[3],
+                                int* block);
+sk_status_t combine_launch(const CombineLaunch& a);
+
+}  // namespace sk

@@ -1,0 +1,223 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, plans splits exactly as the oracle's reading of the pages,
+sizes the workspace as documented, and rejects bad arguments before any HIP
+call."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from split_kv_flash_amd import binding as B
+
+
+def lib():
+    try:
+        return B.lib()
+    except RuntimeError as e:  # the library is built by __graft_entry__.build()
+        pytest.fail(str(e))
+
+
+def gqa_desc(Hq=16, Hkv=4, D=256, cap=4096, kv="f32", q="f32", batch=1, layout="contiguous",
+             page=16, max_pages=None, num_pages=1000):
+    d = B.SkDesc()
+    d.batch, d.num_q_heads, d.num_kv_heads = batch, Hq, Hkv
+    d.head_dim_qk = d.head_dim_v = D
+    d.kv_shared = 0
+    d.scale = 1.0 / D ** 0.5
+    d.q_dtype, d.kv_dtype = B.DTYPES[q], B.DTYPES[kv]
+    if layout == "contiguous":
+        d.layout = B.SK_KV_CONTIGUOUS
+        d.max_seq_len = cap
+        d.stride_head = D
+        d.stride_pos = Hkv * D
+        d.stride_seq = cap * Hkv * D
+    else:
+        d.layout = B.SK_KV_PAGED
+        d.page_size = page
+        d.max_pages_per_seq = max_pages or -(-cap // page)
+        d.num_pages = num_pages
+        d.max_seq_len = cap
+    return d
+
+
+def latent_desc(cap=8192, kv="f32", Hq=96):
+    d = B.SkDesc()
+    d.batch, d.num_q_heads, d.num_kv_heads = 1, Hq, 1
+    d.head_dim_qk, d.head_dim_v, d.kv_shared = 576, 512, 1
+    d.scale = 1 / 24
+    d.q_dtype, d.kv_dtype = B.SK_F32, B.DTYPES[kv]
+    d.layout = B.SK_KV_CONTIGUOUS
+    d.max_seq_len = cap
+    d.stride_head, d.stride_pos, d.stride_seq = 576, 576, cap * 576
+    return d
+
+
+def test_library_loads_and_exports_every_header_function():
+    L = lib()
+    names = B.header_functions()
+    assert {"attn_decode_splitk", "attn_decode_combine", "attn_decode_plan",
+            "attn_decode_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"libsplitkv.so does not export {n}"
+
+
+def test_status_strings():
+    lib()
+    for s in range(6):
+        assert B.attn_decode_status_string(s)
+    assert B.attn_decode_status_string(0) == "ok"
+
+
+@pytest.mark.parametrize("hkv", [1, 4, 8])
+def test_plan_matches_oracle_reading(hkv):
+    lib()
+    rng = np.random.default_rng(hkv)
+    for _ in range(300):
+        batch = int(rng.integers(1, 40))
+        lens = rng.integers(1, 300000, size=batch)
+        cu = int(rng.choice([80, 132, 256, 304]))
+        req = int(rng.choice([0, 0, 0, 1, 3, 8, 64, 512]))
+        d = gqa_desc(Hq=4 * hkv, Hkv=hkv, D=128, cap=int(lens.max()), batch=batch)
+        p = B.attn_decode_plan(d, int(lens.max()), int(lens.sum()), cu, req)
+        assert (p.n_splits, p.chunk) == oracle.plan_splits(lens, hkv, cu, req)
+
+
+def test_plan_latent_matches_oracle_reading():
+    lib()
+    for L in (1, 64, 65, 8192, 131072, 262144):
+        for cu in (132, 256):
+            p = B.attn_decode_plan(latent_desc(cap=L), L, L, cu, 0)
+            assert (p.n_splits, p.chunk) == oracle.plan_splits([L], 1, cu, kv_shared=True)
+
+
+def test_plan_for_the_nine_b_like_layer_at_262144():
+    lib()
+    p = B.attn_decode_plan(gqa_desc(cap=262144), 262144, 262144, 256, 0)
+    assert (p.n_splits, p.chunk) == (256, 1024)  # 4 KV heads x 256 splits = 1024 workgroups
+
+
+def test_workspace_bytes_follow_the_documented_layout():
+    lib()
+    for (bsz, hq, s, dv) in [(1, 16, 256, 256), (32, 32, 9, 128), (1, 4, 3, 64), (1, 96, 256, 512)]:
+        if dv == 512:
+            d = latent_desc()
+        else:
+            d = gqa_desc(Hq=hq, Hkv=hq // 4 if hq >= 4 else 1, D=dv, batch=bsz)
+        p = B.SkPlan(s, 64)
+        rows = bsz * hq * s
+        a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+        want = a256(rows * dv * 4) + a256(rows * 4) + a256(rows * 4)
+        assert B.attn_decode_workspace_bytes(d, p) == want
+
+
+def _split(d, p, q=4096, k=4096, v=4096, bt=None, lens=4096, ws=4096, wsb=1 << 40):
+    L = lib()
+    s = L.attn_decode_splitk(ctypes.byref(d), ctypes.byref(p), q, k, v, bt, lens, ws, wsb, None)
+    return s, B.attn_decode_last_error()
+
+
+def _combine(d, p, lens=4096, ws=4096, wsb=1 << 40, out=4096, lse=None):
+    L = lib()
+    s = L.attn_decode_combine(ctypes.byref(d), ctypes.byref(p), lens, ws, wsb, out, lse, None)
+    return s, B.attn_decode_last_error()
+
+
+def test_argument_errors_are_reported_before_any_launch():
+    """Every case below is rejected by host validation (fake device addresses
+    are never dereferenced), with its own status and a detail message."""
+    lib()
+    good = gqa_desc()
+    plan = B.SkPlan(8, 512)
+    cases = []
+
+    d = gqa_desc(Hq=10, Hkv=4)
+    cases.append(("heads not a multiple", _split(d, plan), B.SK_ERR_INVALID_ARG))
+    d = gqa_desc(D=96)
+    cases.append(("unsupported head dim", _split(d, plan), B.SK_ERR_UNSUPPORTED))
+    d = gqa_desc(Hq=12, Hkv=4)
+    cases.append(("unsupported group size 3", _split(d, plan), B.SK_ERR_UNSUPPORTED))
+    cases.append(("zero splits", _split(good, B.SkPlan(0, 512)), B.SK_ERR_INVALID_ARG))
+    cases.append(("zero chunk", _split(good, B.SkPlan(8, 0)), B.SK_ERR_INVALID_ARG))
+    cases.append(("NULL seq_lens", _split(good, plan, lens=None), B.SK_ERR_INVALID_ARG))
+    cases.append(("NULL q", _split(good, plan, q=None), B.SK_ERR_INVALID_ARG))
+    cases.append(("NULL v for separate K/V", _split(good, plan, v=None), B.SK_ERR_INVALID_ARG))
+    cases.append(("NULL workspace", _split(good, plan, ws=None), B.SK_ERR_INVALID_ARG))
+    cases.append(("misaligned workspace", _split(good, plan, ws=4096 + 16), B.SK_ERR_INVALID_ARG))
+    cases.append(("misaligned K", _split(good, plan, k=4096 + 4), B.SK_ERR_INVALID_ARG))
+    cases.append(("workspace too small", _split(good, plan, wsb=1024), B.SK_ERR_WORKSPACE_TOO_SMALL))
+    cases.append(("table for contiguous", _split(good, plan, bt=4096), B.SK_ERR_INVALID_ARG))
+    d = gqa_desc(layout="paged", D=128, Hq=32, Hkv=8, cap=32768)
+    cases.append(("paged without table", _split(d, plan), B.SK_ERR_INVALID_ARG))
+    d = gqa_desc(layout="paged", D=128, Hq=32, Hkv=8, cap=32768, page=12)
+    cases.append(("page size not a power of two", _split(d, plan, bt=4096), B.SK_ERR_INVALID_ARG))
+    d = gqa_desc(layout="paged", D=128, Hq=32, Hkv=8, cap=32768, max_pages=4)
+    cases.append(("capacity beyond the table", _split(d, plan, bt=4096), B.SK_ERR_INVALID_ARG))
+    d = gqa_desc()
+    d.kv_dtype = 7
+    cases.append(("unknown dtype", _split(d, plan), B.SK_ERR_INVALID_ARG))
+    d = gqa_desc()
+    d.layout = 5
+    cases.append(("unknown layout", _split(d, plan), B.SK_ERR_INVALID_ARG))
+    d = gqa_desc()
+    d.scale = float("inf")
+    cases.append(("infinite scale", _split(d, plan), B.SK_ERR_INVALID_ARG))
+    d = gqa_desc()
+    d.batch = 0
+    cases.append(("zero batch", _split(d, plan), B.SK_ERR_INVALID_ARG))
+    d = gqa_desc()
+    d.stride_pos = 6
+    cases.append(("stride not a 16-byte multiple", _split(d, plan), B.SK_ERR_UNSUPPORTED))
+    d = latent_desc()
+    cases.append(("v given with a shared latent", _split(d, plan, v=4096), B.SK_ERR_INVALID_ARG))
+    d = latent_desc()
+    d.num_kv_heads = 2
+    d.num_q_heads = 96
+    cases.append(("shared latent with 2 KV heads", _split(d, plan, v=None), B.SK_ERR_INVALID_ARG))
+    d = latent_desc(Hq=100)
+    cases.append(("latent head count", _split(d, plan, v=None), B.SK_ERR_UNSUPPORTED))
+    cases.append(("combine: NULL out", _combine(good, plan, out=None), B.SK_ERR_INVALID_ARG))
+    cases.append(("combine: small workspace", _combine(good, plan, wsb=64), B.SK_ERR_WORKSPACE_TOO_SMALL))
+    cases.append(("combine: misaligned out", _combine(good, plan, out=4096 + 4), B.SK_ERR_INVALID_ARG))
+    cases.append(("combine: zero splits", _combine(good, B.SkPlan(0, 1)), B.SK_ERR_INVALID_ARG))
+    for name, (got, msg), want in cases:
+        assert got == want, f"{name}: status {got}, expected {want} ({msg})"
+        assert msg, f"{name}: no detail message"
+
+def test_plan_argument_errors():
+    lib()
+    d = gqa_desc(cap=4096)
+    with pytest.raises(B.SplitKVError) as e:
+        B.attn_decode_plan(d, 5000, 5000, 256, 0)  # longer than the capacity
+    assert e.value.status == B.SK_ERR_INVALID_ARG
+    with pytest.raises(B.SplitKVError):
+        B.attn_decode_plan(d, 0, 0, 256, 0)
+    with pytest.raises(B.SplitKVError):
+        B.attn_decode_plan(d, 100, 50, 256, 0)  # total below the maximum
+    with pytest.raises(B.SplitKVError):
+        B.attn_decode_plan(d, 100, 100, 0, 0)   # no compute units
+    with pytest.raises(B.SplitKVError):
+        B.attn_decode_plan(d, 100, 100, 256, -1)
+    assert lib().attn_decode_workspace_bytes(None, None) == 0
+
+
+def test_synthetic_case_descriptor_fields_round_trip():
+    """The torch-side descriptor builder reads shapes and strides as documented."""
+    torch = pytest.importorskip("torch")
+    from split_kv_flash_amd import make_desc
+    from synthetic.torch_io import to_device
+
+    case = synthetic.gqa_case("t", seq_lens=[37, 20], num_q_heads=8, num_kv_heads=2, head_dim=64,
+                              kv_dtype="f16", capacity=40, seed=1)
+    t = to_device(case, "cpu")
+    d = make_desc(t["q"], t["k"], t["v"], scale=case.scale)
+    assert (d.batch, d.num_q_heads, d.num_kv_heads, d.head_dim_qk, d.kv_dtype) == (2, 8, 2, 64, B.SK_F16)
+    assert (d.stride_seq, d.stride_pos, d.stride_head, d.max_seq_len) == (40 * 2 * 64, 128, 64, 40)
+    case = synthetic.gqa_case("p", seq_lens=[37, 20], num_q_heads=8, num_kv_heads=2, head_dim=64,
+                              kv_dtype="bf16", q_dtype="bf16", layout="paged", page_size=16, seed=1)
+    t = to_device(case, "cpu")
+    assert t["k"].dtype == torch.bfloat16
+    d = make_desc(t["q"], t["k"], t["v"], scale=case.scale, block_table=t["block_table"], page_size=16)
+    assert (d.layout, d.page_size, d.max_pages_per_seq, d.num_pages) == (B.SK_KV_PAGED, 16, 3, 5)
