@@ -26,6 +26,8 @@ sys.path.insert(0, HERE)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
 MALL_FLUSH_BYTES = 512 << 20  # twice the 256 MB Infinity Cache
+# Dense MFMA peaks of MI355X by the input type the latent kernel feeds them.
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "f16": 2500.0}
 
 
 def log(msg):
@@ -132,10 +134,44 @@ def measure(case, steps, warmup, n_splits=0, flush=None):
         "tokens_per_s_per_layer": round(case.batch * 1e6 / us, 1),
         "mall_flushed": flush is not None,
     }
+    if case.kv_shared:
+        # Dense contractions on MFMA: scores (Hq x Dk) and output (Hq x Dv) per position.
+        flops = 2.0 * case.num_q_heads * (case.head_dim_qk + case.head_dim_v) * int(case.seq_lens.sum())
+        peak = MFMA_PEAK_TFLOPS[case.kv_dtype]
+        tf = flops / (statistics.mean(split) * 1e-3) / 1e12
+        res.update({"split_TFLOPs": round(tf, 2), "mfma_peak_TFLOPs": peak,
+                    "mfma_frac": round(tf / peak, 4), "flops_split": flops})
     del call, t
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res, split, wall
+
+
+def bandwidth_control(nbytes=1 << 30, reps=20):
+    """Achievable-bandwidth controls on the same GPU in the same run: torch's
+    read-only sum over a 1 GiB f32 tensor and a 1 GiB device-to-device copy."""
+    import torch
+
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    out = {}
+    for name, fn, traffic in (("read_sum", lambda: x.sum(), nbytes),
+                              ("copy", lambda: y.copy_(x), 2 * nbytes)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        out[name + "_GBps"] = round(traffic / (median(ts) * 1e-3) / 1e9, 1)
+    del x, y
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(case, heads, reps=3):
@@ -219,6 +255,9 @@ def main():
         "algorithmic_bytes_per_launch": head_a["bytes_split"],
     }
 
+    control = bandwidth_control()
+    log(f"bandwidth control {control}")
+
     rungs = []
     if not args.no_rungs:
         flush = torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device="cuda")
@@ -228,6 +267,9 @@ def main():
                 specs.append(lambda kv=kv, L=L: synthetic.qwen9b_like(L, kv, seed=2000 + L))
         specs.append(lambda: synthetic.wide_group_peaky(262144))
         specs.append(lambda: synthetic.ragged_paged())
+        for kv in ("f32", "f16"):
+            for L in (8192, 131072):
+                specs.append(lambda kv=kv, L=L: synthetic.latent_decode(L, kv, seed=3000 + L))
         for mk in specs:
             c = mk()
             small = c.kv_bytes() < 2 * MALL_FLUSH_BYTES
@@ -270,6 +312,7 @@ def main():
         "combine_us": head_a["combine_us"],
         "tokens_per_s_per_layer": head_a["tokens_per_s_per_layer"],
         "aa_noise_floor": round(aa_spread, 4),
+        "bandwidth_control": control,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "rungs": rungs,

@@ -164,7 +164,8 @@ size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan)
  * Supported: GQA with head_dim_qk == head_dim_v in {64, 128, 256}, group size
  * num_q_heads/num_kv_heads in {1, 2, 4, 6, 8}, any q/KV dtype, both layouts; latent
  * (kv_shared) with num_kv_heads == 1, head_dim_qk == 576, head_dim_v == 512, num_q_heads
- * a multiple of 32 up to 128, KV f32 or f16, contiguous. Anything else returns
+ * in {32, 64, 96, 128}, q f32, KV f32 or f16, contiguous. Latent f16 caches run on f16
+ * MFMA: q and the softmax weights are rounded to f16 there (f32 accumulation). Anything else returns
  * SK_ERR_UNSUPPORTED without launching. */
 sk_status_t attn_decode_splitk(const sk_desc_t* desc, const sk_plan_t* plan,
                                const void* q, const void* k, const void* v,

@@ -110,7 +110,7 @@ sk_status_t check_support(const sk_desc_t* d) {
   if (d->kv_shared) {
     if (!sk::latent_supported(*d))
       return fail(SK_ERR_UNSUPPORTED,
-                  "shared latent supports Hkv 1, Dk 576, Dv 512, Hq a multiple of 32 up to 128, "
+                  "shared latent supports Hkv 1, Dk 576, Dv 512, Hq 32/64/96/128, q f32, "
                   "KV f32/f16, contiguous");
   } else if (!sk::gqa_supported(*d)) {
     return fail(SK_ERR_UNSUPPORTED,

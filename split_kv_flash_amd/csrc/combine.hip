@@ -52,8 +52,13 @@ __device__ __forceinline__ float block_reduce(float x, float* scratch, bool is_m
   return r;
 }
 
+// Splits handled per pass: each of the 16 lane-groups owns every 16th split of
+// the pass and issues all its loads before using any of them.
+constexpr int kPass = kCombThreads;
+constexpr int kPerThread = kPass / 16;
+
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
-  __shared__ float s_w[kCombThreads];
+  __shared__ float s_w[kPass];
   __shared__ float4 s_part[kCombThreads / 16][16];
   __shared__ float s_red[kCombThreads / 64];
 
@@ -66,44 +71,62 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
   const float* __restrict__ mrow = a.ws_m + row0;
   const float* __restrict__ lrow = a.ws_l + row0;
 
-  float mx = -INFINITY;
-  for (int i = tid; i < n; i += kCombThreads) mx = fmaxf(mx, mrow[i]);
+  const int c4 = tid & 15;  // which float4 of the 64 columns
+  const int rg = tid >> 4;  // which residue of the split index
+  const int col = cb * kCombCols + c4 * 4;
+  const bool col_ok = col < a.Dv;
+  const float* accp = a.ws_acc + row0 * a.Dv + col;
+
+  // First pass: the partial accumulators, and m and l of the pass's splits,
+  // all requested before anything waits on them.
+  float4 x[kPerThread];
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int i = rg + 16 * k;
+    x[k] = (i < n && col_ok) ? *reinterpret_cast<const float4*>(accp + (int64_t)i * a.Dv)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float mi = tid < n ? mrow[tid] : -INFINITY;
+  float li = tid < n ? lrow[tid] : 0.0f;
+
+  float mx = mi;
+  for (int i = tid + kPass; i < n; i += kPass) mx = fmaxf(mx, mrow[i]);  // only when n > kPass
   mx = block_reduce(mx, s_red, true);
   const float mu = (mx == -INFINITY) ? 0.0f : mx;
 
-  const int c4 = tid & 15;   // which float4 of the 64 columns
-  const int rg = tid >> 4;   // which residue of the split index
-  const int col = cb * kCombCols + c4 * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float lsum = 0.0f;
-  for (int i0 = 0; i0 < n; i0 += kCombThreads) {
-    const int i = i0 + tid;
-    float w = 0.0f;
-    if (i < n) {
-      w = fast_exp2((mrow[i] - mu) * kLog2e);
-      lsum = fmaf(w, lrow[i], lsum);
+  for (int i0 = 0; i0 < n; i0 += kPass) {
+    if (i0 > 0) {
+      const int i = i0 + tid;
+      mi = i < n ? mrow[i] : -INFINITY;
+      li = i < n ? lrow[i] : 0.0f;
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k) {
+        const int j = i0 + rg + 16 * k;
+        x[k] = (j < n && col_ok) ? *reinterpret_cast<const float4*>(accp + (int64_t)j * a.Dv)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
+    const float w = i0 + tid < n ? fast_exp2((mi - mu) * kLog2e) : 0.0f;
+    lsum = fmaf(w, li, lsum);
     __syncthreads();
     s_w[tid] = w;
     __syncthreads();
-    const int cnt = min(kCombThreads, n - i0);
-    if (col < a.Dv) {
-      const float* base = a.ws_acc + (row0 + i0) * a.Dv + col;
-      for (int k = rg; k < cnt; k += 16) {
-        const float4 x = *reinterpret_cast<const float4*>(base + (int64_t)k * a.Dv);
-        const float wk = s_w[k];
-        acc.x = fmaf(wk, x.x, acc.x);
-        acc.y = fmaf(wk, x.y, acc.y);
-        acc.z = fmaf(wk, x.z, acc.z);
-        acc.w = fmaf(wk, x.w, acc.w);
-      }
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      const float wk = s_w[rg + 16 * k];
+      acc.x = fmaf(wk, x[k].x, acc.x);
+      acc.y = fmaf(wk, x[k].y, acc.y);
+      acc.z = fmaf(wk, x[k].z, acc.z);
+      acc.w = fmaf(wk, x[k].w, acc.w);
     }
   }
   const float lstar = block_reduce(lsum, s_red, false);
 
   s_part[rg][c4] = acc;
   __syncthreads();
-  if (tid < 16 && col < a.Dv) {
+  if (tid < 16 && col_ok) {
     float4 t = s_part[0][tid];
     for (int r = 1; r < kCombThreads / 16; ++r) {
       const float4 u = s_part[r][tid];

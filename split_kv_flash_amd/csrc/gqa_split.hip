@@ -63,6 +63,20 @@ struct GqaShape {
   static_assert(kDpl % kVec == 0, "lane slice must be whole vector loads");
 };
 
+// Loads this lane's slice of the G query vectors of one group, scaled into
+// base-2 units. q's storage type is uniform, so the branch is taken once.
+template <int G, int D, int RL, int VEC, int NL, typename QT>
+__device__ __forceinline__ void load_q_slice(float (&qr)[G][D / RL], const QT* q, int li,
+                                             float qscale) {
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+        qr[h][j * VEC + e] = to_f32(q[h * D + j * RL * VEC + li * VEC + e]) * qscale;
+}
+
 template <typename KV, int G, int D, bool PAGED, int RL, int R>
 __global__ __launch_bounds__(256) void gqa_split_kernel(GqaArgs a) {
   using Sh = GqaShape<KV, D, RL, R>;
@@ -71,6 +85,8 @@ __global__ __launch_bounds__(256) void gqa_split_kernel(GqaArgs a) {
   constexpr int NL = Sh::kLoads;
   constexpr int NG = Sh::kGroups;
   constexpr int NW = Sh::kWaves;
+  constexpr int TR = NG * R;  // positions per tile
+  using V = Vec<KV, VEC>;
 
   __shared__ float s_acc[NW][G][D];
   __shared__ float s_m[NW][G];
@@ -107,15 +123,15 @@ __global__ __launch_bounds__(256) void gqa_split_kernel(GqaArgs a) {
 
   // This lane's slice of the G query vectors, pre-scaled into base-2 units.
   float qr[G][DPL];
-  const int64_t qbase = ((int64_t)b * a.Hq + h0) * D;
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int j = 0; j < NL; ++j)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e)
-        qr[h][j * VEC + e] =
-            load_q(a.q, a.q_dtype, qbase + h * D + j * RL * VEC + li * VEC + e) * a.qscale;
+  {
+    const int64_t qbase = ((int64_t)b * a.Hq + h0) * D;
+    if (a.q_dtype == 0)
+      load_q_slice<G, D, RL, VEC, NL>(qr, reinterpret_cast<const float*>(a.q) + qbase, li, a.qscale);
+    else if (a.q_dtype == 1)
+      load_q_slice<G, D, RL, VEC, NL>(qr, reinterpret_cast<const _Float16*>(a.q) + qbase, li, a.qscale);
+    else
+      load_q_slice<G, D, RL, VEC, NL>(qr, reinterpret_cast<const bf16_t*>(a.q) + qbase, li, a.qscale);
+  }
 
   float m[G], l[G], acc[G][DPL];
 #pragma unroll
@@ -126,53 +142,81 @@ __global__ __launch_bounds__(256) void gqa_split_kernel(GqaArgs a) {
     for (int d = 0; d < DPL; ++d) acc[h][d] = 0.0f;
   }
 
-  const KV* __restrict__ kp = reinterpret_cast<const KV*>(a.k);
-  const KV* __restrict__ vp = reinterpret_cast<const KV*>(a.v);
-  const int64_t seq_base = (int64_t)b * a.stride_seq + (int64_t)g * a.stride_head;
+  // Row addressing. Contiguous: element offset pos*stride_pos from this
+  // (sequence, head) base. Paged: (page*page_size + slot)*Hkv*D from this
+  // head's column in the pool; page indices come from the block table.
   const int lane_col = li * VEC;
+  const int64_t head_off =
+      PAGED ? (int64_t)g * D : (int64_t)b * a.stride_seq + (int64_t)g * a.stride_head;
+  const KV* __restrict__ kb = reinterpret_cast<const KV*>(a.k) + head_off + lane_col;
+  const KV* __restrict__ vb = reinterpret_cast<const KV*>(a.v) + head_off + lane_col;
+  const int64_t row_stride = PAGED ? (int64_t)Hkv * D : a.stride_pos;
+  const int ps_mask = (1 << a.page_shift) - 1;
+  const int32_t* __restrict__ table = a.block_table + (int64_t)b * a.max_pages;
 
-  for (int64_t base = start; base < end; base += NG * R) {
-    Vec<KV, VEC> kr[R][NL], vr[R][NL];
-    bool ok[R];
-    bool bad[R];
+  // Rows past `end` read row end-1 instead (in bounds, and a cache hit, since
+  // the same workgroup reads it): their scores are masked to -inf.
+  auto table_page = [&](int64_t pos) -> int {
+    return table[pos >> a.page_shift];
+  };
+  int64_t last_off;
+  if constexpr (PAGED) {
+    int pg = table_page(end - 1);
+    pg = (pg < 0 || (int64_t)pg >= a.num_pages) ? 0 : pg;
+    last_off = (((int64_t)pg << a.page_shift) + ((end - 1) & ps_mask)) * row_stride;
+  } else {
+    last_off = (end - 1) * row_stride;
+  }
+
+  // Page indices for the R rows of a tile (paged layout only). Rows past the
+  // end look up row end-1's page, so the table is never read out of range.
+  auto load_pages = [&](int (&pg)[R], int64_t tb) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      int64_t pos = base + r * NG + grp;
-      ok[r] = pos < end;
-      pos = ok[r] ? pos : end - 1;
+      const int64_t pos = tb + r * NG + grp;
+      pg[r] = table_page(pos < end ? pos : end - 1);
+    }
+  };
+
+  auto issue = [&](V (&kt)[R][NL], V (&vt)[R][NL], int64_t tb, const int (&pg)[R]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t pos = tb + r * NG + grp;
       int64_t off;
       if constexpr (PAGED) {
-        int page = a.block_table[(int64_t)b * a.max_pages + (pos >> a.page_shift)];
-        bad[r] = page < 0 || (int64_t)page >= a.num_pages;
-        page = bad[r] ? 0 : page;
-        const int64_t slot = pos & ((1 << a.page_shift) - 1);
-        off = ((((int64_t)page << a.page_shift) + slot) * Hkv + g) * D;
+        const int p = (pg[r] < 0 || (int64_t)pg[r] >= a.num_pages) ? 0 : pg[r];
+        off = (((int64_t)p << a.page_shift) + (pos & ps_mask)) * row_stride;
       } else {
-        bad[r] = false;
-        off = seq_base + pos * a.stride_pos;
+        off = pos * row_stride;
       }
+      off = pos < end ? off : last_off;
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
-        kr[r][j] = load_vec<KV, VEC>(kp + off + j * RL * VEC + lane_col);
-        vr[r][j] = load_vec<KV, VEC>(vp + off + j * RL * VEC + lane_col);
+        kt[r][j] = load_vec<KV, VEC>(kb + off + j * RL * VEC);
+        vt[r][j] = load_vec<KV, VEC>(vb + off + j * RL * VEC);
       }
     }
+  };
 
+  auto compute = [&](const V (&kt)[R][NL], const V (&vt)[R][NL], int64_t tb, const int (&pg)[R]) {
     float s[G][R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
+      const int64_t pos = tb + r * NG + grp;
+      const bool ok = pos < end;
+      bool bad = false;
+      if constexpr (PAGED) bad = pg[r] < 0 || (int64_t)pg[r] >= a.num_pages;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float p = 0.0f;
 #pragma unroll
         for (int j = 0; j < NL; ++j)
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) p = fmaf(qr[h][j * VEC + e], to_f32(kr[r][j].v[e]), p);
+          for (int e = 0; e < VEC; ++e) p = fmaf(qr[h][j * VEC + e], to_f32(kt[r][j].v[e]), p);
         p = row_sum<RL>(p);
-        s[h][r] = ok[r] ? (bad[r] ? __builtin_nanf("") : p) : -INFINITY;
+        s[h][r] = ok ? (bad ? __builtin_nanf("") : p) : -INFINITY;
       }
     }
-
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float mt = s[h][0];
@@ -195,11 +239,49 @@ __global__ __launch_bounds__(256) void gqa_split_kernel(GqaArgs a) {
         for (int e = 0; e < VEC; ++e) {
           float t = acc[h][j * VEC + e] * al;
 #pragma unroll
-          for (int r = 0; r < R; ++r) t = fmaf(p[r], to_f32(vr[r][j].v[e]), t);
+          for (int r = 0; r < R; ++r) t = fmaf(p[r], to_f32(vt[r][j].v[e]), t);
           acc[h][j * VEC + e] = t;
         }
       m[h] = mn;
     }
+  };
+
+  // Software pipeline: the loads of tile t+1 are issued before tile t's
+  // arithmetic, so every wave keeps a tile of K/V in flight while it computes.
+  // With paging, page indices run one tile further ahead (pc: this tile,
+  // pn: next, pnn: the one after), so a table read never waits behind K/V
+  // loads. Tiles past the end re-read row end-1 (a cache hit).
+  V kA[R][NL], vA[R][NL], kB[R][NL], vB[R][NL];
+  int pc[R], pn[R], pnn[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) pc[r] = pn[r] = pnn[r] = 0;
+  if constexpr (PAGED) {
+    load_pages(pc, start);
+    load_pages(pn, start + TR);
+  }
+  issue(kA, vA, start, pc);
+  auto rotate = [&]() {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      pc[r] = pn[r];
+      pn[r] = pnn[r];
+    }
+  };
+  for (int64_t tb = start;;) {
+    if constexpr (PAGED) load_pages(pnn, tb + 2 * TR);
+    issue(kB, vB, tb + TR, pn);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kA, vA, tb, pc);
+    tb += TR;
+    if (tb >= end) break;
+    if constexpr (PAGED) rotate();
+    if constexpr (PAGED) load_pages(pnn, tb + 2 * TR);
+    issue(kA, vA, tb + TR, pn);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kB, vB, tb, pc);
+    tb += TR;
+    if (tb >= end) break;
+    if constexpr (PAGED) rotate();
   }
 
   // Merge the row groups of each wave, then the waves through LDS.
@@ -249,47 +331,23 @@ __global__ __launch_bounds__(256) void gqa_split_kernel(GqaArgs a) {
   }
 }
 
-// Lane-per-row width and rows per group per tile for each (storage, width).
-// These are the tuning knobs; the values are the ones measured best on MI355X.
-#ifndef SK_GQA_RL256
-#define SK_GQA_RL256 32
-#endif
-#ifndef SK_GQA_R256
-#define SK_GQA_R256 4
-#endif
-#ifndef SK_GQA_RL128
-#define SK_GQA_RL128 16
-#endif
-#ifndef SK_GQA_R128
-#define SK_GQA_R128 2
-#endif
-#ifndef SK_GQA_RL64
-#define SK_GQA_RL64 16
-#endif
-#ifndef SK_GQA_R64
-#define SK_GQA_R64 2
-#endif
-
-template <int D>
-struct Tune;
-template <>
-struct Tune<256> {
-  static constexpr int RL = SK_GQA_RL256, R = SK_GQA_R256;
-};
-template <>
-struct Tune<128> {
-  static constexpr int RL = SK_GQA_RL128, R = SK_GQA_R128;
-};
-template <>
-struct Tune<64> {
-  static constexpr int RL = SK_GQA_RL64, R = SK_GQA_R64;
+// Lanes per KV row (RL) and rows per row group per tile (R) for each storage
+// type, group size and width: the values measured best on MI355X (a sweep of
+// RL in {16, 32} and R in {2, 4, 8} at 131,072 and 262,144 positions). Wider
+// groups carry more query and accumulator registers per lane, so they take the
+// 32-lane rows that halve those.
+template <typename KV, int G, int D>
+struct Tune {
+  static constexpr bool kWideGroup = G > 4;
+  static constexpr int RL = (D == 256 && kWideGroup) ? 32 : 16;
+  static constexpr int R = D == 128 ? 4 : ((D == 256 && kWideGroup && sizeof(KV) == 2) ? 4 : 2);
 };
 
 template <typename KV, int G, int D, bool PAGED>
 static sk_status_t launch_variant(const SplitLaunch& s, bool launch, const void** fn, int grid[3],
                                   int* block) {
   const sk_desc_t& d = *s.d;
-  auto kern = gqa_split_kernel<KV, G, D, PAGED, Tune<D>::RL, Tune<D>::R>;
+  auto kern = gqa_split_kernel<KV, G, D, PAGED, Tune<KV, G, D>::RL, Tune<KV, G, D>::R>;
   const dim3 gr(d.num_kv_heads, s.p->n_splits, d.batch);
   grid[0] = gr.x;
   grid[1] = gr.y;

@@ -47,9 +47,11 @@ __device__ __forceinline__ Vec<T, N> load_vec(const T* p) {
 // row_ror:8, row_ror:4 and two quad permutations give every lane the sum of
 // its 16-lane row in four VALU operations.
 // ---------------------------------------------------------------------------
+// bound_ctrl set: every source lane these patterns name exists, and the flag
+// lets the compiler fold the move into the consuming add (v_add_f32_dpp).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 constexpr int kDppRowRor8 = 0x128;
 constexpr int kDppRowRor4 = 0x124;
@@ -99,7 +101,9 @@ __device__ __forceinline__ float groups_sum(float x) {
   return x;
 }
 
-// exp2 on the hardware transcendental unit through HIP's own math library.
-__device__ __forceinline__ float fast_exp2(float x) { return exp2f(x); }
+// exp2 as the single hardware instruction v_exp_f32 (compiler builtin). Results
+// below the normal range may flush to zero; every use here is exp2 of a
+// non-positive difference, where such terms are below 2^-126 of the largest.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace sk

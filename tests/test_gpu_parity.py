@@ -297,3 +297,67 @@ def test_invalid_lengths_give_nan_for_that_sequence_only():
     case.seq_lens = np.array([50, 40, 30], dtype=np.int32)
     ref, _ = oracle_out(case)
     assert np.abs(out[0] - ref[0]).max() <= 1e-4
+
+
+# ------------------------------------------------------------ shared latent
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16"])
+@pytest.mark.parametrize("L", [64, 8192, 131072])
+def test_latent_matches_oracle(kv, L):
+    """96 heads on one 576-column latent, values = first 512 columns, launched
+    as the bench launches it (heuristic plan)."""
+    case = synthetic.latent_decode(L, kv, seed=3000 + L)
+    out, lse, call = run_gpu(case)
+    ref, rlse = oracle_out(case)
+    assert_parity(case, out, ref, tight=(kv == "f32"), label=f"latent {kv} L={L} plan={call.plan}")
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=ABS_GATE[kv])
+    del call
+    free()
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16"])
+@pytest.mark.parametrize("L,S", [(1, 1), (1, 8), (33, 2), (1000, 3), (1000, 7)])
+def test_latent_explicit_splits_and_padding(kv, L, S):
+    case = synthetic.latent_case(f"lat-{kv}-{L}", seq_len=L, kv_dtype=kv, capacity=L + 5,
+                                 seed=L * 10 + S, scale=1 / 24)
+    out, _, call = run_gpu(case, n_splits=S)
+    ref, _ = oracle_out(case)
+    assert_parity(case, out, ref, tight=(kv == "f32"), label=f"latent {kv} L={L} S={S}")
+    if L == 1:
+        v0 = case.k[0, 0, 0, :512].astype(np.float32)
+        for h in range(case.num_q_heads):
+            assert np.array_equal(out[0, h].astype(np.float32), v0)
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16"])
+def test_latent_dominant_key_in_the_second_tile(kv):
+    """Position 32 is the first row of the second f16 tile (third f32 tile)."""
+    L = 40
+    case = synthetic.latent_case("lat-dom", seq_len=L, kv_dtype="f32", seed=9, scale=1 / 24)
+    q = case.q[0, 0].astype(np.float64)
+    case.q[0, :] = case.q[0, 0]
+    row = (q / np.linalg.norm(q) * 24 * 30 / np.linalg.norm(q))  # score ~ 30
+    case.k[0, 32, 0] = row.astype(np.float32)
+    if kv == "f16":
+        case.k = case.k.astype(np.float16)
+        case.kv_dtype = "f16"
+    ref, _ = oracle_out(case)
+    out, _, _ = run_gpu(case, n_splits=1)
+    assert_parity(case, out, ref, tight=False, label=f"latent dominant {kv}")
+    for h in (0, 50, 95):
+        np.testing.assert_allclose(out[0, h], ref[0, h], rtol=0, atol=ABS_GATE[kv])
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16"])
+def test_latent_split_partials_match_the_oracle_schedule(kv):
+    case = synthetic.latent_decode(1000, kv, seed=31)
+    _, _, call = run_gpu(case, n_splits=4)
+    acc, m, l = (x.double().cpu().numpy() for x in call.partials())
+    rm, rl, racc = oracle.split_partials_f64(
+        case.q, case.k_rows(), None, case.seq_lens, case.scale, call.plan.chunk,
+        call.plan.n_splits, q_dtype=case.q_dtype, kv_dtype=case.kv_dtype, v_cols=512)
+    tol = 2e-5 if kv == "f32" else 2e-3
+    np.testing.assert_allclose(m, rm, rtol=0, atol=tol)
+    np.testing.assert_allclose(l, rl, rtol=tol, atol=0)
+    assert np.abs(acc / l[..., None] - racc / rl[..., None]).max() <= tol
