@@ -339,6 +339,319 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// f16 caches: two waves per 16-head block, softmax in registers, cache tiles
+// staged by direct global-to-LDS loads.
+//
+// Workgroup of 2*NHB waves (768 threads for 96 heads). Wave w = 2*hb + dh owns
+// head block hb (16 heads).
+//  * Staging: tiles of 32 cache rows go straight from HBM into LDS with
+//    global_load_lds_dwordx4 (each lane's 16 bytes land at M0 + 16*lane), three
+//    tiles deep, so no registers hold staged data and the next two tiles are
+//    in flight during the current one. Rows are stored unpadded with the
+//    16-byte chunk index XOR-ed by (row & 7): a lane chooses which global chunk
+//    to fetch so that its fixed LDS slot holds the swizzled layout.
+//  * Scores: the wave computes partial scores of its 16 heads x 32 positions
+//    over latent columns [288*dh, 288*dh + 288) with v_mfma_f32_16x16x32_f16,
+//    its query rows held in registers; the two waves of a block add each
+//    other's partials through LDS (2 KB per wave per tile), so both hold the
+//    block's full scores and run the online softmax over all 32 positions in
+//    registers (row max per head: a 16-lane DPP reduction).
+//  * Output: the same wave owns value columns [256*dh, 256*dh + 256) of its 16
+//    heads, so its rescale factors are already in registers. P goes through
+//    LDS; V operands come straight from the cache tile through the gfx950
+//    transpose read ds_read_b64_tr_b16 (within a 16-lane group, lane i's item
+//    t is element i%4 of the 8-byte chunk addressed by lane 4t + i/4).
+//  * Synchronisation: two barriers per tile. Each wave waits for its own
+//    global-to-LDS loads with an explicit vmcnt before the barrier that
+//    publishes them (a workgroup fence would wait for every load in flight).
+// ---------------------------------------------------------------------------
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef __attribute__((address_space(3))) _Float16 lds_half_t;
+
+// One global_load_lds_dwordx4: each lane's 16 bytes at `g` land in LDS at
+// lds_addr + 16*lane (lds_addr must be wave-uniform; it goes through M0).
+// Issued as inline assembly so the compiler's wait-count tracking does not
+// treat every later LDS read as possibly aliasing it (it would then wait for
+// all loads in flight); the kernel waits for these loads explicitly. M0 is not
+// otherwise used by these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr_of(const _Float16* p) {
+  return (uint32_t)(size_t)(const lds_half_t*)(p);
+}
+
+__device__ __forceinline__ float4_t mfma32(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half4_t lds_read_tr(const _Float16* p) {
+  // p points into LDS; the C-style cast is the generic-to-LDS address-space cast.
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p));
+  return __builtin_bit_cast(half4_t, v);
+}
+
+// s_waitcnt with vmcnt = VM (no wait on exp), lgkmcnt = 0: this wave's LDS
+// writes are done and at most VM of its vector-memory operations remain.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+}
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int kT16 = 32;     // positions per tile
+constexpr int kCpr16 = kLatDk / 8;   // 72 chunks of 16 bytes per cache row
+constexpr int kProw16 = 40;  // LDS row stride of P (halves; rows stay 16-byte aligned)
+
+// LDS offset (halves) of logical chunk cc of tile row r.
+__device__ __forceinline__ int tile_off(int r, int cc) { return r * kLatDk + ((cc ^ (r & 7)) << 3); }
+
+template <int NHB>
+__global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
+  constexpr int H = NHB * 16;
+  constexpr int NW = 2 * NHB;
+  constexpr int NT = NW * 64;
+  constexpr int KH = kLatDk / 2;                  // 288 latent columns per wave
+  constexpr int KS = KH / 32;                     // 9 MFMA steps
+  constexpr int SLOTS = kT16 * kCpr16;            // 2304 chunks per tile
+  constexpr int DPW = SLOTS / NT;                 // global-to-LDS loads per wave per tile
+  static_assert(SLOTS % NT == 0, "every wave issues the same number of tile loads");
+  constexpr int NCB = 16;                         // 16-column blocks per half (256 columns)
+  constexpr int TILE = kT16 * kLatDk;             // halves per tile buffer
+
+  __shared__ __align__(16) _Float16 s_c[3 * TILE];
+  __shared__ __align__(16) float4_t s_sx[NW][2][64];
+  __shared__ __align__(16) _Float16 s_p[H * kProw16];
+
+  const int split = blockIdx.x;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hb = wave >> 1;
+  const int dh = wave & 1;
+  const int l16 = lane & 15;
+  const int lq = lane >> 4;
+
+  const int L = min(a.seq_lens[b], a.cap);
+  const int64_t start = (int64_t)split * a.chunk;
+  const int64_t end = min((int64_t)L, start + a.chunk);
+  const int64_t ws0 = (int64_t)b * a.Hq * a.S + split;
+
+  if (start >= end) {
+    for (int idx = tid; idx < H * kLatDv; idx += NT) {
+      const int h = idx / kLatDv, e = idx - (idx / kLatDv) * kLatDv;
+      a.ws_acc[(ws0 + (int64_t)h * a.S) * kLatDv + e] = 0.0f;
+    }
+    for (int h = tid; h < H; h += NT) {
+      a.ws_m[ws0 + (int64_t)h * a.S] = -INFINITY;
+      a.ws_l[ws0 + (int64_t)h * a.S] = 0.0f;
+    }
+    return;
+  }
+
+  const _Float16* __restrict__ cbase = reinterpret_cast<const _Float16*>(a.c) + (int64_t)b * a.stride_seq;
+  const float* __restrict__ qb = a.q + (int64_t)b * a.Hq * kLatDk;
+
+  // Tile staging: this wave's DPW slots per tile; slot s holds tile row s/72,
+  // logical chunk (s%72) ^ (row & 7). Rows past the end re-read row end-1.
+  int srow[DPW], scol[DPW];
+#pragma unroll
+  for (int c = 0; c < DPW; ++c) {
+    const int sl = (wave * DPW + c) * 64 + lane;
+    srow[c] = sl / kCpr16;
+    scol[c] = ((sl - srow[c] * kCpr16) ^ (srow[c] & 7)) * 8;
+  }
+  const uint32_t lds0 = lds_addr_of(s_c);
+  auto issue_tile = [&](int bi, int64_t tb) {
+#pragma unroll
+    for (int c = 0; c < DPW; ++c) {
+      int64_t pos = tb + srow[c];
+      pos = pos < end ? pos : end - 1;
+      const uint32_t dst = lds0 + (uint32_t)((bi * TILE + (wave * DPW + c) * 64 * 8) * 2);
+      dma16(cbase + pos * a.stride_pos + scol[c], __builtin_amdgcn_readfirstlane(dst));
+    }
+  };
+
+  // Query rows of this head block as MFMA A operands: lane holds head
+  // hb*16 + l16, columns 288*dh + 32*ks + 8*lq .. +7 (rounded to f16 once).
+  half8_t qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      qf[ks][e] = (_Float16)qb[(hb * 16 + l16) * kLatDk + dh * KH + ks * 32 + lq * 8 + e];
+
+  // Running state of heads hb*16 + 4*lq + e (replicated over the 16 lanes of
+  // a row group): max m (base 2) and normaliser l; output accumulators for
+  // columns 256*dh + 16*cb + l16.
+  float m[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    m[e] = -INFINITY;
+    l[e] = 0.0f;
+  }
+  float4_t acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  issue_tile(0, start);
+  issue_tile(1, start + kT16);
+  wait_vm_lgkm0<DPW>();
+  raw_barrier();
+
+  // Per-lane LDS offsets (halves) inside a tile buffer. The XOR swizzle only
+  // touches the low 3 bits of a chunk index, so every operand address is one
+  // of a few per-lane bases plus a compile-time offset:
+  //  * scores, rows l16 (+16 for the second block), chunk c0 + 4*ks:
+  //    base for even ks + 32*ks/2... i.e. bs[ks & 1] + 64*(ks >> 1) halves;
+  //  * transpose reads, rows r0 and r0 + 4, chunk 32*dh + 2*cb + (l16&3)/2:
+  //    bv[row][cb & 3] + 64*(cb >> 2) halves (+4 halves when l16 is odd).
+  const int c0 = dh * 36 + lq;
+  const int sw = l16 & 7;
+  const int bs0 = l16 * kLatDk + ((c0 ^ sw) << 3);
+  const int bs1 = l16 * kLatDk + (((c0 + 4) ^ sw) << 3) - 32;
+  const int r0 = lq * 8 + (l16 >> 2);
+  const int jv = (l16 & 3) >> 1;
+  const int hoff = (l16 & 1) * 4;
+  int bv[2][4];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = r0 + rr * 4;
+      bv[rr][u] = row * kLatDk + ((dh * 32 + ((2 * u + jv) ^ (row & 7))) << 3) + hoff;
+    }
+
+  int cur_i = 0;
+  for (int64_t tb = start; tb < end; tb += kT16) {
+    const _Float16* cur = s_c + cur_i * TILE;
+    const int dma_i = cur_i == 0 ? 2 : cur_i - 1;  // (cur + 2) mod 3
+
+    // ---- partial scores over this wave's 288 columns, both 16-position blocks ----
+    // Operands are read one MFMA step ahead; the scheduling barriers keep the
+    // compiler from hoisting every read (and its registers) to the front.
+    float4_t sp0 = float4_t{0.f, 0.f, 0.f, 0.f}, sp1 = sp0;
+    const _Float16* sb0 = cur + bs0;
+    const _Float16* sb1 = cur + bs1;
+    auto bread = [&](int ks, int row_add) {
+      const _Float16* bp = (ks & 1) ? sb1 : sb0;
+      return *reinterpret_cast<const half8_t*>(bp + row_add * kLatDk + 32 * ks);
+    };
+    half8_t n0 = bread(0, 0), n1 = bread(0, 16);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const half8_t b0 = n0, b1 = n1;
+      if (ks + 1 < KS) {
+        n0 = bread(ks + 1, 0);
+        n1 = bread(ks + 1, 16);
+      }
+      sp0 = mfma32(qf[ks], b0, sp0);
+      sp1 = mfma32(qf[ks], b1, sp1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s_sx[wave][0][lane] = sp0;
+    s_sx[wave][1][lane] = sp1;
+    wait_vm_lgkm0<63>();
+    raw_barrier();
+
+    // ---- full scores (own + partner), online softmax over 32 positions ----
+    // D layout: lane holds heads 4*lq + e at positions l16 and 16 + l16.
+    const float4_t q0 = s_sx[wave ^ 1][0][lane];
+    const float4_t q1 = s_sx[wave ^ 1][1][lane];
+    const bool ok0 = tb + l16 < end;
+    const bool ok1 = tb + 16 + l16 < end;
+    float al[4];
+    bool all_one = true;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v0 = ok0 ? (sp0[e] + q0[e]) * a.qscale : -INFINITY;
+      const float v1 = ok1 ? (sp1[e] + q1[e]) * a.qscale : -INFINITY;
+      float x = fmaxf(v0, v1);
+      x = fmaxf(x, dpp<kDppRowRor8>(x));
+      x = fmaxf(x, dpp<kDppRowRor4>(x));
+      x = fmaxf(x, dpp<kDppQuadXor2>(x));
+      x = fmaxf(x, dpp<kDppQuadXor1>(x));
+      const float mn = fmaxf(m[e], x);
+      const float mu = (mn == -INFINITY) ? 0.0f : mn;
+      al[e] = fast_exp2(m[e] - mu);
+      all_one = all_one && al[e] == 1.0f;
+      const _Float16 p0 = (_Float16)fast_exp2(v0 - mu);
+      const _Float16 p1 = (_Float16)fast_exp2(v1 - mu);
+      l[e] = fmaf(l[e], al[e], row16_sum((float)p0 + (float)p1));
+      m[e] = mn;
+      // Each wave of the pair stores one of the two position blocks.
+      s_p[(hb * 16 + lq * 4 + e) * kProw16 + dh * 16 + l16] = dh ? p1 : p0;
+    }
+    issue_tile(dma_i, tb + 2 * kT16);
+    // The next tile was issued a step ago; only this step's DPW loads may
+    // still be in flight.
+    wait_vm_lgkm0<DPW>();
+    raw_barrier();
+
+    // ---- output: acc = al * acc + P[16 heads][32 positions] x V ----
+    if (!__all(all_one)) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[cb][e] *= al[e];
+    }
+    const half8_t pa = *reinterpret_cast<const half8_t*>(&s_p[(hb * 16 + l16) * kProw16 + lq * 8]);
+    auto vread = [&](int cb) {
+      const half4_t v0 = lds_read_tr(cur + bv[0][cb & 3] + 64 * (cb >> 2));
+      const half4_t v1 = lds_read_tr(cur + bv[1][cb & 3] + 64 * (cb >> 2));
+      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    half8_t vn = vread(0);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const half8_t vb = vn;
+      if (cb + 1 < NCB) vn = vread(cb + 1);
+      acc[cb] = mfma32(pa, vb, acc[cb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    cur_i = cur_i == 2 ? 0 : cur_i + 1;
+  }
+  // Drain the tile loads still in flight before the workgroup can retire.
+  wait_vm_lgkm0<0>();
+
+  // Partials: both waves of a block hold the same m and l.
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int head = hb * 16 + lq * 4 + e;
+      const int col = dh * 256 + cb * 16 + l16;
+      a.ws_acc[(ws0 + (int64_t)head * a.S) * kLatDv + col] = acc[cb][e];
+    }
+  if (dh == 0 && l16 < 4) {
+    float mm = m[0], ll = l[0];
+#pragma unroll
+    for (int e = 1; e < 4; ++e)
+      if (l16 == e) {
+        mm = m[e];
+        ll = l[e];
+      }
+    const int head = hb * 16 + lq * 4 + l16;
+    a.ws_m[ws0 + (int64_t)head * a.S] = mm * kLn2;
+    a.ws_l[ws0 + (int64_t)head * a.S] = ll;
+  }
+}
+
 bool latent_supported(const sk_desc_t& d) {
   return d.kv_shared == 1 && d.num_kv_heads == 1 && d.head_dim_qk == kLatDk &&
          d.head_dim_v == kLatDv && d.layout == SK_KV_CONTIGUOUS && d.q_dtype == SK_F32 &&
@@ -351,12 +664,21 @@ template <typename CT, int NHB>
 static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void** fn, int grid[3],
                                   int* block) {
   const sk_desc_t& d = *s.d;
-  auto kern = mla_split_kernel<CT, NHB>;
+  // f16 caches with 32 or 96 heads take the two-waves-per-head-block kernel
+  // (its tile loads divide evenly over 4 or 12 waves and its registers fit 3
+  // waves per SIMD); the other head counts take the split-K kernel.
+  constexpr bool kFull16 = sizeof(CT) == 2 && (NHB == 2 || NHB == 6);
+  void (*kern)(MlaArgs);
+  if constexpr (kFull16)
+    kern = mla16_split_kernel<NHB>;
+  else
+    kern = mla_split_kernel<CT, NHB>;
+  const int threads = kFull16 ? NHB * 128 : kMlaThreads;
   const dim3 gr(s.p->n_splits, d.batch, 1);
   grid[0] = gr.x;
   grid[1] = gr.y;
   grid[2] = gr.z;
-  *block = kMlaThreads;
+  *block = threads;
   if (fn) *fn = reinterpret_cast<const void*>(kern);
   if (!launch) return SK_OK;
   MlaArgs a;
@@ -373,7 +695,7 @@ static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void*
   a.chunk = s.p->chunk;
   a.cap = d.max_seq_len;
   a.qscale = d.scale * kLog2e;
-  hipLaunchKernelGGL(kern, gr, dim3(kMlaThreads), 0, s.stream, a);
+  hipLaunchKernelGGL(kern, gr, dim3(threads), 0, s.stream, a);
   return SK_OK;
 }
 
