@@ -77,7 +77,8 @@ typedef enum {
    *   base + b*stride_seq + j*stride_pos + g*stride_head + d      (elements),
    * d contiguous. The usual token-major cache [batch][capacity][Hkv][D] has
    * stride_seq = capacity*Hkv*D, stride_pos = Hkv*D, stride_head = D
-   * (issue #3725 design note section 1 reads this layout).                    */
+   * (issue #3725 design note section 1 reads this layout). Strides are
+   * multiples of 16 bytes and stride_pos spans at most 16 MiB.                 */
   SK_KV_CONTIGUOUS = 0,
   /* K and V are pools [num_pages][page_size][Hkv][D]; position j of sequence b
    * lives in page block_table[b*max_pages_per_seq + j/page_size], slot

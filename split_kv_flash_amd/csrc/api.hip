@@ -41,6 +41,9 @@ constexpr int32_t kMinChunk = 64;
 constexpr int32_t kChunkGranule = 64;
 constexpr int32_t kGqaBlocksPerCu = 4;
 constexpr int32_t kMaxGridYZ = 65535;
+// Largest step between consecutive positions of a contiguous cache: a split
+// kernel tile (at most 64 rows) is addressed with 32-bit byte offsets.
+constexpr int64_t kMaxRowStepBytes = int64_t(1) << 24;
 
 // Shape checks shared by every entry point (no pointer checks).
 sk_status_t check_desc(const sk_desc_t* d) {
@@ -81,6 +84,10 @@ sk_status_t check_desc(const sk_desc_t* d) {
     const int64_t vec = d->kv_dtype == SK_F32 ? 4 : 8;  // elements per 16-byte load
     if (d->stride_pos % vec || d->stride_head % vec || d->stride_seq % vec)
       return fail(SK_ERR_UNSUPPORTED, "strides must be multiples of 16 bytes (vector loads)");
+    const int64_t esize = d->kv_dtype == SK_F32 ? 4 : 2;
+    if (d->stride_pos * esize > kMaxRowStepBytes)
+      return fail(SK_ERR_UNSUPPORTED, "stride_pos of %lld bytes exceeds %lld (32-bit tile offsets)",
+                  (long long)(d->stride_pos * esize), (long long)kMaxRowStepBytes);
   } else if (d->layout == SK_KV_PAGED) {
     if (d->kv_shared) return fail(SK_ERR_UNSUPPORTED, "paged shared latent is not supported");
     if (!is_pow2(d->page_size))

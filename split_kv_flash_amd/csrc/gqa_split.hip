@@ -8,23 +8,31 @@
 //
 // Work decomposition (MI355X-first rather than the pages' 32-lane warps):
 //   * 256 threads = 4 waves of 64 lanes. A KV row is held by RL consecutive lanes
-//     (RL = 16 or 32), so a wave holds 64/RL rows at once and one vector load
-//     instruction reads 64/RL contiguous row segments of RL*16 bytes.
-//   * Each lane keeps its D/RL dimensions of the G query vectors and of the G
-//     accumulators in registers; a dot product is a per-lane partial followed by
-//     a 16-lane DPP reduction (plus one swizzle when RL = 32).
-//   * The workgroup's NG = 4*64/RL row groups take interleaved positions
+//     (RL = 16 or 32), so one vector load instruction reads whole contiguous
+//     row segments of RL*16 bytes.
+//   * Each lane keeps its D/RL dimensions of its query vectors and accumulators
+//     in registers; a dot product is a per-lane partial followed by a 16-lane
+//     DPP reduction (plus one swizzle when RL = 32). With HS head slices, HS
+//     sets of RL lanes read the same row and each serves G/HS of the heads,
+//     which divides the per-lane reductions and exponentials by HS.
+//   * The workgroup's NG = 256/(RL*HS) row groups take interleaved positions
 //     base + r*NG + group, R rows per group per tile, and each group carries its
 //     own online-softmax state (m, l, acc) per head; tile-level rescaling follows
 //     the recurrence of "Decoder Block 6" and Lecture 07 ("But Softmax Wants the
 //     Whole Row..."): m' = max(m, tile max), a = exp(m - m'), l = a l + sum p,
-//     acc = a acc + sum p v.
+//     acc = a acc + sum p v. The multiply by a is skipped when no head's
+//     maximum moved anywhere in the wave (a is then exactly 1).
+//   * Contiguous caches are read with raw buffer loads: one resource per tile
+//     bounds the reads to the split, so the tail of the last tile and the
+//     pipeline's look-ahead past the end read nothing from memory.
 //   * Scores are kept in base-2 units (q is pre-multiplied by scale*log2 e) so
 //     every exponential is one exp2; the stored m is converted back to natural
 //     units.
 //   * At the end the row groups merge by cross-lane exchange, the waves merge
 //     through LDS (4*G*D floats, independent of the context length), and the
 //     workgroup writes one partial per query head.
+#include <type_traits>
+
 #include "sk_device.h"
 #include "sk_internal.h"
 
@@ -47,13 +55,15 @@ struct GqaArgs {
   float qscale;
 };
 
-template <typename KV, int D, int RL_, int R_>
+template <typename KV, int D, int RL_, int R_, int HS_>
 struct GqaShape {
   static constexpr int RL = RL_;
   static constexpr int R = R_;
+  static constexpr int HS = HS_;  // head slices: lane sets that share a row, each with G/HS heads
   static constexpr int kWaves = 4;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kGroupsPerWave = 64 / RL;
+  static constexpr int kGroupLanes = RL * HS;
+  static constexpr int kGroupsPerWave = 64 / kGroupLanes;
   static constexpr int kGroups = kGroupsPerWave * kWaves;
   static constexpr int kDpl = D / RL;
   static constexpr int kVecMax = 16 / (int)sizeof(KV);
@@ -77,9 +87,12 @@ __device__ __forceinline__ void load_q_slice(float (&qr)[G][D / RL], const QT* q
         qr[h][j * VEC + e] = to_f32(q[h * D + j * RL * VEC + li * VEC + e]) * qscale;
 }
 
-template <typename KV, int G, int D, bool PAGED, int RL, int R>
-__global__ __launch_bounds__(256) void gqa_split_kernel(GqaArgs a) {
-  using Sh = GqaShape<KV, D, RL, R>;
+template <typename KV, int G, int D, bool PAGED, int RL, int R, int HS, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void gqa_split_kernel(
+    GqaArgs a) {
+  using Sh = GqaShape<KV, D, RL, R, HS>;
+  static_assert(G % HS == 0, "head slices must split the group evenly");
+  constexpr int GH = G / HS;  // query heads per lane
   constexpr int DPL = Sh::kDpl;
   constexpr int VEC = Sh::kVec;
   constexpr int NL = Sh::kLoads;
@@ -100,7 +113,8 @@ __global__ __launch_bounds__(256) void gqa_split_kernel(GqaArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int li = lane & (RL - 1);
-  const int grp = wave * Sh::kGroupsPerWave + lane / RL;
+  const int hs = (lane / RL) % HS;
+  const int grp = wave * Sh::kGroupsPerWave + lane / Sh::kGroupLanes;
   const int h0 = g * G;
 
   const int L = min(a.seq_lens[b], a.cap);
@@ -121,51 +135,57 @@ __global__ __launch_bounds__(256) void gqa_split_kernel(GqaArgs a) {
     return;
   }
 
-  // This lane's slice of the G query vectors, pre-scaled into base-2 units.
-  float qr[G][DPL];
+  // This lane's slice of its GH query vectors (heads h0 + hs*GH ...),
+  // pre-scaled into base-2 units.
+  float qr[GH][DPL];
   {
-    const int64_t qbase = ((int64_t)b * a.Hq + h0) * D;
+    const int64_t qbase = ((int64_t)b * a.Hq + h0 + hs * GH) * D;
     if (a.q_dtype == 0)
-      load_q_slice<G, D, RL, VEC, NL>(qr, reinterpret_cast<const float*>(a.q) + qbase, li, a.qscale);
+      load_q_slice<GH, D, RL, VEC, NL>(qr, reinterpret_cast<const float*>(a.q) + qbase, li, a.qscale);
     else if (a.q_dtype == 1)
-      load_q_slice<G, D, RL, VEC, NL>(qr, reinterpret_cast<const _Float16*>(a.q) + qbase, li, a.qscale);
+      load_q_slice<GH, D, RL, VEC, NL>(qr, reinterpret_cast<const _Float16*>(a.q) + qbase, li, a.qscale);
     else
-      load_q_slice<G, D, RL, VEC, NL>(qr, reinterpret_cast<const bf16_t*>(a.q) + qbase, li, a.qscale);
+      load_q_slice<GH, D, RL, VEC, NL>(qr, reinterpret_cast<const bf16_t*>(a.q) + qbase, li, a.qscale);
   }
 
-  float m[G], l[G], acc[G][DPL];
+  float m[GH], l[GH], acc[GH][DPL];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int h = 0; h < GH; ++h) {
     m[h] = -INFINITY;
     l[h] = 0.0f;
 #pragma unroll
     for (int d = 0; d < DPL; ++d) acc[h][d] = 0.0f;
   }
 
-  // Row addressing. Contiguous: element offset pos*stride_pos from this
-  // (sequence, head) base. Paged: (page*page_size + slot)*Hkv*D from this
-  // head's column in the pool; page indices come from the block table.
+  // Row addressing. Contiguous: a tile's rows sit at fixed 32-bit byte
+  // offsets from the tile's first row, whose address is uniform across the
+  // workgroup (scalar registers). Paged: (page*page_size + slot)*Hkv*D elements from this head's column
+  // of the pool, page indices from the block table.
   const int lane_col = li * VEC;
   const int64_t head_off =
       PAGED ? (int64_t)g * D : (int64_t)b * a.stride_seq + (int64_t)g * a.stride_head;
   const KV* __restrict__ kb = reinterpret_cast<const KV*>(a.k) + head_off + lane_col;
   const KV* __restrict__ vb = reinterpret_cast<const KV*>(a.v) + head_off + lane_col;
+  const KV* __restrict__ kh = reinterpret_cast<const KV*>(a.k) + head_off;
+  const KV* __restrict__ vh = reinterpret_cast<const KV*>(a.v) + head_off;
   const int64_t row_stride = PAGED ? (int64_t)Hkv * D : a.stride_pos;
   const int ps_mask = (1 << a.page_shift) - 1;
   const int32_t* __restrict__ table = a.block_table + (int64_t)b * a.max_pages;
+  const uint32_t row_bytes = (uint32_t)(row_stride * (int64_t)sizeof(KV));  // host-checked < 2^31 / TR
+  uint32_t loff[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) loff[r] = (uint32_t)(r * NG + grp) * row_bytes + (uint32_t)(lane_col * sizeof(KV));
 
-  // Rows past `end` read row end-1 instead (in bounds, and a cache hit, since
-  // the same workgroup reads it): their scores are masked to -inf.
+  // Paged rows past `end` read row end-1 instead (in bounds, a cache hit):
+  // their scores are masked to -inf.
   auto table_page = [&](int64_t pos) -> int {
     return table[pos >> a.page_shift];
   };
-  int64_t last_off;
+  int64_t last_off = 0;
   if constexpr (PAGED) {
     int pg = table_page(end - 1);
     pg = (pg < 0 || (int64_t)pg >= a.num_pages) ? 0 : pg;
     last_off = (((int64_t)pg << a.page_shift) + ((end - 1) & ps_mask)) * row_stride;
-  } else {
-    last_off = (end - 1) * row_stride;
   }
 
   // Page indices for the R rows of a tile (paged layout only). Rows past the
@@ -179,52 +199,94 @@ __global__ __launch_bounds__(256) void gqa_split_kernel(GqaArgs a) {
   };
 
   auto issue = [&](V (&kt)[R][NL], V (&vt)[R][NL], int64_t tb, const int (&pg)[R]) {
+    if constexpr (PAGED) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t pos = tb + r * NG + grp;
-      int64_t off;
-      if constexpr (PAGED) {
+      for (int r = 0; r < R; ++r) {
+        const int64_t pos = tb + r * NG + grp;
         const int p = (pg[r] < 0 || (int64_t)pg[r] >= a.num_pages) ? 0 : pg[r];
-        off = (((int64_t)p << a.page_shift) + (pos & ps_mask)) * row_stride;
-      } else {
-        off = pos * row_stride;
-      }
-      off = pos < end ? off : last_off;
+        int64_t off = (((int64_t)p << a.page_shift) + (pos & ps_mask)) * row_stride;
+        off = pos < end ? off : last_off;
 #pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        kt[r][j] = load_vec<KV, VEC>(kb + off + j * RL * VEC);
-        vt[r][j] = load_vec<KV, VEC>(vb + off + j * RL * VEC);
+        for (int j = 0; j < NL; ++j) {
+          kt[r][j] = load_vec<KV, VEC>(kb + off + j * RL * VEC);
+          vt[r][j] = load_vec<KV, VEC>(vb + off + j * RL * VEC);
+        }
       }
+    } else {
+      // One buffer resource per tile, based at the tile's first row and
+      // covering the rows before `end`: rows past it (the last tile's tail, or
+      // a whole tile past the end) read as zero without a memory access, and
+      // the lane offsets stay loop-invariant.
+      const int64_t left = end - tb;
+      const uint32_t nbytes = left <= 0 ? 0u : (uint32_t)(left < TR ? left : TR) * row_bytes;
+      const auto rk = raw_rsrc(kh + tb * row_stride, nbytes);
+      const auto rv = raw_rsrc(vh + tb * row_stride, nbytes);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          const uint32_t o = loff[r] + (uint32_t)(j * RL * VEC * sizeof(KV));
+          kt[r][j] = load_vec_buf<KV, VEC>(rk, o);
+          vt[r][j] = load_vec_buf<KV, VEC>(rv, o);
+        }
     }
   };
 
   auto compute = [&](const V (&kt)[R][NL], const V (&vt)[R][NL], int64_t tb, const int (&pg)[R]) {
-    float s[G][R];
+    float s[GH][R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int64_t pos = tb + r * NG + grp;
-      const bool ok = pos < end;
-      bool bad = false;
-      if constexpr (PAGED) bad = pg[r] < 0 || (int64_t)pg[r] >= a.num_pages;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+      for (int h = 0; h < GH; ++h) {
         float p = 0.0f;
 #pragma unroll
         for (int j = 0; j < NL; ++j)
 #pragma unroll
           for (int e = 0; e < VEC; ++e) p = fmaf(qr[h][j * VEC + e], to_f32(kt[r][j].v[e]), p);
-        p = row_sum<RL>(p);
-        s[h][r] = ok ? (bad ? __builtin_nanf("") : p) : -INFINITY;
+        s[h][r] = row_sum<RL>(p);
       }
     }
+    if constexpr (PAGED) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+      for (int r = 0; r < R; ++r) {
+        const bool ok = tb + r * NG + grp < end;
+        const bool bad = pg[r] < 0 || (int64_t)pg[r] >= a.num_pages;
+#pragma unroll
+        for (int h = 0; h < GH; ++h) s[h][r] = ok ? (bad ? __builtin_nanf("") : s[h][r]) : -INFINITY;
+      }
+    } else if (tb + TR > end) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const bool ok = tb + r * NG + grp < end;
+#pragma unroll
+        for (int h = 0; h < GH; ++h) s[h][r] = ok ? s[h][r] : -INFINITY;
+      }
+    }
+    // Running max per head. The accumulators and l are rescaled only when some
+    // head's max moved somewhere in the wave (otherwise the factor is exp2(0) = 1).
+    float mn[GH];
+    bool moved = false;
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
       float mt = s[h][0];
 #pragma unroll
       for (int r = 1; r < R; ++r) mt = fmaxf(mt, s[h][r]);
-      const float mn = fmaxf(m[h], mt);
-      const float mu = (mn == -INFINITY) ? 0.0f : mn;
-      const float al = fast_exp2(m[h] - mu);
+      mn[h] = fmaxf(m[h], mt);
+      moved |= mn[h] != m[h];
+    }
+    if (__any(moved)) {
+#pragma unroll
+      for (int h = 0; h < GH; ++h) {
+        const float al = fast_exp2(m[h] - ((mn[h] == -INFINITY) ? 0.0f : mn[h]));
+        l[h] *= al;
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) acc[h][d] *= al;
+        m[h] = mn[h];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+      const float mu = (m[h] == -INFINITY) ? 0.0f : m[h];
       float p[R];
       float ls = 0.0f;
 #pragma unroll
@@ -232,17 +294,16 @@ __global__ __launch_bounds__(256) void gqa_split_kernel(GqaArgs a) {
         p[r] = fast_exp2(s[h][r] - mu);
         ls += p[r];
       }
-      l[h] = fmaf(l[h], al, ls);
+      l[h] += ls;
 #pragma unroll
       for (int j = 0; j < NL; ++j)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          float t = acc[h][j * VEC + e] * al;
+          float t = acc[h][j * VEC + e];
 #pragma unroll
           for (int r = 0; r < R; ++r) t = fmaf(p[r], to_f32(vt[r][j].v[e]), t);
           acc[h][j * VEC + e] = t;
         }
-      m[h] = mn;
     }
   };
 
@@ -250,7 +311,8 @@ __global__ __launch_bounds__(256) void gqa_split_kernel(GqaArgs a) {
   // arithmetic, so every wave keeps a tile of K/V in flight while it computes.
   // With paging, page indices run one tile further ahead (pc: this tile,
   // pn: next, pnn: the one after), so a table read never waits behind K/V
-  // loads. Tiles past the end re-read row end-1 (a cache hit).
+  // loads. Contiguous: the tile after the last one reads nothing (its
+  // resource is empty); paged: it re-reads row end-1 (a cache hit).
   V kA[R][NL], vA[R][NL], kB[R][NL], vB[R][NL];
   int pc[R], pn[R], pnn[R];
 #pragma unroll
@@ -285,23 +347,25 @@ __global__ __launch_bounds__(256) void gqa_split_kernel(GqaArgs a) {
   }
 
   // Merge the row groups of each wave, then the waves through LDS.
+  constexpr int GL = Sh::kGroupLanes;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float mw = groups_max<RL>(m[h]);
+  for (int h = 0; h < GH; ++h) {
+    const float mw = groups_max<GL>(m[h]);
     const float mwu = (mw == -INFINITY) ? 0.0f : mw;
     const float f = fast_exp2(m[h] - mwu);
-    const float lw = groups_sum<RL>(l[h] * f);
+    const float lw = groups_sum<GL>(l[h] * f);
 #pragma unroll
-    for (int d = 0; d < DPL; ++d) acc[h][d] = groups_sum<RL>(acc[h][d] * f);
-    if (lane == 0) {
-      s_m[wave][h] = mw;
-      s_l[wave][h] = lw;
-    }
-    if (lane < RL) {
+    for (int d = 0; d < DPL; ++d) acc[h][d] = groups_sum<GL>(acc[h][d] * f);
+    if (lane < GL) {
+      const int hh = hs * GH + h;
+      if (li == 0) {
+        s_m[wave][hh] = mw;
+        s_l[wave][hh] = lw;
+      }
 #pragma unroll
       for (int j = 0; j < NL; ++j)
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) s_acc[wave][h][j * RL * VEC + lane_col + e] = acc[h][j * VEC + e];
+        for (int e = 0; e < VEC; ++e) s_acc[wave][hh][j * RL * VEC + lane_col + e] = acc[h][j * VEC + e];
     }
   }
   __syncthreads();
@@ -331,23 +395,32 @@ __global__ __launch_bounds__(256) void gqa_split_kernel(GqaArgs a) {
   }
 }
 
-// Lanes per KV row (RL) and rows per row group per tile (R) for each storage
-// type, group size and width: the values measured best on MI355X (a sweep of
-// RL in {16, 32} and R in {2, 4, 8} at 131,072 and 262,144 positions). Wider
-// groups carry more query and accumulator registers per lane, so they take the
-// 32-lane rows that halve those.
+// Lanes per KV row segment (RL), head slices (HS), rows per row group per
+// tile (R) and the waves per SIMD the registers are held to (WPE), for each
+// storage type, group size and width: the values measured best on MI355X.
+// Wider groups carry more query and accumulator registers per lane; the
+// 6-head f16 group splits its heads over two 16-lane slices of each row,
+// which halves its per-lane reductions and exponentials.
 template <typename KV, int G, int D>
 struct Tune {
   static constexpr bool kWideGroup = G > 4;
-  static constexpr int RL = (D == 256 && kWideGroup) ? 32 : 16;
-  static constexpr int R = D == 128 ? 4 : ((D == 256 && kWideGroup && sizeof(KV) == 2) ? 4 : 2);
+  static constexpr bool kSliced = std::is_same<KV, _Float16>::value && D == 256 && G == 6;
+  static constexpr int RL = kSliced ? 16 : ((D == 256 && kWideGroup) ? 32 : 16);
+  static constexpr int HS = kSliced ? 2 : 1;
+  static constexpr int R =
+      kSliced ? 2 : (D == 128 ? 4 : ((D == 256 && kWideGroup && sizeof(KV) == 2) ? 4 : 2));
+  // Two waves per SIMD where the query, accumulator and two in-flight tiles
+  // fit 256 registers without spilling (checked against the compiler's
+  // resource report), else one.
+  static constexpr int WPE = kSliced ? 2 : ((sizeof(KV) == 2 && D == 128 && G <= 4) ? 2 : 1);
 };
 
 template <typename KV, int G, int D, bool PAGED>
 static sk_status_t launch_variant(const SplitLaunch& s, bool launch, const void** fn, int grid[3],
                                   int* block) {
   const sk_desc_t& d = *s.d;
-  auto kern = gqa_split_kernel<KV, G, D, PAGED, Tune<KV, G, D>::RL, Tune<KV, G, D>::R>;
+  using T = Tune<KV, G, D>;
+  auto kern = gqa_split_kernel<KV, G, D, PAGED, T::RL, T::R, T::HS, T::WPE>;
   const dim3 gr(d.num_kv_heads, s.p->n_splits, d.batch);
   grid[0] = gr.x;
   grid[1] = gr.y;

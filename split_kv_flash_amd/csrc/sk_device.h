@@ -42,6 +42,24 @@ __device__ __forceinline__ Vec<T, N> load_vec(const T* p) {
   return *reinterpret_cast<const Vec<T, N>*>(p);
 }
 
+// Raw buffer loads. A buffer resource carries a base address and a byte count;
+// a load whose offset (lane offset plus immediate) lies at or past the count
+// returns zero and touches no memory, which makes the rows past a split's end
+// free to skip. Word 3 of a gfx9 resource: 32-bit data format, raw (unswizzled,
+// no index stride) addressing.
+constexpr int kRawBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRawBufferWord3);
+}
+template <typename T, int N>
+__device__ __forceinline__ Vec<T, N> load_vec_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  static_assert(sizeof(T) * N == 16 || sizeof(T) * N == 8, "buffer loads of 8 or 16 bytes");
+  if constexpr (sizeof(T) * N == 16)
+    return __builtin_bit_cast(Vec<T, N>, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  else
+    return __builtin_bit_cast(Vec<T, N>, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane reductions. A row of 16 lanes is the unit DPP works in on gfx9:
 // row_ror:8, row_ror:4 and two quad permutations give every lane the sum of
@@ -87,17 +105,18 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
-// Combine values across the row groups of a wave (lanes l, l+RL, l+2RL, ...).
-template <int RL>
+// Combine values across the row groups of a wave, GL lanes apart (lanes l,
+// l+GL, l+2GL, ...).
+template <int GL>
 __device__ __forceinline__ float groups_max(float x) {
-  if constexpr (RL <= 16) x = fmaxf(x, xor16(x));
-  if constexpr (RL <= 32) x = fmaxf(x, xor32(x));
+  if constexpr (GL <= 16) x = fmaxf(x, xor16(x));
+  if constexpr (GL <= 32) x = fmaxf(x, xor32(x));
   return x;
 }
-template <int RL>
+template <int GL>
 __device__ __forceinline__ float groups_sum(float x) {
-  if constexpr (RL <= 16) x += xor16(x);
-  if constexpr (RL <= 32) x += xor32(x);
+  if constexpr (GL <= 16) x += xor16(x);
+  if constexpr (GL <= 32) x += xor32(x);
   return x;
 }
 
