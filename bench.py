@@ -75,9 +75,11 @@ def time_steps(call, steps, warmup, flush=None):
     """Per-launch HIP-event times (ms) of split and combine, and wall ms per step.
 
     Events are recorded on torch's current stream, which is the stream the
-    library launches on. With ``flush`` (a device buffer) a fill that evicts the
-    Infinity Cache runs before every step, outside the event pairs and the wall
-    clock is then not reported (None)."""
+    library launches on. With ``flush`` (a device buffer of MALL_FLUSH_BYTES) a
+    read of the whole buffer evicts the Infinity Cache before every step,
+    outside the event pairs; the wall clock is then not reported (None). The
+    eviction reads rather than writes, so no write-back of dirty lines competes
+    with the timed call."""
     import torch
 
     for _ in range(warmup):
@@ -89,7 +91,7 @@ def time_steps(call, steps, warmup, flush=None):
     t0 = time.perf_counter()
     for e0, e1, e2 in ev:
         if flush is not None:
-            flush.fill_(1)
+            flush.sum()
         e0.record()
         call.splitk()
         e1.record()
@@ -260,7 +262,7 @@ def main():
 
     rungs = []
     if not args.no_rungs:
-        flush = torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        flush = torch.zeros(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
         specs = []
         for kv in ("f32", "f16"):
             for L in (4096, 20480, 61440, 151552, 262144):
@@ -272,7 +274,7 @@ def main():
                 specs.append(lambda kv=kv, L=L: synthetic.latent_decode(L, kv, seed=3000 + L))
         for mk in specs:
             c = mk()
-            small = c.kv_bytes() < 2 * MALL_FLUSH_BYTES
+            small = c.kv_bytes() < MALL_FLUSH_BYTES  # could stay cached between calls
             r, _, _ = measure(c, args.rung_steps, 5, 0, flush if small else None)
             log(f"rung {r}")
             rungs.append(r)

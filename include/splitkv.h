@@ -128,10 +128,14 @@ typedef struct {
  *   n_splits_requested  > 0: honoured exactly, chunk = ceil(max_seq_len / S) (trailing
  *                       splits may be empty); 0: heuristic.
  * Heuristic (issue #3725 design note section 2: chunk = max(64, ceil(L/S_target)) and
- * S = ceil(L/chunk) so that no split is empty, S_target about 4 blocks per
- * multiprocessor; budgeted on the product of KV heads and splits summed over the
- * batch, as Lecture 06 section 5.1 asks):
- *   GQA:    chunk = max(64, ceil(Hkv * total_tokens / (4 * cu_count)))
+ * S = ceil(L/chunk) so that no split is empty; budgeted on the product of KV heads and
+ * splits summed over the batch, as Lecture 06 section 5.1 asks):
+ *   GQA:    chunk = max(64, ceil(Hkv * total_tokens / (k * cu_count))), where k is the
+ *           number of workgroups per compute unit measured best on MI355X: 1 (one
+ *           round of one workgroup per compute unit), 2 for the f16 6-head group
+ *           of width 256, and 4 times that for a ragged batch (total_tokens <
+ *           batch * max_seq_len). The note's own S_target is about 4 per
+ *           multiprocessor of its GPU.
  *   latent: chunk = max(64, ceil(total_tokens / cu_count))  (one workgroup serves all
  *           query heads, and each split costs a partial of every head)
  *   chunk is rounded up to a multiple of 64 and S = ceil(max_seq_len / chunk).

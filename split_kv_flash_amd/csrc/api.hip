@@ -39,7 +39,10 @@ bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 constexpr int32_t kMinChunk = 64;
 constexpr int32_t kChunkGranule = 64;
-constexpr int32_t kGqaBlocksPerCu = 4;
+// Ragged batches (total_tokens < batch * max_seq_len) plan this many times
+// more workgroups: their slices differ in length, and more, shorter blocks
+// balance the compute units.
+constexpr int32_t kRaggedBlockFactor = 4;
 constexpr int32_t kMaxGridYZ = 65535;
 // Largest step between consecutive positions of a contiguous cache: a split
 // kernel tile (at most 64 rows) is addressed with 32-bit byte offsets.
@@ -175,7 +178,9 @@ sk_status_t attn_decode_plan(const sk_desc_t* desc, int32_t max_seq_len, int64_t
   if (desc->kv_shared) {
     chunk = ceil_div(total_tokens, cu_count);
   } else {
-    chunk = ceil_div((int64_t)desc->num_kv_heads * total_tokens, (int64_t)kGqaBlocksPerCu * cu_count);
+    const bool ragged = total_tokens < (int64_t)max_seq_len * desc->batch;
+    const int64_t per_cu = (int64_t)sk::gqa_resident_blocks(*desc) * (ragged ? kRaggedBlockFactor : 1);
+    chunk = ceil_div((int64_t)desc->num_kv_heads * total_tokens, per_cu * cu_count);
   }
   if (chunk < kMinChunk) chunk = kMinChunk;
   chunk = ceil_div(chunk, kChunkGranule) * kChunkGranule;

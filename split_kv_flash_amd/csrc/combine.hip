@@ -2,15 +2,20 @@
 //
 // Lecture 06 section 2 and issue #3725 design note section 2 (kernel B): with
 // M = max_i m_i and w_i = exp(m_i - M), l* = sum_i w_i l_i and
-// out = sum_i w_i acc_i / l*. Only the first ceil(L_b/chunk) splits of a
-// sequence hold positions; they are the only ones read. lse = M + ln l*
-// (the log-sum-exp of the scores, "The Kernel Level: Attention and MoE").
+// out = sum_i w_i acc_i / l*. Only the first n = ceil(L_b/chunk) splits of a
+// sequence hold positions; only their values are used. lse = M + ln l* (the
+// log-sum-exp of the scores, "The Kernel Level: Attention and MoE").
 //
-// Launch: grid (ceil(Dv/64), Hq, B), 256 threads. A workgroup owns 64 output
-// columns of one (b, h): 16 lanes cover the 64 columns with float4 loads and
-// the 16 lane-groups take every 16th split, so each split row of the partials
-// is read once, coalesced, and the Dv/64 column blocks multiply the parallelism
-// of small-head problems.
+// Launch: grid (ceil(Dv/64), Hq, B), one wave of 64 lanes per workgroup. The
+// wave owns 64 output columns of one (b, h). Splits are taken 64 at a time:
+// lane i holds m and l of split i of the pass, and the 16-lane quarters of the
+// wave each read every 4th split's 64 columns as float4 rows, so every partial
+// row is read once, coalesced. Every split block of the grid writes its
+// partial (empty slices write the neutral one), so a pass's rows are all
+// requested at once, together with the sequence length; the rows at or past n
+// are then dropped by selection, never by arithmetic, so their values cannot
+// reach the result. The maximum and the sums are wave reductions; no
+// workgroup barrier is needed.
 #include "sk_device.h"
 #include "sk_internal.h"
 
@@ -27,125 +32,108 @@ struct CombineArgs {
 };
 
 constexpr int kCombCols = 64;
-constexpr int kCombThreads = 256;
+constexpr int kPass = 64;             // splits per pass: one per lane
+constexpr int kRowsPerQuarter = kPass / 4;
 
-__device__ __forceinline__ float block_reduce(float x, float* scratch, bool is_max) {
-  // wave reduction through DPP rows, then across the 16-lane rows, then waves.
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (is_max) {
-    x = fmaxf(x, dpp<kDppRowRor8>(x));
-    x = fmaxf(x, dpp<kDppRowRor4>(x));
-    x = fmaxf(x, dpp<kDppQuadXor2>(x));
-    x = fmaxf(x, dpp<kDppQuadXor1>(x));
-    x = fmaxf(x, xor16(x));
-    x = fmaxf(x, xor32(x));
-  } else {
-    x = row16_sum(x);
-    x += xor16(x);
-    x += xor32(x);
-  }
-  __syncthreads();
-  if (lane == 0) scratch[wave] = x;
-  __syncthreads();
-  float r = scratch[0];
-  for (int w = 1; w < kCombThreads / 64; ++w) r = is_max ? fmaxf(r, scratch[w]) : r + scratch[w];
-  return r;
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kDppRowRor8>(x));
+  x = fmaxf(x, dpp<kDppRowRor4>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, xor16(x));
+  return fmaxf(x, xor32(x));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row16_sum(x);
+  x += xor16(x);
+  return x + xor32(x);
+}
+// Value of x held by lane `src` (0..63).
+__device__ __forceinline__ float from_lane(float x, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
 }
 
-// Splits handled per pass: each of the 16 lane-groups owns every 16th split of
-// the pass and issues all its loads before using any of them.
-constexpr int kPass = kCombThreads;
-constexpr int kPerThread = kPass / 16;
-
-__global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
-  __shared__ float s_w[kPass];
-  __shared__ float4 s_part[kCombThreads / 16][16];
-  __shared__ float s_red[kCombThreads / 64];
-
+__global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
   const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int Lraw = a.seq_lens[b];
-  const bool valid = Lraw >= 1 && Lraw <= a.cap && (int64_t)Lraw <= (int64_t)a.S * a.chunk;
-  const int n = valid ? (int)min((int64_t)a.S, ((int64_t)Lraw + a.chunk - 1) / a.chunk) : 0;
+  const int lane = threadIdx.x;
+  const int c4 = lane & 15;  // which float4 of the 64 columns
+  const int qt = lane >> 4;  // quarter: splits qt, qt+4, qt+8, ... of a pass
+  const int col = cb * kCombCols + c4 * 4;
+  const bool col_ok = col < a.Dv;
   const int64_t row0 = ((int64_t)b * a.Hq + h) * a.S;
   const float* __restrict__ mrow = a.ws_m + row0;
   const float* __restrict__ lrow = a.ws_l + row0;
+  const float* __restrict__ accp = a.ws_acc + row0 * a.Dv + col;
 
-  const int c4 = tid & 15;  // which float4 of the 64 columns
-  const int rg = tid >> 4;  // which residue of the split index
-  const int col = cb * kCombCols + c4 * 4;
-  const bool col_ok = col < a.Dv;
-  const float* accp = a.ws_acc + row0 * a.Dv + col;
-
-  // First pass: the partial accumulators, and m and l of the pass's splits,
-  // all requested before anything waits on them.
-  float4 x[kPerThread];
-#pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    const int i = rg + 16 * k;
-    x[k] = (i < n && col_ok) ? *reinterpret_cast<const float4*>(accp + (int64_t)i * a.Dv)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  float mi = tid < n ? mrow[tid] : -INFINITY;
-  float li = tid < n ? lrow[tid] : 0.0f;
-
-  float mx = mi;
-  for (int i = tid + kPass; i < n; i += kPass) mx = fmaxf(mx, mrow[i]);  // only when n > kPass
-  mx = block_reduce(mx, s_red, true);
-  const float mu = (mx == -INFINITY) ? 0.0f : mx;
-
+  const int Lraw = a.seq_lens[b];
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float lsum = 0.0f;
-  for (int i0 = 0; i0 < n; i0 += kPass) {
-    if (i0 > 0) {
-      const int i = i0 + tid;
-      mi = i < n ? mrow[i] : -INFINITY;
-      li = i < n ? lrow[i] : 0.0f;
+  float mrun = -INFINITY, lrun = 0.0f;
+  int n = 0;
+  bool valid = false;
+  for (int i0 = 0; i0 < a.S; i0 += kPass) {
+    // Requests first: this pass's m, l and accumulator rows.
+    const bool in_s = i0 + lane < a.S;
+    float mi = in_s ? mrow[i0 + lane] : -INFINITY;
+    float li = in_s ? lrow[i0 + lane] : 0.0f;
+    float4 x[kRowsPerQuarter];
 #pragma unroll
-      for (int k = 0; k < kPerThread; ++k) {
-        const int j = i0 + rg + 16 * k;
-        x[k] = (j < n && col_ok) ? *reinterpret_cast<const float4*>(accp + (int64_t)j * a.Dv)
+    for (int k = 0; k < kRowsPerQuarter; ++k) {
+      const int i = i0 + qt + 4 * k;
+      x[k] = (i < a.S && col_ok) ? *reinterpret_cast<const float4*>(accp + (int64_t)i * a.Dv)
                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (i0 == 0) {
+      valid = Lraw >= 1 && Lraw <= a.cap && (int64_t)Lraw <= (int64_t)a.S * a.chunk;
+      n = valid ? (int)min((int64_t)a.S, ((int64_t)Lraw + a.chunk - 1) / a.chunk) : 0;
+    }
+    if (i0 >= n) break;  // uniform: no used split left
+    // Keep only the splits that hold positions.
+    const bool use = i0 + lane < n;
+    mi = use ? mi : -INFINITY;
+    li = use ? li : 0.0f;
+    const float mn = fmaxf(mrun, wave_max(mi));
+    const float mu = (mn == -INFINITY) ? 0.0f : mn;  // guard: no finite maximum yet
+    const float al = fast_exp2((mrun - mu) * kLog2e);  // 0 on the first pass
+    const float w = use ? fast_exp2((mi - mu) * kLog2e) : 0.0f;
+    lrun = fmaf(lrun, al, wave_sum(w * li));
+    acc.x *= al;
+    acc.y *= al;
+    acc.z *= al;
+    acc.w *= al;
+#pragma unroll
+    for (int k = 0; k < kRowsPerQuarter; ++k) {
+      const int i = i0 + qt + 4 * k;
+      const float wk = from_lane(w, qt + 4 * k);
+      if (i < n) {
+        acc.x = fmaf(wk, x[k].x, acc.x);
+        acc.y = fmaf(wk, x[k].y, acc.y);
+        acc.z = fmaf(wk, x[k].z, acc.z);
+        acc.w = fmaf(wk, x[k].w, acc.w);
       }
     }
-    const float w = i0 + tid < n ? fast_exp2((mi - mu) * kLog2e) : 0.0f;
-    lsum = fmaf(w, li, lsum);
-    __syncthreads();
-    s_w[tid] = w;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      const float wk = s_w[rg + 16 * k];
-      acc.x = fmaf(wk, x[k].x, acc.x);
-      acc.y = fmaf(wk, x[k].y, acc.y);
-      acc.z = fmaf(wk, x[k].z, acc.z);
-      acc.w = fmaf(wk, x[k].w, acc.w);
-    }
+    mrun = mn;
   }
-  const float lstar = block_reduce(lsum, s_red, false);
-
-  s_part[rg][c4] = acc;
-  __syncthreads();
-  if (tid < 16 && col_ok) {
-    float4 t = s_part[0][tid];
-    for (int r = 1; r < kCombThreads / 16; ++r) {
-      const float4 u = s_part[r][tid];
-      t.x += u.x;
-      t.y += u.y;
-      t.z += u.z;
-      t.w += u.w;
-    }
+  // Sum the four quarters (lanes c4, c4+16, c4+32, c4+48).
+  acc.x += xor16(acc.x);
+  acc.y += xor16(acc.y);
+  acc.z += xor16(acc.z);
+  acc.w += xor16(acc.w);
+  acc.x += xor32(acc.x);
+  acc.y += xor32(acc.y);
+  acc.z += xor32(acc.z);
+  acc.w += xor32(acc.w);
+  if (qt == 0 && col_ok) {
     float* o = a.out + ((int64_t)b * a.Hq + h) * a.Dv + col;
     if (valid) {
-      const float inv = 1.0f / lstar;
-      *reinterpret_cast<float4*>(o) = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+      const float inv = 1.0f / lrun;
+      *reinterpret_cast<float4*>(o) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     } else {
       const float nan = __builtin_nanf("");
       *reinterpret_cast<float4*>(o) = make_float4(nan, nan, nan, nan);
     }
   }
-  if (a.lse && cb == 0 && tid == 0)
-    a.lse[(int64_t)b * a.Hq + h] = valid ? mx + logf(lstar) : __builtin_nanf("");
+  if (a.lse && cb == 0 && lane == 0)
+    a.lse[(int64_t)b * a.Hq + h] = valid ? mrun + logf(lrun) : __builtin_nanf("");
 }
 
 sk_status_t combine_launch(const CombineLaunch& c) {
@@ -163,7 +151,7 @@ sk_status_t combine_launch(const CombineLaunch& c) {
   a.Dv = d.head_dim_v;
   a.cap = d.max_seq_len;
   const dim3 grid((d.head_dim_v + kCombCols - 1) / kCombCols, d.num_q_heads, d.batch);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombThreads), 0, c.stream, a);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(kPass), 0, c.stream, a);
   return SK_OK;
 }
 

@@ -401,10 +401,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 // Wider groups carry more query and accumulator registers per lane; the
 // 6-head f16 group splits its heads over two 16-lane slices of each row,
 // which halves its per-lane reductions and exponentials.
+constexpr bool sliced_variant(bool f16, int D, int G) { return f16 && D == 256 && G == 6; }
+
 template <typename KV, int G, int D>
 struct Tune {
   static constexpr bool kWideGroup = G > 4;
-  static constexpr bool kSliced = std::is_same<KV, _Float16>::value && D == 256 && G == 6;
+  static constexpr bool kSliced = sliced_variant(std::is_same<KV, _Float16>::value, D, G);
   static constexpr int RL = kSliced ? 16 : ((D == 256 && kWideGroup) ? 32 : 16);
   static constexpr int HS = kSliced ? 2 : 1;
   static constexpr int R =
@@ -485,6 +487,14 @@ static sk_status_t by_group(const SplitLaunch& s, bool launch, const void** fn, 
     case 8: return by_dim<KV, 8>(s, launch, fn, grid, block);
     default: return SK_ERR_UNSUPPORTED;
   }
+}
+
+int gqa_resident_blocks(const sk_desc_t& d) {
+  // The 6-head f16 kernel's VALU-heavy loop overlaps memory better with a
+  // second workgroup resident on each compute unit; every other variant
+  // streams best as one workgroup per compute unit.
+  const int G = d.num_kv_heads > 0 ? d.num_q_heads / d.num_kv_heads : 0;
+  return sliced_variant(d.kv_dtype == SK_F16, d.head_dim_qk, G) ? 2 : 1;
 }
 
 bool gqa_supported(const sk_desc_t& d) {

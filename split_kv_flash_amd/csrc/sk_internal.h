@@ -43,6 +43,8 @@ struct CombineLaunch {
 
 // Host-only capability checks (no HIP calls).
 bool gqa_supported(const sk_desc_t& d);
+// Workgroups per compute unit the split heuristic plans for a uniform batch.
+int gqa_resident_blocks(const sk_desc_t& d);
 bool latent_supported(const sk_desc_t& d);
 
 // Launchers: return the kernel function pointer they use through `fn` when

@@ -82,7 +82,8 @@ def test_plan_matches_oracle_reading(hkv):
         req = int(rng.choice([0, 0, 0, 1, 3, 8, 64, 512]))
         d = gqa_desc(Hq=4 * hkv, Hkv=hkv, D=128, cap=int(lens.max()), batch=batch)
         p = B.attn_decode_plan(d, int(lens.max()), int(lens.sum()), cu, req)
-        assert (p.n_splits, p.chunk) == oracle.plan_splits(lens, hkv, cu, req)
+        budget = 4 if int(lens.sum()) < batch * int(lens.max()) else 1  # ragged batches: 4 per CU
+        assert (p.n_splits, p.chunk) == oracle.plan_splits(lens, hkv, cu, req, blocks_per_cu=budget)
 
 
 def test_plan_latent_matches_oracle_reading():
@@ -96,7 +97,18 @@ def test_plan_latent_matches_oracle_reading():
 def test_plan_for_the_nine_b_like_layer_at_262144():
     lib()
     p = B.attn_decode_plan(gqa_desc(cap=262144), 262144, 262144, 256, 0)
-    assert (p.n_splits, p.chunk) == (256, 1024)  # 4 KV heads x 256 splits = 1024 workgroups
+    assert (p.n_splits, p.chunk) == (64, 4096)  # 4 KV heads x 64 splits = one workgroup per CU
+
+
+def test_plan_for_the_wide_f16_group_keeps_two_workgroups_per_cu():
+    lib()
+    d = gqa_desc(Hq=24, Hkv=4, D=256, cap=262144, kv="f16")
+    p = B.attn_decode_plan(d, 262144, 262144, 256, 0)
+    assert (p.n_splits, p.chunk) == (128, 2048)  # 4 x 128 = 512 workgroups, two per CU
+    assert (p.n_splits, p.chunk) == oracle.plan_splits([262144], 4, 256, blocks_per_cu=2)
+    d = gqa_desc(Hq=24, Hkv=4, D=256, cap=262144, kv="f32")  # f32 keeps one per CU
+    p = B.attn_decode_plan(d, 262144, 262144, 256, 0)
+    assert (p.n_splits, p.chunk) == (64, 4096)
 
 
 def test_workspace_bytes_follow_the_documented_layout():
