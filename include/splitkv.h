@@ -136,8 +136,11 @@ typedef struct {
  *           of width 256, and 4 times that for a ragged batch (total_tokens <
  *           batch * max_seq_len). The note's own S_target is about 4 per
  *           multiprocessor of its GPU.
- *   latent: chunk = max(64, ceil(total_tokens / cu_count))  (one workgroup serves all
- *           query heads, and each split costs a partial of every head)
+ *   latent: chunk = max(64, ceil(g * total_tokens / cu_count)) with g workgroups per
+ *           split: 1 for f16 caches (one workgroup serves all query heads), Hq/48
+ *           (Hq/32 when 48 does not divide Hq) for f32 caches, whose FP32-MFMA
+ *           kernel spreads a split's heads over g workgroups of 16-head blocks.
+ *           Each split costs a partial of every head, so splits stay long.
  *   chunk is rounded up to a multiple of 64 and S = ceil(max_seq_len / chunk).
  * Below SK_MIN_SPLIT_CONTEXT positions the heuristic returns S = 1 (Lecture 06
  * section 2 gates the split below a minimum context).

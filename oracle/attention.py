@@ -199,6 +199,7 @@ def plan_splits(
     min_chunk: int = 64,
     blocks_per_cu: int = 4,
     min_ctx: int = 0,
+    latent_groups: int = 1,
 ) -> Tuple[int, int]:
     """Split count S and slice length ``chunk`` for one decode call.
 
@@ -218,10 +219,12 @@ def plan_splits(
       max(min_chunk, ceil(Hkv * sum(L_b) / (blocks_per_cu * cu_count))),
       rounded up to a multiple of ``granule``.
     * Latent attention (``kv_shared``): one block serves every query head of
-      the latent, so the budget is one block per compute unit rather than
-      four: chunk = max(min_chunk, ceil(sum(L_b) / cu_count)), rounded up to
-      ``granule``. Each split costs a partial of all query heads, so fewer,
-      longer splits keep that traffic small against the cache read.
+      the latent (or ``latent_groups`` blocks share a split, each serving a
+      slice of the heads), so the budget is one block per compute unit rather
+      than four: chunk = max(min_chunk, ceil(latent_groups * sum(L_b) /
+      cu_count)), rounded up to ``granule``. Each split costs a partial of all
+      query heads, so fewer, longer splits keep that traffic small against the
+      cache read.
     """
     lens = [int(x) for x in seq_lens]
     if not lens or min(lens) < 1:
@@ -233,7 +236,7 @@ def plan_splits(
         return 1, l_max
     total = sum(lens)
     if kv_shared:
-        chunk = max(min_chunk, -(-total // cu_count))
+        chunk = max(min_chunk, -(-(latent_groups * total) // cu_count))
     else:
         chunk = max(min_chunk, -(-(num_kv_heads * total) // (blocks_per_cu * cu_count)))
     chunk = -(-chunk // granule) * granule

@@ -176,7 +176,7 @@ sk_status_t attn_decode_plan(const sk_desc_t* desc, int32_t max_seq_len, int64_t
   }
   int64_t chunk;
   if (desc->kv_shared) {
-    chunk = ceil_div(total_tokens, cu_count);
+    chunk = ceil_div(total_tokens * sk::latent_blocks_per_split(*desc), (int64_t)cu_count);
   } else {
     const bool ragged = total_tokens < (int64_t)max_seq_len * desc->batch;
     const int64_t per_cu = (int64_t)sk::gqa_resident_blocks(*desc) * (ragged ? kRaggedBlockFactor : 1);

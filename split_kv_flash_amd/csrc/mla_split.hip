@@ -12,22 +12,28 @@
 // The two products are dense contractions, so both run on MFMA:
 //   scores  S[h][j] = sum_d Q[h][d] C[j][d]    (heads x positions, K = 576)
 //   output  acc[h][e] += sum_j P[h][j] C[j][e] (heads x values,    K = positions)
-// with the online-softmax update between them. f16 caches use
-// v_mfma_f32_16x16x16_f16 (q and the probabilities rounded to f16, f32
-// accumulation); f32 caches use v_mfma_f32_16x16x4_f32 (no rounding).
+// with the online-softmax update between them. f16 caches use f16 MFMA (q and
+// the probabilities rounded to f16, f32 accumulation); f32 caches use
+// v_mfma_f32_16x16x4_f32 (no rounding). Three kernels live here:
+//   * mla32_split_kernel (every f32 cache): four waves per 16-head block,
+//     scores computed transposed so P stays in registers; see its comment;
+//   * mla16_split_kernel (f16 caches with 32 or 96 heads): two waves per
+//     16-head block, x32 MFMA, direct-to-LDS tile staging; see its comment;
+//   * mla_split_kernel (f16 caches with 64 or 128 heads), described next.
 //
-// Workgroup: 512 threads = 8 waves, one per split. Per tile of T positions:
+// mla_split_kernel: 512 threads = 8 waves, one workgroup per split. Per tile
+// of T positions:
 //   1. the tile of cache rows (T x 576) is staged in LDS (row-padded); the next
 //      tile's global loads are already in flight;
 //   2. score phase: wave w = (head half, column quarter) computes the partial
-//      scores of its heads over its 144 columns (split K); Q stays in registers
-//      for f16 caches and is read through the cache hierarchy for f32 caches;
+//      scores of its heads over its 144 columns (split K), Q in registers;
 //   3. softmax phase: partials are summed from LDS, each wave updates the
 //      running max / normaliser of 1/8 of the heads and writes the tile's
 //      probabilities and rescale factors to LDS;
 //   4. output phase: wave w owns 64 value columns for every head; it rescales
 //      its accumulators and adds P (from LDS) times the tile's value columns.
-// LDS use depends only on T and the head count, never on the context length.
+// LDS use depends only on the tile size and the head count, never on the
+// context length.
 #include "sk_device.h"
 #include "sk_internal.h"
 
@@ -652,6 +658,253 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// f32 caches: v_mfma_f32_16x16x4_f32 (exact f32 products), four waves per
+// 16-head block, heads of a split spread over HG workgroups.
+//
+// The f32 query block of 16 heads x 576 columns and the 16 x 512 output
+// accumulators do not fit one wave's share of the register file at three waves
+// per SIMD, so each 16-head block has four waves: wave (hb, dq) computes the
+// partial scores over latent columns [144*dq, 144*dq + 144) and owns value
+// columns [128*dq, 128*dq + 128). A workgroup holds NHBB blocks (12 waves for
+// NHBB = 3) and a split's heads are spread over HG = Hq / (16*NHBB)
+// workgroups, each streaming the split's cache rows; the f32 path is bound by
+// the FP32 MFMA rate, not by HBM, so the repeated read costs little.
+//  * Scores are computed transposed, S^T[position][head] = C[position][:] .
+//    Q^T, so the MFMA result leaves lane (head l16, quarter lq) holding the
+//    scores of positions 4*lq + i: after the four partials of the block are
+//    added (through LDS, in a fixed order, so all four waves hold identical
+//    values) and the softmax runs in registers, item t of that lane is
+//    exactly the A operand P[head][4*lq + t] of output step t. P never goes
+//    through LDS.
+//  * The contraction index is ordered so every operand read is 16 bytes:
+//    score step 4*t + u takes columns 144*dq + 16*t + 4*lq + u; output step t
+//    takes positions 4*lq + t, and output column block 4*u + e of lane j is
+//    column 128*dq + 64*u + 4*j + e.
+//  * Tiles of 16 cache rows go straight from HBM into LDS with
+//    global_load_lds_dwordx4, three tiles deep; each row's 144 chunks of 16
+//    bytes are stored with the chunk index XOR-ed by the row (0..15), so both
+//    the score reads (16 rows, one chunk) and the value reads (one row, 16
+//    chunks) hit distinct banks.
+//  * Two barriers per tile: one publishes the partial scores, one the next
+//    tile (each wave first waits for its own tile loads).
+// ---------------------------------------------------------------------------
+constexpr int kT32 = 16;              // positions per tile
+constexpr int kCpr32 = kLatDk / 4;    // 144 chunks of 16 bytes per f32 cache row
+constexpr int kSlots32 = kT32 * kCpr32;
+
+typedef __attribute__((address_space(3))) float lds_float_t;
+__device__ __forceinline__ uint32_t lds_addr_of(const float* p) {
+  return (uint32_t)(size_t)(const lds_float_t*)(p);
+}
+
+// 16-head blocks per workgroup for an f32 latent with Hq heads, and the
+// workgroups that share one split.
+__host__ __device__ constexpr int mla32_blocks(int Hq) { return Hq % 48 == 0 ? 3 : 2; }
+__host__ __device__ constexpr int mla32_groups(int Hq) { return Hq / (16 * mla32_blocks(Hq)); }
+
+template <int NHBB>
+__global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
+  constexpr int NW = 4 * NHBB;
+  constexpr int NT = NW * 64;
+  constexpr int HW = 16 * NHBB;                    // heads per workgroup
+  constexpr int KT = kLatDk / 4 / 16;              // 9 reads of 4 steps over 144 columns
+  constexpr int DPW = (kSlots32 + NT - 1) / NT;    // tile loads per lane
+  constexpr int TSTRIDE = DPW * NT * 4;            // floats per tile buffer (padded slots included)
+
+  __shared__ __align__(16) float s_c[3 * TSTRIDE];
+  __shared__ __align__(16) float4_t s_sx[NW][64];
+
+  const int split = blockIdx.x;
+  const int b = blockIdx.y;
+  const int hg = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hb = wave >> 2;
+  const int dq = wave & 3;
+  const int l16 = lane & 15;
+  const int lq = lane >> 4;
+  const int head0 = hg * HW + hb * 16;
+
+  const int L = min(a.seq_lens[b], a.cap);
+  const int64_t start = (int64_t)split * a.chunk;
+  const int64_t end = min((int64_t)L, start + a.chunk);
+  const int64_t ws0 = (int64_t)b * a.Hq * a.S + split;
+
+  if (start >= end) {
+    for (int idx = tid; idx < HW * kLatDv; idx += NT) {
+      const int h = hg * HW + idx / kLatDv, e = idx - (idx / kLatDv) * kLatDv;
+      a.ws_acc[(ws0 + (int64_t)h * a.S) * kLatDv + e] = 0.0f;
+    }
+    for (int h = tid; h < HW; h += NT) {
+      a.ws_m[ws0 + (int64_t)(hg * HW + h) * a.S] = -INFINITY;
+      a.ws_l[ws0 + (int64_t)(hg * HW + h) * a.S] = 0.0f;
+    }
+    return;
+  }
+
+  const float* __restrict__ cbase = reinterpret_cast<const float*>(a.c) + (int64_t)b * a.stride_seq;
+  const float* __restrict__ qb = a.q + (int64_t)b * a.Hq * kLatDk;
+
+  // Tile staging: slot s of a buffer holds tile row s/144, stored chunk s%144,
+  // i.e. logical chunk (s%144) ^ row. Padding slots (s >= 2304, only when the
+  // slots do not divide evenly over the waves) re-read the split's first row
+  // into the buffer's tail, which nothing reads.
+  int srow[DPW], scol[DPW];
+#pragma unroll
+  for (int c = 0; c < DPW; ++c) {
+    const int sl = (wave * DPW + c) * 64 + lane;
+    const bool real = sl < kSlots32;
+    srow[c] = real ? sl / kCpr32 : -1;
+    scol[c] = real ? ((sl - (sl / kCpr32) * kCpr32) ^ (sl / kCpr32)) * 4 : 0;
+  }
+  const uint32_t lds0 = lds_addr_of(s_c);
+  auto issue_tile = [&](int bi, int64_t tb) {
+#pragma unroll
+    for (int c = 0; c < DPW; ++c) {
+      int64_t pos = srow[c] < 0 ? start : tb + srow[c];
+      pos = pos < end ? pos : end - 1;
+      const uint32_t dst = lds0 + (uint32_t)((bi * TSTRIDE + (wave * DPW + c) * 64 * 4) * 4);
+      dma16(cbase + pos * a.stride_pos + scol[c], __builtin_amdgcn_readfirstlane(dst));
+    }
+  };
+
+  // Query block as B operands, pre-scaled into base-2 units: qv[t][u] is
+  // column 144*dq + 16*t + 4*lq + u of head head0 + l16.
+  float4_t qv[KT];
+  {
+    const float* qrow = qb + (int64_t)(head0 + l16) * kLatDk + dq * 144 + lq * 4;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      const float4 v = *reinterpret_cast<const float4*>(qrow + 16 * t);
+      qv[t] = float4_t{v.x * a.qscale, v.y * a.qscale, v.z * a.qscale, v.w * a.qscale};
+    }
+  }
+
+  // Running max (base 2) and normaliser of head head0 + l16 (replicated over
+  // the four quarters); accumulators acc[4*u + e] hold heads 4*lq + i (items)
+  // at column 128*dq + 64*u + 4*l16 + e.
+  float m = -INFINITY, l = 0.0f;
+  float4_t acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Per-lane LDS offsets (floats) inside a tile buffer: score reads use row
+  // l16 and logical chunk 36*dq + lq + 4*t, i.e. sb[t & 3] + 64*(t >> 2);
+  // value reads use row 4*lq + t and logical chunk 32*dq + 16*u + l16, i.e.
+  // vb[t] + 64*u.
+  int sb[4], vb[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    sb[v] = l16 * kLatDk + (((36 * dq + lq + 4 * v) ^ l16) << 2);
+    const int r = 4 * lq + v;
+    vb[v] = r * kLatDk + ((32 * dq + (l16 ^ r)) << 2);
+  }
+
+  issue_tile(0, start);
+  issue_tile(1, start + kT32);
+  wait_vm_lgkm0<DPW>();
+  raw_barrier();
+
+  int cur_i = 0;
+  for (int64_t tb = start; tb < end; tb += kT32) {
+    const float* cur = s_c + cur_i * TSTRIDE;
+    const int dma_i = cur_i == 0 ? 2 : cur_i - 1;  // (cur + 2) mod 3
+
+    // ---- partial scores S^T over this wave's 144 columns ----
+    float4_t sp = float4_t{0.f, 0.f, 0.f, 0.f};
+    float4_t an = *reinterpret_cast<const float4_t*>(cur + sb[0]);
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      const float4_t av = an;
+      if (t + 1 < KT) an = *reinterpret_cast<const float4_t*>(cur + sb[(t + 1) & 3] + 64 * ((t + 1) >> 2));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sp = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], qv[t][u], sp, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s_sx[wave][lane] = sp;
+    wait_vm_lgkm0<63>();
+    raw_barrier();
+
+    // ---- full scores (the block's four partials in a fixed order), softmax ----
+    const float4_t x0 = s_sx[hb * 4 + 0][lane], x1 = s_sx[hb * 4 + 1][lane];
+    const float4_t x2 = s_sx[hb * 4 + 2][lane], x3 = s_sx[hb * 4 + 3][lane];
+    float p[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = tb + 4 * lq + i < end;
+      p[i] = ok ? (x0[i] + x1[i]) + (x2[i] + x3[i]) : -INFINITY;
+      mx = fmaxf(mx, p[i]);
+    }
+    mx = fmaxf(mx, xor16(mx));
+    mx = fmaxf(mx, xor32(mx));
+    const float mn = fmaxf(m, mx);
+    const float mu = (mn == -INFINITY) ? 0.0f : mn;
+    const float al = fast_exp2(m - mu);
+    float ls = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = fast_exp2(p[i] - mu);
+      ls += p[i];
+    }
+    ls += xor16(ls);
+    ls += xor32(ls);
+    l = fmaf(l, al, ls);
+    m = mn;
+    const bool moved = al != 1.0f;
+
+    issue_tile(dma_i, tb + 2 * kT32);
+    wait_vm_lgkm0<DPW>();
+    raw_barrier();
+
+    // ---- output: acc = al * acc + P[16 heads][16 positions] x V ----
+    if (__any(moved)) {
+      // Accumulator item i is head 4*lq + i, whose factor lane 4*lq + i holds.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * lq + i) << 2, __float_as_int(al)));
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c][i] *= ai;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float4_t v4 = *reinterpret_cast<const float4_t*>(cur + vb[t] + 64 * u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[4 * u + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[t], v4[e], acc[4 * u + e], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    cur_i = cur_i == 2 ? 0 : cur_i + 1;
+  }
+  // Drain the tile loads still in flight before the workgroup can retire.
+  wait_vm_lgkm0<0>();
+
+  // Partials: four consecutive columns per lane and head as one float4.
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int head = head0 + 4 * lq + i;
+      const int col = dq * 128 + 64 * u + 4 * l16;
+      *reinterpret_cast<float4*>(a.ws_acc + (ws0 + (int64_t)head * a.S) * kLatDv + col) =
+          make_float4(acc[4 * u + 0][i], acc[4 * u + 1][i], acc[4 * u + 2][i], acc[4 * u + 3][i]);
+    }
+  if (dq == 0 && lq == 0) {
+    a.ws_m[ws0 + (int64_t)(head0 + l16) * a.S] = m * kLn2;
+    a.ws_l[ws0 + (int64_t)(head0 + l16) * a.S] = l;
+  }
+}
+
+int latent_blocks_per_split(const sk_desc_t& d) {
+  return d.kv_dtype == SK_F32 ? mla32_groups(d.num_q_heads) : 1;
+}
+
 bool latent_supported(const sk_desc_t& d) {
   return d.kv_shared == 1 && d.num_kv_heads == 1 && d.head_dim_qk == kLatDk &&
          d.head_dim_v == kLatDv && d.layout == SK_KV_CONTIGUOUS && d.q_dtype == SK_F32 &&
@@ -664,17 +917,27 @@ template <typename CT, int NHB>
 static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void** fn, int grid[3],
                                   int* block) {
   const sk_desc_t& d = *s.d;
+  // f32 caches take the FP32-MFMA kernel (heads over HG workgroups per split);
   // f16 caches with 32 or 96 heads take the two-waves-per-head-block kernel
   // (its tile loads divide evenly over 4 or 12 waves and its registers fit 3
-  // waves per SIMD); the other head counts take the split-K kernel.
+  // waves per SIMD); the other f16 head counts take the split-K kernel.
+  constexpr int H = NHB * 16;
+  constexpr bool kF32 = sizeof(CT) == 4;
   constexpr bool kFull16 = sizeof(CT) == 2 && (NHB == 2 || NHB == 6);
   void (*kern)(MlaArgs);
-  if constexpr (kFull16)
+  int threads, groups = 1;
+  if constexpr (kF32) {
+    kern = mla32_split_kernel<mla32_blocks(H)>;
+    threads = mla32_blocks(H) * 256;
+    groups = mla32_groups(H);
+  } else if constexpr (kFull16) {
     kern = mla16_split_kernel<NHB>;
-  else
+    threads = NHB * 128;
+  } else {
     kern = mla_split_kernel<CT, NHB>;
-  const int threads = kFull16 ? NHB * 128 : kMlaThreads;
-  const dim3 gr(s.p->n_splits, d.batch, 1);
+    threads = kMlaThreads;
+  }
+  const dim3 gr(s.p->n_splits, d.batch, groups);
   grid[0] = gr.x;
   grid[1] = gr.y;
   grid[2] = gr.z;

@@ -46,6 +46,9 @@ bool gqa_supported(const sk_desc_t& d);
 // Workgroups per compute unit the split heuristic plans for a uniform batch.
 int gqa_resident_blocks(const sk_desc_t& d);
 bool latent_supported(const sk_desc_t& d);
+// Workgroups that share one split of a shared latent (the f32 kernel spreads
+// the heads of a split over several).
+int latent_blocks_per_split(const sk_desc_t& d);
 
 // Launchers: return the kernel function pointer they use through `fn` when
 // non-null (for attribute queries) and launch only when `launch` is true.

@@ -88,10 +88,16 @@ def test_plan_matches_oracle_reading(hkv):
 
 def test_plan_latent_matches_oracle_reading():
     lib()
-    for L in (1, 64, 65, 8192, 131072, 262144):
-        for cu in (132, 256):
-            p = B.attn_decode_plan(latent_desc(cap=L), L, L, cu, 0)
-            assert (p.n_splits, p.chunk) == oracle.plan_splits([L], 1, cu, kv_shared=True)
+    # f16 latents: one workgroup per split; f32 latents spread a split's heads
+    # over Hq/48 (or Hq/32) workgroups of 16-head blocks.
+    groups = {("f16", 96): 1, ("f16", 32): 1, ("f32", 96): 2, ("f32", 32): 1, ("f32", 64): 2,
+              ("f32", 128): 4}
+    for (kv, hq), g in groups.items():
+        for L in (1, 64, 65, 8192, 131072, 262144):
+            for cu in (132, 256):
+                p = B.attn_decode_plan(latent_desc(cap=L, kv=kv, Hq=hq), L, L, cu, 0)
+                want = oracle.plan_splits([L], 1, cu, kv_shared=True, latent_groups=g)
+                assert (p.n_splits, p.chunk) == want, (kv, hq, L, cu)
 
 
 def test_plan_for_the_nine_b_like_layer_at_262144():
