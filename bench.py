@@ -30,6 +30,53 @@ MALL_FLUSH_BYTES = 512 << 20  # twice the 256 MB Infinity Cache
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "f16": 2500.0}
 
 
+# Named single workloads for --only (profiling runs of one kernel).
+ONLY = {
+    "nine-b-f32-131072": ("qwen9b_like", (131072, "f32"), {"seed": 2000 + 131072}),
+    "nine-b-f16-262144": ("qwen9b_like", (262144, "f16"), {"seed": 2000 + 262144}),
+    "wide-peaky-262144": ("wide_group_peaky", (262144,), {}),
+    "ragged-paged": ("ragged_paged", (), {}),
+    "latent-f32-131072": ("latent_decode", (131072, "f32"), {"seed": 3000 + 131072}),
+    "latent-f16-131072": ("latent_decode", (131072, "f16"), {"seed": 3000 + 131072}),
+}
+
+# HBM traffic of the headline split kernel, measured with rocprofv3 counters
+# (FETCH_SIZE and WRITE_SIZE, scaled by a copy kernel of known size) and kept
+# with the hash of the kernel sources it was measured on. It is reported only
+# while those sources are unchanged.
+TRAFFIC_SUMMARY = os.path.join(HERE, "profiles", "gqa_split_9b-like_f32_L131072_traffic.md")
+KERNEL_SOURCES = [os.path.join(HERE, "split_kv_flash_amd", "csrc", f)
+                  for f in ("gqa_split.hip", "sk_device.h", "sk_internal.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(n_splits):
+    """Bytes per launch from the committed counter summary, or None when the
+    kernel sources or the split count differ from the measured ones."""
+    try:
+        fields = {}
+        for line in open(TRAFFIC_SUMMARY):
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+        if fields.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        if int(fields.get("n_splits", -1)) != n_splits:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -45,6 +92,8 @@ def parse():
     ap.add_argument("--no-rungs", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rung-steps", type=int, default=20)
+    ap.add_argument("--only", choices=sorted(ONLY), default=None,
+                    help="time one named workload (prints its dict, no JSON line); for profiling")
     return ap.parse_args()
 
 
@@ -72,36 +121,63 @@ def algorithmic_bytes(case, plan):
 
 
 def time_steps(call, steps, warmup, flush=None):
-    """Per-launch HIP-event times (ms) of split and combine, and wall ms per step.
+    """Timings in ms: (split kernel average, combine kernel average, per-call
+    totals, wall ms per call or None).
 
-    Events are recorded on torch's current stream, which is the stream the
-    library launches on. With ``flush`` (a device buffer of MALL_FLUSH_BYTES) a
-    read of the whole buffer evicts the Infinity Cache before every step,
-    outside the event pairs; the wall clock is then not reported (None). The
-    eviction reads rather than writes, so no write-back of dirty lines competes
-    with the timed call."""
+    * Per-call totals: one HIP event pair around each whole call (split and
+      combine launches), recorded on torch's current stream, which is the
+      stream the library launches on. Nothing is recorded between the two
+      launches, so the pair brackets exactly what a caller runs.
+    * Kernel averages: one event pair around ``steps`` back-to-back launches
+      of that kernel alone, divided by ``steps`` (the inputs do not change, so
+      every launch does the same work); this is the per-launch duration a
+      kernel trace reports.
+    With ``flush`` (a device buffer of MALL_FLUSH_BYTES) a read of the whole
+    buffer evicts the Infinity Cache before every timed call and every timed
+    split launch, outside the event pairs (the split kernel is then timed per
+    launch); the wall clock is then not reported. The eviction reads rather
+    than writes, so no write-back of dirty lines competes with the timed call.
+    """
     import torch
+
+    def pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
+    ev = [pair() for _ in range(steps)]
     t0 = time.perf_counter()
-    for e0, e1, e2 in ev:
+    for e0, e1 in ev:
         if flush is not None:
             flush.sum()
         e0.record()
-        call.splitk()
+        call()
         e1.record()
-        call.combine()
-        e2.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    split = [a.elapsed_time(b) for a, b, _ in ev]
-    comb = [b.elapsed_time(c) for _, b, c in ev]
-    total = [a.elapsed_time(c) for a, _, c in ev]
+    total = [a.elapsed_time(b) for a, b in ev]
+
+    def kernel_avg(fn, evict):
+        if evict is None:
+            e0, e1 = pair()
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps
+        evs = [pair() for _ in range(steps)]
+        for e0, e1 in evs:
+            evict.sum()
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return statistics.mean(a.elapsed_time(b) for a, b in evs)
+
+    split = kernel_avg(call.splitk, flush)
+    comb = kernel_avg(call.combine, None)  # reads the partials the split just wrote
     return split, comb, total, (None if flush is not None else wall)
 
 
@@ -127,11 +203,11 @@ def measure(case, steps, warmup, n_splits=0, flush=None):
         "workload": case.name, "n_splits": call.plan.n_splits, "chunk": call.plan.chunk,
         "us_per_call": round(us, 2), "us_p10": round(pct(total, 0.1) * 1e3, 2),
         "us_p90": round(pct(total, 0.9) * 1e3, 2),
-        "split_us": round(statistics.mean(split) * 1e3, 2),
-        "combine_us": round(statistics.mean(comb) * 1e3, 2),
+        "split_us": round(split * 1e3, 2),
+        "combine_us": round(comb * 1e3, 2),
         "GBps": round(whole_b / (us * 1e-6) / 1e9, 1),
         "frac_of_peak": round(whole_b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-        "split_GBps": round(split_b / (statistics.mean(split) * 1e-3) / 1e9, 1),
+        "split_GBps": round(split_b / (split * 1e-3) / 1e9, 1),
         "bytes_call": whole_b, "bytes_split": split_b,
         "tokens_per_s_per_layer": round(case.batch * 1e6 / us, 1),
         "mall_flushed": flush is not None,
@@ -140,7 +216,7 @@ def measure(case, steps, warmup, n_splits=0, flush=None):
         # Dense contractions on MFMA: scores (Hq x Dk) and output (Hq x Dv) per position.
         flops = 2.0 * case.num_q_heads * (case.head_dim_qk + case.head_dim_v) * int(case.seq_lens.sum())
         peak = MFMA_PEAK_TFLOPS[case.kv_dtype]
-        tf = flops / (statistics.mean(split) * 1e-3) / 1e12
+        tf = flops / (split * 1e-3) / 1e12
         res.update({"split_TFLOPs": round(tf, 2), "mfma_peak_TFLOPs": peak,
                     "mfma_frac": round(tf / peak, 4), "flops_split": flops})
     del call, t
@@ -238,6 +314,13 @@ def main():
     log(f"device: {props.name} CUs={props.multi_processor_count} "
         f"mem={props.total_memory / 2**30:.0f} GiB")
 
+    if args.only:
+        fn, pos, kw = ONLY[args.only]
+        c = getattr(synthetic, fn)(*pos, **kw)
+        r, _, _ = measure(c, args.steps, args.warmup, args.n_splits)
+        log(f"{args.only}: {r}")
+        return
+
     # Headline: A and B runs of the same workload give the A/A noise floor.
     case = synthetic.qwen9b_like(args.seq_len, args.kv, seed=2000 + args.seq_len)
     log(f"headline workload {case.name}: K+V {case.kv_bytes() / 1e9:.3f} GB")
@@ -247,12 +330,12 @@ def main():
     log(f"run B: {head_b}")
     aa_spread = abs(head_a["us_per_call"] - head_b["us_per_call"]) / head_a["us_per_call"]
 
-    split_ms = statistics.mean(split_a)
+    split_ms = split_a
     achieved = head_a["bytes_split"] / (split_ms * 1e-3) / 1e9
     roofline = {
         "kernel": "gqa_split_kernel",
         "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-        "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+        "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(head_a["n_splits"]),
         "avg_launch_us": round(split_ms * 1e3, 2),
         "algorithmic_bytes_per_launch": head_a["bytes_split"],
     }

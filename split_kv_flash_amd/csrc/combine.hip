@@ -6,16 +6,19 @@
 // sequence hold positions; only their values are used. lse = M + ln l* (the
 // log-sum-exp of the scores, "The Kernel Level: Attention and MoE").
 //
-// Launch: grid (ceil(Dv/64), Hq, B), one wave of 64 lanes per workgroup. The
-// wave owns 64 output columns of one (b, h). Splits are taken 64 at a time:
-// lane i holds m and l of split i of the pass, and the 16-lane quarters of the
-// wave each read every 4th split's 64 columns as float4 rows, so every partial
-// row is read once, coalesced. Every split block of the grid writes its
-// partial (empty slices write the neutral one), so a pass's rows are all
-// requested at once, together with the sequence length; the rows at or past n
-// are then dropped by selection, never by arithmetic, so their values cannot
-// reach the result. The maximum and the sums are wave reductions; no
-// workgroup barrier is needed.
+// Launch: grid (ceil(Dv/64), Hq, B); a workgroup of NWC = min(4, ceil(S/64))
+// waves owns 64 output columns of one (b, h). Splits are taken 64 at a time
+// (wave w takes passes w, w + NWC, ...): lane i holds m and l of split i of
+// the pass, and the 16-lane quarters of the wave each read every 4th split's
+// 64 columns as float4 rows, so every partial row is read once, coalesced.
+// Every split block of the grid writes its partial (empty slices write the
+// neutral one), so a pass's rows are all requested at once, together with the
+// sequence length; the rows at or past n are then dropped by selection, never
+// by arithmetic, so their values cannot reach the result. Within a wave the
+// maximum and the sums are wave reductions; the waves' (m, l, acc) are merged
+// once through LDS with the same rescaling.
+#include <algorithm>
+
 #include "sk_device.h"
 #include "sk_internal.h"
 
@@ -53,9 +56,16 @@ __device__ __forceinline__ float from_lane(float x, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
 }
 
-__global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
+constexpr int kMaxCombWaves = 4;
+
+__global__ __launch_bounds__(64 * kMaxCombWaves) void combine_kernel(CombineArgs a) {
+  __shared__ float4 s_acc[kMaxCombWaves][16];
+  __shared__ float s_ml[kMaxCombWaves][2];
+
   const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwc = blockDim.x >> 6;
   const int c4 = lane & 15;  // which float4 of the 64 columns
   const int qt = lane >> 4;  // quarter: splits qt, qt+4, qt+8, ... of a pass
   const int col = cb * kCombCols + c4 * 4;
@@ -68,9 +78,10 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
   const int Lraw = a.seq_lens[b];
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float mrun = -INFINITY, lrun = 0.0f;
-  int n = 0;
-  bool valid = false;
-  for (int i0 = 0; i0 < a.S; i0 += kPass) {
+  const bool valid = Lraw >= 1 && Lraw <= a.cap && (int64_t)Lraw <= (int64_t)a.S * a.chunk;
+  int n = a.S;  // replaced by ceil(L/chunk) once the length has arrived
+  bool first = true;
+  for (int i0 = wave * kPass; i0 < a.S; i0 += nwc * kPass) {
     // Requests first: this pass's m, l and accumulator rows.
     const bool in_s = i0 + lane < a.S;
     float mi = in_s ? mrow[i0 + lane] : -INFINITY;
@@ -82,11 +93,11 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
       x[k] = (i < a.S && col_ok) ? *reinterpret_cast<const float4*>(accp + (int64_t)i * a.Dv)
                                  : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    if (i0 == 0) {
-      valid = Lraw >= 1 && Lraw <= a.cap && (int64_t)Lraw <= (int64_t)a.S * a.chunk;
+    if (first) {
       n = valid ? (int)min((int64_t)a.S, ((int64_t)Lraw + a.chunk - 1) / a.chunk) : 0;
+      first = false;
     }
-    if (i0 >= n) break;  // uniform: no used split left
+    if (i0 >= n) break;  // uniform: no used split left for this wave
     // Keep only the splits that hold positions.
     const bool use = i0 + lane < n;
     mi = use ? mi : -INFINITY;
@@ -122,6 +133,31 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
   acc.y += xor32(acc.y);
   acc.z += xor32(acc.z);
   acc.w += xor32(acc.w);
+  if (nwc > 1) {
+    // Merge the waves: rescale each wave's (l, acc) to the common maximum.
+    if (qt == 0) s_acc[wave][c4] = acc;
+    if (lane == 0) {
+      s_ml[wave][0] = mrun;
+      s_ml[wave][1] = lrun;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float M = s_ml[0][0];
+    for (int w = 1; w < nwc; ++w) M = fmaxf(M, s_ml[w][0]);
+    const float Mu = (M == -INFINITY) ? 0.0f : M;
+    acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    lrun = 0.0f;
+    for (int w = 0; w < nwc; ++w) {
+      const float f = fast_exp2((s_ml[w][0] - Mu) * kLog2e);  // 0 for a wave without splits
+      const float4 v = s_acc[w][c4];
+      lrun = fmaf(f, s_ml[w][1], lrun);
+      acc.x = fmaf(f, v.x, acc.x);
+      acc.y = fmaf(f, v.y, acc.y);
+      acc.z = fmaf(f, v.z, acc.z);
+      acc.w = fmaf(f, v.w, acc.w);
+    }
+    mrun = M;
+  }
   if (qt == 0 && col_ok) {
     float* o = a.out + ((int64_t)b * a.Hq + h) * a.Dv + col;
     if (valid) {
@@ -151,7 +187,8 @@ sk_status_t combine_launch(const CombineLaunch& c) {
   a.Dv = d.head_dim_v;
   a.cap = d.max_seq_len;
   const dim3 grid((d.head_dim_v + kCombCols - 1) / kCombCols, d.num_q_heads, d.batch);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(kPass), 0, c.stream, a);
+  const int waves = (int)std::min<int64_t>(kMaxCombWaves, (a.S + kPass - 1) / kPass);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(64 * waves), 0, c.stream, a);
   return SK_OK;
 }
 
