@@ -87,6 +87,9 @@ sk_status_t check_desc(const sk_desc_t* d) {
     const int64_t vec = d->kv_dtype == SK_F32 ? 4 : 8;  // elements per 16-byte load
     if (d->stride_pos % vec || d->stride_head % vec || d->stride_seq % vec)
       return fail(SK_ERR_UNSUPPORTED, "strides must be multiples of 16 bytes (vector loads)");
+    if (d->stride_pos < d->head_dim_qk)
+      return fail(SK_ERR_INVALID_ARG, "stride_pos %lld overlaps positions of width %d",
+                  (long long)d->stride_pos, d->head_dim_qk);
     const int64_t esize = d->kv_dtype == SK_F32 ? 4 : 2;
     if (d->stride_pos * esize > kMaxRowStepBytes)
       return fail(SK_ERR_UNSUPPORTED, "stride_pos of %lld bytes exceeds %lld (32-bit tile offsets)",

@@ -189,6 +189,9 @@ def test_argument_errors_are_reported_before_any_launch():
     d.stride_pos = 6
     cases.append(("stride not a 16-byte multiple", _split(d, plan), B.SK_ERR_UNSUPPORTED))
     d = gqa_desc()
+    d.stride_pos = 128  # positions overlap (head_dim 256)
+    cases.append(("overlapping positions", _split(d, plan), B.SK_ERR_INVALID_ARG))
+    d = gqa_desc()
     d.stride_pos = (1 << 22) + 4  # f32: just over 16 MiB between positions
     cases.append(("position step beyond 32-bit tile offsets", _split(d, plan), B.SK_ERR_UNSUPPORTED))
     d = latent_desc()
