@@ -18,7 +18,8 @@
 //   * mla32_split_kernel (every f32 cache): four waves per 16-head block,
 //     scores computed transposed so P stays in registers; see its comment;
 //   * mla16_split_kernel (f16 caches with 32 or 96 heads): two waves per
-//     16-head block, x32 MFMA, direct-to-LDS tile staging; see its comment;
+//     16-head block, x32 MFMA, scores transposed, one barrier per tile; see
+//     its comment;
 //   * mla_split_kernel (f16 caches with 64 or 128 heads), described next.
 //
 // mla_split_kernel: 512 threads = 8 waves, one workgroup per split. Per tile
@@ -346,31 +347,18 @@ __global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// f16 caches: two waves per 16-head block, softmax in registers, cache tiles
-// staged by direct global-to-LDS loads.
-//
-// Workgroup of 2*NHB waves (768 threads for 96 heads). Wave w = 2*hb + dh owns
-// head block hb (16 heads).
-//  * Staging: tiles of 32 cache rows go straight from HBM into LDS with
-//    global_load_lds_dwordx4 (each lane's 16 bytes land at M0 + 16*lane), three
-//    tiles deep, so no registers hold staged data and the next two tiles are
-//    in flight during the current one. Rows are stored unpadded with the
-//    16-byte chunk index XOR-ed by (row & 7): a lane chooses which global chunk
-//    to fetch so that its fixed LDS slot holds the swizzled layout.
-//  * Scores: the wave computes partial scores of its 16 heads x 32 positions
-//    over latent columns [288*dh, 288*dh + 288) with v_mfma_f32_16x16x32_f16,
-//    its query rows held in registers; the two waves of a block add each
-//    other's partials through LDS (2 KB per wave per tile), so both hold the
-//    block's full scores and run the online softmax over all 32 positions in
-//    registers (row max per head: a 16-lane DPP reduction).
-//  * Output: the same wave owns value columns [256*dh, 256*dh + 256) of its 16
-//    heads, so its rescale factors are already in registers. P goes through
-//    LDS; V operands come straight from the cache tile through the gfx950
-//    transpose read ds_read_b64_tr_b16 (within a 16-lane group, lane i's item
-//    t is element i%4 of the 8-byte chunk addressed by lane 4t + i/4).
-//  * Synchronisation: two barriers per tile. Each wave waits for its own
-//    global-to-LDS loads with an explicit vmcnt before the barrier that
-//    publishes them (a workgroup fence would wait for every load in flight).
+// Helpers shared by the f16 and f32 latent kernels: direct global-to-LDS tile
+// loads, the gfx950 transpose read, explicit wait counts and a raw barrier.
+//  * global_load_lds_dwordx4 puts each lane's 16 bytes at M0 + 16*lane, so a
+//    tile goes straight from HBM into LDS with no registers holding staged
+//    data; rows are stored unpadded with their 16-byte chunk index XOR-ed by
+//    the row, and a lane chooses which global chunk to fetch so that its fixed
+//    LDS slot holds the swizzled layout.
+//  * ds_read_b64_tr_b16: within a 16-lane group, lane i's item t is element
+//    i%4 of the 8-byte chunk addressed by lane 4t + i/4.
+//  * Each wave waits for its own tile loads with an explicit vmcnt before the
+//    barrier that publishes them (a workgroup fence would wait for every load
+//    in flight).
 // ---------------------------------------------------------------------------
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -389,6 +377,14 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+// The same load with a wave-uniform 64-bit base in scalar registers and a
+// 32-bit per-lane byte offset (global address = base + offset).
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -426,6 +422,30 @@ constexpr int kProw16 = 40;  // LDS row stride of P (halves; rows stay 16-byte a
 // LDS offset (halves) of logical chunk cc of tile row r.
 __device__ __forceinline__ int tile_off(int r, int cc) { return r * kLatDk + ((cc ^ (r & 7)) << 3); }
 
+// ---------------------------------------------------------------------------
+// f16 caches: two waves per 16-head block (workgroup of 2*NHB waves, wave
+// w = 2*hb + dh), tiles of 32 rows staged by direct global-to-LDS loads three
+// deep (chunks XOR-swizzled by row & 7), scores computed transposed, one
+// barrier per tile.
+//  * Wave (hb, dh) computes partial scores of its 16 heads over latent columns
+//    [288*dh, 288*dh + 288) with v_mfma_f32_16x16x32_f16, its query rows held
+//    in registers as B operands; the two waves of a block add each other's
+//    partials through LDS, so both hold the block's full scores and run the
+//    online softmax in registers. The same wave owns value columns
+//    [256*dh, 256*dh + 256).
+//  * Scores S^T[position][head] = C . Q^T: the cache tile is the A operand and
+//    the query rows the B operand of v_mfma_f32_16x16x32_f16, so lane (head
+//    l16, quarter lq) ends with positions 4*lq + i (first 16-position block)
+//    and 16 + 4*lq + i (second). After the two partials of the block are
+//    added and the softmax runs, those eight weights, in that order, are the
+//    lane's A operand for the output product over the tile's 32 positions; the
+//    value operands are read in the same position order (two transpose reads
+//    of four rows each). P stays in registers.
+//  * Software pipeline: iteration i computes the output product of tile i-1
+//    and the scores of tile i, then one barrier publishes the partial scores
+//    (double-buffered by parity) and the next tile; after it the softmax of
+//    tile i runs and tile i+2 is requested into the buffer tile i-1 used.
+// ---------------------------------------------------------------------------
 template <int NHB>
 __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
   constexpr int H = NHB * 16;
@@ -440,8 +460,7 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
   constexpr int TILE = kT16 * kLatDk;             // halves per tile buffer
 
   __shared__ __align__(16) _Float16 s_c[3 * TILE];
-  __shared__ __align__(16) float4_t s_sx[NW][2][64];
-  __shared__ __align__(16) _Float16 s_p[H * kProw16];
+  __shared__ __align__(16) float4_t s_sx[2][NW][2][64];
 
   const int split = blockIdx.x;
   const int b = blockIdx.y;
@@ -475,26 +494,29 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
 
   // Tile staging: this wave's DPW slots per tile; slot s holds tile row s/72,
   // logical chunk (s%72) ^ (row & 7). Rows past the end re-read row end-1.
-  int srow[DPW], scol[DPW];
-#pragma unroll
-  for (int c = 0; c < DPW; ++c) {
-    const int sl = (wave * DPW + c) * 64 + lane;
-    srow[c] = sl / kCpr16;
-    scol[c] = ((sl - srow[c] * kCpr16) ^ (srow[c] & 7)) * 8;
-  }
+  // The slot coordinates are recomputed per tile (a few integer operations)
+  // rather than held in registers across the loop.
+  // The tile base (clamped to the last row) is wave-uniform; a lane's offset
+  // is its row (clamped to the last row) times the row stride plus its chunk.
   const uint32_t lds0 = lds_addr_of(s_c);
+  const uint32_t row_bytes = (uint32_t)(a.stride_pos * 2);
   auto issue_tile = [&](int bi, int64_t tb) {
+    const int64_t tbc = tb < end ? tb : end - 1;
+    const int last = (int)(end - 1 - tbc);  // >= 0
+    const _Float16* tbase = cbase + tbc * a.stride_pos;
 #pragma unroll
     for (int c = 0; c < DPW; ++c) {
-      int64_t pos = tb + srow[c];
-      pos = pos < end ? pos : end - 1;
+      const int sl = (wave * DPW + c) * 64 + lane;
+      const int srow = sl / kCpr16;
+      const int scol = ((sl - srow * kCpr16) ^ (srow & 7)) * 8;
+      const uint32_t off = (uint32_t)min(srow, last) * row_bytes + (uint32_t)(scol * 2);
       const uint32_t dst = lds0 + (uint32_t)((bi * TILE + (wave * DPW + c) * 64 * 8) * 2);
-      dma16(cbase + pos * a.stride_pos + scol[c], __builtin_amdgcn_readfirstlane(dst));
+      dma16s(off, tbase, __builtin_amdgcn_readfirstlane(dst));
     }
   };
 
-  // Query rows of this head block as MFMA A operands: lane holds head
-  // hb*16 + l16, columns 288*dh + 32*ks + 8*lq .. +7 (rounded to f16 once).
+  // Query rows of this head block as B operands: lane holds head hb*16 + l16,
+  // columns 288*dh + 32*ks + 8*lq .. +7 (rounded to f16 once).
   half8_t qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
@@ -502,135 +524,131 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
     for (int e = 0; e < 8; ++e)
       qf[ks][e] = (_Float16)qb[(hb * 16 + l16) * kLatDk + dh * KH + ks * 32 + lq * 8 + e];
 
-  // Running state of heads hb*16 + 4*lq + e (replicated over the 16 lanes of
-  // a row group): max m (base 2) and normaliser l; output accumulators for
-  // columns 256*dh + 16*cb + l16.
-  float m[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    m[e] = -INFINITY;
-    l[e] = 0.0f;
-  }
+  // Running max (base 2) and normaliser of head hb*16 + l16 (replicated over
+  // the quarters); output accumulators: heads 4*lq + e (items), columns
+  // 256*dh + 16*cb + l16.
+  float m = -INFINITY, l = 0.0f;
   float4_t acc[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  issue_tile(0, start);
-  issue_tile(1, start + kT16);
-  wait_vm_lgkm0<DPW>();
-  raw_barrier();
-
-  // Per-lane LDS offsets (halves) inside a tile buffer. The XOR swizzle only
-  // touches the low 3 bits of a chunk index, so every operand address is one
-  // of a few per-lane bases plus a compile-time offset:
-  //  * scores, rows l16 (+16 for the second block), chunk c0 + 4*ks:
-  //    base for even ks + 32*ks/2... i.e. bs[ks & 1] + 64*(ks >> 1) halves;
-  //  * transpose reads, rows r0 and r0 + 4, chunk 32*dh + 2*cb + (l16&3)/2:
-  //    bv[row][cb & 3] + 64*(cb >> 2) halves (+4 halves when l16 is odd).
+  // Per-lane LDS offsets (halves) inside a tile buffer.
+  //  * score reads, rows l16 (+16 for the second block), logical chunk
+  //    36*dh + lq + 4*ks: sb[ks & 1] + 32*ks (+ 16 rows);
+  //  * transpose reads, rows 4*lq + l16/4 (+16), logical chunk
+  //    32*dh + 2*cb + (l16&3)/2: bv[cb & 3] + 64*(cb >> 2) (+ 16 rows), plus
+  //    4 halves for odd l16.
   const int c0 = dh * 36 + lq;
   const int sw = l16 & 7;
-  const int bs0 = l16 * kLatDk + ((c0 ^ sw) << 3);
-  const int bs1 = l16 * kLatDk + (((c0 + 4) ^ sw) << 3) - 32;
-  const int r0 = lq * 8 + (l16 >> 2);
+  const int sb0 = l16 * kLatDk + ((c0 ^ sw) << 3);
+  const int sb1 = l16 * kLatDk + (((c0 + 4) ^ sw) << 3) - 32;
+  const int r0 = 4 * lq + (l16 >> 2);
   const int jv = (l16 & 3) >> 1;
   const int hoff = (l16 & 1) * 4;
-  int bv[2][4];
+  int bv[4];
 #pragma unroll
-  for (int rr = 0; rr < 2; ++rr)
+  for (int u = 0; u < 4; ++u) bv[u] = r0 * kLatDk + ((dh * 32 + ((2 * u + jv) ^ (r0 & 7))) << 3) + hoff;
+  constexpr int kRow16 = 16 * kLatDk;  // 16 rows further down (same swizzle)
+
+  const int ntiles = (int)((end - start + kT16 - 1) / kT16);
+  issue_tile(0, start);
+  issue_tile(1, start + kT16);
+  wait_vm_lgkm0<0>();  // both tiles (and anything issued before them) landed
+  raw_barrier();
+
+  half8_t pp = half8_t{};  // weights of the previous tile (A operand)
+  float alp = 1.0f;        // its rescale factor, head hb*16 + l16
+  bool movedp = false;
+  for (int i = 0;; ++i) {
+    // ---- output of tile i-1: acc = alp * acc + P x V ----
+    if (i > 0) {
+      const _Float16* prv = s_c + ((i - 1) % 3) * TILE;
+      if (__any(movedp)) {
+        // Accumulator item e is head 4*lq + e, whose factor lane 4*lq + e holds.
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int row = r0 + rr * 4;
-      bv[rr][u] = row * kLatDk + ((dh * 32 + ((2 * u + jv) ^ (row & 7))) << 3) + hoff;
+        for (int e = 0; e < 4; ++e) {
+          const float ae = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * lq + e) << 2, __float_as_int(alp)));
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) acc[cb][e] *= ae;
+        }
+      }
+      auto vread = [&](int cb) {
+        const _Float16* vp = prv + bv[cb & 3] + 64 * (cb >> 2);
+        const half4_t v0 = lds_read_tr(vp);
+        const half4_t v1 = lds_read_tr(vp + kRow16);
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      half8_t vn = vread(0);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const half8_t vb = vn;
+        if (cb + 1 < NCB) vn = vread(cb + 1);
+        acc[cb] = mfma32(pp, vb, acc[cb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    if (i == ntiles) break;
+    const int64_t tb = start + (int64_t)i * kT16;
+    const int rel = (int)(end - tb);  // positions of this tile before the end (> 0)
+    const _Float16* cur = s_c + (i % 3) * TILE;
 
-  int cur_i = 0;
-  for (int64_t tb = start; tb < end; tb += kT16) {
-    const _Float16* cur = s_c + cur_i * TILE;
-    const int dma_i = cur_i == 0 ? 2 : cur_i - 1;  // (cur + 2) mod 3
-
-    // ---- partial scores over this wave's 288 columns, both 16-position blocks ----
-    // Operands are read one MFMA step ahead; the scheduling barriers keep the
-    // compiler from hoisting every read (and its registers) to the front.
+    // ---- partial scores S^T over this wave's 288 columns, both blocks ----
     float4_t sp0 = float4_t{0.f, 0.f, 0.f, 0.f}, sp1 = sp0;
-    const _Float16* sb0 = cur + bs0;
-    const _Float16* sb1 = cur + bs1;
-    auto bread = [&](int ks, int row_add) {
-      const _Float16* bp = (ks & 1) ? sb1 : sb0;
-      return *reinterpret_cast<const half8_t*>(bp + row_add * kLatDk + 32 * ks);
+    const _Float16* sbp0 = cur + sb0;
+    const _Float16* sbp1 = cur + sb1;
+    auto bread = [&](int ks, int rows) {
+      const _Float16* bp = (ks & 1) ? sbp1 : sbp0;
+      return *reinterpret_cast<const half8_t*>(bp + rows + 32 * ks);
     };
-    half8_t n0 = bread(0, 0), n1 = bread(0, 16);
+    half8_t n0 = bread(0, 0), n1 = bread(0, kRow16);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const half8_t b0 = n0, b1 = n1;
       if (ks + 1 < KS) {
         n0 = bread(ks + 1, 0);
-        n1 = bread(ks + 1, 16);
+        n1 = bread(ks + 1, kRow16);
       }
-      sp0 = mfma32(qf[ks], b0, sp0);
-      sp1 = mfma32(qf[ks], b1, sp1);
+      sp0 = mfma32(b0, qf[ks], sp0);
+      sp1 = mfma32(b1, qf[ks], sp1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    s_sx[wave][0][lane] = sp0;
-    s_sx[wave][1][lane] = sp1;
-    wait_vm_lgkm0<63>();
+    const int par = i & 1;
+    s_sx[par][wave][0][lane] = sp0;
+    s_sx[par][wave][1][lane] = sp1;
+    // Tile i+1 (requested one iteration ago, or in the prologue) is the only
+    // tile load still in flight: wait for it, then publish it and the partials.
+    wait_vm_lgkm0<0>();
     raw_barrier();
 
-    // ---- full scores (own + partner), online softmax over 32 positions ----
-    // D layout: lane holds heads 4*lq + e at positions l16 and 16 + l16.
-    const float4_t q0 = s_sx[wave ^ 1][0][lane];
-    const float4_t q1 = s_sx[wave ^ 1][1][lane];
-    const bool ok0 = tb + l16 < end;
-    const bool ok1 = tb + 16 + l16 < end;
-    float al[4];
-    bool all_one = true;
+    // ---- full scores (own + partner), online softmax over the 32 positions ----
+    const float4_t q0 = s_sx[par][wave ^ 1][0][lane];
+    const float4_t q1 = s_sx[par][wave ^ 1][1][lane];
+    float v[8];
+    float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float v0 = ok0 ? (sp0[e] + q0[e]) * a.qscale : -INFINITY;
-      const float v1 = ok1 ? (sp1[e] + q1[e]) * a.qscale : -INFINITY;
-      float x = fmaxf(v0, v1);
-      x = fmaxf(x, dpp<kDppRowRor8>(x));
-      x = fmaxf(x, dpp<kDppRowRor4>(x));
-      x = fmaxf(x, dpp<kDppQuadXor2>(x));
-      x = fmaxf(x, dpp<kDppQuadXor1>(x));
-      const float mn = fmaxf(m[e], x);
-      const float mu = (mn == -INFINITY) ? 0.0f : mn;
-      al[e] = fast_exp2(m[e] - mu);
-      all_one = all_one && al[e] == 1.0f;
-      const _Float16 p0 = (_Float16)fast_exp2(v0 - mu);
-      const _Float16 p1 = (_Float16)fast_exp2(v1 - mu);
-      l[e] = fmaf(l[e], al[e], row16_sum((float)p0 + (float)p1));
-      m[e] = mn;
-      // Each wave of the pair stores one of the two position blocks.
-      s_p[(hb * 16 + lq * 4 + e) * kProw16 + dh * 16 + l16] = dh ? p1 : p0;
+      v[e] = 4 * lq + e < rel ? (sp0[e] + q0[e]) * a.qscale : -INFINITY;
+      v[4 + e] = 16 + 4 * lq + e < rel ? (sp1[e] + q1[e]) * a.qscale : -INFINITY;
+      mx = fmaxf(mx, fmaxf(v[e], v[4 + e]));
     }
-    issue_tile(dma_i, tb + 2 * kT16);
-    // The next tile was issued a step ago; only this step's DPW loads may
-    // still be in flight.
-    wait_vm_lgkm0<DPW>();
-    raw_barrier();
-
-    // ---- output: acc = al * acc + P[16 heads][32 positions] x V ----
-    if (!__all(all_one)) {
+    mx = fmaxf(mx, xor16(mx));
+    mx = fmaxf(mx, xor32(mx));
+    const float mn = fmaxf(m, mx);
+    const float mu = (mn == -INFINITY) ? 0.0f : mn;
+    alp = fast_exp2(m - mu);
+    movedp = alp != 1.0f;
+    float ls = 0.0f;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[cb][e] *= al[e];
+    for (int j = 0; j < 8; ++j) {
+      const _Float16 pj = (_Float16)fast_exp2(v[j] - mu);
+      pp[j] = pj;
+      ls += (float)pj;
     }
-    const half8_t pa = *reinterpret_cast<const half8_t*>(&s_p[(hb * 16 + l16) * kProw16 + lq * 8]);
-    auto vread = [&](int cb) {
-      const half4_t v0 = lds_read_tr(cur + bv[0][cb & 3] + 64 * (cb >> 2));
-      const half4_t v1 = lds_read_tr(cur + bv[1][cb & 3] + 64 * (cb >> 2));
-      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    half8_t vn = vread(0);
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const half8_t vb = vn;
-      if (cb + 1 < NCB) vn = vread(cb + 1);
-      acc[cb] = mfma32(pa, vb, acc[cb]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    cur_i = cur_i == 2 ? 0 : cur_i + 1;
+    ls += xor16(ls);
+    ls += xor32(ls);
+    l = fmaf(l, alp, ls);
+    m = mn;
+    issue_tile((i + 2) % 3, tb + 2 * kT16);
   }
   // Drain the tile loads still in flight before the workgroup can retire.
   wait_vm_lgkm0<0>();
@@ -644,17 +662,9 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
       const int col = dh * 256 + cb * 16 + l16;
       a.ws_acc[(ws0 + (int64_t)head * a.S) * kLatDv + col] = acc[cb][e];
     }
-  if (dh == 0 && l16 < 4) {
-    float mm = m[0], ll = l[0];
-#pragma unroll
-    for (int e = 1; e < 4; ++e)
-      if (l16 == e) {
-        mm = m[e];
-        ll = l[e];
-      }
-    const int head = hb * 16 + lq * 4 + l16;
-    a.ws_m[ws0 + (int64_t)head * a.S] = mm * kLn2;
-    a.ws_l[ws0 + (int64_t)head * a.S] = ll;
+  if (dh == 0 && lq == 0) {
+    a.ws_m[ws0 + (int64_t)(hb * 16 + l16) * a.S] = m * kLn2;
+    a.ws_l[ws0 + (int64_t)(hb * 16 + l16) * a.S] = l;
   }
 }
 
