@@ -417,7 +417,6 @@ __device__ __forceinline__ void raw_barrier() {
 
 constexpr int kT16 = 32;     // positions per tile
 constexpr int kCpr16 = kLatDk / 8;   // 72 chunks of 16 bytes per cache row
-constexpr int kProw16 = 40;  // LDS row stride of P (halves; rows stay 16-byte aligned)
 
 // LDS offset (halves) of logical chunk cc of tile row r.
 __device__ __forceinline__ int tile_off(int r, int cc) { return r * kLatDk + ((cc ^ (r & 7)) << 3); }
@@ -723,7 +722,7 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   constexpr int TSTRIDE = DPW * NT * 4;            // floats per tile buffer (padded slots included)
 
   __shared__ __align__(16) float s_c[3 * TSTRIDE];
-  __shared__ __align__(16) float4_t s_sx[NW][64];
+  __shared__ __align__(16) float4_t s_sx[2][NW][64];
 
   const int split = blockIdx.x;
   const int b = blockIdx.y;
@@ -812,15 +811,49 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
     vb[v] = r * kLatDk + ((32 * dq + (l16 ^ r)) << 2);
   }
 
+  const int ntiles = (int)((end - start + kT32 - 1) / kT32);
   issue_tile(0, start);
   issue_tile(1, start + kT32);
-  wait_vm_lgkm0<DPW>();
+  wait_vm_lgkm0<0>();  // both tiles (and anything issued before them) landed
   raw_barrier();
 
-  int cur_i = 0;
-  for (int64_t tb = start; tb < end; tb += kT32) {
-    const float* cur = s_c + cur_i * TSTRIDE;
-    const int dma_i = cur_i == 0 ? 2 : cur_i - 1;  // (cur + 2) mod 3
+  // Software pipeline: iteration i computes the output product of tile i-1
+  // (weights pp from the previous softmax) and the partial scores of tile i;
+  // one barrier then publishes the partials (double-buffered by parity) and
+  // tile i+1; after it the softmax of tile i runs and tile i+2 is requested
+  // into the buffer tile i-1 used.
+  float pp[4] = {0.f, 0.f, 0.f, 0.f};
+  float alp = 1.0f;
+  bool movedp = false;
+  for (int i = 0;; ++i) {
+    // ---- output of tile i-1: acc = alp * acc + P[16 heads][16 positions] x V ----
+    if (i > 0) {
+      const float* prv = s_c + ((i - 1) % 3) * TSTRIDE;
+      if (__any(movedp)) {
+        // Accumulator item e is head 4*lq + e, whose factor lane 4*lq + e holds.
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ae = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * lq + e) << 2, __float_as_int(alp)));
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[c][e] *= ae;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float4_t v4 = *reinterpret_cast<const float4_t*>(prv + vb[t] + 64 * u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[4 * u + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(pp[t], v4[e], acc[4 * u + e], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (i == ntiles) break;
+    const int64_t tb = start + (int64_t)i * kT32;
+    const int rel = (int)(end - tb);  // positions of this tile before the end (> 0)
+    const float* cur = s_c + (i % 3) * TSTRIDE;
 
     // ---- partial scores S^T over this wave's 144 columns ----
     float4_t sp = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -833,64 +866,39 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
       for (int u = 0; u < 4; ++u) sp = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], qv[t][u], sp, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    s_sx[wave][lane] = sp;
-    wait_vm_lgkm0<63>();
+    const int par = i & 1;
+    s_sx[par][wave][lane] = sp;
+    // Tile i+1 (requested one iteration ago, or in the prologue) is the only
+    // tile load still in flight: wait for it, then publish it and the partials.
+    wait_vm_lgkm0<0>();
     raw_barrier();
 
     // ---- full scores (the block's four partials in a fixed order), softmax ----
-    const float4_t x0 = s_sx[hb * 4 + 0][lane], x1 = s_sx[hb * 4 + 1][lane];
-    const float4_t x2 = s_sx[hb * 4 + 2][lane], x3 = s_sx[hb * 4 + 3][lane];
-    float p[4];
+    const float4_t x0 = s_sx[par][hb * 4 + 0][lane], x1 = s_sx[par][hb * 4 + 1][lane];
+    const float4_t x2 = s_sx[par][hb * 4 + 2][lane], x3 = s_sx[par][hb * 4 + 3][lane];
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = tb + 4 * lq + i < end;
-      p[i] = ok ? (x0[i] + x1[i]) + (x2[i] + x3[i]) : -INFINITY;
-      mx = fmaxf(mx, p[i]);
+    for (int e = 0; e < 4; ++e) {
+      pp[e] = 4 * lq + e < rel ? (x0[e] + x1[e]) + (x2[e] + x3[e]) : -INFINITY;
+      mx = fmaxf(mx, pp[e]);
     }
     mx = fmaxf(mx, xor16(mx));
     mx = fmaxf(mx, xor32(mx));
     const float mn = fmaxf(m, mx);
     const float mu = (mn == -INFINITY) ? 0.0f : mn;
-    const float al = fast_exp2(m - mu);
+    alp = fast_exp2(m - mu);
+    movedp = alp != 1.0f;
     float ls = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = fast_exp2(p[i] - mu);
-      ls += p[i];
+    for (int e = 0; e < 4; ++e) {
+      pp[e] = fast_exp2(pp[e] - mu);
+      ls += pp[e];
     }
     ls += xor16(ls);
     ls += xor32(ls);
-    l = fmaf(l, al, ls);
+    l = fmaf(l, alp, ls);
     m = mn;
-    const bool moved = al != 1.0f;
-
-    issue_tile(dma_i, tb + 2 * kT32);
-    wait_vm_lgkm0<DPW>();
-    raw_barrier();
-
-    // ---- output: acc = al * acc + P[16 heads][16 positions] x V ----
-    if (__any(moved)) {
-      // Accumulator item i is head 4*lq + i, whose factor lane 4*lq + i holds.
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * lq + i) << 2, __float_as_int(al)));
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c][i] *= ai;
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float4_t v4 = *reinterpret_cast<const float4_t*>(cur + vb[t] + 64 * u);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[4 * u + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[t], v4[e], acc[4 * u + e], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    cur_i = cur_i == 2 ? 0 : cur_i + 1;
+    issue_tile((i + 2) % 3, tb + 2 * kT32);
   }
   // Drain the tile loads still in flight before the workgroup can retire.
   wait_vm_lgkm0<0>();
