@@ -91,7 +91,8 @@ def parse():
     ap.add_argument("--n-splits", type=int, default=0, help="0 = the library's heuristic")
     ap.add_argument("--no-rungs", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rung-steps", type=int, default=20)
+    ap.add_argument("--rung-steps", type=int, default=30)
+    ap.add_argument("--rung-warmup", type=int, default=10)
     ap.add_argument("--only", choices=sorted(ONLY), default=None,
                     help="time one named workload (prints its dict, no JSON line); for profiling")
     return ap.parse_args()
@@ -358,7 +359,7 @@ def main():
         for mk in specs:
             c = mk()
             small = c.kv_bytes() < MALL_FLUSH_BYTES  # could stay cached between calls
-            r, _, _ = measure(c, args.rung_steps, 5, 0, flush if small else None)
+            r, _, _ = measure(c, args.rung_steps, args.rung_warmup, 0, flush if small else None)
             log(f"rung {r}")
             rungs.append(r)
             del c

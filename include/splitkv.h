@@ -133,7 +133,7 @@ typedef struct {
  *   GQA:    chunk = max(64, ceil(Hkv * total_tokens / (k * cu_count))), where k is the
  *           number of workgroups per compute unit measured best on MI355X: 1 (one
  *           round of one workgroup per compute unit), 2 for the f16 6-head group
- *           of width 256, and 4 times that for a ragged batch (total_tokens <
+ *           of width 256, and 8 times that for a ragged batch (total_tokens <
  *           batch * max_seq_len). The note's own S_target is about 4 per
  *           multiprocessor of its GPU.
  *   latent: chunk = max(64, ceil(g * total_tokens / cu_count)) with g workgroups per

@@ -42,7 +42,7 @@ constexpr int32_t kChunkGranule = 64;
 // Ragged batches (total_tokens < batch * max_seq_len) plan this many times
 // more workgroups: their slices differ in length, and more, shorter blocks
 // balance the compute units.
-constexpr int32_t kRaggedBlockFactor = 4;
+constexpr int32_t kRaggedBlockFactor = 8;
 constexpr int32_t kMaxGridYZ = 65535;
 // Largest step between consecutive positions of a contiguous cache: a split
 // kernel tile (at most 64 rows) is addressed with 32-bit byte offsets.

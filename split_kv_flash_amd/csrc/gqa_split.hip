@@ -52,8 +52,12 @@ struct GqaArgs {
   int32_t q_dtype;
   int32_t Hq, S, chunk, cap;
   int32_t page_shift, max_pages;
+  int32_t paged_fast;  // page size, tile span and split chunk line up (see the tile loop)
   float qscale;
 };
+
+// Addressing modes of the tile loop.
+constexpr int kContig = 0, kPagedFast = 1, kPagedAny = 2;
 
 template <typename KV, int D, int RL_, int R_, int HS_>
 struct GqaShape {
@@ -176,174 +180,231 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 #pragma unroll
   for (int r = 0; r < R; ++r) loff[r] = (uint32_t)(r * NG + grp) * row_bytes + (uint32_t)(lane_col * sizeof(KV));
 
-  // Paged rows past `end` read row end-1 instead (in bounds, a cache hit):
-  // their scores are masked to -inf.
-  auto table_page = [&](int64_t pos) -> int {
-    return table[pos >> a.page_shift];
-  };
-  int64_t last_off = 0;
-  if constexpr (PAGED) {
-    int pg = table_page(end - 1);
-    pg = (pg < 0 || (int64_t)pg >= a.num_pages) ? 0 : pg;
-    last_off = (((int64_t)pg << a.page_shift) + ((end - 1) & ps_mask)) * row_stride;
-  }
+  // The tile loop, instantiated per addressing mode:
+  //  * kContig: one buffer resource per tile (rows before `end` only);
+  //  * kPagedFast: every row set r of a tile (rows r*NG + group) lies in one
+  //    page, the same for the whole workgroup (the host guarantees that page
+  //    size, tile span and split chunk line up), so its page index is one
+  //    scalar table load and its rows are one buffer resource covering the
+  //    page's rows before `end`; lane offsets are loop-invariant;
+  //  * kPagedAny: per-lane page lookups, rows past `end` re-read row end-1.
+  const uint32_t lofp = (uint32_t)grp * row_bytes + (uint32_t)(lane_col * sizeof(KV));
+  auto run = [&](auto mode_tag) {
+    constexpr int MODE = decltype(mode_tag)::value;
 
-  // Page indices for the R rows of a tile (paged layout only). Rows past the
-  // end look up row end-1's page, so the table is never read out of range.
-  auto load_pages = [&](int (&pg)[R], int64_t tb) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t pos = tb + r * NG + grp;
-      pg[r] = table_page(pos < end ? pos : end - 1);
+    // kPagedAny: rows past `end` read row end-1 instead (in bounds, a cache
+    // hit); their scores are masked to -inf.
+    auto table_page = [&](int64_t pos) -> int {
+      return table[pos >> a.page_shift];
+    };
+    int64_t last_off = 0;
+    if constexpr (MODE == kPagedAny) {
+      int pg = table_page(end - 1);
+      pg = (pg < 0 || (int64_t)pg >= a.num_pages) ? 0 : pg;
+      last_off = (((int64_t)pg << a.page_shift) + ((end - 1) & ps_mask)) * row_stride;
     }
-  };
 
-  auto issue = [&](V (&kt)[R][NL], V (&vt)[R][NL], int64_t tb, const int (&pg)[R]) {
-    if constexpr (PAGED) {
+    // Page indices of a tile. kPagedAny: per lane, one per row (rows past the
+    // end look up row end-1's page). kPagedFast: one per row set, uniform.
+    // The table is never read out of range.
+    auto load_pages = [&](int (&pg)[R], int64_t tb) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int64_t pos = tb + r * NG + grp;
-        const int p = (pg[r] < 0 || (int64_t)pg[r] >= a.num_pages) ? 0 : pg[r];
-        int64_t off = (((int64_t)p << a.page_shift) + (pos & ps_mask)) * row_stride;
-        off = pos < end ? off : last_off;
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-          kt[r][j] = load_vec<KV, VEC>(kb + off + j * RL * VEC);
-          vt[r][j] = load_vec<KV, VEC>(vb + off + j * RL * VEC);
+        if constexpr (MODE == kPagedFast) {
+          const int64_t pos0 = tb + r * NG;
+          pg[r] = __builtin_amdgcn_readfirstlane(table_page(pos0 < end ? pos0 : end - 1));
+        } else {
+          const int64_t pos = tb + r * NG + grp;
+          pg[r] = table_page(pos < end ? pos : end - 1);
         }
       }
-    } else {
-      // One buffer resource per tile, based at the tile's first row and
-      // covering the rows before `end`: rows past it (the last tile's tail, or
-      // a whole tile past the end) read as zero without a memory access, and
-      // the lane offsets stay loop-invariant.
-      const int64_t left = end - tb;
-      const uint32_t nbytes = left <= 0 ? 0u : (uint32_t)(left < TR ? left : TR) * row_bytes;
-      const auto rk = raw_rsrc(kh + tb * row_stride, nbytes);
-      const auto rv = raw_rsrc(vh + tb * row_stride, nbytes);
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-          const uint32_t o = loff[r] + (uint32_t)(j * RL * VEC * sizeof(KV));
-          kt[r][j] = load_vec_buf<KV, VEC>(rk, o);
-          vt[r][j] = load_vec_buf<KV, VEC>(rv, o);
-        }
-    }
-  };
+    };
 
-  auto compute = [&](const V (&kt)[R][NL], const V (&vt)[R][NL], int64_t tb, const int (&pg)[R]) {
-    float s[GH][R];
+    auto issue = [&](V (&kt)[R][NL], V (&vt)[R][NL], int64_t tb, const int (&pg)[R]) {
+      if constexpr (MODE == kPagedAny) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+        for (int r = 0; r < R; ++r) {
+          const int64_t pos = tb + r * NG + grp;
+          const int p = (pg[r] < 0 || (int64_t)pg[r] >= a.num_pages) ? 0 : pg[r];
+          int64_t off = (((int64_t)p << a.page_shift) + (pos & ps_mask)) * row_stride;
+          off = pos < end ? off : last_off;
+#pragma unroll
+          for (int j = 0; j < NL; ++j) {
+            kt[r][j] = load_vec<KV, VEC>(kb + off + j * RL * VEC);
+            vt[r][j] = load_vec<KV, VEC>(vb + off + j * RL * VEC);
+          }
+        }
+      } else if constexpr (MODE == kPagedFast) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int64_t pos0 = tb + r * NG;
+          const int64_t left = end - pos0;
+          const bool bad = pg[r] < 0 || (int64_t)pg[r] >= a.num_pages;
+          const uint32_t nbytes =
+              (bad || left <= 0) ? 0u : (uint32_t)(left < NG ? left : NG) * row_bytes;
+          const int64_t row0 = ((int64_t)(bad ? 0 : pg[r]) << a.page_shift) + (pos0 & ps_mask);
+          const auto rk = raw_rsrc(kh + row0 * row_stride, nbytes);
+          const auto rv = raw_rsrc(vh + row0 * row_stride, nbytes);
+#pragma unroll
+          for (int j = 0; j < NL; ++j) {
+            const uint32_t o = lofp + (uint32_t)(j * RL * VEC * sizeof(KV));
+            kt[r][j] = load_vec_buf<KV, VEC>(rk, o);
+            vt[r][j] = load_vec_buf<KV, VEC>(rv, o);
+          }
+        }
+      } else {
+        // One buffer resource per tile, based at the tile's first row and
+        // covering the rows before `end`: rows past it (the last tile's tail,
+        // or a whole tile past the end) read as zero without a memory access,
+        // and the lane offsets stay loop-invariant.
+        const int64_t left = end - tb;
+        const uint32_t nbytes = left <= 0 ? 0u : (uint32_t)(left < TR ? left : TR) * row_bytes;
+        const auto rk = raw_rsrc(kh + tb * row_stride, nbytes);
+        const auto rv = raw_rsrc(vh + tb * row_stride, nbytes);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int j = 0; j < NL; ++j) {
+            const uint32_t o = loff[r] + (uint32_t)(j * RL * VEC * sizeof(KV));
+            kt[r][j] = load_vec_buf<KV, VEC>(rk, o);
+            vt[r][j] = load_vec_buf<KV, VEC>(rv, o);
+          }
+      }
+    };
+
+    auto compute = [&](const V (&kt)[R][NL], const V (&vt)[R][NL], int64_t tb, const int (&pg)[R]) {
+      float s[GH][R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int h = 0; h < GH; ++h) {
+          float p = 0.0f;
+#pragma unroll
+          for (int j = 0; j < NL; ++j)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) p = fmaf(qr[h][j * VEC + e], to_f32(kt[r][j].v[e]), p);
+          s[h][r] = row_sum<RL>(p);
+        }
+      }
+      if constexpr (MODE == kPagedAny) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const bool ok = tb + r * NG + grp < end;
+          const bool bad = pg[r] < 0 || (int64_t)pg[r] >= a.num_pages;
+#pragma unroll
+          for (int h = 0; h < GH; ++h) s[h][r] = ok ? (bad ? __builtin_nanf("") : s[h][r]) : -INFINITY;
+        }
+      } else {
+        // Rows past `end` (last tile only) are masked; a row set whose page
+        // entry is invalid poisons its rows with NaN (paged only).
+        bool anybad = false;
+        if constexpr (MODE == kPagedFast) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) anybad |= pg[r] < 0 || (int64_t)pg[r] >= a.num_pages;
+        }
+        if (tb + TR > end || anybad) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const bool ok = tb + r * NG + grp < end;
+            bool bad = false;
+            if constexpr (MODE == kPagedFast) bad = pg[r] < 0 || (int64_t)pg[r] >= a.num_pages;
+#pragma unroll
+            for (int h = 0; h < GH; ++h) s[h][r] = ok ? (bad ? __builtin_nanf("") : s[h][r]) : -INFINITY;
+          }
+        }
+      }
+      // Running max per head. The accumulators and l are rescaled only when
+      // some head's max moved somewhere in the wave (otherwise the factor is
+      // exp2(0) = 1).
+      float mn[GH];
+      bool moved = false;
 #pragma unroll
       for (int h = 0; h < GH; ++h) {
-        float p = 0.0f;
+        float mt = s[h][0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) mt = fmaxf(mt, s[h][r]);
+        mn[h] = fmaxf(m[h], mt);
+        moved |= mn[h] != m[h];
+      }
+      if (__any(moved)) {
+#pragma unroll
+        for (int h = 0; h < GH; ++h) {
+          const float al = fast_exp2(m[h] - ((mn[h] == -INFINITY) ? 0.0f : mn[h]));
+          l[h] *= al;
+#pragma unroll
+          for (int d = 0; d < DPL; ++d) acc[h][d] *= al;
+          m[h] = mn[h];
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < GH; ++h) {
+        const float mu = (m[h] == -INFINITY) ? 0.0f : m[h];
+        float p[R];
+        float ls = 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          p[r] = fast_exp2(s[h][r] - mu);
+          ls += p[r];
+        }
+        l[h] += ls;
 #pragma unroll
         for (int j = 0; j < NL; ++j)
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) p = fmaf(qr[h][j * VEC + e], to_f32(kt[r][j].v[e]), p);
-        s[h][r] = row_sum<RL>(p);
+          for (int e = 0; e < VEC; ++e) {
+            float t = acc[h][j * VEC + e];
+#pragma unroll
+            for (int r = 0; r < R; ++r) t = fmaf(p[r], to_f32(vt[r][j].v[e]), t);
+            acc[h][j * VEC + e] = t;
+          }
       }
-    }
-    if constexpr (PAGED) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const bool ok = tb + r * NG + grp < end;
-        const bool bad = pg[r] < 0 || (int64_t)pg[r] >= a.num_pages;
-#pragma unroll
-        for (int h = 0; h < GH; ++h) s[h][r] = ok ? (bad ? __builtin_nanf("") : s[h][r]) : -INFINITY;
-      }
-    } else if (tb + TR > end) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const bool ok = tb + r * NG + grp < end;
-#pragma unroll
-        for (int h = 0; h < GH; ++h) s[h][r] = ok ? s[h][r] : -INFINITY;
-      }
-    }
-    // Running max per head. The accumulators and l are rescaled only when some
-    // head's max moved somewhere in the wave (otherwise the factor is exp2(0) = 1).
-    float mn[GH];
-    bool moved = false;
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      float mt = s[h][0];
-#pragma unroll
-      for (int r = 1; r < R; ++r) mt = fmaxf(mt, s[h][r]);
-      mn[h] = fmaxf(m[h], mt);
-      moved |= mn[h] != m[h];
-    }
-    if (__any(moved)) {
-#pragma unroll
-      for (int h = 0; h < GH; ++h) {
-        const float al = fast_exp2(m[h] - ((mn[h] == -INFINITY) ? 0.0f : mn[h]));
-        l[h] *= al;
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) acc[h][d] *= al;
-        m[h] = mn[h];
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      const float mu = (m[h] == -INFINITY) ? 0.0f : m[h];
-      float p[R];
-      float ls = 0.0f;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        p[r] = fast_exp2(s[h][r] - mu);
-        ls += p[r];
-      }
-      l[h] += ls;
-#pragma unroll
-      for (int j = 0; j < NL; ++j)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          float t = acc[h][j * VEC + e];
-#pragma unroll
-          for (int r = 0; r < R; ++r) t = fmaf(p[r], to_f32(vt[r][j].v[e]), t);
-          acc[h][j * VEC + e] = t;
-        }
-    }
-  };
+    };
 
-  // Software pipeline: the loads of tile t+1 are issued before tile t's
-  // arithmetic, so every wave keeps a tile of K/V in flight while it computes.
-  // With paging, page indices run one tile further ahead (pc: this tile,
-  // pn: next, pnn: the one after), so a table read never waits behind K/V
-  // loads. Contiguous: the tile after the last one reads nothing (its
-  // resource is empty); paged: it re-reads row end-1 (a cache hit).
-  V kA[R][NL], vA[R][NL], kB[R][NL], vB[R][NL];
-  int pc[R], pn[R], pnn[R];
+    // Software pipeline: the loads of tile t+1 are issued before tile t's
+    // arithmetic, so every wave keeps a tile of K/V in flight while it
+    // computes. With paging, page indices run one tile further ahead (pc: this
+    // tile, pn: next, pnn: the one after), so a table read never waits behind
+    // K/V loads. The tile after the last one reads nothing (contiguous, fast
+    // paged: its resources are empty) or re-reads row end-1 (a cache hit).
+    V kA[R][NL], vA[R][NL], kB[R][NL], vB[R][NL];
+    int pc[R], pn[R], pnn[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) pc[r] = pn[r] = pnn[r] = 0;
-  if constexpr (PAGED) {
-    load_pages(pc, start);
-    load_pages(pn, start + TR);
-  }
-  issue(kA, vA, start, pc);
-  auto rotate = [&]() {
+    for (int r = 0; r < R; ++r) pc[r] = pn[r] = pnn[r] = 0;
+    if constexpr (MODE != kContig) {
+      load_pages(pc, start);
+      load_pages(pn, start + TR);
+    }
+    issue(kA, vA, start, pc);
+    auto rotate = [&]() {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      pc[r] = pn[r];
-      pn[r] = pnn[r];
+      for (int r = 0; r < R; ++r) {
+        pc[r] = pn[r];
+        pn[r] = pnn[r];
+      }
+    };
+    for (int64_t tb = start;;) {
+      if constexpr (MODE != kContig) load_pages(pnn, tb + 2 * TR);
+      issue(kB, vB, tb + TR, pn);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(kA, vA, tb, pc);
+      tb += TR;
+      if (tb >= end) break;
+      if constexpr (MODE != kContig) rotate();
+      if constexpr (MODE != kContig) load_pages(pnn, tb + 2 * TR);
+      issue(kA, vA, tb + TR, pn);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(kB, vB, tb, pc);
+      tb += TR;
+      if (tb >= end) break;
+      if constexpr (MODE != kContig) rotate();
     }
   };
-  for (int64_t tb = start;;) {
-    if constexpr (PAGED) load_pages(pnn, tb + 2 * TR);
-    issue(kB, vB, tb + TR, pn);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(kA, vA, tb, pc);
-    tb += TR;
-    if (tb >= end) break;
-    if constexpr (PAGED) rotate();
-    if constexpr (PAGED) load_pages(pnn, tb + 2 * TR);
-    issue(kA, vA, tb + TR, pn);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(kB, vB, tb, pc);
-    tb += TR;
-    if (tb >= end) break;
-    if constexpr (PAGED) rotate();
+  if constexpr (!PAGED) {
+    run(std::integral_constant<int, kContig>{});
+  } else {
+    if (a.paged_fast)
+      run(std::integral_constant<int, kPagedFast>{});
+    else
+      run(std::integral_constant<int, kPagedAny>{});
   }
 
   // Merge the row groups of each wave, then the waves through LDS.
@@ -453,6 +514,13 @@ static sk_status_t launch_variant(const SplitLaunch& s, bool launch, const void*
     while ((1 << a.page_shift) < d.page_size) ++a.page_shift;
   }
   a.max_pages = d.max_pages_per_seq;
+  {
+    using Sh = GqaShape<KV, D, T::RL, T::R, T::HS>;
+    constexpr int NG = Sh::kGroups;
+    constexpr int TR = NG * T::R;
+    const int P = d.page_size;
+    a.paged_fast = PAGED && P % NG == 0 && TR % P == 0 && s.p->chunk % P == 0;
+  }
   a.qscale = d.scale * kLog2e;
   hipLaunchKernelGGL(kern, gr, dim3(256), 0, s.stream, a);
   return SK_OK;
