@@ -464,14 +464,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 // which halves its per-lane reductions and exponentials.
 constexpr bool sliced_variant(bool f16, int D, int G) { return f16 && D == 256 && G == 6; }
 
-template <typename KV, int G, int D>
+template <typename KV, int G, int D, bool PAGED>
 struct Tune {
   static constexpr bool kWideGroup = G > 4;
   static constexpr bool kSliced = sliced_variant(std::is_same<KV, _Float16>::value, D, G);
   static constexpr int RL = kSliced ? 16 : ((D == 256 && kWideGroup) ? 32 : 16);
   static constexpr int HS = kSliced ? 2 : 1;
   static constexpr int R =
-      kSliced ? 2 : (D == 128 ? 4 : ((D == 256 && kWideGroup && sizeof(KV) == 2) ? 4 : 2));
+      kSliced ? (PAGED ? 2 : 4) : (D == 128 ? 4 : ((D == 256 && kWideGroup && sizeof(KV) == 2) ? 4 : 2));
   // Two waves per SIMD where the query, accumulator and two in-flight tiles
   // fit 256 registers without spilling (checked against the compiler's
   // resource report), else one.
@@ -482,7 +482,7 @@ template <typename KV, int G, int D, bool PAGED>
 static sk_status_t launch_variant(const SplitLaunch& s, bool launch, const void** fn, int grid[3],
                                   int* block) {
   const sk_desc_t& d = *s.d;
-  using T = Tune<KV, G, D>;
+  using T = Tune<KV, G, D, PAGED>;
   auto kern = gqa_split_kernel<KV, G, D, PAGED, T::RL, T::R, T::HS, T::WPE>;
   const dim3 gr(d.num_kv_heads, s.p->n_splits, d.batch);
   grid[0] = gr.x;
