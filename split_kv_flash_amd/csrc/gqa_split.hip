@@ -140,9 +140,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   }
 
   // This lane's slice of its GH query vectors (heads h0 + hs*GH ...),
-  // pre-scaled into base-2 units.
+  // pre-scaled into base-2 units; loaded after the first tile is requested,
+  // so the query's memory latency overlaps the first K/V loads.
   float qr[GH][DPL];
-  {
+  auto load_q = [&]() {
     const int64_t qbase = ((int64_t)b * a.Hq + h0 + hs * GH) * D;
     if (a.q_dtype == 0)
       load_q_slice<GH, D, RL, VEC, NL>(qr, reinterpret_cast<const float*>(a.q) + qbase, li, a.qscale);
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       load_q_slice<GH, D, RL, VEC, NL>(qr, reinterpret_cast<const _Float16*>(a.q) + qbase, li, a.qscale);
     else
       load_q_slice<GH, D, RL, VEC, NL>(qr, reinterpret_cast<const bf16_t*>(a.q) + qbase, li, a.qscale);
-  }
+  };
 
   float m[GH], l[GH], acc[GH][DPL];
 #pragma unroll
@@ -374,6 +375,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       load_pages(pn, start + TR);
     }
     issue(kA, vA, start, pc);
+    load_q();
     auto rotate = [&]() {
 #pragma unroll
       for (int r = 0; r < R; ++r) {

@@ -514,15 +514,6 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
     }
   };
 
-  // Query rows of this head block as B operands: lane holds head hb*16 + l16,
-  // columns 288*dh + 32*ks + 8*lq .. +7 (rounded to f16 once).
-  half8_t qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      qf[ks][e] = (_Float16)qb[(hb * 16 + l16) * kLatDk + dh * KH + ks * 32 + lq * 8 + e];
-
   // Running max (base 2) and normaliser of head hb*16 + l16 (replicated over
   // the quarters); output accumulators: heads 4*lq + e (items), columns
   // 256*dh + 16*cb + l16.
@@ -552,7 +543,17 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
   const int ntiles = (int)((end - start + kT16 - 1) / kT16);
   issue_tile(0, start);
   issue_tile(1, start + kT16);
-  wait_vm_lgkm0<0>();  // both tiles (and anything issued before them) landed
+  // Query rows of this head block as B operands (requested after the first
+  // tiles, so their latency overlaps): lane holds head hb*16 + l16,
+  // columns 288*dh + 32*ks + 8*lq .. +7 (rounded to f16 once).
+  half8_t qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      qf[ks][e] = (_Float16)qb[(hb * 16 + l16) * kLatDk + dh * KH + ks * 32 + lq * 8 + e];
+
+  wait_vm_lgkm0<0>();  // both tiles and the query rows landed
   raw_barrier();
 
   half8_t pp = half8_t{};  // weights of the previous tile (A operand)
@@ -779,18 +780,6 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
     }
   };
 
-  // Query block as B operands, pre-scaled into base-2 units: qv[t][u] is
-  // column 144*dq + 16*t + 4*lq + u of head head0 + l16.
-  float4_t qv[KT];
-  {
-    const float* qrow = qb + (int64_t)(head0 + l16) * kLatDk + dq * 144 + lq * 4;
-#pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      const float4 v = *reinterpret_cast<const float4*>(qrow + 16 * t);
-      qv[t] = float4_t{v.x * a.qscale, v.y * a.qscale, v.z * a.qscale, v.w * a.qscale};
-    }
-  }
-
   // Running max (base 2) and normaliser of head head0 + l16 (replicated over
   // the four quarters); accumulators acc[4*u + e] hold heads 4*lq + i (items)
   // at column 128*dq + 64*u + 4*l16 + e.
@@ -814,7 +803,20 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   const int ntiles = (int)((end - start + kT32 - 1) / kT32);
   issue_tile(0, start);
   issue_tile(1, start + kT32);
-  wait_vm_lgkm0<0>();  // both tiles (and anything issued before them) landed
+  // Query block as B operands (requested after the first tiles, so their
+  // latency overlaps), pre-scaled into base-2 units: qv[t][u] is
+  // column 144*dq + 16*t + 4*lq + u of head head0 + l16.
+  float4_t qv[KT];
+  {
+    const float* qrow = qb + (int64_t)(head0 + l16) * kLatDk + dq * 144 + lq * 4;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      const float4 v = *reinterpret_cast<const float4*>(qrow + 16 * t);
+      qv[t] = float4_t{v.x * a.qscale, v.y * a.qscale, v.z * a.qscale, v.w * a.qscale};
+    }
+  }
+
+  wait_vm_lgkm0<0>();  // both tiles and the query block landed
   raw_barrier();
 
   // Software pipeline: iteration i computes the output product of tile i-1
