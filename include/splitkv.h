@@ -159,7 +159,8 @@ sk_status_t attn_decode_plan(const sk_desc_t* desc, int32_t max_seq_len, int64_t
 size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan);
 
 /* Split kernel: writes the partial triple of every (b, h, split) into `workspace`.
- *   q            device, [batch][num_q_heads][head_dim_qk] of q_dtype, contiguous
+ *   q            device, [batch][num_q_heads][head_dim_qk] of q_dtype, contiguous,
+ *                16-byte aligned
  *   k, v         device, KV cache of kv_dtype in `layout`; v is NULL iff kv_shared
  *   block_table  device int32 [batch][max_pages_per_seq] when paged, else NULL
  *   seq_lens     device int32 [batch]; 1 <= L_b <= min(max_seq_len, n_splits*chunk)

@@ -223,6 +223,7 @@ static sk_status_t prepare_split(const sk_desc_t* desc, const sk_plan_t* plan, c
     if ((uintptr_t)workspace % 256) return fail(SK_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
     if ((uintptr_t)k % 16 || (v && (uintptr_t)v % 16))
       return fail(SK_ERR_INVALID_ARG, "K and V must be 16-byte aligned");
+    if ((uintptr_t)q % 16) return fail(SK_ERR_INVALID_ARG, "q must be 16-byte aligned");
     const size_t need = sk::ws_layout(*desc, *plan).total;
     if (workspace_bytes < need)
       return fail(SK_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes,

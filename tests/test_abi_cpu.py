@@ -165,6 +165,7 @@ def test_argument_errors_are_reported_before_any_launch():
     cases.append(("NULL workspace", _split(good, plan, ws=None), B.SK_ERR_INVALID_ARG))
     cases.append(("misaligned workspace", _split(good, plan, ws=4096 + 16), B.SK_ERR_INVALID_ARG))
     cases.append(("misaligned K", _split(good, plan, k=4096 + 4), B.SK_ERR_INVALID_ARG))
+    cases.append(("misaligned q", _split(good, plan, q=4096 + 8), B.SK_ERR_INVALID_ARG))
     cases.append(("workspace too small", _split(good, plan, wsb=1024), B.SK_ERR_WORKSPACE_TOO_SMALL))
     cases.append(("table for contiguous", _split(good, plan, bt=4096), B.SK_ERR_INVALID_ARG))
     d = gqa_desc(layout="paged", D=128, Hq=32, Hkv=8, cap=32768)
