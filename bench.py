@@ -1,15 +1,17 @@
 #!/usr/bin/env python3
 """One-GPU benchmark of split-KV decode attention on MI355X.
 
-A step is one decode-attention call: the split kernel and the combine kernel
-over one synthetic batch whose inputs are already resident in HBM. The
+A step is one decode-attention call (the split and the combine of every
+partial) over one synthetic batch whose inputs are already resident in HBM. The
 headline workload is a 9B-like full-attention layer (16 query / 4 KV heads,
 head_dim 256, f32 KV, q f32) at 131,072 positions; other context lengths,
 storage types and workloads are reported in ``rungs``.
 
 Output: one JSON line with the metric, throughput (algorithmic HBM GB/s of the
-whole call), the split kernel's roofline (HIP-event time per launch on the
-launch stream) and the float64 CPU oracle's throughput on a bounded sample.
+whole call through ``attn_decode``: the split kernel, then the combine
+kernel), the split kernel's roofline (HIP-event time per launch on the launch
+stream), the one-launch variant timed beside it, and the float64 CPU oracle's
+throughput on a bounded sample.
 """
 
 from __future__ import annotations
@@ -108,78 +110,79 @@ def decode_call(case, tensors, n_splits=0):
 
 
 def algorithmic_bytes(case, plan):
-    """(whole call, split kernel) algorithmic bytes.
+    """Algorithmic bytes of (whole call, split kernel, one-launch kernel).
 
     Whole call: K and V rows read once (positions < L_b), q read once, out and
-    lse written once. Split kernel: K, V, q read once plus the partials it
-    writes (B*Hq*S*(Dv+2) floats)."""
+    lse written once (plus one block-table entry per page when paged). Split
+    kernel: K, V, q read once plus the partials it writes (B*Hq*S*(Dv+2)
+    floats). One-launch kernel (split and merge in one grid): K, V, q, the
+    partials of the non-empty splits written and read back once, out and lse."""
     qb = case.q.nbytes
     kv = case.kv_bytes()
     out = case.batch * case.num_q_heads * (case.head_dim_v + 1) * 4
-    part = case.batch * case.num_q_heads * plan.n_splits * (case.head_dim_v + 2) * 4
+    row = (case.head_dim_v + 2) * 4
+    part = case.batch * case.num_q_heads * plan.n_splits * row
+    used = sum(-(-int(L) // plan.chunk) for L in case.seq_lens) * case.num_q_heads * row
     table = 0 if case.block_table is None else sum(-(-int(L) // case.page_size) for L in case.seq_lens) * 4
-    return kv + qb + out + table, kv + qb + part + table
+    return kv + qb + out + table, kv + qb + part + table, kv + qb + table + 2 * used + out
 
 
-def time_steps(call, steps, warmup, flush=None):
-    """Timings in ms: (split kernel average, combine kernel average, per-call
-    totals, wall ms per call or None).
-
-    * Per-call totals: one HIP event pair around each whole call (split and
-      combine launches), recorded on torch's current stream, which is the
-      stream the library launches on. Nothing is recorded between the two
-      launches, so the pair brackets exactly what a caller runs.
-    * Kernel averages: one event pair around ``steps`` back-to-back launches
-      of that kernel alone, divided by ``steps`` (the inputs do not change, so
-      every launch does the same work); this is the per-launch duration a
-      kernel trace reports.
-    With ``flush`` (a device buffer of MALL_FLUSH_BYTES) a read of the whole
-    buffer evicts the Infinity Cache before every timed call and every timed
-    split launch, outside the event pairs (the split kernel is then timed per
-    launch); the wall clock is then not reported. The eviction reads rather
-    than writes, so no write-back of dirty lines competes with the timed call.
-    """
+def _pair():
     import torch
 
-    def pair():
-        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_calls(fn, steps, warmup, flush=None):
+    """Per-call times in ms (one HIP event pair around each call, recorded on
+    torch's current stream, which is the stream the library launches on) and
+    the wall-clock ms per call (None when flushing). With ``flush`` (a device
+    buffer of MALL_FLUSH_BYTES) a read of the whole buffer evicts the Infinity
+    Cache before every timed call, outside the event pair; reading rather than
+    writing leaves no dirty lines whose write-back would compete with the
+    timed call."""
+    import torch
 
     for _ in range(warmup):
-        call()
+        fn()
     torch.cuda.synchronize()
-    ev = [pair() for _ in range(steps)]
+    ev = [_pair() for _ in range(steps)]
     t0 = time.perf_counter()
     for e0, e1 in ev:
         if flush is not None:
             flush.sum()
         e0.record()
-        call()
+        fn()
         e1.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    total = [a.elapsed_time(b) for a, b in ev]
+    return [a.elapsed_time(b) for a, b in ev], (None if flush is not None else wall)
 
-    def kernel_avg(fn, evict):
-        if evict is None:
-            e0, e1 = pair()
-            e0.record()
-            for _ in range(steps):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / steps
-        evs = [pair() for _ in range(steps)]
-        for e0, e1 in evs:
-            evict.sum()
-            e0.record()
+
+def kernel_avg(fn, steps, evict=None):
+    """Average duration in ms of one launch of ``fn`` (a single kernel): one
+    event pair around ``steps`` back-to-back launches divided by ``steps`` (the
+    inputs do not change, so every launch does the same work), which is the
+    per-launch duration a kernel trace reports; with ``evict`` the Infinity
+    Cache is evicted before every launch and each launch is timed alone."""
+    import torch
+
+    if evict is None:
+        e0, e1 = _pair()
+        e0.record()
+        for _ in range(steps):
             fn()
-            e1.record()
+        e1.record()
         torch.cuda.synchronize()
-        return statistics.mean(a.elapsed_time(b) for a, b in evs)
-
-    split = kernel_avg(call.splitk, flush)
-    comb = kernel_avg(call.combine, None)  # reads the partials the split just wrote
-    return split, comb, total, (None if flush is not None else wall)
+        return e0.elapsed_time(e1) / steps
+    evs = [_pair() for _ in range(steps)]
+    for e0, e1 in evs:
+        evict.sum()
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return statistics.mean(a.elapsed_time(b) for a, b in evs)
 
 
 def median(x):
@@ -192,13 +195,19 @@ def pct(x, q):
 
 
 def measure(case, steps, warmup, n_splits=0, flush=None):
+    """Times one workload. The call is ``attn_decode`` (the split kernel, then
+    the combine kernel); for separate K and V the one-launch variant
+    (``attn_decode_one_launch``, whose last workgroups merge) is timed beside
+    it, and each kernel alone."""
     import torch
     from synthetic.torch_io import to_device
 
     t = to_device(case)
     call = decode_call(case, t, n_splits)
-    split, comb, total, wall = time_steps(call, steps, warmup, flush)
-    whole_b, split_b = algorithmic_bytes(case, call.plan)
+    total, wall = time_calls(call.decode, steps, warmup, flush)
+    split = kernel_avg(call.splitk, steps, flush)
+    comb = kernel_avg(call.combine, steps)  # reads the partials the split just wrote
+    whole_b, split_b, fused_b = algorithmic_bytes(case, call.plan)
     us = median(total) * 1e3
     res = {
         "workload": case.name, "n_splits": call.plan.n_splits, "chunk": call.plan.chunk,
@@ -213,6 +222,13 @@ def measure(case, steps, warmup, n_splits=0, flush=None):
         "tokens_per_s_per_layer": round(case.batch * 1e6 / us, 1),
         "mall_flushed": flush is not None,
     }
+    if not case.kv_shared:
+        one, _ = time_calls(call.decode_one_launch, steps, warmup, flush)
+        fused = kernel_avg(call.decode_one_launch, steps, flush)
+        us1 = median(one) * 1e3
+        res.update({"one_launch_us_per_call": round(us1, 2),
+                    "one_launch_frac_of_peak": round(whole_b / (us1 * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                    "one_launch_kernel_us": round(fused * 1e3, 2), "bytes_one_launch_kernel": fused_b})
     if case.kv_shared:
         # Dense contractions on MFMA: scores (Hq x Dk) and output (Hq x Dv) per position.
         flops = 2.0 * case.num_q_heads * (case.head_dim_qk + case.head_dim_v) * int(case.seq_lens.sum())
@@ -325,13 +341,13 @@ def main():
     # Headline: A and B runs of the same workload give the A/A noise floor.
     case = synthetic.qwen9b_like(args.seq_len, args.kv, seed=2000 + args.seq_len)
     log(f"headline workload {case.name}: K+V {case.kv_bytes() / 1e9:.3f} GB")
-    head_a, split_a, wall_a = measure(case, args.steps, args.warmup, args.n_splits)
+    head_a, kern_a, wall_a = measure(case, args.steps, args.warmup, args.n_splits)
     log(f"run A: {head_a}")
     head_b, split_b, _ = measure(case, args.steps, args.warmup, args.n_splits)
     log(f"run B: {head_b}")
     aa_spread = abs(head_a["us_per_call"] - head_b["us_per_call"]) / head_a["us_per_call"]
 
-    split_ms = split_a
+    split_ms = kern_a
     achieved = head_a["bytes_split"] / (split_ms * 1e-3) / 1e9
     roofline = {
         "kernel": "gqa_split_kernel",
@@ -397,6 +413,8 @@ def main():
         "split_us": head_a["split_us"],
         "combine_us": head_a["combine_us"],
         "tokens_per_s_per_layer": head_a["tokens_per_s_per_layer"],
+        "one_launch": {k: head_a[k] for k in ("one_launch_us_per_call", "one_launch_frac_of_peak",
+                                             "one_launch_kernel_us")},
         "aa_noise_floor": round(aa_spread, 4),
         "bandwidth_control": control,
         "roofline": roofline,

@@ -10,7 +10,7 @@
  *     out[b,h,:] = sum_j exp(s_j - m) V[b,g,j,:] / sum_j exp(s_j - m),
  *     m = max_j s_j,   lse[b,h] = m + ln sum_j exp(s_j - m)
  *
- * in two launches, as the pages describe the method:
+ * either in two launches, as the pages describe the method, or in one:
  *
  *   attn_decode_splitk   One workgroup per (sequence, KV head or shared
  *                        latent, context split) runs the online-softmax
@@ -27,6 +27,16 @@
  *                        section 2: M = max m_i, l = sum l_i exp(m_i - M),
  *                        acc = sum acc_i exp(m_i - M); issue #3725 design
  *                        note section 2, kernel B).
+ *   attn_decode          Both steps in one call (the two kernels back to back).
+ *   attn_decode_one_launch
+ *                        Both steps in one launch, for separate K and V: the
+ *                        last workgroup of each (sequence, KV head) to finish
+ *                        performs the combine of that group's query heads.
+ *                        It exists for callers that need one kernel per call;
+ *                        on MI355X it measured slower than the two launches
+ *                        enqueued back to back (the combine's launch overlaps
+ *                        the split kernel, while the in-grid merge waits for
+ *                        device-scope round trips at the end of the grid).
  *
  * Conventions shared by every call
  *   - Pointers named "device" are device memory on the device that owns
@@ -154,6 +164,8 @@ sk_status_t attn_decode_plan(const sk_desc_t* desc, int32_t max_seq_len, int64_t
  *   acc [batch][num_q_heads][n_splits][head_dim_v]   un-normalised accumulators
  *   m   [batch][num_q_heads][n_splits]               slice maximum of s_j (natural-log units)
  *   l   [batch][num_q_heads][n_splits]               sum over the slice of exp(s_j - m)
+ *   cnt [batch][num_kv_heads] uint32                 completion counters of
+ *                                                    attn_decode_one_launch
  * (issue #3725 design note section 2: partials of (m, s, acc[D]) per query head and split,
  * acc left un-normalised.) */
 size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan);
@@ -191,6 +203,45 @@ sk_status_t attn_decode_combine(const sk_desc_t* desc, const sk_plan_t* plan,
                                 const int32_t* seq_lens, const void* workspace,
                                 size_t workspace_bytes, float* out, float* lse,
                                 hipStream_t stream);
+
+/* Zeroes the counter section (cnt) of a workspace with a fill kernel on `stream` (no
+ * memset, so the call may be captured in a graph). attn_decode_one_launch needs the
+ * counters at zero when it starts and leaves them at zero when it completes, so this
+ * runs once after the workspace is allocated, or after anything else has written over it.
+ * Errors: SK_ERR_INVALID_ARG, SK_ERR_WORKSPACE_TOO_SMALL (nothing launched), SK_ERR_LAUNCH. */
+sk_status_t attn_decode_workspace_init(const sk_desc_t* desc, const sk_plan_t* plan,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/* The whole decode call: attn_decode_splitk followed by attn_decode_combine on `stream`,
+ * with the same arguments, layouts and contract, every argument checked before the
+ * first launch.
+ *   out  device f32 [batch][num_q_heads][head_dim_v], 16-byte aligned
+ *   lse  device f32 [batch][num_q_heads], or NULL to skip
+ * Errors: as attn_decode_splitk, plus SK_ERR_INVALID_ARG for a NULL or misaligned out. */
+sk_status_t attn_decode(const sk_desc_t* desc, const sk_plan_t* plan, const void* q,
+                        const void* k, const void* v, const int32_t* block_table,
+                        const int32_t* seq_lens, void* workspace, size_t workspace_bytes,
+                        float* out, float* lse, hipStream_t stream);
+
+/* The whole decode call in one launch (separate K and V only), same arguments and results
+ * as attn_decode. Every workgroup holding positions writes its partial to the workspace
+ * with device-scope stores, waits for them to complete and increments cnt[b][g] (a
+ * device-scope atomic); the workgroup whose increment completes the ceil(L_b/chunk)
+ * partials of (b, g) reads them back with device-scope loads and writes out and lse of
+ * the group's query heads (Lecture 06 section 2: M = max m_i, l = sum l_i exp(m_i - M),
+ * out = sum acc_i exp(m_i - M) / l), then sets cnt[b][g] back to zero. No workgroup waits
+ * for another. Workgroups of empty slices exit at once and write no workspace row. A
+ * length outside [1, min(max_seq_len, n_splits*chunk)] makes that sequence's out and lse
+ * NaN. The counter section must be zero when the call starts (attn_decode_workspace_init);
+ * a call that completes leaves it zero. Calls that share a workspace must not overlap in
+ * time (for example on two streams).
+ * Errors: as attn_decode; SK_ERR_UNSUPPORTED for a shared latent. */
+sk_status_t attn_decode_one_launch(const sk_desc_t* desc, const sk_plan_t* plan, const void* q,
+                                   const void* k, const void* v, const int32_t* block_table,
+                                   const int32_t* seq_lens, void* workspace,
+                                   size_t workspace_bytes, float* out, float* lse,
+                                   hipStream_t stream);
 
 /* Static text for a status code. */
 const char* attn_decode_status_string(sk_status_t status);

@@ -4,7 +4,9 @@ The compute path is the HIP library ``libsplitkv.so`` (C ABI in
 ``include/splitkv.h``): a split kernel in which one workgroup serves every
 query head of a KV group (or of a shared latent) over one contiguous slice of
 the context, and a combine kernel that rescales the partials to their common
-maximum and sums them. This package is the thin Python side: ``binding``
+maximum and sums them. ``attn_decode`` runs the two back to back;
+``attn_decode_one_launch`` runs both steps in one launch for separate K and V
+(the last workgroup of each group to finish merges). This package is the thin Python side: ``binding``
 mirrors the C entry points one to one, and :class:`DecodeCall` fills the
 descriptor from torch tensors and owns the workspace. PyTorch is used only for
 device memory and streams.
@@ -17,15 +19,16 @@ from typing import Optional
 from . import binding
 from .binding import (  # noqa: F401
     SK_BF16, SK_F16, SK_F32, SK_KV_CONTIGUOUS, SK_KV_PAGED, SkDesc, SkKernelInfo, SkPlan,
-    SplitKVError, attn_decode_combine, attn_decode_kernel_info, attn_decode_last_error,
-    attn_decode_plan, attn_decode_splitk, attn_decode_status_string,
-    attn_decode_workspace_bytes,
+    SplitKVError, attn_decode, attn_decode_combine, attn_decode_kernel_info,
+    attn_decode_last_error, attn_decode_one_launch, attn_decode_plan, attn_decode_splitk,
+    attn_decode_status_string, attn_decode_workspace_bytes, attn_decode_workspace_init,
 )
 
 __all__ = [
     "DecodeCall", "make_desc", "SkDesc", "SkPlan", "SplitKVError", "attn_decode_plan",
     "attn_decode_workspace_bytes", "attn_decode_splitk", "attn_decode_combine",
     "attn_decode_status_string", "attn_decode_last_error", "attn_decode_kernel_info",
+    "attn_decode", "attn_decode_one_launch", "attn_decode_workspace_init",
 ]
 
 
@@ -123,6 +126,7 @@ class DecodeCall:
                                f"sequence lengths must lie in [1, {limit}]")
         self.ws_bytes = attn_decode_workspace_bytes(self.desc, self.plan)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=q.device)
+        self.init_workspace()
         self.out = torch.empty(self.desc.batch, self.desc.num_q_heads, self.desc.head_dim_v,
                                dtype=torch.float32, device=q.device)
         self.lse = torch.empty(self.desc.batch, self.desc.num_q_heads, dtype=torch.float32,
@@ -138,9 +142,45 @@ class DecodeCall:
                             self.out, self.lse if with_lse else None, _stream_handle(stream))
 
     def __call__(self, stream=None):
+        """Two launches: the split kernel, then the combine kernel."""
         self.splitk(stream)
         self.combine(stream)
         return self.out, self.lse
+
+    def init_workspace(self, stream=None):
+        """Zero the completion counters that :meth:`decode_one_launch` needs (once
+        after the workspace is allocated or overwritten)."""
+        attn_decode_workspace_init(self.desc, self.plan, self.workspace, self.ws_bytes,
+                                   _stream_handle(stream))
+
+    def decode(self, stream=None, with_lse: bool = True):
+        """The whole call through ``attn_decode`` (split kernel, then combine)."""
+        attn_decode(self.desc, self.plan, self.q, self.k, self.v, self.block_table, self.seq_lens,
+                    self.workspace, self.ws_bytes, self.out, self.lse if with_lse else None,
+                    _stream_handle(stream))
+        return self.out, self.lse
+
+    def decode_one_launch(self, stream=None, with_lse: bool = True):
+        """The whole call in one launch (``attn_decode_one_launch``; separate K
+        and V only)."""
+        attn_decode_one_launch(self.desc, self.plan, self.q, self.k, self.v, self.block_table,
+                               self.seq_lens, self.workspace, self.ws_bytes, self.out,
+                               self.lse if with_lse else None, _stream_handle(stream))
+        return self.out, self.lse
+
+    def counters(self):
+        """View of the workspace's completion counters, int32 [B][Hkv]."""
+        import torch
+
+        d, p = self.desc, self.plan
+        rows = d.batch * d.num_q_heads * p.n_splits
+
+        def a256(x):
+            return (x + 255) // 256 * 256
+
+        off = a256(rows * d.head_dim_v * 4) + 2 * a256(rows * 4)
+        n = d.batch * d.num_kv_heads
+        return self.workspace[off:off + 4 * n].view(torch.int32).view(d.batch, d.num_kv_heads)
 
     def partials(self):
         """Views of the workspace: acc [B][Hq][S][Dv], m and l [B][Hq][S] (f32)."""

@@ -86,6 +86,13 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_last_error.restype = c_char_p
     L.attn_decode_kernel_info.argtypes = [PD, PP, POINTER(SkKernelInfo)]
     L.attn_decode_kernel_info.restype = c_int32
+    L.attn_decode_workspace_init.argtypes = [PD, PP, c_void_p, c_size_t, c_void_p]
+    L.attn_decode_workspace_init.restype = c_int32
+    L.attn_decode.argtypes = [PD, PP, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                              c_size_t, c_void_p, c_void_p, c_void_p]
+    L.attn_decode.restype = c_int32
+    L.attn_decode_one_launch.argtypes = L.attn_decode.argtypes
+    L.attn_decode_one_launch.restype = c_int32
     _lib = L
     return L
 
@@ -94,7 +101,7 @@ def header_functions() -> list:
     """Names of the functions include/splitkv.h declares."""
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_decode_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(attn_decode\w*)\s*\(", text)))
 
 
 def _ptr(x) -> Optional[int]:
@@ -145,6 +152,27 @@ def attn_decode_combine(desc: SkDesc, plan: SkPlan, seq_lens, workspace, workspa
     _check(lib().attn_decode_combine(ctypes.byref(desc), ctypes.byref(plan), _ptr(seq_lens),
                                      _ptr(workspace), int(workspace_bytes), _ptr(out), _ptr(lse),
                                      stream))
+
+
+def attn_decode_workspace_init(desc: SkDesc, plan: SkPlan, workspace, workspace_bytes: int,
+                               stream: int) -> None:
+    _check(lib().attn_decode_workspace_init(ctypes.byref(desc), ctypes.byref(plan),
+                                            _ptr(workspace), int(workspace_bytes), stream))
+
+
+def attn_decode(desc: SkDesc, plan: SkPlan, q, k, v, block_table, seq_lens, workspace,
+                workspace_bytes: int, out, lse, stream: int) -> None:
+    _check(lib().attn_decode(ctypes.byref(desc), ctypes.byref(plan), _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(block_table), _ptr(seq_lens), _ptr(workspace),
+                             int(workspace_bytes), _ptr(out), _ptr(lse), stream))
+
+
+def attn_decode_one_launch(desc: SkDesc, plan: SkPlan, q, k, v, block_table, seq_lens, workspace,
+                           workspace_bytes: int, out, lse, stream: int) -> None:
+    _check(lib().attn_decode_one_launch(ctypes.byref(desc), ctypes.byref(plan), _ptr(q), _ptr(k),
+                                        _ptr(v), _ptr(block_table), _ptr(seq_lens),
+                                        _ptr(workspace), int(workspace_bytes), _ptr(out),
+                                        _ptr(lse), stream))
 
 
 def attn_decode_kernel_info(desc: SkDesc, plan: SkPlan) -> SkKernelInfo:

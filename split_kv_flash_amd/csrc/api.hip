@@ -142,7 +142,8 @@ WsLayout ws_layout(const sk_desc_t& d, const sk_plan_t& p) {
   w.acc_off = 0;
   w.m_off = align256(rows * d.head_dim_v * sizeof(float));
   w.l_off = w.m_off + align256(rows * sizeof(float));
-  w.total = w.l_off + align256(rows * sizeof(float));
+  w.cnt_off = w.l_off + align256(rows * sizeof(float));
+  w.total = w.cnt_off + align256((size_t)d.batch * d.num_kv_heads * sizeof(uint32_t));
   return w;
 }
 
@@ -242,6 +243,7 @@ static sk_status_t prepare_split(const sk_desc_t* desc, const sk_plan_t* plan, c
   out->ws_acc = reinterpret_cast<float*>(ws + w.acc_off);
   out->ws_m = reinterpret_cast<float*>(ws + w.m_off);
   out->ws_l = reinterpret_cast<float*>(ws + w.l_off);
+  out->counters = reinterpret_cast<uint32_t*>(ws + w.cnt_off);
   out->stream = nullptr;
   return SK_OK;
 }
@@ -296,6 +298,69 @@ sk_status_t attn_decode_combine(const sk_desc_t* desc, const sk_plan_t* plan,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return fail(SK_ERR_LAUNCH, "combine kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sk_status_t attn_decode_workspace_init(const sk_desc_t* desc, const sk_plan_t* plan,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  sk_status_t s = check_desc(desc);
+  if (s != SK_OK) return s;
+  if ((s = check_plan(desc, plan)) != SK_OK) return s;
+  if (!workspace) return fail(SK_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)workspace % 256) return fail(SK_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const sk::WsLayout w = sk::ws_layout(*desc, *plan);
+  if (workspace_bytes < w.total)
+    return fail(SK_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                w.total);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + w.cnt_off);
+  sk::zero_words_launch(cnt, (size_t)desc->batch * desc->num_kv_heads, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(SK_ERR_LAUNCH, "workspace init launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sk_status_t attn_decode(const sk_desc_t* desc, const sk_plan_t* plan, const void* q,
+                        const void* k, const void* v, const int32_t* block_table,
+                        const int32_t* seq_lens, void* workspace, size_t workspace_bytes,
+                        float* out, float* lse, hipStream_t stream) {
+  // Every check runs before the first launch.
+  sk::SplitLaunch a;
+  sk_status_t s = prepare_split(desc, plan, q, k, v, block_table, seq_lens, workspace,
+                                workspace_bytes, true, &a);
+  if (s != SK_OK) return s;
+  if (!out) return fail(SK_ERR_INVALID_ARG, "out must be non-NULL");
+  if ((uintptr_t)out % 16) return fail(SK_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  s = attn_decode_splitk(desc, plan, q, k, v, block_table, seq_lens, workspace, workspace_bytes,
+                         stream);
+  if (s != SK_OK) return s;
+  return attn_decode_combine(desc, plan, seq_lens, workspace, workspace_bytes, out, lse, stream);
+}
+
+sk_status_t attn_decode_one_launch(const sk_desc_t* desc, const sk_plan_t* plan, const void* q,
+                                   const void* k, const void* v, const int32_t* block_table,
+                                   const int32_t* seq_lens, void* workspace,
+                                   size_t workspace_bytes, float* out, float* lse,
+                                   hipStream_t stream) {
+  sk::SplitLaunch a;
+  sk_status_t s = prepare_split(desc, plan, q, k, v, block_table, seq_lens, workspace,
+                                workspace_bytes, true, &a);
+  if (s != SK_OK) return s;
+  if (desc->kv_shared)
+    return fail(SK_ERR_UNSUPPORTED, "the one-launch decode serves separate K and V only");
+  if (!out) return fail(SK_ERR_INVALID_ARG, "out must be non-NULL");
+  if ((uintptr_t)out % 16) return fail(SK_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  a.stream = stream;
+  a.fused = true;
+  a.out = out;
+  a.lse = lse;
+  int grid[3], block;
+  s = sk::gqa_split_launch(a, true, nullptr, grid, &block);
+  if (s != SK_OK) return fail(s, "no split kernel for this descriptor");
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(SK_ERR_LAUNCH, "one-launch decode kernel failed to launch: %s", hipGetErrorString(e));
   return ok();
 }
 

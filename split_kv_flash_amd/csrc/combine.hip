@@ -172,6 +172,19 @@ __global__ __launch_bounds__(64 * kMaxCombWaves) void combine_kernel(CombineArgs
     a.lse[(int64_t)b * a.Hq + h] = valid ? mrun + logf(lrun) : __builtin_nanf("");
 }
 
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+sk_status_t zero_words_launch(uint32_t* p, size_t n, hipStream_t stream) {
+  if (n == 0) return SK_OK;
+  const int64_t blocks = std::min<int64_t>(1024, ((int64_t)n + 255) / 256);
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, (int64_t)n);
+  return SK_OK;
+}
+
 sk_status_t combine_launch(const CombineLaunch& c) {
   const sk_desc_t& d = *c.d;
   CombineArgs a;

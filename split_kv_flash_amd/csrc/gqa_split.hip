@@ -31,6 +31,17 @@
 //   * At the end the row groups merge by cross-lane exchange, the waves merge
 //     through LDS (4*G*D floats, independent of the context length), and the
 //     workgroup writes one partial per query head.
+//   * One-launch variant (FUSED): the combine step runs inside the same grid.
+//     Each workgroup that holds positions writes its partial with device-scope
+//     stores (they write through this XCD's L2 to the device's coherence
+//     point), waits until they have completed, and counts itself in a
+//     per-(sequence, KV head) counter; the workgroup whose count completes the
+//     set merges the group's partials with device-scope loads (Lecture 06
+//     section 2: M = max m_i, l = sum l_i exp(m_i - M), out = sum acc_i
+//     exp(m_i - M) / l) and resets the counter to zero for the next call. No
+//     workgroup waits for another, and no cache is flushed or invalidated: a
+//     device-scope fence per workgroup writes back or drops a whole L2 and
+//     measured tens of microseconds per launch.
 #include <type_traits>
 
 #include "sk_device.h"
@@ -54,6 +65,10 @@ struct GqaArgs {
   int32_t page_shift, max_pages;
   int32_t paged_fast;  // page size, tile span and split chunk line up (see the tile loop)
   float qscale;
+  // One-launch decode only.
+  uint32_t* counters;  // [B][Hkv], zero between calls
+  float* out;          // [B][Hq][D]
+  float* lse;          // [B][Hq] or null
 };
 
 // Addressing modes of the tile loop.
@@ -91,7 +106,110 @@ __device__ __forceinline__ void load_q_slice(float (&qr)[G][D / RL], const QT* q
         qr[h][j * VEC + e] = to_f32(q[h * D + j * RL * VEC + li * VEC + e]) * qscale;
 }
 
-template <typename KV, int G, int D, bool PAGED, int RL, int R, int HS, int WPE>
+// Device-scope (all XCDs) relaxed accesses for the one-launch variant's
+// partials: the stores write through to the coherence point and the loads read
+// from it, so no cache maintenance is needed between workgroups on different
+// XCDs. The 16-byte loads are raw buffer loads with the device-scope cache
+// policy bit (sc1).
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+constexpr int kCachePolicyDevice = 16;  // sc1
+__device__ __forceinline__ float4 ld_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyDevice));
+}
+
+// Merges the n partials of query heads h0 .. h0+G-1 of sequence b into out
+// and lse (the combine step of the one-launch variant), in passes of P
+// splits: the pass's m and l values of every head are read once into LDS
+// (s_ml, 2*G*P floats), then thread t takes four consecutive columns of one
+// head, finds the pass maximum from LDS, rescales its running sums if it grew,
+// and folds the pass's accumulator rows, 16 per chunk, with the next chunk's
+// loads in flight. Rows past the pass are clamped to its last row (a written
+// partial) and weighted zero, so every read is in range.
+template <int G, int D, int NT, int P>
+__device__ __forceinline__ void merge_group(const GqaArgs& a, int b, int h0, int n, int tid,
+                                            float* s_ml) {
+  constexpr int C4 = D / 4;
+  constexpr int K = 16;
+  const int64_t row0 = ((int64_t)b * a.Hq + h0) * a.S;  // head hh's split i: row0 + hh*S + i
+  const auto racc = raw_rsrc(a.ws_acc + row0 * D, (uint32_t)((int64_t)G * a.S * D * 4));
+  // The column loop's trip count is the same for every thread (the passes
+  // below hold barriers); threads past the last column do no work in it.
+  for (int base = 0; base < G * C4; base += NT) {
+    const int idx = base + tid;
+    const bool active = idx < G * C4;
+    const int hh = active ? idx / C4 : 0;
+    const int c = active ? (idx - hh * C4) * 4 : 0;
+    const uint32_t col_off = (uint32_t)(((int64_t)hh * a.S * D + c) * 4);
+    float M = -INFINITY, ls = 0.0f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p0 = 0; p0 < n; p0 += P) {
+      const int np = min(P, n - p0);
+      __syncthreads();  // the previous pass (or column) is done with s_ml
+      for (int j = tid; j < G * np; j += NT) {
+        const int jh = j / np, i = j - (j / np) * np;
+        const int64_t r = row0 + (int64_t)jh * a.S + p0 + i;
+        s_ml[2 * (jh * P + i)] = ld_dev(a.ws_m + r);
+        s_ml[2 * (jh * P + i) + 1] = ld_dev(a.ws_l + r);
+      }
+      __syncthreads();
+      if (!active) continue;
+      const float* ml = s_ml + 2 * hh * P;
+      float mc = M;
+      for (int i = 0; i < np; ++i) mc = fmaxf(mc, ml[2 * i]);
+      const float mu = (mc == -INFINITY) ? 0.0f : mc;  // guard: no finite maximum yet
+      const float al = fast_exp2((M - mu) * kLog2e);
+      ls *= al;
+      A.x *= al;
+      A.y *= al;
+      A.z *= al;
+      A.w *= al;
+      M = mc;
+      float4 x0[K], x1[K];
+      auto fetch = [&](float4 (&x)[K], int i0) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const int i = p0 + min(i0 + k, np - 1);
+          x[k] = ld_dev4(racc, col_off + (uint32_t)i * (uint32_t)(D * 4));
+        }
+      };
+      auto fold = [&](const float4 (&x)[K], int i0) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const int i = min(i0 + k, np - 1);
+          const float w = (i0 + k < np) ? fast_exp2((ml[2 * i] - mu) * kLog2e) : 0.0f;
+          ls = fmaf(w, ml[2 * i + 1], ls);
+          A.x = fmaf(w, x[k].x, A.x);
+          A.y = fmaf(w, x[k].y, A.y);
+          A.z = fmaf(w, x[k].z, A.z);
+          A.w = fmaf(w, x[k].w, A.w);
+        }
+      };
+      fetch(x0, 0);
+      for (int i0 = 0;;) {
+        if (i0 + K < np) fetch(x1, i0 + K);
+        fold(x0, i0);
+        i0 += K;
+        if (i0 >= np) break;
+        if (i0 + K < np) fetch(x0, i0 + K);
+        fold(x1, i0);
+        i0 += K;
+        if (i0 >= np) break;
+      }
+    }
+    if (!active) continue;
+    const float inv = 1.0f / ls;
+    float* o = a.out + ((int64_t)b * a.Hq + h0 + hh) * D + c;
+    *reinterpret_cast<float4*>(o) = make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+    if (a.lse && c == 0) a.lse[(int64_t)b * a.Hq + h0 + hh] = M + logf(ls);
+  }
+}
+
+template <typename KV, int G, int D, bool PAGED, int RL, int R, int HS, int WPE, bool FUSED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void gqa_split_kernel(
     GqaArgs a) {
   using Sh = GqaShape<KV, D, RL, R, HS>;
@@ -121,12 +239,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   const int grp = wave * Sh::kGroupsPerWave + lane / Sh::kGroupLanes;
   const int h0 = g * G;
 
-  const int L = min(a.seq_lens[b], a.cap);
+  const int Lraw = a.seq_lens[b];
+  if constexpr (FUSED) {
+    // A length outside [1, min(cap, S*chunk)] is a caller error: that
+    // sequence's outputs become NaN and nothing of it is read or counted.
+    const bool valid = Lraw >= 1 && Lraw <= a.cap && (int64_t)Lraw <= (int64_t)a.S * a.chunk;
+    if (!valid) {
+      if (split == 0) {
+        for (int idx = tid; idx < G * D; idx += Sh::kThreads)
+          a.out[((int64_t)b * a.Hq + h0) * D + idx] = __builtin_nanf("");
+        if (a.lse && tid < G) a.lse[(int64_t)b * a.Hq + h0 + tid] = __builtin_nanf("");
+      }
+      return;
+    }
+  }
+  const int L = min(Lraw, a.cap);
   const int64_t start = (int64_t)split * a.chunk;
   const int64_t end = min((int64_t)L, start + a.chunk);
   const int64_t ws0 = ((int64_t)b * a.Hq + h0) * a.S + split;
 
   if (start >= end) {
+    // One-launch variant: an empty slice takes no part in the merge.
+    if constexpr (FUSED) return;
     // Empty slice (or an invalid length): the neutral partial, weight zero.
     for (int idx = tid; idx < G * D; idx += Sh::kThreads) {
       const int h = idx / D, e = idx - (idx / D) * D;
@@ -442,7 +576,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     float t = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) t = fmaf(s_acc[w][h][e], fast_exp2(s_m[w][h] - mbu), t);
-    a.ws_acc[(ws0 + (int64_t)h * a.S) * D + e] = t;
+    float* dst = a.ws_acc + (ws0 + (int64_t)h * a.S) * D + e;
+    if constexpr (FUSED)
+      st_dev(dst, t);
+    else
+      *dst = t;
   }
   if (tid < G) {
     const int h = tid;
@@ -453,8 +591,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     float lt = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) lt = fmaf(s_l[w][h], fast_exp2(s_m[w][h] - mbu), lt);
-    a.ws_m[ws0 + (int64_t)h * a.S] = mb * kLn2;
-    a.ws_l[ws0 + (int64_t)h * a.S] = lt;
+    if constexpr (FUSED) {
+      st_dev(a.ws_m + ws0 + (int64_t)h * a.S, mb * kLn2);
+      st_dev(a.ws_l + ws0 + (int64_t)h * a.S, lt);
+    } else {
+      a.ws_m[ws0 + (int64_t)h * a.S] = mb * kLn2;
+      a.ws_l[ws0 + (int64_t)h * a.S] = lt;
+    }
+  }
+
+  if constexpr (FUSED) {
+    // Every thread waits until its device-scope stores have completed, then
+    // the workgroup counts its partial. Counts are device-scope atomics, so
+    // the workgroup that brings the count to n is the last of the group, and
+    // every other partial was complete before its count: it reads them all.
+    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int n = (int)((L + (int64_t)a.chunk - 1) / a.chunk);
+    if (tid == 0) {
+      uint32_t* cnt = a.counters + (int64_t)b * Hkv + g;
+      const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = prev + 1 == (uint32_t)n;
+      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // The epilogue's LDS is free again: it holds the merge's m and l values.
+    merge_group<G, D, Sh::kThreads, NW * D / 2>(a, b, h0, n, tid, &s_acc[0][0][0]);
   }
 }
 
@@ -485,7 +650,8 @@ static sk_status_t launch_variant(const SplitLaunch& s, bool launch, const void*
                                   int* block) {
   const sk_desc_t& d = *s.d;
   using T = Tune<KV, G, D, PAGED>;
-  auto kern = gqa_split_kernel<KV, G, D, PAGED, T::RL, T::R, T::HS, T::WPE>;
+  auto kern = s.fused ? gqa_split_kernel<KV, G, D, PAGED, T::RL, T::R, T::HS, T::WPE, true>
+                      : gqa_split_kernel<KV, G, D, PAGED, T::RL, T::R, T::HS, T::WPE, false>;
   const dim3 gr(d.num_kv_heads, s.p->n_splits, d.batch);
   grid[0] = gr.x;
   grid[1] = gr.y;
@@ -524,6 +690,9 @@ static sk_status_t launch_variant(const SplitLaunch& s, bool launch, const void*
     a.paged_fast = PAGED && P % NG == 0 && TR % P == 0 && s.p->chunk % P == 0;
   }
   a.qscale = d.scale * kLog2e;
+  a.counters = s.counters;
+  a.out = s.out;
+  a.lse = s.lse;
   hipLaunchKernelGGL(kern, gr, dim3(256), 0, s.stream, a);
   return SK_OK;
 }

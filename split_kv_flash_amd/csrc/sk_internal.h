@@ -8,9 +8,11 @@
 
 namespace sk {
 
-// Workspace section offsets (bytes), each a multiple of 256.
+// Workspace section offsets (bytes), each a multiple of 256. The counter
+// section (one uint32 per (sequence, KV head)) is used by the one-launch
+// decode only.
 struct WsLayout {
-  size_t acc_off, m_off, l_off, total;
+  size_t acc_off, m_off, l_off, cnt_off, total;
 };
 WsLayout ws_layout(const sk_desc_t& d, const sk_plan_t& p);
 
@@ -27,6 +29,12 @@ struct SplitLaunch {
   float* ws_m;
   float* ws_l;
   hipStream_t stream;
+  // One-launch decode (GQA only): the last workgroup of each (sequence, KV
+  // head) to finish merges the partials into out/lse.
+  bool fused = false;
+  uint32_t* counters = nullptr;
+  float* out = nullptr;
+  float* lse = nullptr;
 };
 
 struct CombineLaunch {
@@ -58,5 +66,8 @@ sk_status_t gqa_split_launch(const SplitLaunch& a, bool launch, const void** fn,
 sk_status_t latent_split_launch(const SplitLaunch& a, bool launch, const void** fn, int grid[3],
                                 int* block);
 sk_status_t combine_launch(const CombineLaunch& a);
+// Zeroes n 32-bit words with a fill kernel (no memset node, so a captured
+// graph may hold it).
+sk_status_t zero_words_launch(uint32_t* p, size_t n, hipStream_t stream);
 
 }  // namespace sk

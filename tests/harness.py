@@ -70,3 +70,24 @@ def assert_parity(case, got, ref, *, tight: bool = True, label: str = ""):
     if tight:
         assert er <= REL_L2_F32_ARITH, f"{label}: relL2 {er:.3e} > {REL_L2_F32_ARITH:.1e} (f32 arithmetic)"
     return ea, er
+
+
+def run_gpu_fused(case, *, n_splits: int = 0, tensors=None, call=None):
+    """Run the one-launch decode (attn_decode_one_launch) with a poisoned workspace: every
+    byte 0xFF (NaN partials), then the completion counters zeroed as the
+    header requires. Returns (out, lse, call); the counters must be back at
+    zero afterwards."""
+    import torch
+
+    if tensors is None:
+        tensors = to_device(case)
+    if call is None:
+        call = decode_call(case, tensors, n_splits=n_splits)
+    call.workspace.view(torch.uint8).fill_(0xFF)
+    call.init_workspace()
+    call.out.fill_(float("nan"))
+    call.lse.fill_(float("nan"))
+    call.decode_one_launch()
+    torch.cuda.synchronize()
+    assert int(call.counters().abs().sum().item()) == 0, "completion counters not reset"
+    return call.out.double().cpu().numpy(), call.lse.double().cpu().numpy(), call

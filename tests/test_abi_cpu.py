@@ -59,7 +59,8 @@ def test_library_loads_and_exports_every_header_function():
     L = lib()
     names = B.header_functions()
     assert {"attn_decode_splitk", "attn_decode_combine", "attn_decode_plan",
-            "attn_decode_workspace_bytes"} <= set(names)
+            "attn_decode_workspace_bytes", "attn_decode", "attn_decode_one_launch",
+            "attn_decode_workspace_init"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"libsplitkv.so does not export {n}"
 
@@ -127,7 +128,8 @@ def test_workspace_bytes_follow_the_documented_layout():
         p = B.SkPlan(s, 64)
         rows = bsz * hq * s
         a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-        want = a256(rows * dv * 4) + a256(rows * 4) + a256(rows * 4)
+        counters = a256(bsz * d.num_kv_heads * 4)  # one uint32 per (sequence, KV head)
+        want = a256(rows * dv * 4) + a256(rows * 4) + a256(rows * 4) + counters
         assert B.attn_decode_workspace_bytes(d, p) == want
 
 
@@ -140,6 +142,27 @@ def _split(d, p, q=4096, k=4096, v=4096, bt=None, lens=4096, ws=4096, wsb=1 << 4
 def _combine(d, p, lens=4096, ws=4096, wsb=1 << 40, out=4096, lse=None):
     L = lib()
     s = L.attn_decode_combine(ctypes.byref(d), ctypes.byref(p), lens, ws, wsb, out, lse, None)
+    return s, B.attn_decode_last_error()
+
+
+def _decode(d, p, q=4096, k=4096, v=4096, bt=None, lens=4096, ws=4096, wsb=1 << 40, out=4096,
+            lse=None):
+    L = lib()
+    s = L.attn_decode(ctypes.byref(d), ctypes.byref(p), q, k, v, bt, lens, ws, wsb, out, lse, None)
+    return s, B.attn_decode_last_error()
+
+
+def _one(d, p, q=4096, k=4096, v=4096, bt=None, lens=4096, ws=4096, wsb=1 << 40, out=4096,
+         lse=None):
+    L = lib()
+    s = L.attn_decode_one_launch(ctypes.byref(d), ctypes.byref(p), q, k, v, bt, lens, ws, wsb, out,
+                                 lse, None)
+    return s, B.attn_decode_last_error()
+
+
+def _init(d, p, ws=4096, wsb=1 << 40):
+    L = lib()
+    s = L.attn_decode_workspace_init(ctypes.byref(d), ctypes.byref(p), ws, wsb, None)
     return s, B.attn_decode_last_error()
 
 
@@ -207,6 +230,21 @@ def test_argument_errors_are_reported_before_any_launch():
     cases.append(("combine: small workspace", _combine(good, plan, wsb=64), B.SK_ERR_WORKSPACE_TOO_SMALL))
     cases.append(("combine: misaligned out", _combine(good, plan, out=4096 + 4), B.SK_ERR_INVALID_ARG))
     cases.append(("combine: zero splits", _combine(good, B.SkPlan(0, 1)), B.SK_ERR_INVALID_ARG))
+    cases.append(("decode: NULL out", _decode(good, plan, out=None), B.SK_ERR_INVALID_ARG))
+    cases.append(("decode: misaligned out", _decode(good, plan, out=4096 + 8), B.SK_ERR_INVALID_ARG))
+    cases.append(("decode: NULL q", _decode(good, plan, q=None), B.SK_ERR_INVALID_ARG))
+    cases.append(("decode: small workspace", _decode(good, plan, wsb=64), B.SK_ERR_WORKSPACE_TOO_SMALL))
+    cases.append(("decode: group size 3", _decode(gqa_desc(Hq=12, Hkv=4), plan), B.SK_ERR_UNSUPPORTED))
+    cases.append(("decode: latent NULL out", _decode(latent_desc(), plan, v=None, out=None),
+                  B.SK_ERR_INVALID_ARG))
+    cases.append(("one launch: NULL out", _one(good, plan, out=None), B.SK_ERR_INVALID_ARG))
+    cases.append(("one launch: misaligned out", _one(good, plan, out=4100), B.SK_ERR_INVALID_ARG))
+    cases.append(("one launch: shared latent", _one(latent_desc(), plan, v=None), B.SK_ERR_UNSUPPORTED))
+    cases.append(("one launch: small workspace", _one(good, plan, wsb=64), B.SK_ERR_WORKSPACE_TOO_SMALL))
+    cases.append(("init: NULL workspace", _init(good, plan, ws=None), B.SK_ERR_INVALID_ARG))
+    cases.append(("init: misaligned workspace", _init(good, plan, ws=4096 + 64), B.SK_ERR_INVALID_ARG))
+    cases.append(("init: small workspace", _init(good, plan, wsb=64), B.SK_ERR_WORKSPACE_TOO_SMALL))
+    cases.append(("init: zero splits", _init(good, B.SkPlan(0, 1)), B.SK_ERR_INVALID_ARG))
     for name, (got, msg), want in cases:
         assert got == want, f"{name}: status {got}, expected {want} ({msg})"
         assert msg, f"{name}: no detail message"
