@@ -28,6 +28,8 @@ from .attention import (  # noqa: F401
     merge_partials_lse_f64,
     online_partial_f64,
     plan_splits,
+    project_heads_f64,
+    project_per_slice_f64,
     split_partials_f64,
     split_ranges,
     split_twin_f64,

@@ -412,3 +412,55 @@ def split_twin_f64(
             out[b, h], lse[b, h] = merge_partials_f64(
                 m[b, h, :n_b], l[b, h, :n_b], acc[b, h, :n_b], rescale=rescale)
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# Per-head output projection after the merge
+# --------------------------------------------------------------------------
+
+
+def project_heads_f64(out, w, w_dtype: str = "f32") -> np.ndarray:
+    """Per-head projection of merged attention outputs.
+
+    [L06] section 2 ("The output projection moves into the combine"): the
+    value up-projection wv_b acts on the *merged* latent of each head, so it
+    runs after the combine, never per slice. With W_h of shape [P][Dv] for
+    head h, the result is y[b, h, :] = W_h @ out[b, h, :] for every sequence
+    b and head h (the latent geometry of [L06] section 6 is Dv = 512, P = 128).
+
+    ``out`` is [B][Hq][Dv] (float64), ``w`` is [Hq][P][Dv] in the named
+    storage type (widened exactly). Returns [B][Hq][P] float64.
+    """
+    o = np.asarray(out, dtype=np.float64)
+    W = widen(w, w_dtype)
+    B, Hq, Dv = o.shape
+    if W.shape[0] != Hq or W.shape[2] != Dv:
+        raise ValueError(f"weights {W.shape} do not match outputs {o.shape}")
+    y = np.empty((B, Hq, W.shape[1]))
+    for h in range(Hq):
+        y[:, h, :] = o[:, h, :] @ W[h].T
+    return y
+
+
+def project_per_slice_f64(m, l, acc, n_used: int, w_h, w_dtype: str = "f32",
+                          *, normalised_mean: bool = False) -> np.ndarray:
+    """Projection applied to each slice's partial before the merge, for one head.
+
+    With ``normalised_mean=False`` each slice's un-normalised accumulator is
+    projected and the projected partials are merged with the combine's own
+    weights exp(m_i - M) and normaliser: because W is linear this equals the
+    projection of the merged output exactly (up to rounding), at n_used times
+    the projection work. ``normalised_mean=True`` is the mistake [L06] section
+    2 warns about: project each slice's normalised output acc_i / l_i and
+    average the slices with equal weights, ignoring their maxima and masses.
+    """
+    m = np.asarray(m, dtype=np.float64)[:n_used]
+    l = np.asarray(l, dtype=np.float64)[:n_used]
+    acc = np.asarray(acc, dtype=np.float64)[:n_used]
+    W = widen(w_h, w_dtype)
+    proj = acc @ W.T  # [n_used][P]
+    if normalised_mean:
+        return (proj / l[:, None]).mean(axis=0)
+    M = m.max()
+    wt = np.exp(m - M)
+    return (wt[:, None] * proj).sum(axis=0) / (wt * l).sum()

@@ -345,3 +345,13 @@ def wide_group_peaky(seq_len: int = 262144, seed: int = 5000) -> Case:
     return gqa_case(f"gqa24x4-d256-f16-peaky-L{seq_len}", seq_lens=[seq_len],
                     num_q_heads=24, num_kv_heads=4, head_dim=256, kv_dtype="f16",
                     seed=seed, peaky_fraction=0.01)
+
+
+def projection_weights(num_heads: int, out_dim: int, in_dim: int, dtype: str = "f32",
+                       seed: int = 6000) -> np.ndarray:
+    """Per-head projection matrices [num_heads][out_dim][in_dim]: float32
+    N(0,1) draws times 1/sqrt(in_dim) (so that a unit-scale input gives a
+    unit-scale output), rounded to ``dtype``. The latent geometry uses
+    in_dim = 512 (the merged latent) and out_dim = 128."""
+    w = normal_f32(np.random.SeedSequence(seed), (num_heads, out_dim, in_dim))
+    return to_storage(w * np.float32(1.0 / math.sqrt(in_dim)), dtype)

@@ -415,3 +415,98 @@ def test_plan_ragged_batch_is_budgeted_on_the_product():
 def test_plan_minimum_context_gate():
     assert oracle.plan_splits([4000], 4, 256, min_ctx=4096) == (1, 4000)
     assert oracle.plan_splits([4096], 4, 256, min_ctx=4096)[0] > 1
+
+
+# ------------------------------------------------- projection after the merge
+
+
+def _brute_project(out, w):
+    B, Hq, Dv = len(out), len(out[0]), len(out[0][0])
+    P = len(w[0])
+    return np.array([[[math.fsum(float(w[h][r][c]) * float(out[b][h][c]) for c in range(Dv))
+                       for r in range(P)] for h in range(Hq)] for b in range(B)])
+
+
+def test_projection_matches_exact_brute_force():
+    rng = np.random.default_rng(5)
+    out = rng.standard_normal((2, 3, 7))
+    w = rng.standard_normal((3, 4, 7))
+    got = oracle.project_heads_f64(out, w, "f64")
+    assert np.abs(got - _brute_project(out, w)).max() <= 1e-14
+
+
+def test_projection_identity_and_one_hot_rows_are_exact():
+    rng = np.random.default_rng(6)
+    out = rng.standard_normal((2, 4, 16))
+    eye = np.broadcast_to(np.eye(16), (4, 16, 16)).copy()
+    assert np.array_equal(oracle.project_heads_f64(out, eye, "f64"), out)
+    cols = [3, 0, 15, 7, 7]
+    onehot = np.zeros((4, len(cols), 16))
+    for r, c in enumerate(cols):
+        onehot[:, r, c] = 1.0
+    assert np.array_equal(oracle.project_heads_f64(out, onehot, "f64"), out[:, :, cols])
+    # each head uses its own matrix: scaling one head's W scales only that head
+    w = rng.standard_normal((4, 5, 16))
+    w2 = w.copy()
+    w2[2] *= 3.0
+    a, b = oracle.project_heads_f64(out, w, "f64"), oracle.project_heads_f64(out, w2, "f64")
+    assert np.abs(b[:, 2] - 3 * a[:, 2]).max() <= 1e-12
+    assert np.array_equal(np.delete(a, 2, axis=1), np.delete(b, 2, axis=1))
+
+
+def test_projection_is_linear_in_the_output():
+    rng = np.random.default_rng(7)
+    o1, o2 = rng.standard_normal((2, 1, 3, 9))
+    w = rng.standard_normal((3, 5, 9))
+    lhs = oracle.project_heads_f64(2.5 * o1 - o2, w, "f64")
+    rhs = 2.5 * oracle.project_heads_f64(o1, w, "f64") - oracle.project_heads_f64(o2, w, "f64")
+    assert np.abs(lhs - rhs).max() <= 1e-12
+
+
+def test_projection_storage_widening_reads_stored_weights():
+    w32 = synthetic.projection_weights(2, 3, 8, "f32", seed=1)
+    w16 = synthetic.projection_weights(2, 3, 8, "f16", seed=1)
+    wbf = synthetic.projection_weights(2, 3, 8, "bf16", seed=1)
+    out = np.ones((1, 2, 8))
+    assert np.array_equal(oracle.project_heads_f64(out, w16, "f16")[0],
+                          w16.astype(np.float64).sum(axis=2))
+    got = oracle.project_heads_f64(out, wbf, "bf16")[0]
+    assert np.array_equal(got, oracle.bf16_bits_to_f64(wbf).sum(axis=2))
+    assert np.abs(got - w32.astype(np.float64).sum(axis=2)).max() < 0.05
+
+
+def _latent_partials(L, S, seed):
+    case = synthetic.latent_case("proj", seq_len=L, kv_dtype="f32", seed=seed, scale=1 / 24)
+    chunk = -(-L // S)
+    m, l, acc = oracle.split_partials_f64(case.q, case.k_rows(), None, case.seq_lens, case.scale,
+                                          chunk, S, v_cols=512)
+    ref, _ = oracle.attend_f64(case.q, case.k_rows(), None, case.seq_lens, case.scale, v_cols=512)
+    return case, m, l, acc, ref
+
+
+def test_projection_commutes_with_the_rescaled_merge():
+    """W is linear, so projecting each slice's un-normalised accumulator and
+    merging with the combine's own weights equals projecting the merged output
+    (at S times the projection work): the projection of the definition is the
+    unique correct result."""
+    case, m, l, acc, ref = _latent_partials(1000, 4, 11)
+    w = synthetic.projection_weights(96, 128, 512, "f32", seed=2)
+    want = oracle.project_heads_f64(ref, w, "f32")
+    for h in (0, 37, 95):
+        got = oracle.project_per_slice_f64(m[0, h], l[0, h], acc[0, h], 4, w[h], "f32")
+        assert np.abs(got - want[0, h]).max() <= 1e-12
+
+
+@pytest.mark.parametrize("L,S", [(1000, 3), (8192, 16)])
+def test_negative_control_projecting_normalised_slices_fails(L, S):
+    """[L06] section 2: the projection is a function of the merged latent.
+    Projecting each slice's normalised output and averaging the slices with
+    equal weights must miss the f32 gate by far (test power)."""
+    case, m, l, acc, ref = _latent_partials(L, S, 12)
+    w = synthetic.projection_weights(96, 128, 512, "f32", seed=3)
+    want = oracle.project_heads_f64(ref, w, "f32")
+    bad = np.stack([oracle.project_per_slice_f64(m[0, h], l[0, h], acc[0, h], S, w[h], "f32",
+                                                 normalised_mean=True) for h in range(96)])
+    err = float(np.abs(bad - want[0]).max())
+    rel = float(np.linalg.norm(bad - want[0]) / np.linalg.norm(want[0]))
+    assert err > 10 * GATES[0] and rel > 100 * 1e-5, (err, rel)
