@@ -40,6 +40,7 @@ ONLY = {
     "ragged-paged": ("ragged_paged", (), {}),
     "latent-f32-131072": ("latent_decode", (131072, "f32"), {"seed": 3000 + 131072}),
     "latent-f16-131072": ("latent_decode", (131072, "f16"), {"seed": 3000 + 131072}),
+    "latent-f16-131072-project": ("latent_decode", (131072, "f16"), {"seed": 3000 + 131072}),
 }
 
 # HBM traffic of the headline split kernel, measured with rocprofv3 counters
@@ -133,6 +134,25 @@ def _pair():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
+# Untimed warm-up runs at least this long as well as at least W calls: after
+# the host has spent seconds generating a workload the GPU has been idle, and
+# the first few dozen calls then run up to 25% slower while its clocks ramp.
+WARMUP_MIN_MS = 100.0
+
+
+def warm_up(fn, calls, min_ms=WARMUP_MIN_MS):
+    """Runs fn at least ``calls`` times and for at least ``min_ms`` of GPU time."""
+    import torch
+
+    n = 0
+    t0 = time.perf_counter()
+    while n < calls or (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(max(1, calls)):
+            fn()
+        n += max(1, calls)
+        torch.cuda.synchronize()
+
+
 def time_calls(fn, steps, warmup, flush=None):
     """Per-call times in ms (one HIP event pair around each call, recorded on
     torch's current stream, which is the stream the library launches on) and
@@ -140,12 +160,10 @@ def time_calls(fn, steps, warmup, flush=None):
     buffer of MALL_FLUSH_BYTES) a read of the whole buffer evicts the Infinity
     Cache before every timed call, outside the event pair; reading rather than
     writing leaves no dirty lines whose write-back would compete with the
-    timed call."""
+    timed call. Warm-up: ``warmup`` calls and at least WARMUP_MIN_MS."""
     import torch
 
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm_up(fn, warmup)
     ev = [_pair() for _ in range(steps)]
     t0 = time.perf_counter()
     for e0, e1 in ev:
@@ -167,6 +185,7 @@ def kernel_avg(fn, steps, evict=None):
     Cache is evicted before every launch and each launch is timed alone."""
     import torch
 
+    warm_up(fn, 1, min_ms=20.0)
     if evict is None:
         e0, e1 = _pair()
         e0.record()
@@ -240,6 +259,48 @@ def measure(case, steps, warmup, n_splits=0, flush=None):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res, split, wall
+
+
+def measure_project(case, steps, warmup, w_dtype="bf16", proj_dim=128, flush=None):
+    """The latent call with the per-head output projection after the merge:
+    the split kernel, then the combine-project kernel (merge, then W_h o per
+    head). Algorithmic bytes of the combine-project kernel: the partials of
+    the non-empty splits read once, the weights read once, out and lse."""
+    import numpy as np
+    import torch
+
+    import synthetic
+    from synthetic.torch_io import to_device
+
+    t = to_device(case)
+    call = decode_call(case, t, 0)
+    w = synthetic.projection_weights(case.num_q_heads, proj_dim, case.head_dim_v, w_dtype,
+                                     seed=6000 + case.num_q_heads)
+    wt = (torch.from_numpy(w.view(np.int16)).view(torch.bfloat16) if w_dtype == "bf16"
+          else torch.from_numpy(w)).cuda()
+    y = torch.empty(case.batch, case.num_q_heads, proj_dim, device="cuda")
+
+    def whole():
+        call.splitk()
+        call.combine_project(wt, y)
+
+    total, _ = time_calls(whole, steps, warmup, flush)
+    call.splitk()
+    cp = kernel_avg(lambda: call.combine_project(wt, y), steps)
+    row = (case.head_dim_v + 2) * 4
+    used = sum(-(-int(L) // call.plan.chunk) for L in case.seq_lens) * case.num_q_heads * row
+    cp_b = used + wt.numel() * wt.element_size() + y.numel() * 4 + case.batch * case.num_q_heads * 4
+    us = median(total) * 1e3
+    res = {"workload": f"{case.name} + per-head projection {case.head_dim_v}->{proj_dim} ({w_dtype})",
+           "n_splits": call.plan.n_splits, "chunk": call.plan.chunk,
+           "us_per_call": round(us, 2), "us_p10": round(pct(total, 0.1) * 1e3, 2),
+           "combine_project_us": round(cp * 1e3, 2), "bytes_combine_project": cp_b,
+           "combine_project_GBps": round(cp_b / (cp * 1e-3) / 1e9, 1),
+           "mall_flushed": flush is not None}
+    del call, t, wt, y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def bandwidth_control(nbytes=1 << 30, reps=20):
@@ -334,7 +395,10 @@ def main():
     if args.only:
         fn, pos, kw = ONLY[args.only]
         c = getattr(synthetic, fn)(*pos, **kw)
-        r, _, _ = measure(c, args.steps, args.warmup, args.n_splits)
+        if args.only.endswith("-project"):
+            r = measure_project(c, args.steps, args.warmup, "bf16", 128)
+        else:
+            r, _, _ = measure(c, args.steps, args.warmup, args.n_splits)
         log(f"{args.only}: {r}")
         return
 
@@ -378,6 +442,10 @@ def main():
             r, _, _ = measure(c, args.rung_steps, args.rung_warmup, 0, flush if small else None)
             log(f"rung {r}")
             rungs.append(r)
+            if c.kv_shared and int(c.seq_lens[0]) == 131072:
+                r = measure_project(c, args.rung_steps, args.rung_warmup, "bf16", 128, flush)
+                log(f"rung {r}")
+                rungs.append(r)
             del c
         del flush
         torch.cuda.empty_cache()

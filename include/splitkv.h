@@ -243,6 +243,27 @@ sk_status_t attn_decode_one_launch(const sk_desc_t* desc, const sk_plan_t* plan,
                                    size_t workspace_bytes, float* out, float* lse,
                                    hipStream_t stream);
 
+/* Combine followed by a per-head output projection, in one kernel: for every sequence b
+ * and query head h, the merged output o[b][h] (as attn_decode_combine computes it) is
+ * multiplied by that head's matrix, out[b][h][r] = sum_c w_proj[h][r][c] * o[b][h][c]
+ * ("Part 4 · Lecture 06 — Attention at 128k", section 2: the value up-projection wv_b is a
+ * function of the merged latent, so it runs after the merge, never per slice).
+ *   w_proj    device, [num_q_heads][proj_dim][head_dim_v] of w_dtype, row-major,
+ *             16-byte aligned; widened to f32, f32 accumulation
+ *   proj_dim  P >= 1 (the latent geometry of the pages: head_dim_v 512, P 128)
+ *   out       device f32 [batch][num_q_heads][proj_dim]
+ *   lse       device f32 [batch][num_q_heads], or NULL to skip
+ * The workspace must hold partials written by attn_decode_splitk with the same desc and
+ * plan, earlier on the same stream. An invalid length makes that sequence's out and lse
+ * NaN. Supported: head_dim_v in {64, 128, 256, 512}, w_dtype f32, f16 or bf16.
+ * Errors: SK_ERR_INVALID_ARG (NULL or misaligned pointers, proj_dim < 1, unknown dtype),
+ * SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE_TOO_SMALL (nothing launched), SK_ERR_LAUNCH. */
+sk_status_t attn_decode_combine_project(const sk_desc_t* desc, const sk_plan_t* plan,
+                                        const int32_t* seq_lens, const void* workspace,
+                                        size_t workspace_bytes, const void* w_proj,
+                                        int32_t w_dtype, int32_t proj_dim, float* out, float* lse,
+                                        hipStream_t stream);
+
 /* Static text for a status code. */
 const char* attn_decode_status_string(sk_status_t status);
 

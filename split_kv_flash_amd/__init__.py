@@ -19,7 +19,8 @@ from typing import Optional
 from . import binding
 from .binding import (  # noqa: F401
     SK_BF16, SK_F16, SK_F32, SK_KV_CONTIGUOUS, SK_KV_PAGED, SkDesc, SkKernelInfo, SkPlan,
-    SplitKVError, attn_decode, attn_decode_combine, attn_decode_kernel_info,
+    SplitKVError, attn_decode, attn_decode_combine, attn_decode_combine_project,
+    attn_decode_kernel_info,
     attn_decode_last_error, attn_decode_one_launch, attn_decode_plan, attn_decode_splitk,
     attn_decode_status_string, attn_decode_workspace_bytes, attn_decode_workspace_init,
 )
@@ -29,6 +30,7 @@ __all__ = [
     "attn_decode_workspace_bytes", "attn_decode_splitk", "attn_decode_combine",
     "attn_decode_status_string", "attn_decode_last_error", "attn_decode_kernel_info",
     "attn_decode", "attn_decode_one_launch", "attn_decode_workspace_init",
+    "attn_decode_combine_project",
 ]
 
 
@@ -167,6 +169,14 @@ class DecodeCall:
                                self.seq_lens, self.workspace, self.ws_bytes, self.out,
                                self.lse if with_lse else None, _stream_handle(stream))
         return self.out, self.lse
+
+    def combine_project(self, w_proj, out, stream=None, with_lse: bool = True):
+        """Combine the partials and apply the per-head projection ``w_proj``
+        ([Hq][P][Dv], f32/f16/bf16) into ``out`` ([B][Hq][P] f32)."""
+        attn_decode_combine_project(self.desc, self.plan, self.seq_lens, self.workspace,
+                                    self.ws_bytes, w_proj, _dtype_code(w_proj), w_proj.shape[1],
+                                    out, self.lse if with_lse else None, _stream_handle(stream))
+        return out, self.lse
 
     def counters(self):
         """View of the workspace's completion counters, int32 [B][Hkv]."""

@@ -91,6 +91,9 @@ def lib() -> ctypes.CDLL:
     L.attn_decode.argtypes = [PD, PP, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                               c_size_t, c_void_p, c_void_p, c_void_p]
     L.attn_decode.restype = c_int32
+    L.attn_decode_combine_project.argtypes = [PD, PP, c_void_p, c_void_p, c_size_t, c_void_p,
+                                              c_int32, c_int32, c_void_p, c_void_p, c_void_p]
+    L.attn_decode_combine_project.restype = c_int32
     L.attn_decode_one_launch.argtypes = L.attn_decode.argtypes
     L.attn_decode_one_launch.restype = c_int32
     _lib = L
@@ -173,6 +176,15 @@ def attn_decode_one_launch(desc: SkDesc, plan: SkPlan, q, k, v, block_table, seq
                                         _ptr(v), _ptr(block_table), _ptr(seq_lens),
                                         _ptr(workspace), int(workspace_bytes), _ptr(out),
                                         _ptr(lse), stream))
+
+
+def attn_decode_combine_project(desc: SkDesc, plan: SkPlan, seq_lens, workspace,
+                                workspace_bytes: int, w_proj, w_dtype: int, proj_dim: int, out,
+                                lse, stream: int) -> None:
+    _check(lib().attn_decode_combine_project(ctypes.byref(desc), ctypes.byref(plan),
+                                             _ptr(seq_lens), _ptr(workspace), int(workspace_bytes),
+                                             _ptr(w_proj), int(w_dtype), int(proj_dim), _ptr(out),
+                                             _ptr(lse), stream))
 
 
 def attn_decode_kernel_info(desc: SkDesc, plan: SkPlan) -> SkKernelInfo:

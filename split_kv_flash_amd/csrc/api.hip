@@ -301,6 +301,49 @@ sk_status_t attn_decode_combine(const sk_desc_t* desc, const sk_plan_t* plan,
   return ok();
 }
 
+sk_status_t attn_decode_combine_project(const sk_desc_t* desc, const sk_plan_t* plan,
+                                        const int32_t* seq_lens, const void* workspace,
+                                        size_t workspace_bytes, const void* w_proj,
+                                        int32_t w_dtype, int32_t proj_dim, float* out, float* lse,
+                                        hipStream_t stream) {
+  sk_status_t s = check_desc(desc);
+  if (s != SK_OK) return s;
+  if ((s = check_plan(desc, plan)) != SK_OK) return s;
+  if (!seq_lens || !workspace || !w_proj || !out)
+    return fail(SK_ERR_INVALID_ARG, "seq_lens, workspace, w_proj and out must be non-NULL");
+  if ((uintptr_t)workspace % 256) return fail(SK_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if ((uintptr_t)w_proj % 16) return fail(SK_ERR_INVALID_ARG, "w_proj must be 16-byte aligned");
+  if (w_dtype < SK_F32 || w_dtype > SK_BF16)
+    return fail(SK_ERR_INVALID_ARG, "unknown weight dtype %d", w_dtype);
+  if (proj_dim < 1) return fail(SK_ERR_INVALID_ARG, "proj_dim must be >= 1 (got %d)", proj_dim);
+  if (!sk::project_supported(*desc, w_dtype))
+    return fail(SK_ERR_UNSUPPORTED, "the projection supports head_dim_v 64/128/256/512");
+  const sk::WsLayout w = sk::ws_layout(*desc, *plan);
+  if (workspace_bytes < w.total)
+    return fail(SK_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                w.total);
+  const char* ws = static_cast<const char*>(workspace);
+  sk::ProjectLaunch c;
+  c.d = desc;
+  c.p = plan;
+  c.seq_lens = seq_lens;
+  c.ws_acc = reinterpret_cast<const float*>(ws + w.acc_off);
+  c.ws_m = reinterpret_cast<const float*>(ws + w.m_off);
+  c.ws_l = reinterpret_cast<const float*>(ws + w.l_off);
+  c.w = w_proj;
+  c.w_dtype = w_dtype;
+  c.proj_dim = proj_dim;
+  c.out = out;
+  c.lse = lse;
+  c.stream = stream;
+  s = sk::combine_project_launch(c);
+  if (s != SK_OK) return fail(s, "combine-project launch rejected");
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(SK_ERR_LAUNCH, "combine-project kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 sk_status_t attn_decode_workspace_init(const sk_desc_t* desc, const sk_plan_t* plan,
                                        void* workspace, size_t workspace_bytes,
                                        hipStream_t stream) {

@@ -49,6 +49,21 @@ struct CombineLaunch {
   hipStream_t stream;
 };
 
+struct ProjectLaunch {
+  const sk_desc_t* d;
+  const sk_plan_t* p;
+  const int32_t* seq_lens;
+  const float* ws_acc;
+  const float* ws_m;
+  const float* ws_l;
+  const void* w;
+  int32_t w_dtype;
+  int32_t proj_dim;
+  float* out;
+  float* lse;
+  hipStream_t stream;
+};
+
 // Host-only capability checks (no HIP calls).
 bool gqa_supported(const sk_desc_t& d);
 // Workgroups per compute unit the split heuristic plans for a uniform batch.
@@ -66,6 +81,8 @@ sk_status_t gqa_split_launch(const SplitLaunch& a, bool launch, const void** fn,
 sk_status_t latent_split_launch(const SplitLaunch& a, bool launch, const void** fn, int grid[3],
                                 int* block);
 sk_status_t combine_launch(const CombineLaunch& a);
+bool project_supported(const sk_desc_t& d, int w_dtype);
+sk_status_t combine_project_launch(const ProjectLaunch& a);
 // Zeroes n 32-bit words with a fill kernel (no memset node, so a captured
 // graph may hold it).
 sk_status_t zero_words_launch(uint32_t* p, size_t n, hipStream_t stream);

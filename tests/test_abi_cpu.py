@@ -60,7 +60,7 @@ def test_library_loads_and_exports_every_header_function():
     names = B.header_functions()
     assert {"attn_decode_splitk", "attn_decode_combine", "attn_decode_plan",
             "attn_decode_workspace_bytes", "attn_decode", "attn_decode_one_launch",
-            "attn_decode_workspace_init"} <= set(names)
+            "attn_decode_workspace_init", "attn_decode_combine_project"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"libsplitkv.so does not export {n}"
 
@@ -160,6 +160,13 @@ def _one(d, p, q=4096, k=4096, v=4096, bt=None, lens=4096, ws=4096, wsb=1 << 40,
     return s, B.attn_decode_last_error()
 
 
+def _proj(d, p, lens=4096, ws=4096, wsb=1 << 40, w=4096, wdt=0, P=128, out=4096, lse=None):
+    L = lib()
+    s = L.attn_decode_combine_project(ctypes.byref(d), ctypes.byref(p), lens, ws, wsb, w, wdt, P,
+                                      out, lse, None)
+    return s, B.attn_decode_last_error()
+
+
 def _init(d, p, ws=4096, wsb=1 << 40):
     L = lib()
     s = L.attn_decode_workspace_init(ctypes.byref(d), ctypes.byref(p), ws, wsb, None)
@@ -241,6 +248,16 @@ def test_argument_errors_are_reported_before_any_launch():
     cases.append(("one launch: misaligned out", _one(good, plan, out=4100), B.SK_ERR_INVALID_ARG))
     cases.append(("one launch: shared latent", _one(latent_desc(), plan, v=None), B.SK_ERR_UNSUPPORTED))
     cases.append(("one launch: small workspace", _one(good, plan, wsb=64), B.SK_ERR_WORKSPACE_TOO_SMALL))
+    lat = latent_desc()
+    cases.append(("project: NULL weights", _proj(lat, plan, w=None), B.SK_ERR_INVALID_ARG))
+    cases.append(("project: misaligned weights", _proj(lat, plan, w=4096 + 4), B.SK_ERR_INVALID_ARG))
+    cases.append(("project: zero rows", _proj(lat, plan, P=0), B.SK_ERR_INVALID_ARG))
+    cases.append(("project: unknown weight dtype", _proj(lat, plan, wdt=9), B.SK_ERR_INVALID_ARG))
+    cases.append(("project: NULL out", _proj(lat, plan, out=None), B.SK_ERR_INVALID_ARG))
+    cases.append(("project: small workspace", _proj(lat, plan, wsb=64), B.SK_ERR_WORKSPACE_TOO_SMALL))
+    d = latent_desc()
+    d.head_dim_v = 320
+    cases.append(("project: value width 320", _proj(d, plan), B.SK_ERR_UNSUPPORTED))
     cases.append(("init: NULL workspace", _init(good, plan, ws=None), B.SK_ERR_INVALID_ARG))
     cases.append(("init: misaligned workspace", _init(good, plan, ws=4096 + 64), B.SK_ERR_INVALID_ARG))
     cases.append(("init: small workspace", _init(good, plan, wsb=64), B.SK_ERR_WORKSPACE_TOO_SMALL))
