@@ -23,6 +23,7 @@ No function is "parity unpinned".
 from .attention import (  # noqa: F401
     attend_f64,
     bf16_bits_to_f64,
+    gather_indexed,
     gather_paged,
     merge_partials_f64,
     merge_partials_lse_f64,

@@ -89,6 +89,22 @@ def gather_paged(pool, table_row: Sequence[int], length: int, page_size: int) ->
     return np.asarray(pool)[pages, j % page_size]
 
 
+def gather_indexed(pool, index_row: Sequence[int], length: int) -> np.ndarray:
+    """Rows of one sequence named by an index list: position j is pool row
+    ``index_row[j]`` for j < length.
+
+    [L07] section "Decode Starves the SMs ..." (sparsity): the sparse decode
+    path takes an indices tensor (batch, qlen, top-k) and gathers the selected
+    tokens straight from the KV pool by index, materialising nothing. ``pool``
+    is [rows][kv_heads][dim]; the result is [length][kv_heads][dim] in the
+    pool's storage type (no arithmetic happens here).
+    """
+    idx = np.asarray(index_row, dtype=np.int64)[:length]
+    if length and (idx.min() < 0 or idx.max() >= np.asarray(pool).shape[0]):
+        raise ValueError("index list names a row outside the pool")
+    return np.asarray(pool)[idx]
+
+
 # --------------------------------------------------------------------------
 # The definition
 # --------------------------------------------------------------------------

@@ -152,6 +152,8 @@ class Case:
     def capacity(self) -> int:
         if self.layout == "paged":
             return self.block_table.shape[1] * self.page_size
+        if self.layout == "indexed":
+            return self.block_table.shape[1]
         return self.k.shape[1]
 
     def kv_bytes(self) -> int:
@@ -175,6 +177,8 @@ class Case:
                 ps = self.page_size
                 j = np.arange(L)
                 rows.append(x[self.block_table[b][j // ps], j % ps])
+            elif self.layout == "indexed":
+                rows.append(x[self.block_table[b][:L]])
             else:
                 rows.append(x[b, :L])
         return rows
@@ -355,3 +359,57 @@ def projection_weights(num_heads: int, out_dim: int, in_dim: int, dtype: str = "
     in_dim = 512 (the merged latent) and out_dim = 128."""
     w = normal_f32(np.random.SeedSequence(seed), (num_heads, out_dim, in_dim))
     return to_storage(w * np.float32(1.0 / math.sqrt(in_dim)), dtype)
+
+
+def indexed_case(
+    name: str,
+    *,
+    pool_rows: int,
+    seq_lens: Sequence[int],
+    num_q_heads: int,
+    num_kv_heads: int,
+    head_dim: int,
+    kv_dtype: str = "f32",
+    q_dtype: str = "f32",
+    latent_value_dim: Optional[int] = None,
+    max_indices: Optional[int] = None,
+    seed: int = 0,
+    scale: Optional[float] = None,
+) -> Case:
+    """Sparse (top-k) decode: every sequence attends the pool rows named by its
+    index list. The pool holds ``pool_rows`` rows [rows][Hkv][D] (the whole
+    cache of one request, or a paged pool of physical slots); sequence b's list
+    has seq_lens[b] distinct rows in random order (a top-k selection is not
+    sorted), padded with -1 to ``max_indices``. With ``latent_value_dim`` the
+    pool is a shared latent (one row of ``head_dim`` columns, values are its
+    first ``latent_value_dim``)."""
+    kids = _spawn(seed)
+    lens = np.asarray(seq_lens, dtype=np.int32)
+    width = int(max_indices or lens.max())
+    latent = latent_value_dim is not None
+    hkv = 1 if latent else num_kv_heads
+    q = draw(kids[ROLE_Q], (len(lens), num_q_heads, head_dim), q_dtype)
+    k = draw(kids[ROLE_K], (pool_rows, hkv, head_dim), kv_dtype)
+    v = None if latent else draw(kids[ROLE_V], (pool_rows, hkv, head_dim), kv_dtype)
+    rng = np.random.default_rng(kids[ROLE_PERM])
+    table = np.full((len(lens), width), -1, dtype=np.int32)
+    for b, L in enumerate(lens):
+        table[b, :L] = rng.choice(pool_rows, size=int(L), replace=False)
+    return Case(
+        name=name, batch=len(lens), num_q_heads=num_q_heads, num_kv_heads=hkv,
+        head_dim_qk=head_dim, head_dim_v=latent_value_dim if latent else head_dim,
+        kv_shared=latent,
+        scale=(1.0 / math.sqrt(head_dim)) if scale is None else float(scale),
+        q_dtype=q_dtype, kv_dtype=kv_dtype, layout="indexed", q=q, k=k, v=v, seq_lens=lens,
+        block_table=table, page_size=1, seed=seed,
+    )
+
+
+def dsa_latent(topk: int = 2048, pool_rows: int = 131072, kv_dtype: str = "f16",
+               seed: int = 8000) -> Case:
+    """Sparse latent decode as the DSA chain runs it: 96 query heads over one
+    576-column latent row per position (512 value columns), the top-k rows of
+    a 131,072-row cache selected by an index list."""
+    return indexed_case(f"dsa-latent96-{kv_dtype}-top{topk}-of{pool_rows}", pool_rows=pool_rows,
+                        seq_lens=[topk], num_q_heads=96, num_kv_heads=1, head_dim=576,
+                        kv_dtype=kv_dtype, latent_value_dim=512, seed=seed, scale=1.0 / 24.0)

@@ -510,3 +510,59 @@ def test_negative_control_projecting_normalised_slices_fails(L, S):
     err = float(np.abs(bad - want[0]).max())
     rel = float(np.linalg.norm(bad - want[0]) / np.linalg.norm(want[0]))
     assert err > 10 * GATES[0] and rel > 100 * 1e-5, (err, rel)
+
+
+# ------------------------------------------------------- sparse (index-list)
+
+
+def test_index_list_gather_of_every_row_in_order_is_the_contiguous_cache():
+    rng = np.random.default_rng(21)
+    pool = rng.standard_normal((50, 2, 8))
+    assert np.array_equal(oracle.gather_indexed(pool, np.arange(50), 50), pool)
+    assert np.array_equal(oracle.gather_indexed(pool, np.arange(50), 17), pool[:17])
+    # the same rows through a block table of one-row pages
+    table = rng.permutation(50)
+    got = oracle.gather_indexed(pool, table, 30)
+    paged = oracle.gather_paged(pool[:, None], table, 30, 1)
+    assert np.array_equal(got, paged)
+    with pytest.raises(ValueError):
+        oracle.gather_indexed(pool, [3, 50], 2)
+    with pytest.raises(ValueError):
+        oracle.gather_indexed(pool, [-1, 0], 2)
+
+
+def test_sparse_attention_matches_exact_brute_force_over_the_listed_rows():
+    case = synthetic.indexed_case("sp", pool_rows=40, seq_lens=[5, 1, 9], num_q_heads=4,
+                                  num_kv_heads=2, head_dim=6, seed=22)
+    got, glse = oracle.attend_f64(case.q, case.k_rows(), case.v_rows(), case.seq_lens, case.scale)
+    q = case.q.astype(np.float64).tolist()
+    for b, L in enumerate(case.seq_lens):
+        idx = case.block_table[b, :L]
+        k = [[case.k[r].astype(np.float64).tolist() for r in idx]]
+        v = [[case.v[r].astype(np.float64).tolist() for r in idx]]
+        want, wlse = brute_force([q[b]], k, v, [int(L)], case.scale)
+        assert np.abs(got[b] - want[0]).max() <= 1e-14
+        assert np.abs(glse[b] - wlse[0]).max() <= 1e-13
+
+
+def test_sparse_attention_does_not_depend_on_the_order_of_the_list():
+    case = synthetic.indexed_case("sp", pool_rows=3000, seq_lens=[2048, 700], num_q_heads=8,
+                                  num_kv_heads=2, head_dim=64, kv_dtype="f16", seed=23)
+    a, _ = oracle.attend_f64(case.q, case.k_rows(), case.v_rows(), case.seq_lens, case.scale,
+                             kv_dtype="f16")
+    rng = np.random.default_rng(1)
+    for b, L in enumerate(case.seq_lens):
+        case.block_table[b, :L] = rng.permutation(case.block_table[b, :L])
+    bb, _ = oracle.attend_f64(case.q, case.k_rows(), case.v_rows(), case.seq_lens, case.scale,
+                              kv_dtype="f16")
+    assert np.abs(a - bb).max() <= 1e-13
+
+
+def test_negative_control_ignoring_the_index_list_fails():
+    """Attending the first L pool rows instead of the listed ones must miss the
+    gates by far (so a kernel that drops the indirection cannot pass)."""
+    case = synthetic.dsa_latent(topk=2048, pool_rows=16384, kv_dtype="f32", seed=24)
+    want, _ = oracle.attend_f64(case.q, case.k_rows(), None, case.seq_lens, case.scale, v_cols=512)
+    first = [case.k[: int(case.seq_lens[0])]]
+    bad, _ = oracle.attend_f64(case.q, first, None, case.seq_lens, case.scale, v_cols=512)
+    assert _err(bad, want) > 5 * max(GATES)
