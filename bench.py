@@ -41,6 +41,7 @@ ONLY = {
     "latent-f32-131072": ("latent_decode", (131072, "f32"), {"seed": 3000 + 131072}),
     "latent-f16-131072": ("latent_decode", (131072, "f16"), {"seed": 3000 + 131072}),
     "latent-f16-131072-project": ("latent_decode", (131072, "f16"), {"seed": 3000 + 131072}),
+    "dsa-latent-f16": ("dsa_latent", (2048, 131072, "f16"), {}),
 }
 
 # HBM traffic of the headline split kernel, measured with rocprofv3 counters
@@ -436,6 +437,8 @@ def main():
         for kv in ("f32", "f16"):
             for L in (8192, 131072):
                 specs.append(lambda kv=kv, L=L: synthetic.latent_decode(L, kv, seed=3000 + L))
+        for kv in ("f32", "f16"):  # sparse: top-2048 rows of a 131,072-row latent cache
+            specs.append(lambda kv=kv: synthetic.dsa_latent(2048, 131072, kv))
         for mk in specs:
             c = mk()
             small = c.kv_bytes() < MALL_FLUSH_BYTES  # could stay cached between calls

@@ -94,7 +94,16 @@ typedef enum {
    * lives in page block_table[b*max_pages_per_seq + j/page_size], slot
    * j % page_size ("The Kernel Level: Attention and MoE": the kernel indexes
    * KV through the block table; the table pointer stays fixed across steps). */
-  SK_KV_PAGED = 1
+  SK_KV_PAGED = 1,
+  /* Sparse (top-k) decode over an index list: K and V (or the shared latent) are row
+   * pools of num_pages rows, row r of KV head g at base + r*stride_pos + g*stride_head
+   * + d (elements; strides as for SK_KV_CONTIGUOUS, stride_seq unused); position j of
+   * sequence b is row block_table[b*max_pages_per_seq + j], j < L_b ("The Kernel Level:
+   * Attention and MoE", sparsity: the decode kernel takes an indices tensor (batch,
+   * qlen, top-k) and gathers the selected tokens from the pool by index). page_size is
+   * unused; max_seq_len <= max_pages_per_seq. An index outside [0, num_pages) is never
+   * followed: its position scores NaN, so that head's output is NaN.                   */
+  SK_KV_INDEXED = 2
 } sk_kv_layout_t;
 
 /* Shape and layout of one decode call. Plain data; the caller fills it. */
@@ -174,7 +183,8 @@ size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan)
  *   q            device, [batch][num_q_heads][head_dim_qk] of q_dtype, contiguous,
  *                16-byte aligned
  *   k, v         device, KV cache of kv_dtype in `layout`; v is NULL iff kv_shared
- *   block_table  device int32 [batch][max_pages_per_seq] when paged, else NULL
+ *   block_table  device int32 [batch][max_pages_per_seq] when paged (page numbers) or
+ *                indexed (pool rows), else NULL
  *   seq_lens     device int32 [batch]; 1 <= L_b <= min(max_seq_len, n_splits*chunk)
  *   workspace    device, >= attn_decode_workspace_bytes(desc, plan) bytes, 256-byte aligned
  *   stream       HIP stream of the device holding every buffer
@@ -183,9 +193,10 @@ size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan)
  * sequence. A block-table entry outside [0, num_pages) is likewise never followed;
  * the rows it names poison that head's output with NaN.
  * Supported: GQA with head_dim_qk == head_dim_v in {64, 128, 256}, group size
- * num_q_heads/num_kv_heads in {1, 2, 4, 6, 8}, any q/KV dtype, both layouts; latent
+ * num_q_heads/num_kv_heads in {1, 2, 4, 6, 8}, any q/KV dtype, every layout; latent
  * (kv_shared) with num_kv_heads == 1, head_dim_qk == 576, head_dim_v == 512, num_q_heads
- * in {32, 64, 96, 128}, q f32, KV f32 or f16, contiguous. Latent f16 caches run on f16
+ * in {32, 64, 96, 128}, q f32, KV f32 or f16, contiguous, or indexed (f32 KV, or f16 KV
+ * with 32 or 96 heads). Latent f16 caches run on f16
  * MFMA: q and the softmax weights are rounded to f16 there (f32 accumulation). Anything else returns
  * SK_ERR_UNSUPPORTED without launching. */
 sk_status_t attn_decode_splitk(const sk_desc_t* desc, const sk_plan_t* plan,

@@ -50,18 +50,23 @@ def make_desc(q, k, v=None, *, scale: float, block_table=None, page_size: int = 
     q            [B][Hq][Dk], contiguous
     k, v         contiguous cache [B][capacity][Hkv][D] (any strides with unit
                  last stride), or pools [pages][page_size][Hkv][D] when
-                 ``block_table`` ([B][max_pages] int32) is given
+                 ``block_table`` ([B][max_pages] int32) is given, or row pools
+                 [rows][Hkv][D] with ``block_table`` [B][max_indices] naming
+                 the pool row of every position (sparse, index-list decode)
     v = None     shared latent: values are the first ``v_cols`` key columns
     """
     d = SkDesc()
     if q.dim() != 3 or not q.is_contiguous():
         raise SplitKVError(binding.SK_ERR_INVALID_ARG, "q must be a contiguous [B][Hq][Dk] tensor")
     B, Hq, Dk = q.shape
-    if k.dim() != 4 or k.stride(3) != 1:
+    indexed = block_table is not None and k.dim() == 3
+    if not indexed and (k.dim() != 4 or k.stride(3) != 1):
         raise SplitKVError(binding.SK_ERR_INVALID_ARG, "k must be 4-D with unit last stride")
+    if indexed and k.stride(2) != 1:
+        raise SplitKVError(binding.SK_ERR_INVALID_ARG, "a row pool must have unit last stride")
     d.batch, d.num_q_heads, d.head_dim_qk = B, Hq, Dk
-    d.num_kv_heads = k.shape[2]
-    if k.shape[3] != Dk:
+    d.num_kv_heads = k.shape[-2]
+    if k.shape[-1] != Dk:
         raise SplitKVError(binding.SK_ERR_INVALID_ARG, "k's last dimension must equal q's")
     d.kv_shared = 1 if v is None else 0
     if v is None:
@@ -71,11 +76,18 @@ def make_desc(q, k, v=None, *, scale: float, block_table=None, page_size: int = 
     else:
         if v.shape != k.shape or v.stride() != k.stride() or v.dtype != k.dtype:
             raise SplitKVError(binding.SK_ERR_INVALID_ARG, "v must match k's shape, strides and dtype")
-        d.head_dim_v = v.shape[3]
+        d.head_dim_v = v.shape[-1]
     d.scale = float(scale)
     d.q_dtype = _dtype_code(q)
     d.kv_dtype = _dtype_code(k)
-    if block_table is None:
+    if indexed:
+        d.layout = binding.SK_KV_INDEXED
+        d.stride_pos, d.stride_head, d.stride_seq = k.stride(0), k.stride(1), 0
+        d.max_pages_per_seq = block_table.shape[1]
+        d.num_pages = k.shape[0]
+        d.page_size = 1
+        d.max_seq_len = int(d.max_pages_per_seq if max_seq_len is None else max_seq_len)
+    elif block_table is None:
         d.layout = SK_KV_CONTIGUOUS
         d.max_seq_len = int(k.shape[1] if max_seq_len is None else max_seq_len)
         d.stride_seq, d.stride_pos, d.stride_head = k.stride(0), k.stride(1), k.stride(2)

@@ -22,7 +22,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "splitkv.h")
 
 SK_OK, SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE_TOO_SMALL, SK_ERR_LAUNCH, SK_ERR_HIP = range(6)
 SK_F32, SK_F16, SK_BF16 = 0, 1, 2
-SK_KV_CONTIGUOUS, SK_KV_PAGED = 0, 1
+SK_KV_CONTIGUOUS, SK_KV_PAGED, SK_KV_INDEXED = 0, 1, 2
 DTYPES = {"f32": SK_F32, "f16": SK_F16, "bf16": SK_BF16}
 
 

@@ -78,7 +78,14 @@ sk_status_t check_desc(const sk_desc_t* d) {
   if (d->q_dtype < SK_F32 || d->q_dtype > SK_BF16 || d->kv_dtype < SK_F32 || d->kv_dtype > SK_BF16)
     return fail(SK_ERR_INVALID_ARG, "unknown dtype (q %d, kv %d)", d->q_dtype, d->kv_dtype);
   if (d->max_seq_len < 1) return fail(SK_ERR_INVALID_ARG, "max_seq_len must be >= 1");
-  if (d->layout == SK_KV_CONTIGUOUS) {
+  if (d->layout == SK_KV_CONTIGUOUS || d->layout == SK_KV_INDEXED) {
+    if (d->layout == SK_KV_INDEXED) {
+      if (d->max_pages_per_seq < 1 || d->num_pages < 1)
+        return fail(SK_ERR_INVALID_ARG, "indexed: max_pages_per_seq and num_pages must be >= 1");
+      if (d->max_seq_len > d->max_pages_per_seq)
+        return fail(SK_ERR_INVALID_ARG, "indexed: max_seq_len %d exceeds the index row length %d",
+                    d->max_seq_len, d->max_pages_per_seq);
+    }
     if (d->stride_pos < 1 || d->stride_head < 0 || d->stride_seq < 0)
       return fail(SK_ERR_INVALID_ARG, "contiguous strides must be non-negative (stride_pos >= 1)");
     if (d->num_kv_heads > 1 && d->stride_head < d->head_dim_qk)
@@ -124,7 +131,7 @@ sk_status_t check_support(const sk_desc_t* d) {
     if (!sk::latent_supported(*d))
       return fail(SK_ERR_UNSUPPORTED,
                   "shared latent supports Hkv 1, Dk 576, Dv 512, Hq 32/64/96/128, q f32, "
-                  "KV f32/f16, contiguous");
+                  "KV f32/f16, contiguous or indexed (f16 indexed: Hq 32/96)");
   } else if (!sk::gqa_supported(*d)) {
     return fail(SK_ERR_UNSUPPORTED,
                 "GQA supports head_dim 64/128/256 (qk == v) and group size 1/2/4/6/8");
@@ -217,8 +224,8 @@ static sk_status_t prepare_split(const sk_desc_t* desc, const sk_plan_t* plan, c
     if (desc->kv_shared && v)
       return fail(SK_ERR_INVALID_ARG, "v must be NULL when keys and values share the latent");
     if (!desc->kv_shared && !v) return fail(SK_ERR_INVALID_ARG, "v is NULL");
-    if (desc->layout == SK_KV_PAGED && !block_table)
-      return fail(SK_ERR_INVALID_ARG, "paged layout needs block_table");
+    if (desc->layout != SK_KV_CONTIGUOUS && !block_table)
+      return fail(SK_ERR_INVALID_ARG, "paged and indexed layouts need block_table");
     if (desc->layout == SK_KV_CONTIGUOUS && block_table)
       return fail(SK_ERR_INVALID_ARG, "contiguous layout takes no block_table");
     if ((uintptr_t)workspace % 256) return fail(SK_ERR_INVALID_ARG, "workspace is not 256-byte aligned");

@@ -302,12 +302,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   // of the pool, page indices from the block table.
   const int lane_col = li * VEC;
   const int64_t head_off =
-      PAGED ? (int64_t)g * D : (int64_t)b * a.stride_seq + (int64_t)g * a.stride_head;
+      PAGED ? (int64_t)g * a.stride_head : (int64_t)b * a.stride_seq + (int64_t)g * a.stride_head;
   const KV* __restrict__ kb = reinterpret_cast<const KV*>(a.k) + head_off + lane_col;
   const KV* __restrict__ vb = reinterpret_cast<const KV*>(a.v) + head_off + lane_col;
   const KV* __restrict__ kh = reinterpret_cast<const KV*>(a.k) + head_off;
   const KV* __restrict__ vh = reinterpret_cast<const KV*>(a.v) + head_off;
-  const int64_t row_stride = PAGED ? (int64_t)Hkv * D : a.stride_pos;
+  const int64_t row_stride = a.stride_pos;  // paged: Hkv*D (pool rows); indexed: the caller's
   const int ps_mask = (1 << a.page_shift) - 1;
   const int32_t* __restrict__ table = a.block_table + (int64_t)b * a.max_pages;
   const uint32_t row_bytes = (uint32_t)(row_stride * (int64_t)sizeof(KV));  // host-checked < 2^31 / TR
@@ -671,14 +671,18 @@ static sk_status_t launch_variant(const SplitLaunch& s, bool launch, const void*
   a.stride_seq = d.stride_seq;
   a.stride_pos = d.stride_pos;
   a.stride_head = d.stride_head;
+  if (d.layout == SK_KV_PAGED) {  // pools [pages][page_size][Hkv][D]
+    a.stride_pos = (int64_t)d.num_kv_heads * D;
+    a.stride_head = D;
+  }
   a.num_pages = d.num_pages;
   a.q_dtype = d.q_dtype;
   a.Hq = d.num_q_heads;
   a.S = s.p->n_splits;
   a.chunk = s.p->chunk;
   a.cap = d.max_seq_len;
-  a.page_shift = 0;
-  if (PAGED) {
+  a.page_shift = 0;  // indexed: pages of one row, the table names rows
+  if (d.layout == SK_KV_PAGED) {
     while ((1 << a.page_shift) < d.page_size) ++a.page_shift;
   }
   a.max_pages = d.max_pages_per_seq;
@@ -687,7 +691,7 @@ static sk_status_t launch_variant(const SplitLaunch& s, bool launch, const void*
     constexpr int NG = Sh::kGroups;
     constexpr int TR = NG * T::R;
     const int P = d.page_size;
-    a.paged_fast = PAGED && P % NG == 0 && TR % P == 0 && s.p->chunk % P == 0;
+    a.paged_fast = d.layout == SK_KV_PAGED && P % NG == 0 && TR % P == 0 && s.p->chunk % P == 0;
   }
   a.qscale = d.scale * kLog2e;
   a.counters = s.counters;
@@ -700,7 +704,7 @@ static sk_status_t launch_variant(const SplitLaunch& s, bool launch, const void*
 template <typename KV, int G, int D>
 static sk_status_t by_layout(const SplitLaunch& s, bool launch, const void** fn, int grid[3],
                              int* block) {
-  if (s.d->layout == SK_KV_PAGED) return launch_variant<KV, G, D, true>(s, launch, fn, grid, block);
+  if (s.d->layout != SK_KV_CONTIGUOUS) return launch_variant<KV, G, D, true>(s, launch, fn, grid, block);
   return launch_variant<KV, G, D, false>(s, launch, fn, grid, block);
 }
 

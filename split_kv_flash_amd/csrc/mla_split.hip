@@ -61,7 +61,37 @@ struct MlaArgs {
   int64_t stride_seq, stride_pos;
   int32_t Hq, S, chunk, cap;
   float qscale;  // scale * log2(e): scores are kept in base-2 units
+  // Index-list layout: position j of sequence b is pool row
+  // table[b * max_idx + j]; rows outside [0, num_rows) are never read.
+  const int32_t* table;
+  int32_t max_idx;
+  int64_t num_rows;
 };
+
+// Index-list tiles (IDX kernels): lane r < T of every wave holds the pool row
+// of tile row r (positions past the split's end repeat the last one), loaded
+// one tile ahead of the tile's own loads. A row outside the pool is replaced
+// by row 0 for the load and its bit in the tile's mask makes its scores NaN.
+__device__ __forceinline__ int32_t load_tile_index(const MlaArgs& a, int b, int64_t tb,
+                                                   int64_t end, int T) {
+  const int lane = threadIdx.x & 63;
+  if (lane >= T) return 0;
+  const int64_t pos = (tb + lane < end) ? tb + lane : end - 1;
+  return a.table[(int64_t)b * a.max_idx + pos];
+}
+__device__ __forceinline__ bool index_bad(const MlaArgs& a, int32_t r) {
+  return r < 0 || (int64_t)r >= a.num_rows;
+}
+// The tile mask of bad rows (bit r: tile row r) and the row each lane reads
+// for tile row `row` (taken from lane `row`).
+__device__ __forceinline__ uint32_t tile_bad_mask(const MlaArgs& a, int32_t idx, int T) {
+  const int lane = threadIdx.x & 63;
+  return (uint32_t)__ballot(lane < T && index_bad(a, idx));
+}
+__device__ __forceinline__ int32_t row_of(const MlaArgs& a, int32_t idx, int row) {
+  const int32_t safe = index_bad(a, idx) ? 0 : idx;
+  return __builtin_amdgcn_ds_bpermute(row << 2, safe);
+}
 
 template <typename CT>
 struct MlaCfg;
@@ -445,7 +475,7 @@ __device__ __forceinline__ int tile_off(int r, int cc) { return r * kLatDk + ((c
 //    (double-buffered by parity) and the next tile; after it the softmax of
 //    tile i runs and tile i+2 is requested into the buffer tile i-1 used.
 // ---------------------------------------------------------------------------
-template <int NHB>
+template <int NHB, bool IDX>
 __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
   constexpr int H = NHB * 16;
   constexpr int NW = 2 * NHB;
@@ -488,7 +518,8 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
     return;
   }
 
-  const _Float16* __restrict__ cbase = reinterpret_cast<const _Float16*>(a.c) + (int64_t)b * a.stride_seq;
+  const _Float16* __restrict__ cbase =
+      reinterpret_cast<const _Float16*>(a.c) + (IDX ? 0 : (int64_t)b * a.stride_seq);
   const float* __restrict__ qb = a.q + (int64_t)b * a.Hq * kLatDk;
 
   // Tile staging: this wave's DPW slots per tile; slot s holds tile row s/72,
@@ -499,18 +530,39 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
   // is its row (clamped to the last row) times the row stride plus its chunk.
   const uint32_t lds0 = lds_addr_of(s_c);
   const uint32_t row_bytes = (uint32_t)(a.stride_pos * 2);
+  // Index-list layout: the next tile's rows (lane r < 32) and the bad-row
+  // masks of the tiles in the three buffers.
+  int32_t nidx = 0;
+  uint32_t bad0 = 0, bad1 = 0, bad2 = 0;
   auto issue_tile = [&](int bi, int64_t tb) {
-    const int64_t tbc = tb < end ? tb : end - 1;
-    const int last = (int)(end - 1 - tbc);  // >= 0
-    const _Float16* tbase = cbase + tbc * a.stride_pos;
+    if constexpr (IDX) {
+      const uint32_t bad = tile_bad_mask(a, nidx, kT16);
+      bad0 = bi == 0 ? bad : bad0;
+      bad1 = bi == 1 ? bad : bad1;
+      bad2 = bi == 2 ? bad : bad2;
 #pragma unroll
-    for (int c = 0; c < DPW; ++c) {
-      const int sl = (wave * DPW + c) * 64 + lane;
-      const int srow = sl / kCpr16;
-      const int scol = ((sl - srow * kCpr16) ^ (srow & 7)) * 8;
-      const uint32_t off = (uint32_t)min(srow, last) * row_bytes + (uint32_t)(scol * 2);
-      const uint32_t dst = lds0 + (uint32_t)((bi * TILE + (wave * DPW + c) * 64 * 8) * 2);
-      dma16s(off, tbase, __builtin_amdgcn_readfirstlane(dst));
+      for (int c = 0; c < DPW; ++c) {
+        const int sl = (wave * DPW + c) * 64 + lane;
+        const int srow = sl / kCpr16;
+        const int scol = ((sl - srow * kCpr16) ^ (srow & 7)) * 8;
+        const int32_t r = row_of(a, nidx, srow);
+        const uint32_t dst = lds0 + (uint32_t)((bi * TILE + (wave * DPW + c) * 64 * 8) * 2);
+        dma16(cbase + (int64_t)r * a.stride_pos + scol, __builtin_amdgcn_readfirstlane(dst));
+      }
+      nidx = load_tile_index(a, b, tb + kT16, end, kT16);  // the next tile's rows
+    } else {
+      const int64_t tbc = tb < end ? tb : end - 1;
+      const int last = (int)(end - 1 - tbc);  // >= 0
+      const _Float16* tbase = cbase + tbc * a.stride_pos;
+#pragma unroll
+      for (int c = 0; c < DPW; ++c) {
+        const int sl = (wave * DPW + c) * 64 + lane;
+        const int srow = sl / kCpr16;
+        const int scol = ((sl - srow * kCpr16) ^ (srow & 7)) * 8;
+        const uint32_t off = (uint32_t)min(srow, last) * row_bytes + (uint32_t)(scol * 2);
+        const uint32_t dst = lds0 + (uint32_t)((bi * TILE + (wave * DPW + c) * 64 * 8) * 2);
+        dma16s(off, tbase, __builtin_amdgcn_readfirstlane(dst));
+      }
     }
   };
 
@@ -541,7 +593,12 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
   constexpr int kRow16 = 16 * kLatDk;  // 16 rows further down (same swizzle)
 
   const int ntiles = (int)((end - start + kT16 - 1) / kT16);
+  if constexpr (IDX) {
+    nidx = load_tile_index(a, b, start, end, kT16);
+    wait_vm_lgkm0<0>();
+  }
   issue_tile(0, start);
+  if constexpr (IDX) wait_vm_lgkm0<0>();  // the second tile's rows
   issue_tile(1, start + kT16);
   // Query rows of this head block as B operands (requested after the first
   // tiles, so their latency overlaps): lane holds head hb*16 + l16,
@@ -625,10 +682,16 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
     const float4_t q1 = s_sx[par][wave ^ 1][1][lane];
     float v[8];
     float mx = -INFINITY;
+    uint32_t badt = 0;  // rows of this tile whose index lies outside the pool
+    if constexpr (IDX) badt = (i % 3 == 0) ? bad0 : ((i % 3 == 1) ? bad1 : bad2);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[e] = 4 * lq + e < rel ? (sp0[e] + q0[e]) * a.qscale : -INFINITY;
       v[4 + e] = 16 + 4 * lq + e < rel ? (sp1[e] + q1[e]) * a.qscale : -INFINITY;
+      if constexpr (IDX) {
+        v[e] = ((badt >> (4 * lq + e)) & 1) ? __builtin_nanf("") : v[e];
+        v[4 + e] = ((badt >> (16 + 4 * lq + e)) & 1) ? __builtin_nanf("") : v[4 + e];
+      }
       mx = fmaxf(mx, fmaxf(v[e], v[4 + e]));
     }
     mx = fmaxf(mx, xor16(mx));
@@ -713,7 +776,7 @@ __device__ __forceinline__ uint32_t lds_addr_of(const float* p) {
 __host__ __device__ constexpr int mla32_blocks(int Hq) { return Hq % 48 == 0 ? 3 : 2; }
 __host__ __device__ constexpr int mla32_groups(int Hq) { return Hq / (16 * mla32_blocks(Hq)); }
 
-template <int NHBB>
+template <int NHBB, bool IDX>
 __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   constexpr int NW = 4 * NHBB;
   constexpr int NT = NW * 64;
@@ -754,7 +817,8 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
     return;
   }
 
-  const float* __restrict__ cbase = reinterpret_cast<const float*>(a.c) + (int64_t)b * a.stride_seq;
+  const float* __restrict__ cbase =
+      reinterpret_cast<const float*>(a.c) + (IDX ? 0 : (int64_t)b * a.stride_seq);
   const float* __restrict__ qb = a.q + (int64_t)b * a.Hq * kLatDk;
 
   // Tile staging: slot s of a buffer holds tile row s/144, stored chunk s%144,
@@ -770,13 +834,31 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
     scol[c] = real ? ((sl - (sl / kCpr32) * kCpr32) ^ (sl / kCpr32)) * 4 : 0;
   }
   const uint32_t lds0 = lds_addr_of(s_c);
+  // Index-list layout: the next tile's rows (lane r < 16) and the bad-row
+  // masks of the tiles in the three buffers. Padding slots read tile row 0.
+  int32_t nidx = 0;
+  uint32_t bad0 = 0, bad1 = 0, bad2 = 0;
   auto issue_tile = [&](int bi, int64_t tb) {
+    if constexpr (IDX) {
+      const uint32_t bad = tile_bad_mask(a, nidx, kT32);
+      bad0 = bi == 0 ? bad : bad0;
+      bad1 = bi == 1 ? bad : bad1;
+      bad2 = bi == 2 ? bad : bad2;
 #pragma unroll
-    for (int c = 0; c < DPW; ++c) {
-      int64_t pos = srow[c] < 0 ? start : tb + srow[c];
-      pos = pos < end ? pos : end - 1;
-      const uint32_t dst = lds0 + (uint32_t)((bi * TSTRIDE + (wave * DPW + c) * 64 * 4) * 4);
-      dma16(cbase + pos * a.stride_pos + scol[c], __builtin_amdgcn_readfirstlane(dst));
+      for (int c = 0; c < DPW; ++c) {
+        const int32_t r = row_of(a, nidx, srow[c] < 0 ? 0 : srow[c]);
+        const uint32_t dst = lds0 + (uint32_t)((bi * TSTRIDE + (wave * DPW + c) * 64 * 4) * 4);
+        dma16(cbase + (int64_t)r * a.stride_pos + scol[c], __builtin_amdgcn_readfirstlane(dst));
+      }
+      nidx = load_tile_index(a, b, tb + kT32, end, kT32);  // the next tile's rows
+    } else {
+#pragma unroll
+      for (int c = 0; c < DPW; ++c) {
+        int64_t pos = srow[c] < 0 ? start : tb + srow[c];
+        pos = pos < end ? pos : end - 1;
+        const uint32_t dst = lds0 + (uint32_t)((bi * TSTRIDE + (wave * DPW + c) * 64 * 4) * 4);
+        dma16(cbase + pos * a.stride_pos + scol[c], __builtin_amdgcn_readfirstlane(dst));
+      }
     }
   };
 
@@ -801,7 +883,12 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   }
 
   const int ntiles = (int)((end - start + kT32 - 1) / kT32);
+  if constexpr (IDX) {
+    nidx = load_tile_index(a, b, start, end, kT32);
+    wait_vm_lgkm0<0>();
+  }
   issue_tile(0, start);
+  if constexpr (IDX) wait_vm_lgkm0<0>();  // the second tile's rows
   issue_tile(1, start + kT32);
   // Query block as B operands (requested after the first tiles, so their
   // latency overlaps), pre-scaled into base-2 units: qv[t][u] is
@@ -879,9 +966,12 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
     const float4_t x0 = s_sx[par][hb * 4 + 0][lane], x1 = s_sx[par][hb * 4 + 1][lane];
     const float4_t x2 = s_sx[par][hb * 4 + 2][lane], x3 = s_sx[par][hb * 4 + 3][lane];
     float mx = -INFINITY;
+    uint32_t badt = 0;  // rows of this tile whose index lies outside the pool
+    if constexpr (IDX) badt = (i % 3 == 0) ? bad0 : ((i % 3 == 1) ? bad1 : bad2);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       pp[e] = 4 * lq + e < rel ? (x0[e] + x1[e]) + (x2[e] + x3[e]) : -INFINITY;
+      if constexpr (IDX) pp[e] = ((badt >> (4 * lq + e)) & 1) ? __builtin_nanf("") : pp[e];
       mx = fmaxf(mx, pp[e]);
     }
     mx = fmaxf(mx, xor16(mx));
@@ -926,11 +1016,17 @@ int latent_blocks_per_split(const sk_desc_t& d) {
 }
 
 bool latent_supported(const sk_desc_t& d) {
+  const bool heads_ok = d.num_q_heads == 32 || d.num_q_heads == 64 || d.num_q_heads == 96 ||
+                        d.num_q_heads == 128;
+  // Index lists: every f32 head count; f16 with 32 or 96 heads (the kernels
+  // that stage tiles with direct-to-LDS loads).
+  const bool layout_ok =
+      d.layout == SK_KV_CONTIGUOUS ||
+      (d.layout == SK_KV_INDEXED &&
+       (d.kv_dtype == SK_F32 || d.num_q_heads == 32 || d.num_q_heads == 96));
   return d.kv_shared == 1 && d.num_kv_heads == 1 && d.head_dim_qk == kLatDk &&
-         d.head_dim_v == kLatDv && d.layout == SK_KV_CONTIGUOUS && d.q_dtype == SK_F32 &&
-         (d.kv_dtype == SK_F32 || d.kv_dtype == SK_F16) &&
-         (d.num_q_heads == 32 || d.num_q_heads == 64 || d.num_q_heads == 96 ||
-          d.num_q_heads == 128);
+         d.head_dim_v == kLatDv && layout_ok && d.q_dtype == SK_F32 &&
+         (d.kv_dtype == SK_F32 || d.kv_dtype == SK_F16) && heads_ok;
 }
 
 template <typename CT, int NHB>
@@ -946,14 +1042,16 @@ static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void*
   constexpr bool kFull16 = sizeof(CT) == 2 && (NHB == 2 || NHB == 6);
   void (*kern)(MlaArgs);
   int threads, groups = 1;
+  const bool idx = d.layout == SK_KV_INDEXED;
   if constexpr (kF32) {
-    kern = mla32_split_kernel<mla32_blocks(H)>;
+    kern = idx ? mla32_split_kernel<mla32_blocks(H), true> : mla32_split_kernel<mla32_blocks(H), false>;
     threads = mla32_blocks(H) * 256;
     groups = mla32_groups(H);
   } else if constexpr (kFull16) {
-    kern = mla16_split_kernel<NHB>;
+    kern = idx ? mla16_split_kernel<NHB, true> : mla16_split_kernel<NHB, false>;
     threads = NHB * 128;
   } else {
+    if (idx) return SK_ERR_UNSUPPORTED;
     kern = mla_split_kernel<CT, NHB>;
     threads = kMlaThreads;
   }
@@ -978,6 +1076,9 @@ static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void*
   a.chunk = s.p->chunk;
   a.cap = d.max_seq_len;
   a.qscale = d.scale * kLog2e;
+  a.table = s.block_table;
+  a.max_idx = d.max_pages_per_seq;
+  a.num_rows = d.num_pages;
   hipLaunchKernelGGL(kern, gr, dim3(threads), 0, s.stream, a);
   return SK_OK;
 }

@@ -225,6 +225,16 @@ def test_argument_errors_are_reported_before_any_launch():
     d = gqa_desc()
     d.stride_pos = (1 << 22) + 4  # f32: just over 16 MiB between positions
     cases.append(("position step beyond 32-bit tile offsets", _split(d, plan), B.SK_ERR_UNSUPPORTED))
+    d = gqa_desc()
+    d.layout, d.max_pages_per_seq, d.num_pages = B.SK_KV_INDEXED, 4096, 100000
+    cases.append(("indexed without table", _split(d, plan), B.SK_ERR_INVALID_ARG))
+    d.max_pages_per_seq = 100
+    cases.append(("indexed: capacity beyond the table", _split(d, plan, bt=4096), B.SK_ERR_INVALID_ARG))
+    d.max_pages_per_seq, d.num_pages = 4096, 0
+    cases.append(("indexed: empty pool", _split(d, plan, bt=4096), B.SK_ERR_INVALID_ARG))
+    d = latent_desc(kv="f16", Hq=64)
+    d.layout, d.max_pages_per_seq, d.num_pages = B.SK_KV_INDEXED, 8192, 100000
+    cases.append(("indexed f16 latent, 64 heads", _split(d, plan, v=None, bt=4096), B.SK_ERR_UNSUPPORTED))
     d = latent_desc()
     cases.append(("v given with a shared latent", _split(d, plan, v=4096), B.SK_ERR_INVALID_ARG))
     d = latent_desc()
