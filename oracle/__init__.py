@@ -22,6 +22,8 @@ No function is "parity unpinned".
 
 from .attention import (  # noqa: F401
     attend_f64,
+    attend_multiquery_f64,
+    causal_limits,
     bf16_bits_to_f64,
     gather_indexed,
     gather_paged,
@@ -31,6 +33,7 @@ from .attention import (  # noqa: F401
     plan_splits,
     project_heads_f64,
     project_per_slice_f64,
+    query_tile_twin_f64,
     split_partials_f64,
     split_ranges,
     split_twin_f64,

@@ -480,3 +480,82 @@ def project_per_slice_f64(m, l, acc, n_used: int, w_h, w_dtype: str = "f32",
     M = m.max()
     wt = np.exp(m - M)
     return (wt[:, None] * proj).sum(axis=0) / (wt * l).sum()
+
+
+# --------------------------------------------------------------------------
+# Several query positions per sequence (query tiles)
+# --------------------------------------------------------------------------
+
+
+def causal_limits(seq_len: int, q_len: int) -> np.ndarray:
+    """Positions visible to each of the q_len newest queries of a sequence of
+    seq_len positions: query t sits at position seq_len - q_len + t and sees
+    positions [0, seq_len - q_len + t] (causal attention, [DB6])."""
+    return np.asarray([seq_len - q_len + t + 1 for t in range(q_len)], dtype=np.int64)
+
+
+def attend_multiquery_f64(q, k, v, seq_lens: Sequence[int], scale: float, *,
+                          q_dtype: str = "f32", kv_dtype: str = "f32", causal: bool = True,
+                          heads: Optional[Sequence[Tuple[int, int, int]]] = None):
+    """Causal attention of the q_len newest positions of every sequence.
+
+    q is [B][Q][Hq][Dk]; query t of sequence b attends positions
+    [0, L_b - Q + t] by the definition (``attend_f64`` with that length), so
+    Q = 1 is single-token decode and Q = L_b is causal self-attention over the
+    whole sequence ([DB6]: every query row carries its own running max,
+    normaliser and accumulator over the tiles it can see). ``causal=False``
+    (every query sees all L_b positions) is a negative control only.
+    ``heads`` optionally lists (b, t, h) triples to compute. Returns
+    (out [B][Q][Hq][Dv], lse [B][Q][Hq]).
+    """
+    qa = np.asarray(q)
+    B, Q, Hq, _ = qa.shape
+    Dv = np.asarray(v[0]).shape[-1]
+    out = np.full((B, Q, Hq, Dv), np.nan)
+    lse = np.full((B, Q, Hq), np.nan)
+    want = None if heads is None else set((int(b), int(t), int(h)) for b, t, h in heads)
+    for b in range(B):
+        L = int(seq_lens[b])
+        lims = causal_limits(L, Q) if causal else np.full(Q, L)
+        for t in range(Q):
+            if lims[t] < 1:
+                continue  # no visible position: undefined, left NaN
+            hs = [h for h in range(Hq) if want is None or (b, t, h) in want]
+            if not hs:
+                continue
+            o, s = attend_f64(qa[b:b + 1, t], [np.asarray(k[b])], [np.asarray(v[b])],
+                              [int(lims[t])], scale, q_dtype=q_dtype, kv_dtype=kv_dtype,
+                              heads=[(0, h) for h in hs])
+            out[b, t, hs] = o[0, hs]
+            lse[b, t, hs] = s[0, hs]
+    return out, lse
+
+
+def query_tile_twin_f64(q, k, v, seq_lens: Sequence[int], scale: float, *, tile: int = 32,
+                        q_dtype: str = "f32", kv_dtype: str = "f32", alpha: bool = True):
+    """The query-tile schedule of [DB6] for one call: every query row walks the
+    K/V tiles of ``tile`` positions it can see, carrying (m, l, acc) with the
+    per-tile rescale alpha = exp(m_old - m_new), and divides by l at the end.
+    ``alpha=False`` drops the rescale (the negative control [DB6] names: wrong
+    as soon as the running maximum moves between tiles). Returns out
+    [B][Q][Hq][Dv]."""
+    qa = np.asarray(q)
+    B, Q, Hq, _ = qa.shape
+    Hkv = np.asarray(k[0]).shape[1]
+    G = Hq // Hkv
+    Dv = np.asarray(v[0]).shape[-1]
+    out = np.full((B, Q, Hq, Dv), np.nan)
+    for b in range(B):
+        L = int(seq_lens[b])
+        kb = widen(np.asarray(k[b])[:L], kv_dtype)
+        vb = widen(np.asarray(v[b])[:L], kv_dtype)
+        qb = widen(qa[b], q_dtype)
+        for t, lim in enumerate(causal_limits(L, Q)):
+            if lim < 1:
+                continue
+            for h in range(Hq):
+                g = h // G
+                s = (kb[:lim, g, :] @ qb[t, h]) * scale
+                m, l, acc = online_partial_f64(s, vb[:lim, g, :], tile, alpha=alpha)
+                out[b, t, h] = acc / l
+    return out

@@ -413,3 +413,64 @@ def dsa_latent(topk: int = 2048, pool_rows: int = 131072, kv_dtype: str = "f16",
     return indexed_case(f"dsa-latent96-{kv_dtype}-top{topk}-of{pool_rows}", pool_rows=pool_rows,
                         seq_lens=[topk], num_q_heads=96, num_kv_heads=1, head_dim=576,
                         kv_dtype=kv_dtype, latent_value_dim=512, seed=seed, scale=1.0 / 24.0)
+
+
+def multiquery_case(
+    name: str,
+    *,
+    seq_lens: Sequence[int],
+    q_len: int,
+    num_q_heads: int,
+    num_kv_heads: int,
+    head_dim: int,
+    kv_dtype: str = "f16",
+    q_dtype: str = "f32",
+    capacity: Optional[int] = None,
+    seed: int = 0,
+) -> Case:
+    """The q_len newest positions of every sequence query its cache at once
+    (speculative verify, chunked prefill, causal self-attention when
+    q_len = L): q is [B][q_len][Hq][D]; K/V are token-major [B][cap][Hkv][D]
+    with NaN past each length."""
+    kids = _spawn(seed)
+    lens = np.asarray(seq_lens, dtype=np.int32)
+    cap = int(capacity or lens.max())
+    B = len(lens)
+    q = draw(kids[ROLE_Q], (B, q_len, num_q_heads, head_dim), q_dtype)
+    k = draw(kids[ROLE_K], (B, cap, num_kv_heads, head_dim), kv_dtype)
+    v = draw(kids[ROLE_V], (B, cap, num_kv_heads, head_dim), kv_dtype)
+    for b, L in enumerate(lens):
+        k[b, L:] = nan_value(kv_dtype)
+        v[b, L:] = nan_value(kv_dtype)
+    return Case(
+        name=name, batch=B, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+        head_dim_qk=head_dim, head_dim_v=head_dim, kv_shared=False,
+        scale=1.0 / math.sqrt(head_dim), q_dtype=q_dtype, kv_dtype=kv_dtype,
+        layout="contiguous", q=q, k=k, v=v, seq_lens=lens, seed=seed, meta={"q_len": q_len},
+    )
+
+
+def causal_block(seq_len: int = 2048, kv_dtype: str = "f16", seed: int = 8100) -> Case:
+    """Causal self-attention over a whole sequence with head_dim 64, the
+    teaching decoder block's shape (4 heads of 64, 2048 tokens)."""
+    return multiquery_case(f"causal-block4x64-{kv_dtype}-L{seq_len}", seq_lens=[seq_len],
+                           q_len=seq_len, num_q_heads=4, num_kv_heads=4, head_dim=64,
+                           kv_dtype=kv_dtype, seed=seed)
+
+
+def spec_verify(seq_len: int = 131072, q_len: int = 4, kv_dtype: str = "f16",
+                seed: int = 8200) -> Case:
+    """Speculative verify on the 9B-like layer: q_len drafted tokens at the end
+    of a seq_len-position cache (16 query / 4 KV heads, head_dim 256)."""
+    return multiquery_case(f"verify{q_len}-gqa16x4-d256-{kv_dtype}-L{seq_len}", seq_lens=[seq_len],
+                           q_len=q_len, num_q_heads=16, num_kv_heads=4, head_dim=256,
+                           kv_dtype=kv_dtype, seed=seed)
+
+
+def chunked_prefill(seq_len: int = 8192, q_len: int = 512, kv_dtype: str = "f16",
+                    seed: int = 8300) -> Case:
+    """Chunked prefill on the 9B-like layer: the last q_len positions of a
+    seq_len-position sequence (16 query / 4 KV heads, head_dim 256)."""
+    return multiquery_case(f"prefill{q_len}-gqa16x4-d256-{kv_dtype}-L{seq_len}", seq_lens=[seq_len],
+                           q_len=q_len, num_q_heads=16, num_kv_heads=4, head_dim=256,
+                           kv_dtype=kv_dtype, seed=seed)

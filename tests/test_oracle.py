@@ -566,3 +566,101 @@ def test_negative_control_ignoring_the_index_list_fails():
     first = [case.k[: int(case.seq_lens[0])]]
     bad, _ = oracle.attend_f64(case.q, first, None, case.seq_lens, case.scale, v_cols=512)
     assert _err(bad, want) > 5 * max(GATES)
+
+
+# ------------------------------------------------- several queries (query tiles)
+
+
+def _brute_causal(case):
+    """Plain-Python causal attention with exact summation."""
+    B, Q, Hq, D = case.q.shape
+    G = Hq // case.num_kv_heads
+    out = np.full((B, Q, Hq, D), np.nan)
+    for b in range(B):
+        L = int(case.seq_lens[b])
+        for t in range(Q):
+            lim = L - Q + t + 1
+            if lim < 1:
+                continue
+            for h in range(Hq):
+                g = h // G
+                qv = [float(x) for x in case.q[b, t, h]]
+                s = [case.scale * math.fsum(qv[d] * float(case.k[b, j, g, d]) for d in range(D))
+                     for j in range(lim)]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                den = math.fsum(w)
+                out[b, t, h] = [math.fsum(w[j] * float(case.v[b, j, g, e]) for j in range(lim)) / den
+                                for e in range(D)]
+    return out
+
+
+def test_multiquery_definition_matches_exact_brute_force():
+    case = synthetic.multiquery_case("mq", seq_lens=[9, 4, 2], q_len=3, num_q_heads=4,
+                                     num_kv_heads=2, head_dim=5, kv_dtype="f32", seed=31)
+    got, _ = oracle.attend_multiquery_f64(case.q, case.k, case.v, case.seq_lens, case.scale)
+    want = _brute_causal(case)
+    assert np.array_equal(np.isnan(got), np.isnan(want))  # L=2 < Q=3: query 0 sees nothing
+    assert np.nanmax(np.abs(got - want)) <= 1e-14
+
+
+def test_multiquery_is_causal():
+    """Changing the key and value rows at position p changes exactly the
+    queries that can see p (lim > p) and leaves every other bit unchanged."""
+    case = synthetic.multiquery_case("mq", seq_lens=[40], q_len=16, num_q_heads=4,
+                                     num_kv_heads=1, head_dim=8, kv_dtype="f32", seed=32)
+    a, _ = oracle.attend_multiquery_f64(case.q, case.k, case.v, case.seq_lens, case.scale)
+    p = 30
+    case.k[0, p] += 1.0
+    case.v[0, p] -= 2.0
+    b, _ = oracle.attend_multiquery_f64(case.q, case.k, case.v, case.seq_lens, case.scale)
+    lims = oracle.causal_limits(40, 16)
+    for t in range(16):
+        if lims[t] > p:
+            assert np.abs(a[0, t] - b[0, t]).max() > 1e-6
+        else:
+            assert np.array_equal(a[0, t], b[0, t])
+
+
+def test_full_self_attention_first_query_sees_only_position_zero():
+    case = synthetic.causal_block(64, kv_dtype="f32", seed=33)
+    out, _ = oracle.attend_multiquery_f64(case.q, case.k, case.v, case.seq_lens, case.scale)
+    for h in range(4):
+        assert np.array_equal(out[0, 0, h], case.v[0, 0, h].astype(np.float64))
+
+
+@pytest.mark.parametrize("L,Q", [(33, 33), (33, 5), (1000, 40)])
+def test_query_tile_twin_equals_definition(L, Q):
+    case = synthetic.multiquery_case("mq", seq_lens=[L], q_len=Q, num_q_heads=4, num_kv_heads=2,
+                                     head_dim=16, kv_dtype="f16", seed=L + Q)
+    want, _ = oracle.attend_multiquery_f64(case.q, case.k, case.v, case.seq_lens, case.scale,
+                                           kv_dtype="f16")
+    for tile in (1, 7, 32):
+        got = oracle.query_tile_twin_f64(case.q, case.k, case.v, case.seq_lens, case.scale,
+                                         tile=tile, kv_dtype="f16")
+        assert np.abs(got - want).max() <= 1e-12
+
+
+def test_negative_control_query_tiles_without_alpha_fail_at_length_33():
+    """[DB6]: without the rescale the block is wrong once the running maximum
+    moves between tiles; length 33 puts the rows past 32 in two tiles. Make
+    position 32 the dominant key so the maximum moves for every row that sees it."""
+    case = synthetic.multiquery_case("mq33", seq_lens=[33], q_len=33, num_q_heads=4,
+                                     num_kv_heads=1, head_dim=64, kv_dtype="f32", seed=34)
+    qd = case.q[0, 32, 0].astype(np.float64)
+    case.q[0, :, :] = case.q[0, 32, 0]
+    case.k[0, 32, 0] = (qd / np.linalg.norm(qd) * 8 * 6 / np.linalg.norm(qd)).astype(np.float32)
+    want, _ = oracle.attend_multiquery_f64(case.q, case.k, case.v, case.seq_lens, case.scale)
+    bad = oracle.query_tile_twin_f64(case.q, case.k, case.v, case.seq_lens, case.scale,
+                                     tile=32, alpha=False)
+    assert _err(bad[0, 32], want[0, 32]) > 5 * max(GATES)
+    assert _err(bad[0, :32], want[0, :32]) <= 1e-12  # one tile: no rescale needed
+
+
+def test_negative_control_without_the_causal_mask_fails():
+    case = synthetic.chunked_prefill(2048, 64, kv_dtype="f32", seed=35)
+    want, _ = oracle.attend_multiquery_f64(case.q, case.k, case.v, case.seq_lens, case.scale,
+                                           heads=[(0, t, 0) for t in range(64)])
+    bad, _ = oracle.attend_multiquery_f64(case.q, case.k, case.v, case.seq_lens, case.scale,
+                                          causal=False, heads=[(0, t, 0) for t in range(64)])
+    assert np.nanmax(np.abs(bad - want)) > 5 * max(GATES)
