@@ -42,6 +42,8 @@ ONLY = {
     "latent-f16-131072": ("latent_decode", (131072, "f16"), {"seed": 3000 + 131072}),
     "latent-f16-131072-project": ("latent_decode", (131072, "f16"), {"seed": 3000 + 131072}),
     "dsa-latent-f16": ("dsa_latent", (2048, 131072, "f16"), {}),
+    "verify4-131072": ("spec_verify", (131072, 4, "f16"), {}),
+    "prefill512-8192": ("chunked_prefill", (8192, 512, "f16"), {}),
 }
 
 # HBM traffic of the headline split kernel, measured with rocprofv3 counters
@@ -304,6 +306,41 @@ def measure_project(case, steps, warmup, w_dtype="bf16", proj_dim=128, flush=Non
     return res
 
 
+def measure_query_tiles(case, steps, warmup, flush=None):
+    """Several queries per sequence (attn_query_tiles: query-tile split kernel,
+    then the combine). Algorithmic bytes: K and V rows read once (positions <
+    L_b), q read once, out and lse written once. Algorithmic flops: 4*D per
+    visible (query, head, position) triple (scores and weighted values; the
+    kernel issues twice that on MFMA for its high/low 16-bit split)."""
+    import torch
+
+    import oracle
+    from split_kv_flash_amd import QueryTileCall
+    from synthetic.torch_io import to_device
+
+    t = to_device(case)
+    call = QueryTileCall(t["q"], t["k"], t["v"], t["seq_lens"], case.seq_lens, scale=case.scale)
+    total, _ = time_calls(call, steps, warmup, flush)
+    Q = call.q_len
+    vis = sum(int(x) for L in case.seq_lens for x in oracle.causal_limits(int(L), Q) if x > 0)
+    flops = 4.0 * case.head_dim_qk * case.num_q_heads * vis
+    byts = case.kv_bytes() + case.q.nbytes + case.batch * Q * case.num_q_heads * (case.head_dim_v + 1) * 4
+    us = median(total) * 1e3
+    res = {"workload": case.name, "q_len": Q, "n_splits": call.plan.n_splits, "chunk": call.plan.chunk,
+           "us_per_call": round(us, 2), "us_p10": round(pct(total, 0.1) * 1e3, 2),
+           "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+           "frac_of_peak": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+           "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2),
+           "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS["f16"], 4),
+           "bytes_call": byts, "flops_call": flops,
+           "tokens_per_s_per_layer": round(case.batch * Q * 1e6 / us, 1),
+           "mall_flushed": flush is not None}
+    del call, t
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def bandwidth_control(nbytes=1 << 30, reps=20):
     """Achievable-bandwidth controls on the same GPU in the same run: torch's
     read-only sum over a 1 GiB f32 tensor and a 1 GiB device-to-device copy."""
@@ -398,6 +435,8 @@ def main():
         c = getattr(synthetic, fn)(*pos, **kw)
         if args.only.endswith("-project"):
             r = measure_project(c, args.steps, args.warmup, "bf16", 128)
+        elif "q_len" in c.meta:
+            r = measure_query_tiles(c, args.steps, args.warmup)
         else:
             r, _, _ = measure(c, args.steps, args.warmup, args.n_splits)
         log(f"{args.only}: {r}")
@@ -439,6 +478,10 @@ def main():
                 specs.append(lambda kv=kv, L=L: synthetic.latent_decode(L, kv, seed=3000 + L))
         for kv in ("f32", "f16"):  # sparse: top-2048 rows of a 131,072-row latent cache
             specs.append(lambda kv=kv: synthetic.dsa_latent(2048, 131072, kv))
+        # several queries per sequence (query tiles)
+        qspecs = [lambda: synthetic.spec_verify(131072, 4, "f16"),
+                  lambda: synthetic.chunked_prefill(8192, 512, "f16"),
+                  lambda: synthetic.causal_block(2048, "f16")]
         for mk in specs:
             c = mk()
             small = c.kv_bytes() < MALL_FLUSH_BYTES  # could stay cached between calls
@@ -449,6 +492,13 @@ def main():
                 r = measure_project(c, args.rung_steps, args.rung_warmup, "bf16", 128, flush)
                 log(f"rung {r}")
                 rungs.append(r)
+            del c
+        for mk in qspecs:
+            c = mk()
+            small = c.kv_bytes() < MALL_FLUSH_BYTES
+            r = measure_query_tiles(c, args.rung_steps, args.rung_warmup, flush if small else None)
+            log(f"rung {r}")
+            rungs.append(r)
             del c
         del flush
         torch.cuda.empty_cache()

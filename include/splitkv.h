@@ -275,6 +275,43 @@ sk_status_t attn_decode_combine_project(const sk_desc_t* desc, const sk_plan_t* 
                                         int32_t w_dtype, int32_t proj_dim, float* out, float* lse,
                                         hipStream_t stream);
 
+/* Several query positions per sequence (speculative verify, chunked prefill, causal
+ * self-attention): the q_len newest positions of every sequence attend their cache
+ * causally. Query t (0 <= t < q_len) of sequence b sits at position L_b - q_len + t and
+ * attends positions [0, L_b - q_len + t] ("Decoder Block 6: Online Attention, the
+ * Capstone": a tile of query rows stays resident while each K/V tile is staged on chip
+ * once, every row carrying its own running max, normaliser and accumulator). The context
+ * is split as for single queries and the same combine merges the slices.
+ *   q         device, [batch][q_len][num_q_heads][head_dim_qk] of q_dtype, contiguous
+ *   k, v      device, contiguous caches as for SK_KV_CONTIGUOUS, f16 or bf16
+ *   seq_lens  device int32 [batch]: L_b, the positions in the cache including the q_len
+ *             newest; 1 <= L_b <= min(max_seq_len, n_splits*chunk)
+ *   workspace >= attn_query_tiles_workspace_bytes(desc, plan, q_len) bytes, 256-byte aligned;
+ *             partials of the (query, head) rows, row t*num_q_heads + h
+ *   out       device f32 [batch][q_len][num_q_heads][head_dim_v]
+ *   lse       device f32 [batch][q_len][num_q_heads], or NULL
+ * Two launches (the query-tile split kernel, then the combine). A query with no visible
+ * position (L_b < q_len) gets NaN. Products run on 16-bit MFMA with q and the softmax
+ * weights each split into a high and a low 16-bit part, f32 accumulation.
+ * Supported: separate K and V, contiguous, f16/bf16 KV, head_dim 64/128/256, any group size.
+ * Errors: SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE_TOO_SMALL (nothing
+ * launched), SK_ERR_LAUNCH. */
+sk_status_t attn_query_tiles(const sk_desc_t* desc, const sk_plan_t* plan, int32_t q_len,
+                             const void* q, const void* k, const void* v,
+                             const int32_t* seq_lens, void* workspace, size_t workspace_bytes,
+                             float* out, float* lse, hipStream_t stream);
+
+/* Split plan for attn_query_tiles (host only): as attn_decode_plan with the workgroup
+ * budget counted over (KV head, 64-row query tile, slice); an explicit n_splits is
+ * honoured with chunk = ceil(max_seq_len / n_splits). */
+sk_status_t attn_query_tiles_plan(const sk_desc_t* desc, int32_t q_len, int32_t max_seq_len,
+                                  int64_t total_tokens, int32_t cu_count,
+                                  int32_t n_splits_requested, sk_plan_t* plan);
+
+/* Workspace bytes attn_query_tiles needs (0 if the arguments are invalid). */
+size_t attn_query_tiles_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan,
+                                        int32_t q_len);
+
 /* Static text for a status code. */
 const char* attn_decode_status_string(sk_status_t status);
 

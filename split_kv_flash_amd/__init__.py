@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     attn_decode_kernel_info,
     attn_decode_last_error, attn_decode_one_launch, attn_decode_plan, attn_decode_splitk,
     attn_decode_status_string, attn_decode_workspace_bytes, attn_decode_workspace_init,
+    attn_query_tiles, attn_query_tiles_plan, attn_query_tiles_workspace_bytes,
 )
 
 __all__ = [
@@ -30,7 +31,8 @@ __all__ = [
     "attn_decode_workspace_bytes", "attn_decode_splitk", "attn_decode_combine",
     "attn_decode_status_string", "attn_decode_last_error", "attn_decode_kernel_info",
     "attn_decode", "attn_decode_one_launch", "attn_decode_workspace_init",
-    "attn_decode_combine_project",
+    "attn_decode_combine_project", "QueryTileCall", "attn_query_tiles", "attn_query_tiles_plan",
+    "attn_query_tiles_workspace_bytes",
 ]
 
 
@@ -222,3 +224,42 @@ class DecodeCall:
         m = ws[m_off:m_off + rows * 4].view(torch.float32).view(d.batch, d.num_q_heads, p.n_splits)
         l = ws[l_off:l_off + rows * 4].view(torch.float32).view(d.batch, d.num_q_heads, p.n_splits)
         return acc, m, l
+
+
+class QueryTileCall:
+    """Several query positions per sequence (``attn_query_tiles``): q is
+    [B][q_len][Hq][D]; query t of sequence b attends positions
+    [0, L_b - q_len + t]. Owns the plan, workspace and outputs
+    (out [B][q_len][Hq][D], lse [B][q_len][Hq])."""
+
+    def __init__(self, q, k, v, seq_lens, host_seq_lens, *, scale: float, n_splits: int = 0,
+                 cu_count: Optional[int] = None):
+        import torch
+
+        if q.dim() != 4 or not q.is_contiguous():
+            raise SplitKVError(binding.SK_ERR_INVALID_ARG, "q must be a contiguous [B][Q][Hq][D] tensor")
+        B, Q, Hq, D = q.shape
+        self.q_len = int(Q)
+        # The descriptor of one query position: [B][Hq][D].
+        self.desc = make_desc(q[:, 0].contiguous(), k, v, scale=scale)
+        lens = [int(x) for x in host_seq_lens]
+        if len(lens) != B:
+            raise SplitKVError(binding.SK_ERR_INVALID_ARG, "host_seq_lens has the wrong length")
+        if cu_count is None:
+            cu_count = torch.cuda.get_device_properties(q.device).multi_processor_count
+        self.plan = attn_query_tiles_plan(self.desc, self.q_len, max(lens), sum(lens),
+                                          int(cu_count), n_splits)
+        limit = min(self.desc.max_seq_len, self.plan.n_splits * self.plan.chunk)
+        if min(lens) < 1 or max(lens) > limit:
+            raise SplitKVError(binding.SK_ERR_INVALID_ARG, f"sequence lengths must lie in [1, {limit}]")
+        self.ws_bytes = attn_query_tiles_workspace_bytes(self.desc, self.plan, self.q_len)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=q.device)
+        self.out = torch.empty(B, Q, Hq, D, dtype=torch.float32, device=q.device)
+        self.lse = torch.empty(B, Q, Hq, dtype=torch.float32, device=q.device)
+        self.q, self.k, self.v, self.seq_lens = q, k, v, seq_lens
+
+    def __call__(self, stream=None, with_lse: bool = True):
+        attn_query_tiles(self.desc, self.plan, self.q_len, self.q, self.k, self.v, self.seq_lens,
+                         self.workspace, self.ws_bytes, self.out, self.lse if with_lse else None,
+                         _stream_handle(stream))
+        return self.out, self.lse

@@ -94,6 +94,13 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_combine_project.argtypes = [PD, PP, c_void_p, c_void_p, c_size_t, c_void_p,
                                               c_int32, c_int32, c_void_p, c_void_p, c_void_p]
     L.attn_decode_combine_project.restype = c_int32
+    L.attn_query_tiles.argtypes = [PD, PP, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_void_p, c_size_t, c_void_p, c_void_p, c_void_p]
+    L.attn_query_tiles.restype = c_int32
+    L.attn_query_tiles_plan.argtypes = [PD, c_int32, c_int32, c_int64, c_int32, c_int32, PP]
+    L.attn_query_tiles_plan.restype = c_int32
+    L.attn_query_tiles_workspace_bytes.argtypes = [PD, PP, c_int32]
+    L.attn_query_tiles_workspace_bytes.restype = c_size_t
     L.attn_decode_one_launch.argtypes = L.attn_decode.argtypes
     L.attn_decode_one_launch.restype = c_int32
     _lib = L
@@ -185,6 +192,29 @@ def attn_decode_combine_project(desc: SkDesc, plan: SkPlan, seq_lens, workspace,
                                              _ptr(seq_lens), _ptr(workspace), int(workspace_bytes),
                                              _ptr(w_proj), int(w_dtype), int(proj_dim), _ptr(out),
                                              _ptr(lse), stream))
+
+
+def attn_query_tiles_plan(desc: SkDesc, q_len: int, max_seq_len: int, total_tokens: int,
+                          cu_count: int, n_splits_requested: int = 0) -> SkPlan:
+    plan = SkPlan()
+    _check(lib().attn_query_tiles_plan(ctypes.byref(desc), int(q_len), int(max_seq_len),
+                                       int(total_tokens), int(cu_count), int(n_splits_requested),
+                                       ctypes.byref(plan)))
+    return plan
+
+
+def attn_query_tiles_workspace_bytes(desc: SkDesc, plan: SkPlan, q_len: int) -> int:
+    n = lib().attn_query_tiles_workspace_bytes(ctypes.byref(desc), ctypes.byref(plan), int(q_len))
+    if n == 0:
+        raise SplitKVError(SK_ERR_INVALID_ARG, attn_decode_last_error())
+    return int(n)
+
+
+def attn_query_tiles(desc: SkDesc, plan: SkPlan, q_len: int, q, k, v, seq_lens, workspace,
+                     workspace_bytes: int, out, lse, stream: int) -> None:
+    _check(lib().attn_query_tiles(ctypes.byref(desc), ctypes.byref(plan), int(q_len), _ptr(q),
+                                  _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(workspace),
+                                  int(workspace_bytes), _ptr(out), _ptr(lse), stream))
 
 
 def attn_decode_kernel_info(desc: SkDesc, plan: SkPlan) -> SkKernelInfo:

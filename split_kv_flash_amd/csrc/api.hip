@@ -351,6 +351,123 @@ sk_status_t attn_decode_combine_project(const sk_desc_t* desc, const sk_plan_t* 
   return ok();
 }
 
+// Several queries per sequence: the combine sees q_len * num_q_heads rows per
+// sequence ((query position, head) pairs), as if they were heads.
+static sk_desc_t rows_desc(const sk_desc_t& d, int32_t q_len) {
+  sk_desc_t r = d;
+  r.num_q_heads = d.num_q_heads * q_len;
+  return r;
+}
+
+static sk_status_t check_query_tiles(const sk_desc_t* desc, int32_t q_len) {
+  sk_status_t s = check_desc(desc);
+  if (s != SK_OK) return s;
+  if (q_len < 1) return fail(SK_ERR_INVALID_ARG, "q_len must be >= 1 (got %d)", q_len);
+  if ((int64_t)q_len * desc->num_q_heads > (1 << 24))
+    return fail(SK_ERR_INVALID_ARG, "q_len * num_q_heads exceeds 2^24");
+  if ((int64_t)desc->num_kv_heads * sk::query_tile_rows_tiles(*desc, q_len) > 0x7fffffff)
+    return fail(SK_ERR_INVALID_ARG, "too many query tiles");
+  if (!sk::query_tile_supported(*desc))
+    return fail(SK_ERR_UNSUPPORTED,
+                "query tiles support separate K and V, contiguous, f16/bf16 KV, head_dim 64/128/256");
+  return SK_OK;
+}
+
+sk_status_t attn_query_tiles_plan(const sk_desc_t* desc, int32_t q_len, int32_t max_seq_len,
+                                  int64_t total_tokens, int32_t cu_count,
+                                  int32_t n_splits_requested, sk_plan_t* plan) {
+  sk_status_t s = check_query_tiles(desc, q_len);
+  if (s != SK_OK) return s;
+  if (!plan) return fail(SK_ERR_INVALID_ARG, "plan is NULL");
+  if (max_seq_len < 1 || max_seq_len > desc->max_seq_len)
+    return fail(SK_ERR_INVALID_ARG, "max_seq_len %d outside [1, %d]", max_seq_len, desc->max_seq_len);
+  if (total_tokens < max_seq_len || total_tokens > (int64_t)max_seq_len * desc->batch)
+    return fail(SK_ERR_INVALID_ARG, "total_tokens %lld is inconsistent with max_seq_len and batch",
+                (long long)total_tokens);
+  if (cu_count < 1) return fail(SK_ERR_INVALID_ARG, "cu_count must be >= 1");
+  if (n_splits_requested < 0 || n_splits_requested > kMaxGridYZ)
+    return fail(SK_ERR_INVALID_ARG, "n_splits_requested %d out of range", n_splits_requested);
+  if (n_splits_requested > 0) {
+    plan->n_splits = n_splits_requested;
+    plan->chunk = (int32_t)ceil_div(max_seq_len, n_splits_requested);
+    return ok();
+  }
+  // One round of one workgroup per compute unit over (KV head, query tile,
+  // slice), as for single queries ([I3725] section 2's rule on the product).
+  const int64_t tiles = (int64_t)desc->num_kv_heads * sk::query_tile_rows_tiles(*desc, q_len);
+  int64_t chunk = ceil_div(tiles * total_tokens, (int64_t)cu_count);
+  if (chunk < kMinChunk) chunk = kMinChunk;
+  chunk = ceil_div(chunk, kChunkGranule) * kChunkGranule;
+  int64_t n = ceil_div(max_seq_len, chunk);
+  if (n > kMaxGridYZ) {
+    n = kMaxGridYZ;
+    chunk = ceil_div(max_seq_len, n);
+  }
+  plan->n_splits = (int32_t)n;
+  plan->chunk = (int32_t)chunk;
+  return ok();
+}
+
+size_t attn_query_tiles_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan,
+                                        int32_t q_len) {
+  if (check_desc(desc) != SK_OK || check_plan(desc, plan) != SK_OK || q_len < 1) return 0;
+  const sk_desc_t r = rows_desc(*desc, q_len);
+  return sk::ws_layout(r, *plan).total;
+}
+
+sk_status_t attn_query_tiles(const sk_desc_t* desc, const sk_plan_t* plan, int32_t q_len,
+                             const void* q, const void* k, const void* v,
+                             const int32_t* seq_lens, void* workspace, size_t workspace_bytes,
+                             float* out, float* lse, hipStream_t stream) {
+  sk_status_t s = check_query_tiles(desc, q_len);
+  if (s != SK_OK) return s;
+  if ((s = check_plan(desc, plan)) != SK_OK) return s;
+  if (!q || !k || !v || !seq_lens || !workspace || !out)
+    return fail(SK_ERR_INVALID_ARG, "q, k, v, seq_lens, workspace and out must be non-NULL");
+  if ((uintptr_t)workspace % 256) return fail(SK_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if ((uintptr_t)k % 16 || (uintptr_t)v % 16 || (uintptr_t)q % 16 || (uintptr_t)out % 16)
+    return fail(SK_ERR_INVALID_ARG, "q, K, V and out must be 16-byte aligned");
+  const sk_desc_t r = rows_desc(*desc, q_len);
+  const sk::WsLayout w = sk::ws_layout(r, *plan);
+  if (workspace_bytes < w.total)
+    return fail(SK_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                w.total);
+  char* ws = static_cast<char*>(workspace);
+  sk::QueryTileLaunch a;
+  a.d = desc;
+  a.p = plan;
+  a.q_len = q_len;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.seq_lens = seq_lens;
+  a.ws_acc = reinterpret_cast<float*>(ws + w.acc_off);
+  a.ws_m = reinterpret_cast<float*>(ws + w.m_off);
+  a.ws_l = reinterpret_cast<float*>(ws + w.l_off);
+  a.stream = stream;
+  s = sk::query_tile_launch(a);
+  if (s != SK_OK) return fail(s, "no query-tile kernel for this descriptor");
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(SK_ERR_LAUNCH, "query-tile kernel launch failed: %s", hipGetErrorString(e));
+  sk::CombineLaunch c;
+  c.d = &r;
+  c.p = plan;
+  c.seq_lens = seq_lens;
+  c.ws_acc = a.ws_acc;
+  c.ws_m = a.ws_m;
+  c.ws_l = a.ws_l;
+  c.out = out;
+  c.lse = lse;
+  c.stream = stream;
+  s = sk::combine_launch(c);
+  if (s != SK_OK) return fail(s, "combine launch rejected");
+  e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(SK_ERR_LAUNCH, "combine kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 sk_status_t attn_decode_workspace_init(const sk_desc_t* desc, const sk_plan_t* plan,
                                        void* workspace, size_t workspace_bytes,
                                        hipStream_t stream) {

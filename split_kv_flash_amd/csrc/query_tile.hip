@@ -1,0 +1,325 @@
+// Query-tile online attention: several query positions per sequence, causal.
+//
+// "Decoder Block 6: Online Attention, the Capstone": keep a tile of query rows
+// resident, stage each K/V tile on chip once and let every row of the tile
+// consume it; each row carries its running maximum m, normaliser l and
+// unnormalised accumulator, and at every K/V tile
+//     m' = max(m, tile max), alpha = exp(m - m'),
+//     l  = alpha l + sum_j exp(s_j - m'),  acc = alpha acc + sum_j exp(s_j - m') v_j.
+// The query rows here are the (query position, head) pairs of one KV group:
+// query t of a sequence of L positions sits at position L - q_len + t and sees
+// positions [0, L - q_len + t] (q_len = 1 is decode, q_len = L is causal
+// self-attention). The context is also split (Lecture 06 section 2): a
+// workgroup covers one slice and writes the partial (m, l, acc) of each of its
+// rows, and the combine kernel merges the slices, so a few query rows over a
+// long context (speculative verify) still fill the GPU.
+//
+// Work decomposition (MI355X-first):
+//   * One workgroup (4 waves) per (sequence, KV head, 64-row query tile,
+//     context slice); wave w owns rows 16w .. 16w+15 of the tile, rows ordered
+//     (position t, head) so a tile's rows have neighbouring causal limits.
+//   * K/V tiles of 32 positions are staged in LDS (row stride D + 8 halves),
+//     double-buffered: the next tile's global loads are in flight in
+//     registers while the current tile is consumed; one barrier per tile.
+//   * Scores are computed transposed, S^T = K Q^T, with
+//     v_mfma_f32_16x16x32_{f16,bf16}: the K rows are the A operand and the
+//     query rows (held in registers) the B operand. The result leaves lane
+//     (row l16, quarter lq) holding positions 4lq+i and 16+4lq+i of its row,
+//     which, with the contraction index ordered the same way, is exactly that
+//     lane's A operand of the output product P V; the V operands come from the
+//     gfx950 transpose read ds_read_b64_tr_b16 in the same position order. P
+//     never goes through LDS.
+//   * Precision: the MFMA inputs are 16-bit, so q and P are each split into a
+//     high and a low 16-bit part (two products each): x = hi + lo carries
+//     about 22 bits (f16) or 16 bits (bf16) of x, so scores and weights keep
+//     close to f32 accuracy while K and V are used exactly as stored.
+#include "sk_device.h"
+#include "sk_internal.h"
+
+namespace sk {
+
+typedef _Float16 qt_half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 qt_bf8 __attribute__((ext_vector_type(8)));
+typedef float qt_f4 __attribute__((ext_vector_type(4)));
+typedef short qt_s4 __attribute__((ext_vector_type(4)));
+typedef short qt_s8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) qt_s4 qt_lds_s4;
+typedef uint32_t qt_u4 __attribute__((ext_vector_type(4)));  // one 16-byte chunk
+
+struct QtArgs {
+  const void* q;  // [B][Q][Hq][D]
+  const void* k;
+  const void* v;
+  const int32_t* seq_lens;
+  float* ws_acc;  // [B][Q*Hq][S][D], row (t, h) = t*Hq + h
+  float* ws_m;
+  float* ws_l;
+  int64_t stride_seq, stride_pos, stride_head;
+  int32_t q_dtype;
+  int32_t Q, Hq, G, S, chunk, cap, nqt;  // nqt: 64-row query tiles per KV head
+  float qscale;                          // scale * log2(e)
+};
+
+// 16-bit storage types: round-to-nearest-even conversion from f32, widening,
+// and the 16x16x32 MFMA of that type.
+template <typename KT>
+struct QtType;
+template <>
+struct QtType<_Float16> {
+  static __device__ __forceinline__ short from(float x) { return __builtin_bit_cast(short, (_Float16)x); }
+  static __device__ __forceinline__ float to(short b) { return (float)__builtin_bit_cast(_Float16, b); }
+  static __device__ __forceinline__ qt_f4 mma(qt_s8 a, qt_s8 b, qt_f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(qt_half8, a),
+                                                  __builtin_bit_cast(qt_half8, b), c, 0, 0, 0);
+  }
+};
+template <>
+struct QtType<bf16_t> {
+  static __device__ __forceinline__ short from(float x) { return __builtin_bit_cast(short, (__bf16)x); }
+  static __device__ __forceinline__ float to(short b) {
+    return __uint_as_float(((uint32_t)(uint16_t)b) << 16);
+  }
+  static __device__ __forceinline__ qt_f4 mma(qt_s8 a, qt_s8 b, qt_f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(qt_bf8, a),
+                                                   __builtin_bit_cast(qt_bf8, b), c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ qt_s4 qt_read_tr(const short* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((qt_lds_s4*)(p));
+}
+
+template <typename KT, int D>
+__global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
+  using TT = QtType<KT>;
+  constexpr int T = 32;        // positions per K/V tile
+  constexpr int RS = D + 8;    // LDS row stride (16-bit elements)
+  constexpr int KS = D / 32;   // score MFMA steps
+  constexpr int CB = D / 16;   // output column blocks
+  constexpr int CPR = D / 8;   // 16-byte chunks per row
+  constexpr int NCH = D / 64;  // chunks per thread per tile (K and V each): 32*CPR / 256
+  static_assert(D % 64 == 0, "head width");
+
+  __shared__ __align__(16) short s_kv[2][2][T * RS];  // [buffer][K, V][row * RS + column]
+
+  const int g = blockIdx.x / a.nqt;
+  const int qt = blockIdx.x - g * a.nqt;
+  const int split = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int lq = lane >> 4;
+  const int QG = a.Q * a.G;
+  const int QH = a.Q * a.Hq;
+
+  const int L = min(a.seq_lens[b], a.cap);
+  const int64_t start = (int64_t)split * a.chunk;
+  const int64_t end = min((int64_t)L, start + a.chunk);
+
+  // This lane's query row (scores and softmax): row l16 of the wave.
+  const int rho = qt * 64 + wave * 16 + l16;
+  const bool rvalid = rho < QG;
+  const int t = rvalid ? rho / a.G : 0;
+  const int hh = rvalid ? rho - t * a.G : 0;
+  const int64_t lim = rvalid ? (int64_t)L - a.Q + t + 1 : 0;  // visible: positions < lim
+  // The tile's rows are ordered by position, so its last row sees the most.
+  const int rho_last = min(qt * 64 + 63, QG - 1);
+  const int64_t lim_max = (int64_t)L - a.Q + rho_last / a.G + 1;
+  const int64_t stop = min(end, lim_max);  // this workgroup reads positions [start, stop)
+
+  float m = -INFINITY, l = 0.0f;  // row l16 (replicated over the quarters), base-2 units
+  qt_f4 acc[CB];
+#pragma unroll
+  for (int c = 0; c < CB; ++c) acc[c] = qt_f4{0.f, 0.f, 0.f, 0.f};
+
+  if (start < stop) {
+    // Query row as B operands: lane (l16, lq) holds columns 32ks + 8lq .. +7 of
+    // row l16, pre-scaled into base-2 units and split into high and low parts.
+    qt_s8 qh[KS], ql[KS];
+    {
+      const int64_t qbase = (((int64_t)b * a.Q + t) * a.Hq + g * a.G + hh) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = rvalid ? load_q(a.q, a.q_dtype, qbase + 32 * ks + 8 * lq + e) * a.qscale : 0.0f;
+          const short hi = TT::from(x);
+          qh[ks][e] = hi;
+          ql[ks][e] = TT::from(x - TT::to(hi));
+        }
+    }
+
+    const KT* __restrict__ kp = reinterpret_cast<const KT*>(a.k) + (int64_t)b * a.stride_seq + (int64_t)g * a.stride_head;
+    const KT* __restrict__ vp = reinterpret_cast<const KT*>(a.v) + (int64_t)b * a.stride_seq + (int64_t)g * a.stride_head;
+    // Tile rows past `stop` re-read row stop-1 (in range; their scores are masked).
+    auto gload = [&](qt_u4 (&kr)[NCH], qt_u4 (&vr)[NCH], int64_t tb) {
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int c = tid + 256 * j;
+        const int row = c / CPR, col = (c - (c / CPR) * CPR) * 8;
+        const int64_t pos = min(tb + row, stop - 1);
+        const int64_t off = pos * a.stride_pos + col;
+        kr[j] = *reinterpret_cast<const qt_u4*>(kp + off);
+        vr[j] = *reinterpret_cast<const qt_u4*>(vp + off);
+      }
+    };
+    auto swrite = [&](int buf, const qt_u4 (&kr)[NCH], const qt_u4 (&vr)[NCH]) {
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int c = tid + 256 * j;
+        const int row = c / CPR, col = (c - (c / CPR) * CPR) * 8;
+        *reinterpret_cast<qt_u4*>(&s_kv[buf][0][row * RS + col]) = kr[j];
+        *reinterpret_cast<qt_u4*>(&s_kv[buf][1][row * RS + col]) = vr[j];
+      }
+    };
+
+    const int ntiles = (int)((stop - start + T - 1) / T);
+    qt_u4 kr[NCH], vr[NCH];
+    gload(kr, vr, start);
+    swrite(0, kr, vr);
+    __syncthreads();
+    for (int i = 0; i < ntiles; ++i) {
+      const int64_t tb = start + (int64_t)i * T;
+      const bool more = i + 1 < ntiles;
+      if (more) gload(kr, vr, tb + T);  // the next tile, in flight during this one
+      const short* kb = s_kv[i & 1][0];
+      const short* vb = s_kv[i & 1][1];
+
+      // ---- scores S^T: two blocks of 16 positions, this wave's 16 rows ----
+      qt_f4 sp[2] = {qt_f4{0.f, 0.f, 0.f, 0.f}, qt_f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const qt_s8 av = *reinterpret_cast<const qt_s8*>(kb + (16 * pb + l16) * RS + 32 * ks + 8 * lq);
+          sp[pb] = TT::mma(av, qh[ks], sp[pb]);
+          sp[pb] = TT::mma(av, ql[ks], sp[pb]);
+        }
+
+      // ---- online softmax of row l16 over the tile's visible positions ----
+      float s[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t pos = tb + 16 * pb + 4 * lq + e;
+          s[4 * pb + e] = (pos < stop && pos < lim) ? sp[pb][e] : -INFINITY;
+          mx = fmaxf(mx, s[4 * pb + e]);
+        }
+      mx = fmaxf(mx, xor16(mx));
+      mx = fmaxf(mx, xor32(mx));
+      const float mn = fmaxf(m, mx);
+      const float mu = (mn == -INFINITY) ? 0.0f : mn;
+      const float al = fast_exp2(m - mu);
+      float ls = 0.0f;
+      qt_s8 ph, pl;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = fast_exp2(s[j] - mu);
+        ls += p;
+        const short hi = TT::from(p);
+        ph[j] = hi;
+        pl[j] = TT::from(p - TT::to(hi));
+      }
+      ls += xor16(ls);
+      ls += xor32(ls);
+      l = fmaf(l, al, ls);
+      m = mn;
+      // Accumulator item e is row 4lq + e, whose factor lane 4lq + e holds.
+      if (__any(al != 1.0f)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ae = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * lq + e) << 2, __float_as_int(al)));
+#pragma unroll
+          for (int c = 0; c < CB; ++c) acc[c][e] *= ae;
+        }
+      }
+
+      // ---- output: acc += P V, positions in the scores' order ----
+      const short* vrow = vb + (4 * lq + (l16 >> 2)) * RS + 4 * (l16 & 3);
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const qt_s4 v0 = qt_read_tr(vrow + 16 * c);
+        const qt_s4 v1 = qt_read_tr(vrow + 16 * RS + 16 * c);
+        const qt_s8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[c] = TT::mma(ph, vv, acc[c]);
+        acc[c] = TT::mma(pl, vv, acc[c]);
+      }
+      if (more) swrite((i + 1) & 1, kr, vr);
+      __syncthreads();
+    }
+  }
+
+  // ---- partials of this wave's rows (rows with nothing visible: neutral) ----
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int re = qt * 64 + wave * 16 + 4 * lq + e;
+    if (re < QG) {
+      const int te = re / a.G;
+      const int w = te * a.Hq + g * a.G + (re - te * a.G);
+      float* dst = a.ws_acc + (((int64_t)b * QH + w) * a.S + split) * D + l16;
+#pragma unroll
+      for (int c = 0; c < CB; ++c) dst[16 * c] = acc[c][e];
+    }
+  }
+  if (lq == 0 && rvalid) {
+    const int64_t r = ((int64_t)b * QH + t * a.Hq + g * a.G + hh) * a.S + split;
+    a.ws_m[r] = m * kLn2;
+    a.ws_l[r] = l;
+  }
+}
+
+bool query_tile_supported(const sk_desc_t& d) {
+  return !d.kv_shared && d.layout == SK_KV_CONTIGUOUS && d.head_dim_qk == d.head_dim_v &&
+         (d.head_dim_qk == 64 || d.head_dim_qk == 128 || d.head_dim_qk == 256) &&
+         (d.kv_dtype == SK_F16 || d.kv_dtype == SK_BF16);
+}
+
+int query_tile_rows_tiles(const sk_desc_t& d, int q_len) {
+  const int G = d.num_q_heads / d.num_kv_heads;
+  return (q_len * G + 63) / 64;
+}
+
+template <typename KT>
+static sk_status_t qt_by_dim(const QueryTileLaunch& s, const QtArgs& a, dim3 grid) {
+  switch (s.d->head_dim_qk) {
+    case 64: hipLaunchKernelGGL((query_tile_kernel<KT, 64>), grid, dim3(256), 0, s.stream, a); break;
+    case 128: hipLaunchKernelGGL((query_tile_kernel<KT, 128>), grid, dim3(256), 0, s.stream, a); break;
+    case 256: hipLaunchKernelGGL((query_tile_kernel<KT, 256>), grid, dim3(256), 0, s.stream, a); break;
+    default: return SK_ERR_UNSUPPORTED;
+  }
+  return SK_OK;
+}
+
+sk_status_t query_tile_launch(const QueryTileLaunch& s) {
+  const sk_desc_t& d = *s.d;
+  if (!query_tile_supported(d)) return SK_ERR_UNSUPPORTED;
+  QtArgs a;
+  a.q = s.q;
+  a.k = s.k;
+  a.v = s.v;
+  a.seq_lens = s.seq_lens;
+  a.ws_acc = s.ws_acc;
+  a.ws_m = s.ws_m;
+  a.ws_l = s.ws_l;
+  a.stride_seq = d.stride_seq;
+  a.stride_pos = d.stride_pos;
+  a.stride_head = d.stride_head;
+  a.q_dtype = d.q_dtype;
+  a.Q = s.q_len;
+  a.Hq = d.num_q_heads;
+  a.G = d.num_q_heads / d.num_kv_heads;
+  a.S = s.p->n_splits;
+  a.chunk = s.p->chunk;
+  a.cap = d.max_seq_len;
+  a.nqt = query_tile_rows_tiles(d, s.q_len);
+  a.qscale = d.scale * kLog2e;
+  const dim3 grid(d.num_kv_heads * a.nqt, s.p->n_splits, d.batch);
+  if (d.kv_dtype == SK_F16) return qt_by_dim<_Float16>(s, a, grid);
+  return qt_by_dim<bf16_t>(s, a, grid);
+}
+
+}  // namespace sk

@@ -64,6 +64,20 @@ struct ProjectLaunch {
   hipStream_t stream;
 };
 
+struct QueryTileLaunch {
+  const sk_desc_t* d;
+  const sk_plan_t* p;
+  int32_t q_len;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seq_lens;
+  float* ws_acc;
+  float* ws_m;
+  float* ws_l;
+  hipStream_t stream;
+};
+
 // Host-only capability checks (no HIP calls).
 bool gqa_supported(const sk_desc_t& d);
 // Workgroups per compute unit the split heuristic plans for a uniform batch.
@@ -82,6 +96,10 @@ sk_status_t latent_split_launch(const SplitLaunch& a, bool launch, const void** 
                                 int* block);
 sk_status_t combine_launch(const CombineLaunch& a);
 bool project_supported(const sk_desc_t& d, int w_dtype);
+bool query_tile_supported(const sk_desc_t& d);
+// 64-row query tiles per KV head for q_len queries.
+int query_tile_rows_tiles(const sk_desc_t& d, int q_len);
+sk_status_t query_tile_launch(const QueryTileLaunch& a);
 sk_status_t combine_project_launch(const ProjectLaunch& a);
 // Zeroes n 32-bit words with a fill kernel (no memset node, so a captured
 // graph may hold it).

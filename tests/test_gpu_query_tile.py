@@ -1,0 +1,167 @@
+"""GPU parity of query-tile attention (attn_query_tiles: several query
+positions per sequence, causal) against the float64 oracle.
+
+Query t of a sequence of L positions sits at L - q_len + t and attends
+positions [0, L - q_len + t] ("Decoder Block 6: Online Attention, the
+Capstone"). K/V padding past each length is NaN, so an over-read poisons the
+output; the workspace is NaN beforehand. Gates as for decode (max abs 2e-3
+and relL2 1e-3 for 16-bit KV); q and the weights are split into high and low
+16-bit parts, so the f16 path also meets the tight f32-arithmetic bound.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from harness import ABS_GATE, REL_L2_F32_ARITH, REL_L2_GATE, errors
+from synthetic.torch_io import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import split_kv_flash_amd.binding as B
+
+    B.lib()  # fail loudly if the HIP library is missing
+
+
+def run_qt(case, *, n_splits=0, tensors=None):
+    import torch
+    from split_kv_flash_amd import QueryTileCall
+
+    t = to_device(case) if tensors is None else tensors
+    call = QueryTileCall(t["q"], t["k"], t["v"], t["seq_lens"], case.seq_lens, scale=case.scale,
+                         n_splits=n_splits)
+    call.workspace.fill_(0xFF)
+    call.out.fill_(float("nan"))
+    call.lse.fill_(float("nan"))
+    call()
+    torch.cuda.synchronize()
+    return call.out.double().cpu().numpy(), call.lse.double().cpu().numpy(), call
+
+
+def ref_qt(case, heads=None):
+    return oracle.attend_multiquery_f64(case.q, case.k, case.v, case.seq_lens, case.scale,
+                                        q_dtype=case.q_dtype, kv_dtype=case.kv_dtype, heads=heads)
+
+
+def check(case, out, ref, label, tight=None):
+    mask = ~np.isnan(ref)
+    assert np.all(np.isfinite(out[mask])), f"{label}: non-finite output"
+    ea, er, _ = errors(out, ref)
+    assert ea <= ABS_GATE[case.kv_dtype], f"{label}: max abs err {ea:.3e}"
+    assert er <= REL_L2_GATE[case.kv_dtype], f"{label}: relL2 {er:.3e}"
+    if tight if tight is not None else case.kv_dtype == "f16":
+        assert er <= REL_L2_F32_ARITH, f"{label}: relL2 {er:.3e} (hi/lo products)"
+
+
+@pytest.mark.parametrize("L,Q", [(1, 1), (33, 1), (33, 33), (33, 5), (100, 40), (64, 64), (2, 3)])
+@pytest.mark.parametrize("kv", ["f16", "bf16"])
+def test_small_causal_cases(L, Q, kv):
+    case = synthetic.multiquery_case(f"qt-{L}-{Q}", seq_lens=[L], q_len=Q, num_q_heads=4,
+                                     num_kv_heads=1, head_dim=64, kv_dtype=kv, capacity=L + 5,
+                                     seed=L * 100 + Q)
+    ref, rlse = ref_qt(case)
+    for S in (0, 1, 3):
+        out, lse, call = run_qt(case, n_splits=S)
+        check(case, out, ref, f"L={L} Q={Q} S={S} plan={call.plan}")
+        m = ~np.isnan(rlse)
+        np.testing.assert_allclose(lse[m], rlse[m], rtol=0, atol=1e-4)
+        # queries that see no position (L < Q) give NaN
+        assert np.all(np.isnan(out[np.isnan(ref)]))
+
+
+def test_length_33_with_the_maximum_in_the_second_tile():
+    """Position 32 opens the second 32-position tile and holds every row's
+    dominant key: rows that see it must rescale what they gathered in tile 1."""
+    case = synthetic.multiquery_case("qt33", seq_lens=[33], q_len=33, num_q_heads=4,
+                                     num_kv_heads=1, head_dim=64, kv_dtype="f16", seed=3333)
+    qd = case.q[0, 32, 0].astype(np.float64)
+    case.q[0, :, :] = case.q[0, 32, 0]
+    case.k[0, 32, 0] = (qd / np.linalg.norm(qd) * 8 * 6 / np.linalg.norm(qd)).astype(np.float16)
+    ref, _ = ref_qt(case)
+    out, _, _ = run_qt(case, n_splits=1)
+    check(case, out, ref, "L=33 dominant at 32")
+
+
+@pytest.mark.parametrize("G,D,kv", list(itertools.product([1, 2, 4, 6, 8], [64, 128, 256], ["f16", "bf16"])))
+def test_every_group_and_width(G, D, kv):
+    q_dtype = ["f32", "f16", "bf16"][(G + D // 64) % 3]
+    case = synthetic.multiquery_case(f"qt-G{G}-D{D}-{kv}", seq_lens=[300, 77], q_len=5,
+                                     num_q_heads=2 * G, num_kv_heads=2, head_dim=D, kv_dtype=kv,
+                                     q_dtype=q_dtype, capacity=310, seed=7700 + G * 10 + D)
+    ref, _ = ref_qt(case)
+    for S in (0, 4):
+        out, _, call = run_qt(case, n_splits=S)
+        check(case, out, ref, f"G={G} D={D} {kv} q={q_dtype} plan={call.plan}")
+
+
+def test_one_query_equals_the_decode_path():
+    case = synthetic.multiquery_case("qt1", seq_lens=[5000, 1200], q_len=1, num_q_heads=16,
+                                     num_kv_heads=4, head_dim=128, kv_dtype="f16", seed=41)
+    out, _, _ = run_qt(case)
+    import torch
+    from split_kv_flash_amd import DecodeCall
+
+    t = to_device(case)
+    dc = DecodeCall(t["q"][:, 0].contiguous(), t["k"], t["v"], t["seq_lens"], case.seq_lens,
+                    scale=case.scale)
+    dc()
+    torch.cuda.synchronize()
+    dec = dc.out.double().cpu().numpy()
+    assert np.abs(out[:, 0] - dec).max() <= 1e-5
+
+
+def test_causal_self_attention_block_2048():
+    """Decoder Block 6's shape: 4 heads of 64, 2048 tokens, every position a
+    query (q_len = L), checked on a sample of query positions."""
+    case = synthetic.causal_block(2048, kv_dtype="f16", seed=8101)
+    out, _, call = run_qt(case)
+    ts = [0, 1, 31, 32, 33, 511, 1024, 2047]
+    ref, _ = ref_qt(case, heads=[(0, t, h) for t in ts for h in range(4)])
+    check(case, out[:, ts], ref[:, ts], f"causal block plan={call.plan}")
+
+
+def test_speculative_verify_at_131072():
+    case = synthetic.spec_verify(131072, 4, kv_dtype="f16")
+    out, _, call = run_qt(case)
+    heads = [(0, t, h) for t in range(4) for h in (0, 5, 10, 15)]
+    ref, _ = ref_qt(case, heads=heads)
+    check(case, out, ref, f"verify plan={call.plan}")
+    import torch
+
+    torch.cuda.empty_cache()
+
+
+def test_chunked_prefill_512_of_8192_bf16():
+    case = synthetic.chunked_prefill(8192, 512, kv_dtype="bf16")
+    out, _, call = run_qt(case)
+    heads = [(0, t, h) for t in (0, 100, 255, 256, 511) for h in (0, 7, 15)]
+    ref, _ = ref_qt(case, heads=heads)
+    check(case, out, ref, f"prefill plan={call.plan}")
+
+
+def test_ragged_batch_and_invalid_length():
+    import torch
+
+    case = synthetic.multiquery_case("qt-rag", seq_lens=[900, 40, 3], q_len=8, num_q_heads=8,
+                                     num_kv_heads=2, head_dim=128, kv_dtype="bf16", capacity=1000,
+                                     seed=42)
+    t = to_device(case)
+    out, _, call = run_qt(case, n_splits=3, tensors=t)
+    ref, _ = ref_qt(case)
+    check(case, out, ref, "ragged")
+    t["seq_lens"][1] = 5000  # beyond the capacity: that sequence's outputs are NaN
+    call.workspace.fill_(0xFF)
+    call()
+    torch.cuda.synchronize()
+    o2 = call.out.double().cpu().numpy()
+    assert np.all(np.isnan(o2[1]))
+    assert np.array_equal(o2[0], out[0])
