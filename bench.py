@@ -139,8 +139,9 @@ def _pair():
 
 # Untimed warm-up runs at least this long as well as at least W calls: after
 # the host has spent seconds generating a workload the GPU has been idle, and
-# the first few dozen calls then run up to 25% slower while its clocks ramp.
-WARMUP_MIN_MS = 100.0
+# the first calls then run up to 25% slower while its clocks ramp; 100 ms of
+# calls still left the first of two identical timed runs 4% slower.
+WARMUP_MIN_MS = 500.0
 
 
 def warm_up(fn, calls, min_ms=WARMUP_MIN_MS):
@@ -188,7 +189,7 @@ def kernel_avg(fn, steps, evict=None):
     Cache is evicted before every launch and each launch is timed alone."""
     import torch
 
-    warm_up(fn, 1, min_ms=20.0)
+    warm_up(fn, 1, min_ms=100.0)
     if evict is None:
         e0, e1 = _pair()
         e0.record()

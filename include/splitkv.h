@@ -151,9 +151,12 @@ typedef struct {
  * splits summed over the batch, as Lecture 06 section 5.1 asks):
  *   GQA:    chunk = max(64, ceil(Hkv * total_tokens / (k * cu_count))), where k is the
  *           number of workgroups per compute unit measured best on MI355X: 1 (one
- *           round of one workgroup per compute unit), 2 for the f16 6-head group
- *           of width 256, and 8 times that for a ragged batch (total_tokens <
- *           batch * max_seq_len). The note's own S_target is about 4 per
+ *           round of one workgroup per compute unit), 8 for a ragged batch
+ *           (total_tokens < batch * max_seq_len). For a batch that is not ragged,
+ *           when that chunk is at least 1024 positions, k becomes 3/4 (192
+ *           concurrent sequential readers stream HBM faster than 256), except
+ *           for the f16 6-head group of width 256, whose VALU-heavy loop needs
+ *           every compute unit. The note's own S_target is about 4 per
  *           multiprocessor of its GPU.
  *   latent: chunk = max(64, ceil(g * total_tokens / cu_count)) with g workgroups per
  *           split: 1 for f16 caches (one workgroup serves all query heads), Hq/48

@@ -32,6 +32,7 @@ arithmetic from storage rounding ([I3725] design note, section 4,
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -213,7 +214,7 @@ def plan_splits(
     kv_shared: bool = False,
     granule: int = 64,
     min_chunk: int = 64,
-    blocks_per_cu: int = 4,
+    blocks_per_cu=4,
     min_ctx: int = 0,
     latent_groups: int = 1,
 ) -> Tuple[int, int]:
@@ -233,7 +234,8 @@ def plan_splits(
       KV heads — is budgeted on the product of blocks, as [L06] section 5.1
       asks (KV heads x splits, summed over the sequences of a batch): chunk =
       max(min_chunk, ceil(Hkv * sum(L_b) / (blocks_per_cu * cu_count))),
-      rounded up to a multiple of ``granule``.
+      rounded up to a multiple of ``granule``. ``blocks_per_cu`` may be a
+      fraction (an int or ``fractions.Fraction``; the ceiling is exact).
     * Latent attention (``kv_shared``): one block serves every query head of
       the latent (or ``latent_groups`` blocks share a split, each serving a
       slice of the heads), so the budget is one block per compute unit rather
@@ -254,7 +256,8 @@ def plan_splits(
     if kv_shared:
         chunk = max(min_chunk, -(-(latent_groups * total) // cu_count))
     else:
-        chunk = max(min_chunk, -(-(num_kv_heads * total) // (blocks_per_cu * cu_count)))
+        budget = Fraction(blocks_per_cu) * cu_count
+        chunk = max(min_chunk, math.ceil(Fraction(num_kv_heads * total) / budget))
     chunk = -(-chunk // granule) * granule
     return -(-l_max // chunk), chunk
 

@@ -732,12 +732,18 @@ static sk_status_t by_group(const SplitLaunch& s, bool launch, const void** fn, 
   }
 }
 
-int gqa_resident_blocks(const sk_desc_t& d) {
-  // The 6-head f16 kernel's VALU-heavy loop overlaps memory better with a
-  // second workgroup resident on each compute unit; every other variant
-  // streams best as one workgroup per compute unit.
+int gqa_resident_blocks(const sk_desc_t&) {
+  // One round of one workgroup per compute unit (measured best on MI355X for
+  // every variant, the 6-head f16 one included: 0.737 of peak per call at
+  // 64 splits against 0.710 at 128 for the 27B-like layer).
+  return 1;
+}
+
+bool gqa_prefers_fewer_streams(const sk_desc_t& d) {
+  // The memory-bound variants stream long slices faster from three quarters
+  // of the compute units; the 6-head f16 kernel's VALU-heavy loop needs all.
   const int G = d.num_kv_heads > 0 ? d.num_q_heads / d.num_kv_heads : 0;
-  return sliced_variant(d.kv_dtype == SK_F16, d.head_dim_qk, G) ? 2 : 1;
+  return !sliced_variant(d.kv_dtype == SK_F16, d.head_dim_qk, G);
 }
 
 bool gqa_supported(const sk_desc_t& d) {

@@ -82,6 +82,8 @@ struct QueryTileLaunch {
 bool gqa_supported(const sk_desc_t& d);
 // Workgroups per compute unit the split heuristic plans for a uniform batch.
 int gqa_resident_blocks(const sk_desc_t& d);
+// Whether long slices are planned for three quarters of the compute units.
+bool gqa_prefers_fewer_streams(const sk_desc_t& d);
 bool latent_supported(const sk_desc_t& d);
 // Workgroups that share one split of a shared latent (the f32 kernel spreads
 // the heads of a split over several).
