@@ -343,14 +343,27 @@ def measure_query_tiles(case, steps, warmup, flush=None):
 
 
 def bandwidth_control(nbytes=1 << 30, reps=20):
-    """Achievable-bandwidth controls on the same GPU in the same run: torch's
+    """Achievable-bandwidth controls on the same GPU in the same run: the
+    library's streaming-read probe over 2 GiB (16-byte loads, 4 workgroups of
+    512 threads per compute unit: the practical read ceiling), torch's
     read-only sum over a 1 GiB f32 tensor and a 1 GiB device-to-device copy."""
     import torch
 
+    from split_kv_flash_amd import binding
+
     x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     y = torch.empty_like(x)
+    big = torch.zeros(2 * nbytes // 4, dtype=torch.float32, device="cuda")
+    scratch = torch.zeros(65536, dtype=torch.float32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def probe():
+        binding.attn_decode_read_probe(big, big.numel() * 4, 4 * cus, scratch, stream)
+
     out = {}
-    for name, fn, traffic in (("read_sum", lambda: x.sum(), nbytes),
+    for name, fn, traffic in (("read_kernel", probe, 2 * nbytes),
+                              ("read_sum", lambda: x.sum(), nbytes),
                               ("copy", lambda: y.copy_(x), 2 * nbytes)):
         for _ in range(3):
             fn()
@@ -364,7 +377,7 @@ def bandwidth_control(nbytes=1 << 30, reps=20):
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
         out[name + "_GBps"] = round(traffic / (median(ts) * 1e-3) / 1e9, 1)
-    del x, y
+    del x, y, big, scratch
     torch.cuda.empty_cache()
     return out
 
@@ -464,6 +477,7 @@ def main():
 
     control = bandwidth_control()
     log(f"bandwidth control {control}")
+    roofline["frac_of_read_ceiling"] = round(achieved / control["read_kernel_GBps"], 4)
 
     rungs = []
     if not args.no_rungs:

@@ -315,6 +315,17 @@ sk_status_t attn_query_tiles_plan(const sk_desc_t* desc, int32_t q_len, int32_t 
 size_t attn_query_tiles_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan,
                                         int32_t q_len);
 
+/* Measurement aid (not part of a decode call): reads the first
+ * (bytes/16/workgroups)*workgroups*16 bytes of `buf` once with 16-byte vector loads,
+ * each of `workgroups` workgroups of 512 threads streaming one contiguous slice, and
+ * writes nothing unless the data sum to an impossible value (scratch: device, >=
+ * workgroups floats). Timed by the caller, it gives the device's achievable streaming
+ * read rate, the practical ceiling beside the published HBM peak for the split kernel's
+ * roofline. Errors: SK_ERR_INVALID_ARG (NULL or misaligned buf, workgroups outside
+ * [1, 65535], buffer smaller than one 16-byte load per workgroup), SK_ERR_LAUNCH. */
+sk_status_t attn_decode_read_probe(const void* buf, size_t bytes, int32_t workgroups,
+                                   float* scratch, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* attn_decode_status_string(sk_status_t status);
 

@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
     L.attn_query_tiles_plan.restype = c_int32
     L.attn_query_tiles_workspace_bytes.argtypes = [PD, PP, c_int32]
     L.attn_query_tiles_workspace_bytes.restype = c_size_t
+    L.attn_decode_read_probe.argtypes = [c_void_p, c_size_t, c_int32, c_void_p, c_void_p]
+    L.attn_decode_read_probe.restype = c_int32
     L.attn_decode_one_launch.argtypes = L.attn_decode.argtypes
     L.attn_decode_one_launch.restype = c_int32
     _lib = L
@@ -111,7 +113,7 @@ def header_functions() -> list:
     """Names of the functions include/splitkv.h declares."""
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_decode\w*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
 
 
 def _ptr(x) -> Optional[int]:
@@ -215,6 +217,11 @@ def attn_query_tiles(desc: SkDesc, plan: SkPlan, q_len: int, q, k, v, seq_lens, 
     _check(lib().attn_query_tiles(ctypes.byref(desc), ctypes.byref(plan), int(q_len), _ptr(q),
                                   _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(workspace),
                                   int(workspace_bytes), _ptr(out), _ptr(lse), stream))
+
+
+def attn_decode_read_probe(buf, nbytes: int, workgroups: int, scratch, stream: int) -> None:
+    _check(lib().attn_decode_read_probe(_ptr(buf), int(nbytes), int(workgroups), _ptr(scratch),
+                                        stream))
 
 
 def attn_decode_kernel_info(desc: SkDesc, plan: SkPlan) -> SkKernelInfo:

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libsplitkv.so"
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "gqa_split.hip", "combine.hip", "mla_split.hip", "project.hip", "query_tile.hip"]
+SOURCES = ["api.hip", "gqa_split.hip", "combine.hip", "mla_split.hip", "project.hip", "query_tile.hip", "read_probe.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed FP32 arithmetic; the
 # host pass warns that it does not know the feature, which is harmless.

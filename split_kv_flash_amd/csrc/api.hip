@@ -540,6 +540,22 @@ sk_status_t attn_decode_one_launch(const sk_desc_t* desc, const sk_plan_t* plan,
   return ok();
 }
 
+sk_status_t attn_decode_read_probe(const void* buf, size_t bytes, int32_t workgroups,
+                                   float* scratch, hipStream_t stream) {
+  if (!buf || !scratch) return fail(SK_ERR_INVALID_ARG, "buf and scratch must be non-NULL");
+  if ((uintptr_t)buf % 16) return fail(SK_ERR_INVALID_ARG, "buf must be 16-byte aligned");
+  if (workgroups < 1 || workgroups > kMaxGridYZ)
+    return fail(SK_ERR_INVALID_ARG, "workgroups must lie in [1, %d]", kMaxGridYZ);
+  if (bytes / 16 < (size_t)workgroups)
+    return fail(SK_ERR_INVALID_ARG, "buffer of %zu bytes is too small for %d workgroups", bytes,
+                workgroups);
+  sk::read_probe_launch(buf, bytes, workgroups, scratch, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(SK_ERR_LAUNCH, "read probe launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* attn_decode_status_string(sk_status_t status) {
   switch (status) {
     case SK_OK: return "ok";

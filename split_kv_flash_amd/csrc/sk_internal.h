@@ -106,5 +106,7 @@ sk_status_t combine_project_launch(const ProjectLaunch& a);
 // Zeroes n 32-bit words with a fill kernel (no memset node, so a captured
 // graph may hold it).
 sk_status_t zero_words_launch(uint32_t* p, size_t n, hipStream_t stream);
+sk_status_t read_probe_launch(const void* buf, size_t bytes, int32_t workgroups, float* out,
+                              hipStream_t stream);
 
 }  // namespace sk

@@ -61,7 +61,9 @@ def test_library_loads_and_exports_every_header_function():
     names = B.header_functions()
     assert {"attn_decode_splitk", "attn_decode_combine", "attn_decode_plan",
             "attn_decode_workspace_bytes", "attn_decode", "attn_decode_one_launch",
-            "attn_decode_workspace_init", "attn_decode_combine_project"} <= set(names)
+            "attn_decode_workspace_init", "attn_decode_combine_project", "attn_query_tiles",
+            "attn_query_tiles_plan", "attn_query_tiles_workspace_bytes",
+            "attn_decode_read_probe"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"libsplitkv.so does not export {n}"
 
@@ -276,6 +278,13 @@ def test_argument_errors_are_reported_before_any_launch():
     d = latent_desc()
     d.head_dim_v = 320
     cases.append(("project: value width 320", _proj(d, plan), B.SK_ERR_UNSUPPORTED))
+    L = lib()
+    for name, args in (("probe: NULL buffer", (None, 1 << 20, 64, 4096, None)),
+                       ("probe: misaligned buffer", (4100, 1 << 20, 64, 4096, None)),
+                       ("probe: zero workgroups", (4096, 1 << 20, 0, 4096, None)),
+                       ("probe: buffer too small", (4096, 64, 64, 4096, None))):
+        cases.append((name, (L.attn_decode_read_probe(*args), B.attn_decode_last_error()),
+                      B.SK_ERR_INVALID_ARG))
     cases.append(("init: NULL workspace", _init(good, plan, ws=None), B.SK_ERR_INVALID_ARG))
     cases.append(("init: misaligned workspace", _init(good, plan, ws=4096 + 64), B.SK_ERR_INVALID_ARG))
     cases.append(("init: small workspace", _init(good, plan, wsb=64), B.SK_ERR_WORKSPACE_TOO_SMALL))
