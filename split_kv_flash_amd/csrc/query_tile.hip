@@ -19,8 +19,8 @@
 //     context slice); wave w owns rows 16w .. 16w+15 of the tile, rows ordered
 //     (position t, head) so a tile's rows have neighbouring causal limits.
 //   * K/V tiles of 32 positions are staged in LDS (row stride D + 8 halves),
-//     double-buffered: the next tile's global loads are in flight in
-//     registers while the current tile is consumed; one barrier per tile.
+//     double-buffered, with the loads of the next two tiles in flight in two
+//     register sets while the current tile is consumed; one barrier per tile.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_16x16x32_{f16,bf16}: the K rows are the A operand and the
 //     query rows (held in registers) the B operand. The result leaves lane
@@ -176,14 +176,9 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
     };
 
     const int ntiles = (int)((stop - start + T - 1) / T);
-    qt_u4 kr[NCH], vr[NCH];
-    gload(kr, vr, start);
-    swrite(0, kr, vr);
-    __syncthreads();
-    for (int i = 0; i < ntiles; ++i) {
+    // Consumes tile i from LDS buffer i & 1: scores, online softmax, output.
+    auto consume = [&](int i) {
       const int64_t tb = start + (int64_t)i * T;
-      const bool more = i + 1 < ntiles;
-      if (more) gload(kr, vr, tb + T);  // the next tile, in flight during this one
       const short* kb = s_kv[i & 1][0];
       const short* vb = s_kv[i & 1][1];
 
@@ -248,8 +243,27 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
         acc[c] = TT::mma(ph, vv, acc[c]);
         acc[c] = TT::mma(pl, vv, acc[c]);
       }
-      if (more) swrite((i + 1) & 1, kr, vr);
+    };
+    // Two register sets keep two tiles' loads in flight: while tile i is
+    // consumed, tile i+1 (loaded one iteration earlier) waits in one set and
+    // tile i+2 is requested into the other; tile i+1 then goes to the LDS
+    // buffer tile i-1 used, which every wave left at the previous barrier.
+    qt_u4 kA[NCH], vA[NCH], kB[NCH], vB[NCH];
+    gload(kA, vA, start);
+    if (ntiles > 1) gload(kB, vB, start + T);
+    swrite(0, kA, vA);
+    __syncthreads();
+    for (int i = 0;;) {
+      if (i + 2 < ntiles) gload(kA, vA, start + (int64_t)(i + 2) * T);
+      consume(i);
+      if (i + 1 < ntiles) swrite((i + 1) & 1, kB, vB);
       __syncthreads();
+      if (++i >= ntiles) break;
+      if (i + 2 < ntiles) gload(kB, vB, start + (int64_t)(i + 2) * T);
+      consume(i);
+      if (i + 1 < ntiles) swrite((i + 1) & 1, kA, vA);
+      __syncthreads();
+      if (++i >= ntiles) break;
     }
   }
 
