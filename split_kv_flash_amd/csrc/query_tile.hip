@@ -15,9 +15,12 @@
 // long context (speculative verify) still fill the GPU.
 //
 // Work decomposition (MI355X-first):
-//   * One workgroup (4 waves) per (sequence, KV head, 64-row query tile,
-//     context slice); wave w owns rows 16w .. 16w+15 of the tile, rows ordered
-//     (position t, head) so a tile's rows have neighbouring causal limits.
+//   * One workgroup (4 waves) per (sequence, KV head, query tile, context
+//     slice), rows ordered (position t, head) so a tile's rows have
+//     neighbouring causal limits. A tile is 64 rows, wave w owning rows
+//     16w .. 16w+15; when a KV head has only 16 or 32 query rows the tile
+//     shrinks to them and the waves of a 16-row block share out the head
+//     width instead (see the DS parameter).
 //   * K/V tiles of 32 positions are staged in LDS (row stride D + 8 halves),
 //     double-buffered, with the loads of the next two tiles in flight in two
 //     register sets while the current tile is consumed; one barrier per tile.
@@ -89,18 +92,29 @@ __device__ __forceinline__ qt_s4 qt_read_tr(const short* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((qt_lds_s4*)(p));
 }
 
-template <typename KT, int D>
+// DS: waves sharing one 16-row block. With DS > 1, wave w takes row block
+// w / DS and the column part w % DS of the head width: it forms the partial
+// scores over its columns, the DS partials meet in LDS and are summed in a
+// fixed order (so every wave of the block derives the same softmax), and it
+// accumulates its own output columns. Few query rows (speculative verify) then
+// keep all four waves busy instead of one.
+template <typename KT, int D, int DS>
 __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
   using TT = QtType<KT>;
-  constexpr int T = 32;        // positions per K/V tile
-  constexpr int RS = D + 8;    // LDS row stride (16-bit elements)
-  constexpr int KS = D / 32;   // score MFMA steps
-  constexpr int CB = D / 16;   // output column blocks
-  constexpr int CPR = D / 8;   // 16-byte chunks per row
-  constexpr int NCH = D / 64;  // chunks per thread per tile (K and V each): 32*CPR / 256
-  static_assert(D % 64 == 0, "head width");
+  constexpr int T = 32;         // positions per K/V tile
+  constexpr int RS = D + 8;     // LDS row stride (16-bit elements)
+  constexpr int KS = D / 32;    // score MFMA steps over the head width
+  constexpr int CB = D / 16;    // output column blocks over the head width
+  constexpr int KSW = KS / DS;  // score steps of one wave
+  constexpr int CBW = CB / DS;  // output column blocks of one wave
+  constexpr int RB = 4 / DS;    // row blocks per workgroup
+  constexpr int RW = 16 * RB;   // query rows per workgroup
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  constexpr int NCH = D / 64;   // chunks per thread per tile (K and V each): 32*CPR / 256
+  static_assert(D % 64 == 0 && KS % DS == 0 && (DS == 1 || DS == 2 || DS == 4), "head width / split");
 
   __shared__ __align__(16) short s_kv[2][2][T * RS];  // [buffer][K, V][row * RS + column]
+  __shared__ __align__(16) float s_sc[DS > 1 ? 4 : 1][64][8];  // partial scores per wave and lane
 
   const int g = blockIdx.x / a.nqt;
   const int qt = blockIdx.x - g * a.nqt;
@@ -111,6 +125,8 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
   const int wave = tid >> 6;
   const int l16 = lane & 15;
   const int lq = lane >> 4;
+  const int rb = wave / DS;       // row block
+  const int dq = wave - rb * DS;  // column part
   const int QG = a.Q * a.G;
   const int QH = a.Q * a.Hq;
 
@@ -118,30 +134,31 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
   const int64_t start = (int64_t)split * a.chunk;
   const int64_t end = min((int64_t)L, start + a.chunk);
 
-  // This lane's query row (scores and softmax): row l16 of the wave.
-  const int rho = qt * 64 + wave * 16 + l16;
+  // This lane's query row (scores and softmax): row l16 of the row block.
+  const int rho = qt * RW + rb * 16 + l16;
   const bool rvalid = rho < QG;
   const int t = rvalid ? rho / a.G : 0;
   const int hh = rvalid ? rho - t * a.G : 0;
   const int64_t lim = rvalid ? (int64_t)L - a.Q + t + 1 : 0;  // visible: positions < lim
   // The tile's rows are ordered by position, so its last row sees the most.
-  const int rho_last = min(qt * 64 + 63, QG - 1);
+  const int rho_last = min(qt * RW + RW - 1, QG - 1);
   const int64_t lim_max = (int64_t)L - a.Q + rho_last / a.G + 1;
   const int64_t stop = min(end, lim_max);  // this workgroup reads positions [start, stop)
 
   float m = -INFINITY, l = 0.0f;  // row l16 (replicated over the quarters), base-2 units
-  qt_f4 acc[CB];
+  qt_f4 acc[CBW];  // output columns 16 (dq CBW + c) + l16
 #pragma unroll
-  for (int c = 0; c < CB; ++c) acc[c] = qt_f4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < CBW; ++c) acc[c] = qt_f4{0.f, 0.f, 0.f, 0.f};
 
   if (start < stop) {
     // Query row as B operands: lane (l16, lq) holds columns 32ks + 8lq .. +7 of
-    // row l16, pre-scaled into base-2 units and split into high and low parts.
-    qt_s8 qh[KS], ql[KS];
+    // row l16 (ks over this wave's column part), pre-scaled into base-2 units
+    // and split into high and low parts.
+    qt_s8 qh[KSW], ql[KSW];
     {
-      const int64_t qbase = (((int64_t)b * a.Q + t) * a.Hq + g * a.G + hh) * D;
+      const int64_t qbase = (((int64_t)b * a.Q + t) * a.Hq + g * a.G + hh) * D + 32 * KSW * dq;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KSW; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float x = rvalid ? load_q(a.q, a.q_dtype, qbase + 32 * ks + 8 * lq + e) * a.qscale : 0.0f;
@@ -175,23 +192,44 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
       }
     };
 
-    const int ntiles = (int)((stop - start + T - 1) / T);
+    // Uniform over the workgroup; said so, the loop exits on a scalar branch
+    // instead of an exec-masked one (whose merged paths cost the loads' overlap).
+    const int ntiles = __builtin_amdgcn_readfirstlane((int)((stop - start + T - 1) / T));
     // Consumes tile i from LDS buffer i & 1: scores, online softmax, output.
     auto consume = [&](int i) {
       const int64_t tb = start + (int64_t)i * T;
       const short* kb = s_kv[i & 1][0];
       const short* vb = s_kv[i & 1][1];
 
-      // ---- scores S^T: two blocks of 16 positions, this wave's 16 rows ----
+      // ---- scores S^T: two blocks of 16 positions, this block's 16 rows ----
       qt_f4 sp[2] = {qt_f4{0.f, 0.f, 0.f, 0.f}, qt_f4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const qt_s8 av = *reinterpret_cast<const qt_s8*>(kb + (16 * pb + l16) * RS + 32 * ks + 8 * lq);
+        for (int ks = 0; ks < KSW; ++ks) {
+          const qt_s8 av =
+              *reinterpret_cast<const qt_s8*>(kb + (16 * pb + l16) * RS + 32 * (KSW * dq + ks) + 8 * lq);
           sp[pb] = TT::mma(av, qh[ks], sp[pb]);
           sp[pb] = TT::mma(av, ql[ks], sp[pb]);
         }
+      if constexpr (DS > 1) {
+        // Partial scores of the block's DS waves: same lane layout, summed in
+        // wave order. The buffer is rewritten only after the tile's closing
+        // barrier, which every wave reaches after this read.
+        qt_f4* mine = reinterpret_cast<qt_f4*>(&s_sc[wave][lane][0]);
+        mine[0] = sp[0];
+        mine[1] = sp[1];
+        __syncthreads();
+        const qt_f4* p0 = reinterpret_cast<const qt_f4*>(&s_sc[rb * DS][lane][0]);
+        sp[0] = p0[0];
+        sp[1] = p0[1];
+#pragma unroll
+        for (int j = 1; j < DS; ++j) {
+          const qt_f4* pj = reinterpret_cast<const qt_f4*>(&s_sc[rb * DS + j][lane][0]);
+          sp[0] += pj[0];
+          sp[1] += pj[1];
+        }
+      }
 
       // ---- online softmax of row l16 over the tile's visible positions ----
       float s[8];
@@ -229,14 +267,14 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
         for (int e = 0; e < 4; ++e) {
           const float ae = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * lq + e) << 2, __float_as_int(al)));
 #pragma unroll
-          for (int c = 0; c < CB; ++c) acc[c][e] *= ae;
+          for (int c = 0; c < CBW; ++c) acc[c][e] *= ae;
         }
       }
 
-      // ---- output: acc += P V, positions in the scores' order ----
-      const short* vrow = vb + (4 * lq + (l16 >> 2)) * RS + 4 * (l16 & 3);
+      // ---- output: acc += P V over this wave's columns, positions in the scores' order ----
+      const short* vrow = vb + (4 * lq + (l16 >> 2)) * RS + 4 * (l16 & 3) + 16 * CBW * dq;
 #pragma unroll
-      for (int c = 0; c < CB; ++c) {
+      for (int c = 0; c < CBW; ++c) {
         const qt_s4 v0 = qt_read_tr(vrow + 16 * c);
         const qt_s4 v1 = qt_read_tr(vrow + 16 * RS + 16 * c);
         const qt_s8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -245,41 +283,45 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
       }
     };
     // Two register sets keep two tiles' loads in flight: while tile i is
-    // consumed, tile i+1 (loaded one iteration earlier) waits in one set and
-    // tile i+2 is requested into the other; tile i+1 then goes to the LDS
-    // buffer tile i-1 used, which every wave left at the previous barrier.
+    // consumed, tile i+1 (loaded one step earlier) waits in one set and tile
+    // i+2 is requested into the other; tile i+1 then goes to the LDS buffer
+    // tile i-1 used, which every wave left at the previous barrier. Tiles go
+    // in pairs with one exit test per pair, and loads and LDS writes are
+    // unconditional: past the end every row re-reads row stop-1 and an odd
+    // count's last, empty tile is consumed as a no-op (all its scores are
+    // masked). A branch around a load or a mid-pair exit would make the
+    // compiler's wait counting assume the worst path and drain both register
+    // sets before the next use.
     qt_u4 kA[NCH], vA[NCH], kB[NCH], vB[NCH];
     gload(kA, vA, start);
-    if (ntiles > 1) gload(kB, vB, start + T);
+    gload(kB, vB, start + T);
     swrite(0, kA, vA);
     __syncthreads();
-    for (int i = 0;;) {
-      if (i + 2 < ntiles) gload(kA, vA, start + (int64_t)(i + 2) * T);
+    for (int i = 0; i < ntiles; i += 2) {
+      gload(kA, vA, start + (int64_t)(i + 2) * T);
       consume(i);
-      if (i + 1 < ntiles) swrite((i + 1) & 1, kB, vB);
+      swrite(1, kB, vB);
       __syncthreads();
-      if (++i >= ntiles) break;
-      if (i + 2 < ntiles) gload(kB, vB, start + (int64_t)(i + 2) * T);
-      consume(i);
-      if (i + 1 < ntiles) swrite((i + 1) & 1, kA, vA);
+      gload(kB, vB, start + (int64_t)(i + 3) * T);
+      consume(i + 1);
+      swrite(0, kA, vA);
       __syncthreads();
-      if (++i >= ntiles) break;
     }
   }
 
-  // ---- partials of this wave's rows (rows with nothing visible: neutral) ----
+  // ---- partials of this wave's rows and columns (rows with nothing visible: neutral) ----
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int re = qt * 64 + wave * 16 + 4 * lq + e;
+    const int re = qt * RW + rb * 16 + 4 * lq + e;
     if (re < QG) {
       const int te = re / a.G;
       const int w = te * a.Hq + g * a.G + (re - te * a.G);
-      float* dst = a.ws_acc + (((int64_t)b * QH + w) * a.S + split) * D + l16;
+      float* dst = a.ws_acc + (((int64_t)b * QH + w) * a.S + split) * D + 16 * CBW * dq + l16;
 #pragma unroll
-      for (int c = 0; c < CB; ++c) dst[16 * c] = acc[c][e];
+      for (int c = 0; c < CBW; ++c) dst[16 * c] = acc[c][e];
     }
   }
-  if (lq == 0 && rvalid) {
+  if (lq == 0 && rvalid && dq == 0) {
     const int64_t r = ((int64_t)b * QH + t * a.Hq + g * a.G + hh) * a.S + split;
     a.ws_m[r] = m * kLn2;
     a.ws_l[r] = l;
@@ -297,12 +339,34 @@ int query_tile_rows_tiles(const sk_desc_t& d, int q_len) {
   return (q_len * G + 63) / 64;
 }
 
+// Waves per 16-row block: the head width is shared out when the query rows of
+// a KV head fill only one or two row blocks (every choice keeps
+// ceil(rows / 64) workgroups per KV head and slice).
+static int query_tile_ways(int rows, int D) {
+  if (rows <= 16 && D >= 128) return 4;
+  if (rows <= 32) return 2;
+  return 1;
+}
+
+template <typename KT, int D>
+static void qt_launch(int ways, dim3 grid, hipStream_t stream, const QtArgs& a) {
+  if (ways == 4) {
+    if constexpr (D >= 128) hipLaunchKernelGGL((query_tile_kernel<KT, D, 4>), grid, dim3(256), 0, stream, a);
+  } else if (ways == 2) {
+    hipLaunchKernelGGL((query_tile_kernel<KT, D, 2>), grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((query_tile_kernel<KT, D, 1>), grid, dim3(256), 0, stream, a);
+  }
+}
+
 template <typename KT>
 static sk_status_t qt_by_dim(const QueryTileLaunch& s, const QtArgs& a, dim3 grid) {
-  switch (s.d->head_dim_qk) {
-    case 64: hipLaunchKernelGGL((query_tile_kernel<KT, 64>), grid, dim3(256), 0, s.stream, a); break;
-    case 128: hipLaunchKernelGGL((query_tile_kernel<KT, 128>), grid, dim3(256), 0, s.stream, a); break;
-    case 256: hipLaunchKernelGGL((query_tile_kernel<KT, 256>), grid, dim3(256), 0, s.stream, a); break;
+  const int D = s.d->head_dim_qk;
+  const int ways = query_tile_ways(a.Q * a.G, D);
+  switch (D) {
+    case 64: qt_launch<KT, 64>(ways, grid, s.stream, a); break;
+    case 128: qt_launch<KT, 128>(ways, grid, s.stream, a); break;
+    case 256: qt_launch<KT, 256>(ways, grid, s.stream, a); break;
     default: return SK_ERR_UNSUPPORTED;
   }
   return SK_OK;
