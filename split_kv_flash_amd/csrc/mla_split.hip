@@ -472,8 +472,8 @@ __device__ __forceinline__ int tile_off(int r, int cc) { return r * kLatDk + ((c
 //    of four rows each). P stays in registers.
 //  * Software pipeline: iteration i computes the output product of tile i-1
 //    and the scores of tile i, then one barrier publishes the partial scores
-//    (double-buffered by parity) and the next tile; after it the softmax of
-//    tile i runs and tile i+2 is requested into the buffer tile i-1 used.
+//    (double-buffered by parity) and the next tile; after it tile i+2 is
+//    requested into the buffer tile i-1 used and the softmax of tile i runs.
 // ---------------------------------------------------------------------------
 template <int NHB, bool IDX>
 __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
@@ -676,6 +676,9 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
     // tile load still in flight: wait for it, then publish it and the partials.
     wait_vm_lgkm0<0>();
     raw_barrier();
+    // Every wave has finished the output product of tile i-1: its buffer takes
+    // tile i+2 now, so the load overlaps the softmax as well.
+    issue_tile((i + 2) % 3, tb + 2 * kT16);
 
     // ---- full scores (own + partner), online softmax over the 32 positions ----
     const float4_t q0 = s_sx[par][wave ^ 1][0][lane];
@@ -711,7 +714,6 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
     ls += xor32(ls);
     l = fmaf(l, alp, ls);
     m = mn;
-    issue_tile((i + 2) % 3, tb + 2 * kT16);
   }
   // Drain the tile loads still in flight before the workgroup can retire.
   wait_vm_lgkm0<0>();
@@ -909,8 +911,8 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   // Software pipeline: iteration i computes the output product of tile i-1
   // (weights pp from the previous softmax) and the partial scores of tile i;
   // one barrier then publishes the partials (double-buffered by parity) and
-  // tile i+1; after it the softmax of tile i runs and tile i+2 is requested
-  // into the buffer tile i-1 used.
+  // tile i+1; after it tile i+2 is requested into the buffer tile i-1 used and
+  // the softmax of tile i runs.
   float pp[4] = {0.f, 0.f, 0.f, 0.f};
   float alp = 1.0f;
   bool movedp = false;
@@ -961,6 +963,9 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
     // tile load still in flight: wait for it, then publish it and the partials.
     wait_vm_lgkm0<0>();
     raw_barrier();
+    // Every wave has finished the output product of tile i-1: its buffer takes
+    // tile i+2 now, so the load overlaps the softmax as well.
+    issue_tile((i + 2) % 3, tb + 2 * kT32);
 
     // ---- full scores (the block's four partials in a fixed order), softmax ----
     const float4_t x0 = s_sx[par][hb * 4 + 0][lane], x1 = s_sx[par][hb * 4 + 1][lane];
@@ -990,7 +995,6 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
     ls += xor32(ls);
     l = fmaf(l, alp, ls);
     m = mn;
-    issue_tile((i + 2) % 3, tb + 2 * kT32);
   }
   // Drain the tile loads still in flight before the workgroup can retire.
   wait_vm_lgkm0<0>();
