@@ -10,6 +10,7 @@ and relL2 1e-3 for 16-bit KV); q and the weights are split into high and low
 """
 
 import itertools
+import math
 
 import numpy as np
 import pytest
@@ -89,6 +90,28 @@ def test_length_33_with_the_maximum_in_the_second_tile():
     ref, _ = ref_qt(case)
     out, _, _ = run_qt(case, n_splits=1)
     check(case, out, ref, "L=33 dominant at 32")
+
+
+@pytest.mark.parametrize("Q,G,D,kv", [(4, 4, 256, "f16"), (2, 8, 128, "bf16"), (8, 4, 128, "f16"),
+                                        (3, 4, 64, "bf16"), (1, 16, 256, "bf16")])
+def test_head_width_split_with_a_late_dominant_key(Q, G, D, kv):
+    """16 or 32 query rows per KV group: the waves of a row block share the
+    head width, their partial scores summed in LDS. A key that dominates
+    every row sits in the slice's third tile, so each row must rescale what
+    it gathered before it (and the partial sums must agree across waves for
+    the softmax to be consistent)."""
+    L = 200
+    case = synthetic.multiquery_case(f"qt-ds-Q{Q}-G{G}-D{D}", seq_lens=[L, 150], q_len=Q,
+                                     num_q_heads=2 * G, num_kv_heads=2, head_dim=D, kv_dtype=kv,
+                                     capacity=L + 8, seed=9100 + Q * 100 + D)
+    qd = case.q[0, 0, 0].astype(np.float64)
+    case.q[0, :, :] = case.q[0, 0, 0]
+    dom = (qd / np.linalg.norm(qd) * 10 * math.sqrt(D) / np.linalg.norm(qd))
+    case.k[0, 70, :] = synthetic.to_storage(dom.astype(np.float32), kv)
+    ref, _ = ref_qt(case)
+    for S in (1, 2):
+        out, _, call = run_qt(case, n_splits=S)
+        check(case, out, ref, f"Q={Q} G={G} D={D} {kv} S={S} plan={call.plan}")
 
 
 @pytest.mark.parametrize("G,D,kv", list(itertools.product([1, 2, 4, 6, 8], [64, 128, 256], ["f16", "bf16"])))
