@@ -159,9 +159,9 @@ typedef struct {
  *           every compute unit. The note's own S_target is about 4 per
  *           multiprocessor of its GPU.
  *   latent: chunk = max(64, ceil(g * total_tokens / cu_count)) with g workgroups per
- *           split: 1 for f16 caches (one workgroup serves all query heads), Hq/48
- *           (Hq/32 when 48 does not divide Hq) for f32 caches, whose FP32-MFMA
- *           kernel spreads a split's heads over g workgroups of 16-head blocks.
+ *           split, each serving a slice of the query heads: for f16 caches 1 up to
+ *           96 heads and 2 (of 64 heads) at 128; for f32 caches Hq/48 (Hq/32 when
+ *           48 does not divide Hq), whose FP32-MFMA kernel holds fewer heads.
  *           Each split costs a partial of every head, so splits stay long.
  *   chunk is rounded up to a multiple of 64 and S = ceil(max_seq_len / chunk).
  * Below SK_MIN_SPLIT_CONTEXT positions the heuristic returns S = 1 (Lecture 06
@@ -198,8 +198,7 @@ size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan)
  * Supported: GQA with head_dim_qk == head_dim_v in {64, 128, 256}, group size
  * num_q_heads/num_kv_heads in {1, 2, 4, 6, 8}, any q/KV dtype, every layout; latent
  * (kv_shared) with num_kv_heads == 1, head_dim_qk == 576, head_dim_v == 512, num_q_heads
- * in {32, 64, 96, 128}, q f32, KV f32 or f16, contiguous, or indexed (f32 KV, or f16 KV
- * with 32 or 96 heads). Latent f16 caches run on f16
+ * in {32, 64, 96, 128}, q f32, KV f32 or f16, contiguous or indexed. Latent f16 caches run on f16
  * MFMA: q and the softmax weights are rounded to f16 there (f32 accumulation). Anything else returns
  * SK_ERR_UNSUPPORTED without launching. */
 sk_status_t attn_decode_splitk(const sk_desc_t* desc, const sk_plan_t* plan,

@@ -14,27 +14,14 @@
 //   output  acc[h][e] += sum_j P[h][j] C[j][e] (heads x values,    K = positions)
 // with the online-softmax update between them. f16 caches use f16 MFMA (q and
 // the probabilities rounded to f16, f32 accumulation); f32 caches use
-// v_mfma_f32_16x16x4_f32 (no rounding). Three kernels live here:
-//   * mla32_split_kernel (every f32 cache): four waves per 16-head block,
-//     scores computed transposed so P stays in registers; see its comment;
-//   * mla16_split_kernel (f16 caches with 32 or 96 heads): two waves per
-//     16-head block, x32 MFMA, scores transposed, one barrier per tile; see
-//     its comment;
-//   * mla_split_kernel (f16 caches with 64 or 128 heads), described next.
-//
-// mla_split_kernel: 512 threads = 8 waves, one workgroup per split. Per tile
-// of T positions:
-//   1. the tile of cache rows (T x 576) is staged in LDS (row-padded); the next
-//      tile's global loads are already in flight;
-//   2. score phase: wave w = (head half, column quarter) computes the partial
-//      scores of its heads over its 144 columns (split K), Q in registers;
-//   3. softmax phase: partials are summed from LDS, each wave updates the
-//      running max / normaliser of 1/8 of the heads and writes the tile's
-//      probabilities and rescale factors to LDS;
-//   4. output phase: wave w owns 64 value columns for every head; it rescales
-//      its accumulators and adds P (from LDS) times the tile's value columns.
-// LDS use depends only on the tile size and the head count, never on the
-// context length.
+// v_mfma_f32_16x16x4_f32 (no rounding). Two kernels live here, each described
+// at its definition:
+//   * mla16_split_kernel (f16 caches): two waves per 16-head block, x32 MFMA,
+//     scores transposed, one barrier per tile; 32, 64 and 96 heads in one
+//     workgroup per split, 128 heads as two workgroups of 64;
+//   * mla32_split_kernel (f32 caches): four waves per 16-head block, scores
+//     transposed so P stays in registers, heads over one or more workgroups
+//     per split.
 #include "sk_device.h"
 #include "sk_internal.h"
 
@@ -45,11 +32,6 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kLatDk = 576;
 constexpr int kLatDv = 512;
-constexpr int kMlaWaves = 8;
-constexpr int kMlaThreads = 64 * kMlaWaves;
-constexpr int kDimSplit = 4;                   // score phase: 2 head halves x 4 column quarters
-constexpr int kDimQ = kLatDk / kDimSplit;      // 144 columns per quarter
-constexpr int kColsPerWave = kLatDv / kMlaWaves;  // 64 value columns per wave
 
 struct MlaArgs {
   const float* q;
@@ -91,289 +73,6 @@ __device__ __forceinline__ uint32_t tile_bad_mask(const MlaArgs& a, int32_t idx,
 __device__ __forceinline__ int32_t row_of(const MlaArgs& a, int32_t idx, int row) {
   const int32_t safe = index_bad(a, idx) ? 0 : idx;
   return __builtin_amdgcn_ds_bpermute(row << 2, safe);
-}
-
-template <typename CT>
-struct MlaCfg;
-template <>
-struct MlaCfg<_Float16> {
-  static constexpr int T = 32;     // positions per tile
-  static constexpr int KW = 16;    // MFMA K per instruction
-  static constexpr int ROW = 584;  // LDS row stride (elements): 576 + 8
-  using PT = _Float16;
-};
-template <>
-struct MlaCfg<float> {
-  static constexpr int T = 16;
-  static constexpr int KW = 4;
-  static constexpr int ROW = 596;  // 576 + 20: conflict-free score-phase reads
-  using PT = float;
-};
-
-__device__ __forceinline__ float4_t mfma(half4_t a, half4_t b, float4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ float4_t mfma(float a, float b, float4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Max / sum over the T consecutive lanes that hold one head's tile (T = 16: a
-// DPP row; T = 32: two rows joined by a swizzle).
-template <int T>
-__device__ __forceinline__ float seg_max(float x) {
-  x = fmaxf(x, dpp<kDppRowRor8>(x));
-  x = fmaxf(x, dpp<kDppRowRor4>(x));
-  x = fmaxf(x, dpp<kDppQuadXor2>(x));
-  x = fmaxf(x, dpp<kDppQuadXor1>(x));
-  if constexpr (T == 32) x = fmaxf(x, xor16(x));
-  return x;
-}
-template <int T>
-__device__ __forceinline__ float seg_sum(float x) {
-  x = row16_sum(x);
-  if constexpr (T == 32) x += xor16(x);
-  return x;
-}
-
-template <typename CT, int NHB>
-__global__ __launch_bounds__(kMlaThreads) void mla_split_kernel(MlaArgs a) {
-  using Cfg = MlaCfg<CT>;
-  using PT = typename Cfg::PT;
-  constexpr int T = Cfg::T, KW = Cfg::KW, ROW = Cfg::ROW;
-  constexpr int H = NHB * 16;           // query heads
-  constexpr int HBW = NHB / 2;          // head blocks per wave in the score phase
-  constexpr int KSTEPS = kDimQ / KW;    // MFMA steps over a column quarter
-  constexpr int PB = T / 16;            // 16-position blocks per tile
-  constexpr int PROW = T + 4;           // LDS row stride of P (elements)
-  constexpr int EPC = 16 / (int)sizeof(CT);            // elements per 16-byte chunk
-  constexpr int CPR = kLatDk / EPC;                    // chunks per cache row
-  constexpr int CHUNKS = T * CPR;                      // chunks per tile
-  constexpr int CPT = (CHUNKS + kMlaThreads - 1) / kMlaThreads;
-  constexpr int HPI = 64 / T;                          // heads per softmax step per wave
-  constexpr int ITER = H / kMlaWaves / HPI;            // softmax steps per wave
-  constexpr bool kQInRegs = sizeof(CT) == 2;
-  static_assert(H % (kMlaWaves * HPI) == 0, "head count must split over the waves");
-  using CV = Vec<CT, EPC>;
-
-  __shared__ __align__(16) CT s_c[T * ROW];
-  __shared__ float s_sp[kDimSplit][H][T + 1];
-  __shared__ __align__(16) PT s_p[H * PROW];
-  __shared__ float s_alpha[H];
-
-  const int split = blockIdx.x;
-  const int b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l16 = lane & 15;
-  const int lq = lane >> 4;
-
-  const int L = min(a.seq_lens[b], a.cap);
-  const int64_t start = (int64_t)split * a.chunk;
-  const int64_t end = min((int64_t)L, start + a.chunk);
-  const int64_t ws0 = (int64_t)b * a.Hq * a.S + split;  // + h*S for head h
-
-  if (start >= end) {
-    for (int idx = tid; idx < H * kLatDv; idx += kMlaThreads) {
-      const int h = idx / kLatDv, e = idx - (idx / kLatDv) * kLatDv;
-      a.ws_acc[(ws0 + (int64_t)h * a.S) * kLatDv + e] = 0.0f;
-    }
-    for (int h = tid; h < H; h += kMlaThreads) {
-      a.ws_m[ws0 + (int64_t)h * a.S] = -INFINITY;
-      a.ws_l[ws0 + (int64_t)h * a.S] = 0.0f;
-    }
-    return;
-  }
-
-  const CT* __restrict__ cbase = reinterpret_cast<const CT*>(a.c) + (int64_t)b * a.stride_seq;
-  const float* __restrict__ qb = a.q + (int64_t)b * a.Hq * kLatDk;
-
-  // Staging of one tile: rows past the end re-read row end-1 (a cache hit).
-  CV stage[CPT];
-  auto load_tile = [&](int64_t tb) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * kMlaThreads;
-      if (CHUNKS % kMlaThreads == 0 || idx < CHUNKS) {
-        const int r = idx / CPR, cc = idx - (idx / CPR) * CPR;
-        int64_t pos = tb + r;
-        pos = pos < end ? pos : end - 1;
-        stage[c] = load_vec<CT, EPC>(cbase + pos * a.stride_pos + cc * EPC);
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * kMlaThreads;
-      if (CHUNKS % kMlaThreads == 0 || idx < CHUNKS) {
-        const int r = idx / CPR, cc = idx - (idx / CPR) * CPR;
-        *reinterpret_cast<CV*>(&s_c[r * ROW + cc * EPC]) = stage[c];
-      }
-    }
-  };
-
-  // Score-phase role and the f16 query fragments (rounded once).
-  const int hh = wave >> 2;  // head half
-  const int dq = wave & 3;   // column quarter
-  half4_t qf[kQInRegs ? HBW : 1][kQInRegs ? KSTEPS : 1];
-  if constexpr (kQInRegs) {
-#pragma unroll
-    for (int hbl = 0; hbl < HBW; ++hbl)
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int head = (hh * HBW + hbl) * 16 + l16;
-          const int dim = dq * kDimQ + ks * KW + lq * 4 + e;
-          qf[hbl][ks][e] = (_Float16)qb[head * kLatDk + dim];
-        }
-  }
-
-  // Softmax-phase state: this lane's head for step `it` is
-  // wave + 8 * (it * HPI + lane / T), position lane % T.
-  const int hsub = lane / T;
-  const int spos = lane % T;
-  float m_r[ITER], l_r[ITER];
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    m_r[it] = -INFINITY;
-    l_r[it] = 0.0f;
-  }
-
-  // Output-phase accumulators: heads hb*16 + 4*lq + e, columns
-  // 64*wave + 16*cb + l16.
-  float4_t acc[NHB][4];
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[hb][cb] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  load_tile(start);
-  for (int64_t tb = start; tb < end; tb += T) {
-    __syncthreads();  // the previous tile's readers of s_c and s_p are done
-    store_tile();
-    if constexpr (kQInRegs) load_tile(tb + T);
-    __syncthreads();
-
-    // ---- scores: partial over this wave's 144 columns ----
-    float4_t sacc[HBW][PB];
-#pragma unroll
-    for (int hbl = 0; hbl < HBW; ++hbl)
-#pragma unroll
-      for (int pb = 0; pb < PB; ++pb) sacc[hbl][pb] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-      for (int pb = 0; pb < PB; ++pb) {
-        const int prow = pb * 16 + l16;
-        if constexpr (kQInRegs) {
-          const int dim = dq * kDimQ + ks * KW + lq * 4;
-          const half4_t bv = *reinterpret_cast<const half4_t*>(&s_c[prow * ROW + dim]);
-#pragma unroll
-          for (int hbl = 0; hbl < HBW; ++hbl) sacc[hbl][pb] = mfma(qf[hbl][ks], bv, sacc[hbl][pb]);
-        } else {
-          const int dim = dq * kDimQ + ks * KW + lq;
-          const float bv = (float)s_c[prow * ROW + dim];
-#pragma unroll
-          for (int hbl = 0; hbl < HBW; ++hbl) {
-            const int head = (hh * HBW + hbl) * 16 + l16;
-            const float av = qb[head * kLatDk + dim];
-            sacc[hbl][pb] = mfma(av, bv, sacc[hbl][pb]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int hbl = 0; hbl < HBW; ++hbl)
-#pragma unroll
-      for (int pb = 0; pb < PB; ++pb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          s_sp[dq][(hh * HBW + hbl) * 16 + lq * 4 + e][pb * 16 + l16] = sacc[hbl][pb][e];
-    if constexpr (!kQInRegs) load_tile(tb + T);
-    __syncthreads();
-
-    // ---- online softmax over the tile, 1/8 of the heads per wave ----
-    {
-      const bool ok = tb + spos < end;
-#pragma unroll
-      for (int it = 0; it < ITER; ++it) {
-        const int h = wave + kMlaWaves * (it * HPI + hsub);
-        float s = (s_sp[0][h][spos] + s_sp[1][h][spos]) + (s_sp[2][h][spos] + s_sp[3][h][spos]);
-        s = ok ? s * a.qscale : -INFINITY;
-        const float mn = fmaxf(m_r[it], seg_max<T>(s));
-        const float mu = (mn == -INFINITY) ? 0.0f : mn;
-        const float al = fast_exp2(m_r[it] - mu);
-        const PT pr = (PT)fast_exp2(s - mu);
-        l_r[it] = fmaf(l_r[it], al, seg_sum<T>((float)pr));
-        m_r[it] = mn;
-        s_p[h * PROW + spos] = pr;
-        if (spos == 0) s_alpha[h] = al;
-      }
-    }
-    __syncthreads();
-
-    // ---- output: rescale, then acc += P x V for this wave's 64 columns ----
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
-      float al[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) al[e] = s_alpha[hb * 16 + lq * 4 + e];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[hb][cb][e] *= al[e];
-    }
-    const int col0 = wave * kColsPerWave + l16;
-#pragma unroll
-    for (int ks = 0; ks < T / KW; ++ks) {
-      if constexpr (kQInRegs) {
-        half4_t vb[4];
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vb[cb][e] = s_c[(ks * KW + lq * 4 + e) * ROW + col0 + cb * 16];
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) {
-          const half4_t pa =
-              *reinterpret_cast<const half4_t*>(&s_p[(hb * 16 + l16) * PROW + ks * KW + lq * 4]);
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) acc[hb][cb] = mfma(pa, vb[cb], acc[hb][cb]);
-        }
-      } else {
-        float vb[4];
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) vb[cb] = (float)s_c[(ks * KW + lq) * ROW + col0 + cb * 16];
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) {
-          const float pa = (float)s_p[(hb * 16 + l16) * PROW + ks * KW + lq];
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) acc[hb][cb] = mfma(pa, vb[cb], acc[hb][cb]);
-        }
-      }
-    }
-  }
-
-  // Partials: accumulators by the column owner, (m, l) by the softmax owner.
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int head = hb * 16 + lq * 4 + e;
-        const int col = wave * kColsPerWave + cb * 16 + l16;
-        a.ws_acc[(ws0 + (int64_t)head * a.S) * kLatDv + col] = acc[hb][cb][e];
-      }
-  if (spos == 0) {
-#pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int h = wave + kMlaWaves * (it * HPI + hsub);
-      a.ws_m[ws0 + (int64_t)h * a.S] = m_r[it] * kLn2;
-      a.ws_l[ws0 + (int64_t)h * a.S] = l_r[it];
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -474,17 +173,31 @@ __device__ __forceinline__ int tile_off(int r, int cc) { return r * kLatDk + ((c
 //    and the scores of tile i, then one barrier publishes the partial scores
 //    (double-buffered by parity) and the next tile; after it tile i+2 is
 //    requested into the buffer tile i-1 used and the softmax of tile i runs.
+//  * A tile is 36 wave-loads of 64 chunks; wave w issues loads
+//    [w*base + min(w, extra), ...) of them, base + (w < extra) in all
+//    (base = 36 / NW, extra = 36 % NW: 9, 4 + 1 for waves 0-3, or 3 per wave
+//    for 4, 8 or 12 waves).
+//  * Heads: one workgroup per split holds NHB blocks; a split's heads are
+//    spread over gridDim.z workgroups of NHB*16 (two for 128 heads, whose
+//    eight blocks would not fit the registers of 16 waves), each streaming
+//    the split's rows.
 // ---------------------------------------------------------------------------
+// f16: 16-head blocks per workgroup and workgroups per split (128 heads: two
+// workgroups of 64, whose 8 waves keep two waves per SIMD).
+__host__ __device__ constexpr int mla16_blocks(int Hq) { return Hq == 128 ? 4 : Hq / 16; }
+__host__ __device__ constexpr int mla16_groups(int Hq) { return Hq / (16 * mla16_blocks(Hq)); }
+
 template <int NHB, bool IDX>
 __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
   constexpr int H = NHB * 16;
   constexpr int NW = 2 * NHB;
-  constexpr int NT = NW * 64;
   constexpr int KH = kLatDk / 2;                  // 288 latent columns per wave
   constexpr int KS = KH / 32;                     // 9 MFMA steps
   constexpr int SLOTS = kT16 * kCpr16;            // 2304 chunks per tile
-  constexpr int DPW = SLOTS / NT;                 // global-to-LDS loads per wave per tile
-  static_assert(SLOTS % NT == 0, "every wave issues the same number of tile loads");
+  constexpr int WLOADS = SLOTS / 64;              // 36 wave-loads per tile
+  constexpr int LBASE = WLOADS / NW, LEXTRA = WLOADS % NW;
+  constexpr int DPW = LBASE + (LEXTRA > 0 ? 1 : 0);  // most loads one wave issues per tile
+  static_assert(SLOTS % 64 == 0, "a tile is whole wave-loads");
   constexpr int NCB = 16;                         // 16-column blocks per half (256 columns)
   constexpr int TILE = kT16 * kLatDk;             // halves per tile buffer
 
@@ -493,25 +206,28 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
 
   const int split = blockIdx.x;
   const int b = blockIdx.y;
+  const int h0 = blockIdx.z * H;  // first head of this workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hb = wave >> 1;
   const int dh = wave & 1;
   const int l16 = lane & 15;
   const int lq = lane >> 4;
+  const int wl0 = wave * LBASE + min(wave, LEXTRA);       // this wave's first wave-load
+  const int nwl = LBASE + (wave < LEXTRA ? 1 : 0);        // and their count
 
   const int L = min(a.seq_lens[b], a.cap);
   const int64_t start = (int64_t)split * a.chunk;
   const int64_t end = min((int64_t)L, start + a.chunk);
-  const int64_t ws0 = (int64_t)b * a.Hq * a.S + split;
+  const int64_t ws0 = ((int64_t)b * a.Hq + h0) * a.S + split;
 
   if (start >= end) {
-    for (int idx = tid; idx < H * kLatDv; idx += NT) {
+    for (int idx = tid; idx < H * kLatDv; idx += NW * 64) {
       const int h = idx / kLatDv, e = idx - (idx / kLatDv) * kLatDv;
       a.ws_acc[(ws0 + (int64_t)h * a.S) * kLatDv + e] = 0.0f;
     }
-    for (int h = tid; h < H; h += NT) {
+    for (int h = tid; h < H; h += NW * 64) {
       a.ws_m[ws0 + (int64_t)h * a.S] = -INFINITY;
       a.ws_l[ws0 + (int64_t)h * a.S] = 0.0f;
     }
@@ -520,9 +236,9 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
 
   const _Float16* __restrict__ cbase =
       reinterpret_cast<const _Float16*>(a.c) + (IDX ? 0 : (int64_t)b * a.stride_seq);
-  const float* __restrict__ qb = a.q + (int64_t)b * a.Hq * kLatDk;
+  const float* __restrict__ qb = a.q + ((int64_t)b * a.Hq + h0) * kLatDk;
 
-  // Tile staging: this wave's DPW slots per tile; slot s holds tile row s/72,
+  // Tile staging: this wave's wave-loads per tile; slot s holds tile row s/72,
   // logical chunk (s%72) ^ (row & 7). Rows past the end re-read row end-1.
   // The slot coordinates are recomputed per tile (a few integer operations)
   // rather than held in registers across the loop.
@@ -542,11 +258,12 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
       bad2 = bi == 2 ? bad : bad2;
 #pragma unroll
       for (int c = 0; c < DPW; ++c) {
-        const int sl = (wave * DPW + c) * 64 + lane;
+        if (LEXTRA != 0 && c >= nwl) break;  // wave-uniform
+        const int sl = (wl0 + c) * 64 + lane;
         const int srow = sl / kCpr16;
         const int scol = ((sl - srow * kCpr16) ^ (srow & 7)) * 8;
         const int32_t r = row_of(a, nidx, srow);
-        const uint32_t dst = lds0 + (uint32_t)((bi * TILE + (wave * DPW + c) * 64 * 8) * 2);
+        const uint32_t dst = lds0 + (uint32_t)((bi * TILE + (wl0 + c) * 64 * 8) * 2);
         dma16(cbase + (int64_t)r * a.stride_pos + scol, __builtin_amdgcn_readfirstlane(dst));
       }
       nidx = load_tile_index(a, b, tb + kT16, end, kT16);  // the next tile's rows
@@ -556,11 +273,12 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
       const _Float16* tbase = cbase + tbc * a.stride_pos;
 #pragma unroll
       for (int c = 0; c < DPW; ++c) {
-        const int sl = (wave * DPW + c) * 64 + lane;
+        if (LEXTRA != 0 && c >= nwl) break;  // wave-uniform
+        const int sl = (wl0 + c) * 64 + lane;
         const int srow = sl / kCpr16;
         const int scol = ((sl - srow * kCpr16) ^ (srow & 7)) * 8;
         const uint32_t off = (uint32_t)min(srow, last) * row_bytes + (uint32_t)(scol * 2);
-        const uint32_t dst = lds0 + (uint32_t)((bi * TILE + (wave * DPW + c) * 64 * 8) * 2);
+        const uint32_t dst = lds0 + (uint32_t)((bi * TILE + (wl0 + c) * 64 * 8) * 2);
         dma16s(off, tbase, __builtin_amdgcn_readfirstlane(dst));
       }
     }
@@ -1016,18 +734,13 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
 }
 
 int latent_blocks_per_split(const sk_desc_t& d) {
-  return d.kv_dtype == SK_F32 ? mla32_groups(d.num_q_heads) : 1;
+  return d.kv_dtype == SK_F32 ? mla32_groups(d.num_q_heads) : mla16_groups(d.num_q_heads);
 }
 
 bool latent_supported(const sk_desc_t& d) {
   const bool heads_ok = d.num_q_heads == 32 || d.num_q_heads == 64 || d.num_q_heads == 96 ||
                         d.num_q_heads == 128;
-  // Index lists: every f32 head count; f16 with 32 or 96 heads (the kernels
-  // that stage tiles with direct-to-LDS loads).
-  const bool layout_ok =
-      d.layout == SK_KV_CONTIGUOUS ||
-      (d.layout == SK_KV_INDEXED &&
-       (d.kv_dtype == SK_F32 || d.num_q_heads == 32 || d.num_q_heads == 96));
+  const bool layout_ok = d.layout == SK_KV_CONTIGUOUS || d.layout == SK_KV_INDEXED;
   return d.kv_shared == 1 && d.num_kv_heads == 1 && d.head_dim_qk == kLatDk &&
          d.head_dim_v == kLatDv && layout_ok && d.q_dtype == SK_F32 &&
          (d.kv_dtype == SK_F32 || d.kv_dtype == SK_F16) && heads_ok;
@@ -1037,27 +750,22 @@ template <typename CT, int NHB>
 static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void** fn, int grid[3],
                                   int* block) {
   const sk_desc_t& d = *s.d;
-  // f32 caches take the FP32-MFMA kernel (heads over HG workgroups per split);
-  // f16 caches with 32 or 96 heads take the two-waves-per-head-block kernel
-  // (its tile loads divide evenly over 4 or 12 waves and its registers fit 3
-  // waves per SIMD); the other f16 head counts take the split-K kernel.
+  // f32 caches take the FP32-MFMA kernel, f16 caches the x32 f16 kernel; each
+  // spreads a split's heads over one or more workgroups (mla32_groups,
+  // mla16_groups).
   constexpr int H = NHB * 16;
   constexpr bool kF32 = sizeof(CT) == 4;
-  constexpr bool kFull16 = sizeof(CT) == 2 && (NHB == 2 || NHB == 6);
   void (*kern)(MlaArgs);
-  int threads, groups = 1;
+  int threads, groups;
   const bool idx = d.layout == SK_KV_INDEXED;
   if constexpr (kF32) {
     kern = idx ? mla32_split_kernel<mla32_blocks(H), true> : mla32_split_kernel<mla32_blocks(H), false>;
     threads = mla32_blocks(H) * 256;
     groups = mla32_groups(H);
-  } else if constexpr (kFull16) {
-    kern = idx ? mla16_split_kernel<NHB, true> : mla16_split_kernel<NHB, false>;
-    threads = NHB * 128;
   } else {
-    if (idx) return SK_ERR_UNSUPPORTED;
-    kern = mla_split_kernel<CT, NHB>;
-    threads = kMlaThreads;
+    kern = idx ? mla16_split_kernel<mla16_blocks(H), true> : mla16_split_kernel<mla16_blocks(H), false>;
+    threads = mla16_blocks(H) * 128;
+    groups = mla16_groups(H);
   }
   const dim3 gr(s.p->n_splits, d.batch, groups);
   grid[0] = gr.x;

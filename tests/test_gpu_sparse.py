@@ -86,7 +86,8 @@ def test_dsa_latent_top_2048(kv):
     free()
 
 
-@pytest.mark.parametrize("kv,hq", [("f32", 32), ("f32", 64), ("f32", 128), ("f16", 32)])
+@pytest.mark.parametrize("kv,hq", [("f32", 32), ("f32", 64), ("f32", 128), ("f16", 32), ("f16", 64),
+                                   ("f16", 128)])
 def test_latent_index_list_head_counts(kv, hq):
     for L, S in ((1000, 0), (33, 2), (1, 1), (4097, 5)):
         case = synthetic.indexed_case(f"lat-idx-{kv}-{hq}-{L}", pool_rows=L + 2000, seq_lens=[L],
@@ -96,18 +97,6 @@ def test_latent_index_list_head_counts(kv, hq):
         out, _, call = run_gpu(case, n_splits=S)
         ref, _ = oracle_out(case)
         assert_parity(case, out, ref, tight=(kv == "f32"), label=f"{kv} hq={hq} L={L} plan={call.plan}")
-
-
-def test_latent_f16_with_64_heads_refuses_index_lists():
-    from split_kv_flash_amd import SplitKVError
-    from split_kv_flash_amd.binding import SK_ERR_UNSUPPORTED
-
-    case = synthetic.indexed_case("lat64", pool_rows=200, seq_lens=[100], num_q_heads=64,
-                                  num_kv_heads=1, head_dim=576, kv_dtype="f16",
-                                  latent_value_dim=512, seed=1, scale=1 / 24)
-    with pytest.raises(SplitKVError) as e:
-        run_gpu(case)
-    assert e.value.status == SK_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("kv", ["f32", "f16"])

@@ -53,7 +53,8 @@ def test_every_gqa_variant_matches_oracle(G, D, kv, layout):
 def test_latent_head_counts(kv, hq):
     """32, 64 and 128 heads take other kernel variants than the 96-head layer
     (f32: two 16-head blocks per workgroup and 1, 2 or 4 workgroups per split;
-    f16: the two-wave kernel at 32 heads, the split-K kernel at 64 and 128)."""
+    f16: 2 or 4 blocks per workgroup, and two workgroups per split at 128,
+    whose 4-block workgroups split a tile's 36 wave-loads unevenly))."""
     for L, S in ((1000, 0), (33, 2), (4097, 5)):
         case = synthetic.latent_case(f"latent{hq}-{kv}-L{L}", seq_len=L, kv_dtype=kv,
                                      num_q_heads=hq, capacity=L + 9, seed=7000 + hq + L,
