@@ -186,6 +186,7 @@ __device__ __forceinline__ int tile_off(int r, int cc) { return r * kLatDk + ((c
 // workgroups of 64, whose 8 waves keep two waves per SIMD).
 __host__ __device__ constexpr int mla16_blocks(int Hq) { return Hq == 128 ? 4 : Hq / 16; }
 __host__ __device__ constexpr int mla16_groups(int Hq) { return Hq / (16 * mla16_blocks(Hq)); }
+constexpr int64_t kHalveHeadsAt = 128;  // (split, sequence) pairs, half of MI355X's CUs
 
 template <int NHB, bool IDX>
 __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
@@ -766,6 +767,17 @@ static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void*
     kern = idx ? mla16_split_kernel<mla16_blocks(H), true> : mla16_split_kernel<mla16_blocks(H), false>;
     threads = mla16_blocks(H) * 128;
     groups = mla16_groups(H);
+    if constexpr (H == 64 || H == 96) {
+      // A short context leaves most of the 256 compute units idle with one
+      // workgroup per split: up to 128 (split, sequence) pairs, the heads go
+      // to two workgroups of half as many (results unchanged: each head's
+      // arithmetic does not depend on its workgroup).
+      if ((int64_t)s.p->n_splits * d.batch <= kHalveHeadsAt) {
+        kern = idx ? mla16_split_kernel<H / 32, true> : mla16_split_kernel<H / 32, false>;
+        threads = (H / 32) * 128;
+        groups = 2;
+      }
+    }
   }
   const dim3 gr(s.p->n_splits, d.batch, groups);
   grid[0] = gr.x;

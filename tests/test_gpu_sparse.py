@@ -89,7 +89,7 @@ def test_dsa_latent_top_2048(kv):
 @pytest.mark.parametrize("kv,hq", [("f32", 32), ("f32", 64), ("f32", 128), ("f16", 32), ("f16", 64),
                                    ("f16", 128)])
 def test_latent_index_list_head_counts(kv, hq):
-    for L, S in ((1000, 0), (33, 2), (1, 1), (4097, 5)):
+    for L, S in ((1000, 0), (33, 2), (1, 1), (4097, 5), (4097, 130)):
         case = synthetic.indexed_case(f"lat-idx-{kv}-{hq}-{L}", pool_rows=L + 2000, seq_lens=[L],
                                       num_q_heads=hq, num_kv_heads=1, head_dim=576, kv_dtype=kv,
                                       latent_value_dim=512, max_indices=L + 9, seed=9800 + hq + L,

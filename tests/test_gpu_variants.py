@@ -55,7 +55,9 @@ def test_latent_head_counts(kv, hq):
     (f32: two 16-head blocks per workgroup and 1, 2 or 4 workgroups per split;
     f16: 2 or 4 blocks per workgroup, and two workgroups per split at 128,
     whose 4-block workgroups split a tile's 36 wave-loads unevenly))."""
-    for L, S in ((1000, 0), (33, 2), (4097, 5)):
+    # S = 130: more than 128 (split, sequence) pairs, so 64 and 96 f16 heads
+    # stay in one workgroup per split; the short plans split them in two.
+    for L, S in ((1000, 0), (33, 2), (4097, 5), (4097, 130)):
         case = synthetic.latent_case(f"latent{hq}-{kv}-L{L}", seq_len=L, kv_dtype=kv,
                                      num_q_heads=hq, capacity=L + 9, seed=7000 + hq + L,
                                      scale=1.0 / 24.0)  # NaN rows past the end
