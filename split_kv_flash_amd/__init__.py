@@ -32,7 +32,7 @@ __all__ = [
     "attn_decode_status_string", "attn_decode_last_error", "attn_decode_kernel_info",
     "attn_decode", "attn_decode_one_launch", "attn_decode_workspace_init",
     "attn_decode_combine_project", "QueryTileCall", "attn_query_tiles", "attn_query_tiles_plan",
-    "attn_query_tiles_workspace_bytes",
+    "attn_query_tiles_workspace_bytes", "decode",
 ]
 
 
@@ -106,6 +106,13 @@ def make_desc(q, k, v=None, *, scale: float, block_table=None, page_size: int = 
     return d
 
 
+def _on_gpu(*tensors) -> None:
+    """Refuses host tensors up front (the kernels take device addresses only)."""
+    for t in tensors:
+        if t is not None and not getattr(t, "is_cuda", False):
+            raise SplitKVError(binding.SK_ERR_INVALID_ARG, "tensor arguments must live on the GPU")
+
+
 def _stream_handle(stream) -> int:
     import torch
 
@@ -127,6 +134,7 @@ class DecodeCall:
                  cu_count: Optional[int] = None, max_seq_len: Optional[int] = None):
         import torch
 
+        _on_gpu(q, k, v, seq_lens, block_table)
         self.desc = make_desc(q, k, v, scale=scale, block_table=block_table, page_size=page_size,
                               v_cols=v_cols, max_seq_len=max_seq_len)
         lens = [int(x) for x in host_seq_lens]
@@ -236,6 +244,7 @@ class QueryTileCall:
                  cu_count: Optional[int] = None):
         import torch
 
+        _on_gpu(q, k, v, seq_lens)
         if q.dim() != 4 or not q.is_contiguous():
             raise SplitKVError(binding.SK_ERR_INVALID_ARG, "q must be a contiguous [B][Q][Hq][D] tensor")
         B, Q, Hq, D = q.shape
@@ -263,3 +272,52 @@ class QueryTileCall:
                          self.workspace, self.ws_bytes, self.out, self.lse if with_lse else None,
                          _stream_handle(stream))
         return self.out, self.lse
+
+
+def decode(q, k, v=None, *, seq_lens, scale: float, n_splits: int = 0, block_table=None,
+           page_size: int = 0, v_cols: Optional[int] = None, host_seq_lens=None, out=None,
+           lse=None, workspace=None, stream=None):
+    """One decode-attention call in a single function: plan, workspace and
+    ``attn_decode`` (split kernel, then combine) on the current torch stream.
+
+    ``seq_lens`` is the int32 [B] device tensor the kernels read. The plan
+    needs the longest and the total length on the host: pass them as
+    ``host_seq_lens`` (any int sequence), or they are copied from
+    ``seq_lens``, which synchronises the stream. ``out`` ([B][Hq][Dv] f32),
+    ``lse`` ([B][Hq] f32) and ``workspace`` (uint8, at least
+    ``attn_decode_workspace_bytes``) are allocated when not given; a given
+    workspace must have had ``attn_decode_workspace_init`` only if it is also
+    used with ``attn_decode_one_launch``. Returns (out, lse); lse is None
+    unless requested with ``lse=True`` or given as a tensor."""
+    import torch
+
+    _on_gpu(q, k, v, seq_lens, block_table, out, workspace)
+    if isinstance(lse, torch.Tensor):
+        _on_gpu(lse)
+    desc = make_desc(q, k, v, scale=scale, block_table=block_table, page_size=page_size,
+                     v_cols=v_cols)
+    lens = [int(x) for x in (seq_lens.tolist() if host_seq_lens is None else host_seq_lens)]
+    if len(lens) != desc.batch:
+        raise SplitKVError(binding.SK_ERR_INVALID_ARG, "seq_lens has the wrong length")
+    cu = torch.cuda.get_device_properties(q.device).multi_processor_count
+    plan = attn_decode_plan(desc, max(lens), sum(lens), cu, n_splits)
+    limit = min(desc.max_seq_len, plan.n_splits * plan.chunk)
+    if min(lens) < 1 or max(lens) > limit:
+        raise SplitKVError(binding.SK_ERR_INVALID_ARG, f"sequence lengths must lie in [1, {limit}]")
+    ws_bytes = attn_decode_workspace_bytes(desc, plan)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < ws_bytes:
+        raise SplitKVError(binding.SK_ERR_WORKSPACE_TOO_SMALL,
+                           f"workspace holds {workspace.numel() * workspace.element_size()} "
+                           f"bytes, the plan needs {ws_bytes}")
+    if out is None:
+        out = torch.empty(desc.batch, desc.num_q_heads, desc.head_dim_v, dtype=torch.float32,
+                          device=q.device)
+    if lse is True:
+        lse = torch.empty(desc.batch, desc.num_q_heads, dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    attn_decode(desc, plan, q, k, v, block_table, seq_lens, workspace,
+                workspace.numel() * workspace.element_size(), out, lse, _stream_handle(stream))
+    return out, lse

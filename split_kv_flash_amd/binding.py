@@ -117,10 +117,14 @@ def header_functions() -> list:
 
 
 def _ptr(x) -> Optional[int]:
+    """Device address of a tensor (None for NULL; an int passes through as an
+    address). A host tensor is refused: the kernels would fault on it."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not getattr(x, "is_cuda", False):
+        raise SplitKVError(SK_ERR_INVALID_ARG, "tensor arguments must live on the GPU")
     return x.data_ptr()
 
 

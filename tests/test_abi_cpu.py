@@ -326,3 +326,23 @@ def test_synthetic_case_descriptor_fields_round_trip():
     assert t["k"].dtype == torch.bfloat16
     d = make_desc(t["q"], t["k"], t["v"], scale=case.scale, block_table=t["block_table"], page_size=16)
     assert (d.layout, d.page_size, d.max_pages_per_seq, d.num_pages) == (B.SK_KV_PAGED, 16, 3, 5)
+
+
+def test_host_tensors_are_refused_before_the_library_is_called():
+    """The binding passes device addresses only: a host tensor raises before
+    any entry point runs (a kernel would fault on a host address)."""
+    import torch
+
+    lib()
+    d = gqa_desc()
+    plan = B.attn_decode_plan(d, 4096, 4096, 256, 0)
+    q = torch.zeros(1, 16, 256)
+    with pytest.raises(B.SplitKVError) as e:
+        B.attn_decode_splitk(d, plan, q, 4096, 4096, None, 4096, 4096, 1 << 30, 0)
+    assert e.value.status == B.SK_ERR_INVALID_ARG and "GPU" in e.value.message
+    import split_kv_flash_amd as skf
+
+    with pytest.raises(B.SplitKVError):
+        skf.decode(q, torch.zeros(1, 4096, 4, 256), torch.zeros(1, 4096, 4, 256),
+                   seq_lens=torch.full((1,), 4096, dtype=torch.int32), scale=1 / 16,
+                   host_seq_lens=[4096], out=torch.zeros(1, 16, 256))
