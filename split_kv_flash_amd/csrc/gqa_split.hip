@@ -365,8 +365,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
           off = pos < end ? off : last_off;
 #pragma unroll
           for (int j = 0; j < NL; ++j) {
-            kt[r][j] = load_vec<KV, VEC>(kb + off + j * RL * VEC);
-            vt[r][j] = load_vec<KV, VEC>(vb + off + j * RL * VEC);
+            kt[r][j] = load_vec_stream<KV, VEC>(kb + off + j * RL * VEC);
+            vt[r][j] = load_vec_stream<KV, VEC>(vb + off + j * RL * VEC);
           }
         }
       } else if constexpr (MODE == kPagedFast) {
@@ -383,8 +383,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 #pragma unroll
           for (int j = 0; j < NL; ++j) {
             const uint32_t o = lofp + (uint32_t)(j * RL * VEC * sizeof(KV));
-            kt[r][j] = load_vec_buf<KV, VEC>(rk, o);
-            vt[r][j] = load_vec_buf<KV, VEC>(rv, o);
+            kt[r][j] = load_vec_stream<KV, VEC>(rk, o);
+            vt[r][j] = load_vec_stream<KV, VEC>(rv, o);
           }
         }
       } else {
@@ -401,8 +401,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 #pragma unroll
           for (int j = 0; j < NL; ++j) {
             const uint32_t o = loff[r] + (uint32_t)(j * RL * VEC * sizeof(KV));
-            kt[r][j] = load_vec_buf<KV, VEC>(rk, o);
-            vt[r][j] = load_vec_buf<KV, VEC>(rv, o);
+            kt[r][j] = load_vec_stream<KV, VEC>(rk, o);
+            vt[r][j] = load_vec_stream<KV, VEC>(rv, o);
           }
       }
     };

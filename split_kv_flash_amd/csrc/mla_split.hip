@@ -48,6 +48,7 @@ struct MlaArgs {
   const int32_t* table;
   int32_t max_idx;
   int64_t num_rows;
+  int32_t nt;  // 1: this workgroup is its rows' only reader (non-temporal tile loads)
 };
 
 // Index-list tiles (IDX kernels): lane r < T of every wave holds the pool row
@@ -96,25 +97,42 @@ typedef __attribute__((address_space(3))) _Float16 lds_half_t;
 
 // One global_load_lds_dwordx4: each lane's 16 bytes at `g` land in LDS at
 // lds_addr + 16*lane (lds_addr must be wave-uniform; it goes through M0).
+// `nt` (wave-uniform) selects the non-temporal policy: used when the workgroup
+// is the only reader of its rows (one workgroup per split), with which MI355X
+// streams HBM measurably faster; when a split's heads span several
+// workgroups, each re-reading the rows, the plain policy lets the later reads
+// hit the caches.
 // Issued as inline assembly so the compiler's wait-count tracking does not
 // treat every later LDS read as possibly aliasing it (it would then wait for
 // all loads in flight); the kernel waits for these loads explicitly. M0 is not
 // otherwise used by these kernels.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds_addr)
-               : "memory", "m0");
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr, bool nt) {
+  if (nt)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :
+                 : "v"(g), "s"(lds_addr)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds_addr)
+                 : "memory", "m0");
 }
 // The same load with a wave-uniform 64-bit base in scalar registers and a
 // 32-bit per-lane byte offset (global address = base + offset).
-__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds_addr)
-               : "memory", "m0");
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_addr, bool nt) {
+  if (nt)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_addr_of(const _Float16* p) {
@@ -265,7 +283,7 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
         const int scol = ((sl - srow * kCpr16) ^ (srow & 7)) * 8;
         const int32_t r = row_of(a, nidx, srow);
         const uint32_t dst = lds0 + (uint32_t)((bi * TILE + (wl0 + c) * 64 * 8) * 2);
-        dma16(cbase + (int64_t)r * a.stride_pos + scol, __builtin_amdgcn_readfirstlane(dst));
+        dma16(cbase + (int64_t)r * a.stride_pos + scol, __builtin_amdgcn_readfirstlane(dst), a.nt);
       }
       nidx = load_tile_index(a, b, tb + kT16, end, kT16);  // the next tile's rows
     } else {
@@ -280,7 +298,7 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
         const int scol = ((sl - srow * kCpr16) ^ (srow & 7)) * 8;
         const uint32_t off = (uint32_t)min(srow, last) * row_bytes + (uint32_t)(scol * 2);
         const uint32_t dst = lds0 + (uint32_t)((bi * TILE + (wl0 + c) * 64 * 8) * 2);
-        dma16s(off, tbase, __builtin_amdgcn_readfirstlane(dst));
+        dma16s(off, tbase, __builtin_amdgcn_readfirstlane(dst), a.nt);
       }
     }
   };
@@ -569,7 +587,7 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
       for (int c = 0; c < DPW; ++c) {
         const int32_t r = row_of(a, nidx, srow[c] < 0 ? 0 : srow[c]);
         const uint32_t dst = lds0 + (uint32_t)((bi * TSTRIDE + (wave * DPW + c) * 64 * 4) * 4);
-        dma16(cbase + (int64_t)r * a.stride_pos + scol[c], __builtin_amdgcn_readfirstlane(dst));
+        dma16(cbase + (int64_t)r * a.stride_pos + scol[c], __builtin_amdgcn_readfirstlane(dst), a.nt);
       }
       nidx = load_tile_index(a, b, tb + kT32, end, kT32);  // the next tile's rows
     } else {
@@ -578,7 +596,7 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
         int64_t pos = srow[c] < 0 ? start : tb + srow[c];
         pos = pos < end ? pos : end - 1;
         const uint32_t dst = lds0 + (uint32_t)((bi * TSTRIDE + (wave * DPW + c) * 64 * 4) * 4);
-        dma16(cbase + pos * a.stride_pos + scol[c], __builtin_amdgcn_readfirstlane(dst));
+        dma16(cbase + pos * a.stride_pos + scol[c], __builtin_amdgcn_readfirstlane(dst), a.nt);
       }
     }
   };
@@ -803,6 +821,7 @@ static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void*
   a.table = s.block_table;
   a.max_idx = d.max_pages_per_seq;
   a.num_rows = d.num_pages;
+  a.nt = groups == 1;
   hipLaunchKernelGGL(kern, gr, dim3(threads), 0, s.stream, a);
   return SK_OK;
 }

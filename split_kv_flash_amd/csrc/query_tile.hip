@@ -171,6 +171,10 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
     const KT* __restrict__ kp = reinterpret_cast<const KT*>(a.k) + (int64_t)b * a.stride_seq + (int64_t)g * a.stride_head;
     const KT* __restrict__ vp = reinterpret_cast<const KT*>(a.v) + (int64_t)b * a.stride_seq + (int64_t)g * a.stride_head;
     // Tile rows past `stop` re-read row stop-1 (in range; their scores are masked).
+    // With DS > 1 the KV group's query rows fit one workgroup, the only
+    // reader of its rows: non-temporal loads (nt), which stream HBM faster on
+    // MI355X. Otherwise several query tiles read the same rows and the plain
+    // policy lets the later reads hit the caches.
     auto gload = [&](qt_u4 (&kr)[NCH], qt_u4 (&vr)[NCH], int64_t tb) {
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
@@ -178,8 +182,13 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
         const int row = c / CPR, col = (c - (c / CPR) * CPR) * 8;
         const int64_t pos = min(tb + row, stop - 1);
         const int64_t off = pos * a.stride_pos + col;
-        kr[j] = *reinterpret_cast<const qt_u4*>(kp + off);
-        vr[j] = *reinterpret_cast<const qt_u4*>(vp + off);
+        if constexpr (DS > 1) {
+          kr[j] = __builtin_nontemporal_load(reinterpret_cast<const qt_u4*>(kp + off));
+          vr[j] = __builtin_nontemporal_load(reinterpret_cast<const qt_u4*>(vp + off));
+        } else {
+          kr[j] = *reinterpret_cast<const qt_u4*>(kp + off);
+          vr[j] = *reinterpret_cast<const qt_u4*>(vp + off);
+        }
       }
     };
     auto swrite = [&](int buf, const qt_u4 (&kr)[NCH], const qt_u4 (&vr)[NCH]) {

@@ -60,6 +60,30 @@ __device__ __forceinline__ Vec<T, N> load_vec_buf(__amdgpu_buffer_rsrc_t r, uint
     return __builtin_bit_cast(Vec<T, N>, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
+// Streaming loads for data read once (the K/V cache): the non-temporal cache
+// policy (the nt bit, cache-policy operand 2 of the buffer load; the
+// nontemporal builtin for a plain address). On MI355X a stream of 16-byte
+// loads reads HBM at about 7.0 TB/s with it and about 6.2 TB/s without.
+constexpr int kCacheStream = 2;
+template <typename T, int N>
+__device__ __forceinline__ Vec<T, N> load_vec_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  static_assert(sizeof(T) * N == 16 || sizeof(T) * N == 8, "buffer loads of 8 or 16 bytes");
+  if constexpr (sizeof(T) * N == 16)
+    return __builtin_bit_cast(Vec<T, N>, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCacheStream));
+  else
+    return __builtin_bit_cast(Vec<T, N>, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCacheStream));
+}
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+template <typename T, int N>
+__device__ __forceinline__ Vec<T, N> load_vec_stream(const T* p) {
+  static_assert(sizeof(T) * N == 16 || sizeof(T) * N == 8, "loads of 8 or 16 bytes");
+  if constexpr (sizeof(T) * N == 16)
+    return __builtin_bit_cast(Vec<T, N>, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+  else
+    return __builtin_bit_cast(Vec<T, N>, __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p)));
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane reductions. A row of 16 lanes is the unit DPP works in on gfx9:
 // row_ror:8, row_ror:4 and two quad permutations give every lane the sum of
