@@ -429,8 +429,8 @@ def _cpu_model():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark measures one GPU; every box here has one GPU and "
-                                   "the multi-GPU path is a design note only (run with --gpus 1)"}))
+        print(json.dumps({"error": "this benchmark measures one GPU; sharding over several GPUs is "
+                                   "designed but not built (run with --gpus 1)"}))
         sys.exit(2)
     import torch
 
