@@ -77,8 +77,8 @@ __device__ __forceinline__ int32_t row_of(const MlaArgs& a, int32_t idx, int row
 }
 
 // ---------------------------------------------------------------------------
-// Helpers shared by the f16 and f32 latent kernels: direct global-to-LDS tile
-// loads, the gfx950 transpose read, explicit wait counts and a raw barrier.
+// How the latent kernels stage tiles (the direct-to-LDS load, its explicit
+// wait and the raw barrier live in sk_device.h) and read them:
 //  * global_load_lds_dwordx4 puts each lane's 16 bytes at M0 + 16*lane, so a
 //    tile goes straight from HBM into LDS with no registers holding staged
 //    data; rows are stored unpadded with their 16-byte chunk index XOR-ed by
@@ -95,46 +95,6 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 typedef __attribute__((address_space(3))) _Float16 lds_half_t;
 
-// One global_load_lds_dwordx4: each lane's 16 bytes at `g` land in LDS at
-// lds_addr + 16*lane (lds_addr must be wave-uniform; it goes through M0).
-// `nt` (wave-uniform) selects the non-temporal policy: used when the workgroup
-// is the only reader of its rows (one workgroup per split), with which MI355X
-// streams HBM measurably faster; when a split's heads span several
-// workgroups, each re-reading the rows, the plain policy lets the later reads
-// hit the caches.
-// Issued as inline assembly so the compiler's wait-count tracking does not
-// treat every later LDS read as possibly aliasing it (it would then wait for
-// all loads in flight); the kernel waits for these loads explicitly. M0 is not
-// otherwise used by these kernels.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr, bool nt) {
-  if (nt)
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-                 :
-                 : "v"(g), "s"(lds_addr)
-                 : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(g), "s"(lds_addr)
-                 : "memory", "m0");
-}
-// The same load with a wave-uniform 64-bit base in scalar registers and a
-// 32-bit per-lane byte offset (global address = base + offset).
-__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_addr, bool nt) {
-  if (nt)
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-                 :
-                 : "v"(voff), "s"(sbase), "s"(lds_addr)
-                 : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(voff), "s"(sbase), "s"(lds_addr)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_addr_of(const _Float16* p) {
   return (uint32_t)(size_t)(const lds_half_t*)(p);
 }
@@ -149,18 +109,6 @@ __device__ __forceinline__ half4_t lds_read_tr(const _Float16* p) {
   return __builtin_bit_cast(half4_t, v);
 }
 
-// s_waitcnt with vmcnt = VM (no wait on exp), lgkmcnt = 0: this wave's LDS
-// writes are done and at most VM of its vector-memory operations remain.
-template <int VM>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(VM >= 0 && VM < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
-}
-__device__ __forceinline__ void raw_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 constexpr int kT16 = 32;     // positions per tile
 constexpr int kCpr16 = kLatDk / 8;   // 72 chunks of 16 bytes per cache row

@@ -102,7 +102,6 @@ template <typename KT, int D, int DS>
 __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
   using TT = QtType<KT>;
   constexpr int T = 32;         // positions per K/V tile
-  constexpr int RS = D + 8;     // LDS row stride (16-bit elements)
   constexpr int KS = D / 32;    // score MFMA steps over the head width
   constexpr int CB = D / 16;    // output column blocks over the head width
   constexpr int KSW = KS / DS;  // score steps of one wave
@@ -110,10 +109,15 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
   constexpr int RB = 4 / DS;    // row blocks per workgroup
   constexpr int RW = 16 * RB;   // query rows per workgroup
   constexpr int CPR = D / 8;    // 16-byte chunks per row
-  constexpr int NCH = D / 64;   // chunks per thread per tile (K and V each): 32*CPR / 256
+  constexpr int NB = 4;         // LDS tile buffers: three tiles in flight while one is consumed
+  constexpr int WLH = T * CPR / 64;  // wave-loads of 64 chunks per tile half (K or V)
+  constexpr int DPW = 2 * WLH / 4;   // wave-loads per wave per tile (waves 0-1: K, 2-3: V)
   static_assert(D % 64 == 0 && KS % DS == 0 && (DS == 1 || DS == 2 || DS == 4), "head width / split");
+  static_assert(WLH % DPW == 0 && CPR >= 8, "a wave's loads stay within K or V; 8-chunk swizzle");
 
-  __shared__ __align__(16) short s_kv[2][2][T * RS];  // [buffer][K, V][row * RS + column]
+  // [buffer][K, V][row * D + column], rows unpadded, the 16-byte chunk index of
+  // row r stored XOR-ed with r & 7 (conflict-free score and transpose reads).
+  __shared__ __align__(16) short s_kv[NB][2][T * D];
   __shared__ __align__(16) float s_sc[DS > 1 ? 4 : 1][64][8];  // partial scores per wave and lane
 
   const int g = blockIdx.x / a.nqt;
@@ -157,11 +161,57 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
     qt_s8 qh[KSW], ql[KSW];
     {
       const int64_t qbase = (((int64_t)b * a.Q + t) * a.Hq + g * a.G + hh) * D + 32 * KSW * dq;
+      // Eight consecutive elements per step, widened to f32: every load is
+      // issued before the first conversion, under uniform branches on the
+      // run-time type (0 f32, 1 f16, 2 bf16).
+      float qv[KSW][8];
+#pragma unroll
+      for (int ks = 0; ks < KSW; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[ks][e] = 0.0f;
+      if (rvalid) {
+        const int64_t q0 = qbase + 8 * lq;
+        if (a.q_dtype == 0) {
+          float4 w[KSW][2];
+#pragma unroll
+          for (int ks = 0; ks < KSW; ++ks) {
+            w[ks][0] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.q) + q0 + 32 * ks);
+            w[ks][1] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.q) + q0 + 32 * ks + 4);
+          }
+#pragma unroll
+          for (int ks = 0; ks < KSW; ++ks) {
+            qv[ks][0] = w[ks][0].x; qv[ks][1] = w[ks][0].y; qv[ks][2] = w[ks][0].z; qv[ks][3] = w[ks][0].w;
+            qv[ks][4] = w[ks][1].x; qv[ks][5] = w[ks][1].y; qv[ks][6] = w[ks][1].z; qv[ks][7] = w[ks][1].w;
+          }
+        } else {
+          qt_u4 w[KSW];
+#pragma unroll
+          for (int ks = 0; ks < KSW; ++ks)
+            w[ks] = *reinterpret_cast<const qt_u4*>(reinterpret_cast<const uint16_t*>(a.q) + q0 + 32 * ks);
+          if (a.q_dtype == 1) {
+#pragma unroll
+            for (int ks = 0; ks < KSW; ++ks)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                qv[ks][2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[ks][e] & 0xffffu));
+                qv[ks][2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[ks][e] >> 16));
+              }
+          } else {
+#pragma unroll
+            for (int ks = 0; ks < KSW; ++ks)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                qv[ks][2 * e] = __uint_as_float(w[ks][e] << 16);
+                qv[ks][2 * e + 1] = __uint_as_float(w[ks][e] & 0xffff0000u);
+              }
+          }
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < KSW; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float x = rvalid ? load_q(a.q, a.q_dtype, qbase + 32 * ks + 8 * lq + e) * a.qscale : 0.0f;
+          const float x = qv[ks][e] * a.qscale;
           const short hi = TT::from(x);
           qh[ks][e] = hi;
           ql[ks][e] = TT::from(x - TT::to(hi));
@@ -170,34 +220,28 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
 
     const KT* __restrict__ kp = reinterpret_cast<const KT*>(a.k) + (int64_t)b * a.stride_seq + (int64_t)g * a.stride_head;
     const KT* __restrict__ vp = reinterpret_cast<const KT*>(a.v) + (int64_t)b * a.stride_seq + (int64_t)g * a.stride_head;
-    // Tile rows past `stop` re-read row stop-1 (in range; their scores are masked).
-    // With DS > 1 the KV group's query rows fit one workgroup, the only
-    // reader of its rows: non-temporal loads (nt), which stream HBM faster on
-    // MI355X. Otherwise several query tiles read the same rows and the plain
-    // policy lets the later reads hit the caches.
-    auto gload = [&](qt_u4 (&kr)[NCH], qt_u4 (&vr)[NCH], int64_t tb) {
+    // Tile staging by direct global-to-LDS loads: wave-load wl of a tile
+    // (0 .. 2*WLH-1; K first, then V) fills 1 KB of the half's LDS rows; lane
+    // slot s of it is row s / CPR, physical chunk p = s % CPR, which holds
+    // logical chunk p ^ (row & 7). Rows past `stop` re-read row stop-1 (in
+    // range; their scores are masked). With DS > 1 the KV group's query rows
+    // fit one workgroup, the only reader of its rows: non-temporal loads,
+    // which stream HBM faster on MI355X. Otherwise several query tiles read
+    // the same rows and the plain policy lets the later reads hit the caches.
+    const uint32_t lds_kv = (uint32_t)(size_t)(const __attribute__((address_space(3))) short*)(&s_kv[0][0][0]);
+    const int wl0 = __builtin_amdgcn_readfirstlane(wave * DPW);
+    const int half = wl0 / WLH;  // 0: K, 1: V (wave-uniform)
+    const KT* __restrict__ src0 = half ? vp : kp;
+    auto issue = [&](int buf, int64_t tb) {
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const int c = tid + 256 * j;
-        const int row = c / CPR, col = (c - (c / CPR) * CPR) * 8;
+      for (int c = 0; c < DPW; ++c) {
+        const int wh = wl0 - half * WLH + c;  // wave-load within the half
+        const int sl = wh * 64 + lane;
+        const int row = sl / CPR, p = sl - (sl / CPR) * CPR;
         const int64_t pos = min(tb + row, stop - 1);
-        const int64_t off = pos * a.stride_pos + col;
-        if constexpr (DS > 1) {
-          kr[j] = __builtin_nontemporal_load(reinterpret_cast<const qt_u4*>(kp + off));
-          vr[j] = __builtin_nontemporal_load(reinterpret_cast<const qt_u4*>(vp + off));
-        } else {
-          kr[j] = *reinterpret_cast<const qt_u4*>(kp + off);
-          vr[j] = *reinterpret_cast<const qt_u4*>(vp + off);
-        }
-      }
-    };
-    auto swrite = [&](int buf, const qt_u4 (&kr)[NCH], const qt_u4 (&vr)[NCH]) {
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const int c = tid + 256 * j;
-        const int row = c / CPR, col = (c - (c / CPR) * CPR) * 8;
-        *reinterpret_cast<qt_u4*>(&s_kv[buf][0][row * RS + col]) = kr[j];
-        *reinterpret_cast<qt_u4*>(&s_kv[buf][1][row * RS + col]) = vr[j];
+        const KT* src = src0 + pos * a.stride_pos + ((p ^ (row & 7)) * 8);
+        const uint32_t dst = lds_kv + (uint32_t)(((buf * 2 + half) * T * D + wh * 512) * 2);
+        dma16(src, __builtin_amdgcn_readfirstlane(dst), DS > 1);
       }
     };
 
@@ -207,8 +251,8 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
     // Consumes tile i from LDS buffer i & 1: scores, online softmax, output.
     auto consume = [&](int i) {
       const int64_t tb = start + (int64_t)i * T;
-      const short* kb = s_kv[i & 1][0];
-      const short* vb = s_kv[i & 1][1];
+      const short* kb = s_kv[i % NB][0];
+      const short* vb = s_kv[i % NB][1];
 
       // ---- scores S^T: two blocks of 16 positions, this block's 16 rows ----
       qt_f4 sp[2] = {qt_f4{0.f, 0.f, 0.f, 0.f}, qt_f4{0.f, 0.f, 0.f, 0.f}};
@@ -216,8 +260,9 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
       for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
         for (int ks = 0; ks < KSW; ++ks) {
-          const qt_s8 av =
-              *reinterpret_cast<const qt_s8*>(kb + (16 * pb + l16) * RS + 32 * (KSW * dq + ks) + 8 * lq);
+          // row 16 pb + l16 (swizzle l16 & 7), logical chunk 4 (KSW dq + ks) + lq
+          const qt_s8 av = *reinterpret_cast<const qt_s8*>(
+              kb + (16 * pb + l16) * D + (((4 * (KSW * dq + ks) + lq) ^ (l16 & 7)) << 3));
           sp[pb] = TT::mma(av, qh[ks], sp[pb]);
           sp[pb] = TT::mma(av, ql[ks], sp[pb]);
         }
@@ -228,7 +273,8 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
         qt_f4* mine = reinterpret_cast<qt_f4*>(&s_sc[wave][lane][0]);
         mine[0] = sp[0];
         mine[1] = sp[1];
-        __syncthreads();
+        wait_vm_lgkm0<63>();  // this wave's LDS writes done; tile loads stay in flight
+        raw_barrier();
         const qt_f4* p0 = reinterpret_cast<const qt_f4*>(&s_sc[rb * DS][lane][0]);
         sp[0] = p0[0];
         sp[1] = p0[1];
@@ -281,41 +327,38 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
       }
 
       // ---- output: acc += P V over this wave's columns, positions in the scores' order ----
-      const short* vrow = vb + (4 * lq + (l16 >> 2)) * RS + 4 * (l16 & 3) + 16 * CBW * dq;
+      // Rows rv = 4 lq + l16/4 and rv + 16 (same swizzle rv & 7), columns
+      // 16 (CBW dq + c) + 4 (l16 & 3): logical chunk 2 (CBW dq + c) + (l16 & 3)/2,
+      // at half 4 (l16 & 1) within it.
+      const int rv = 4 * lq + (l16 >> 2);
+      const short* vrow = vb + rv * D + 4 * (l16 & 1);
 #pragma unroll
       for (int c = 0; c < CBW; ++c) {
-        const qt_s4 v0 = qt_read_tr(vrow + 16 * c);
-        const qt_s4 v1 = qt_read_tr(vrow + 16 * RS + 16 * c);
+        const int vch = ((2 * (CBW * dq + c) + ((l16 & 3) >> 1)) ^ (rv & 7)) << 3;
+        const qt_s4 v0 = qt_read_tr(vrow + vch);
+        const qt_s4 v1 = qt_read_tr(vrow + 16 * D + vch);
         const qt_s8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
         acc[c] = TT::mma(ph, vv, acc[c]);
         acc[c] = TT::mma(pl, vv, acc[c]);
       }
     };
-    // Two register sets keep two tiles' loads in flight: while tile i is
-    // consumed, tile i+1 (loaded one step earlier) waits in one set and tile
-    // i+2 is requested into the other; tile i+1 then goes to the LDS buffer
-    // tile i-1 used, which every wave left at the previous barrier. Tiles go
-    // in pairs with one exit test per pair, and loads and LDS writes are
-    // unconditional: past the end every row re-reads row stop-1 and an odd
-    // count's last, empty tile is consumed as a no-op (all its scores are
-    // masked). A branch around a load or a mid-pair exit would make the
-    // compiler's wait counting assume the worst path and drain both register
-    // sets before the next use.
-    qt_u4 kA[NCH], vA[NCH], kB[NCH], vB[NCH];
-    gload(kA, vA, start);
-    gload(kB, vB, start + T);
-    swrite(0, kA, vA);
-    __syncthreads();
-    for (int i = 0; i < ntiles; i += 2) {
-      gload(kA, vA, start + (int64_t)(i + 2) * T);
+    // Ring of NB = 4 buffers: tiles i+1 .. i+3 are in flight while tile i is
+    // consumed. Tile i+3 goes to the buffer tile i-1 used, which every wave
+    // left at the previous barrier; each wave then waits for its own loads of
+    // tile i+1 (at most 2 DPW of its loads, tiles i+2 and i+3, remain) and the
+    // barrier publishes the tile. Loads past the end re-read row stop-1.
+    issue(0, start);
+    issue(1, start + T);
+    issue(2, start + 2 * T);
+    wait_vm_lgkm0<2 * DPW>();
+    raw_barrier();
+    for (int i = 0; i < ntiles; ++i) {
+      issue((i + 3) % NB, start + (int64_t)(i + 3) * T);
       consume(i);
-      swrite(1, kB, vB);
-      __syncthreads();
-      gload(kB, vB, start + (int64_t)(i + 3) * T);
-      consume(i + 1);
-      swrite(0, kA, vA);
-      __syncthreads();
+      wait_vm_lgkm0<2 * DPW>();
+      raw_barrier();
     }
+    wait_vm_lgkm0<0>();  // no load into LDS outlives the workgroup
   }
 
   // ---- partials of this wave's rows and columns (rows with nothing visible: neutral) ----

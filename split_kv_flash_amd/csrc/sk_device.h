@@ -85,6 +85,62 @@ __device__ __forceinline__ Vec<T, N> load_vec_stream(const T* p) {
 }
 
 // ---------------------------------------------------------------------------
+// Direct global-to-LDS tile loads and the explicit waits they need.
+// ---------------------------------------------------------------------------
+// One global_load_lds_dwordx4: each lane's 16 bytes at `g` land in LDS at
+// lds_addr + 16*lane (lds_addr must be wave-uniform; it goes through M0).
+// `nt` (wave-uniform) selects the non-temporal policy: used when the workgroup
+// is the only reader of its rows, with which MI355X streams HBM measurably
+// faster; when several workgroups re-read the same rows, the plain policy
+// lets the later reads hit the caches.
+// Issued as inline assembly so the compiler's wait-count tracking does not
+// treat every later LDS read as possibly aliasing it (it would then wait for
+// all loads in flight); the kernel waits for these loads explicitly. The
+// kernels that use it do not otherwise use M0 (the asm declares it clobbered).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr, bool nt) {
+  if (nt)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :
+                 : "v"(g), "s"(lds_addr)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds_addr)
+                 : "memory", "m0");
+}
+// The same load with a wave-uniform 64-bit base in scalar registers and a
+// 32-bit per-lane byte offset (global address = base + offset).
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_addr, bool nt) {
+  if (nt)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt with vmcnt = VM (no wait on exp), lgkmcnt = 0: this wave's LDS
+// writes are done and at most VM of its vector-memory operations remain.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+}
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // Cross-lane reductions. A row of 16 lanes is the unit DPP works in on gfx9:
 // row_ror:8, row_ror:4 and two quad permutations give every lane the sum of
 // its 16-lane row in four VALU operations.
