@@ -21,9 +21,10 @@
 //     16w .. 16w+15; when a KV head has only 16 or 32 query rows the tile
 //     shrinks to them and the waves of a 16-row block share out the head
 //     width instead (see the DS parameter).
-//   * K/V tiles of 32 positions are staged in LDS (row stride D + 8 halves),
-//     double-buffered, with the loads of the next two tiles in flight in two
-//     register sets while the current tile is consumed; one barrier per tile.
+//   * K/V tiles of 32 positions go from HBM straight into LDS
+//     (global_load_lds_dwordx4) in a ring of four buffers, three tiles in
+//     flight while one is consumed; rows unpadded, 16-byte chunks XOR-swizzled
+//     by row & 7; one barrier per tile (two with the score exchange).
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_16x16x32_{f16,bf16}: the K rows are the A operand and the
 //     query rows (held in registers) the B operand. The result leaves lane
