@@ -23,14 +23,6 @@ __device__ __forceinline__ float to_f32(bf16_t x) {
   return __uint_as_float(((uint32_t)x.bits) << 16);
 }
 
-// Reads element i of a q vector whose type is known only at run time (q is
-// read once per workgroup, so the switch costs nothing measurable).
-__device__ __forceinline__ float load_q(const void* q, int dtype, int64_t i) {
-  if (dtype == 0) return reinterpret_cast<const float*>(q)[i];
-  if (dtype == 1) return (float)reinterpret_cast<const _Float16*>(q)[i];
-  return __uint_as_float(((uint32_t)reinterpret_cast<const uint16_t*>(q)[i]) << 16);
-}
-
 // A vector of N storage elements loaded with one instruction (4, 8 or 16 bytes).
 template <typename T, int N>
 struct alignas(sizeof(T) * N) Vec {
@@ -51,15 +43,6 @@ constexpr int kRawBufferWord3 = 0x00020000;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRawBufferWord3);
 }
-template <typename T, int N>
-__device__ __forceinline__ Vec<T, N> load_vec_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  static_assert(sizeof(T) * N == 16 || sizeof(T) * N == 8, "buffer loads of 8 or 16 bytes");
-  if constexpr (sizeof(T) * N == 16)
-    return __builtin_bit_cast(Vec<T, N>, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-  else
-    return __builtin_bit_cast(Vec<T, N>, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
-
 // Streaming loads for data read once (the K/V cache): the non-temporal cache
 // policy (the nt bit, cache-policy operand 2 of the buffer load; the
 // nontemporal builtin for a plain address). On MI355X a stream of 16-byte
