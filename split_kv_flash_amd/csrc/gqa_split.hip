@@ -370,6 +370,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
           }
         }
       } else if constexpr (MODE == kPagedFast) {
+        // Each K load beside the V load of the same row: for 16-token pages this
+        // measured faster than the contiguous path's K-then-V order.
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int64_t pos0 = tb + r * NG;
@@ -396,14 +398,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
         const uint32_t nbytes = left <= 0 ? 0u : (uint32_t)(left < TR ? left : TR) * row_bytes;
         const auto rk = raw_rsrc(kh + tb * row_stride, nbytes);
         const auto rv = raw_rsrc(vh + tb * row_stride, nbytes);
+        // All of the tile's K loads, then all of its V loads: pairing each K
+        // load with the V load of the same row measured up to 3% slower here,
+        // depending on where K and V sit relative to each other in HBM.
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-          for (int j = 0; j < NL; ++j) {
-            const uint32_t o = loff[r] + (uint32_t)(j * RL * VEC * sizeof(KV));
-            kt[r][j] = load_vec_stream<KV, VEC>(rk, o);
-            vt[r][j] = load_vec_stream<KV, VEC>(rv, o);
-          }
+          for (int j = 0; j < NL; ++j)
+            kt[r][j] = load_vec_stream<KV, VEC>(rk, loff[r] + (uint32_t)(j * RL * VEC * sizeof(KV)));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int j = 0; j < NL; ++j)
+            vt[r][j] = load_vec_stream<KV, VEC>(rv, loff[r] + (uint32_t)(j * RL * VEC * sizeof(KV)));
       }
     };
 
