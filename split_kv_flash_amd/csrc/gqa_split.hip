@@ -24,7 +24,9 @@
 //     maximum moved anywhere in the wave (a is then exactly 1).
 //   * Contiguous caches are read with raw buffer loads: one resource per tile
 //     bounds the reads to the split, so the tail of the last tile and the
-//     pipeline's look-ahead past the end read nothing from memory.
+//     pipeline's look-ahead past the end read nothing from memory. Every K/V
+//     load carries the non-temporal policy (the rows are read once), and a
+//     contiguous tile's K loads all go out before its V loads.
 //   * Scores are kept in base-2 units (q is pre-multiplied by scale*log2 e) so
 //     every exponential is one exp2; the stored m is converted back to natural
 //     units.
