@@ -647,21 +647,29 @@ struct Tune {
   static constexpr bool kSliced = sliced_variant(std::is_same<KV, _Float16>::value, D, G);
   static constexpr int RL = kSliced ? 16 : ((D == 256 && kWideGroup) ? 32 : 16);
   static constexpr int HS = kSliced ? 2 : 1;
+  // Rows per tile and row group.
   static constexpr int R =
       kSliced ? (PAGED ? 2 : 4) : (D == 128 ? 4 : ((D == 256 && kWideGroup && sizeof(KV) == 2) ? 4 : 2));
+  // Rows for slices of at least kLongRowsFrom positions. The contiguous 4-head
+  // width-256 layer takes four there: same-tensor A/B against two measured
+  // 165.9 vs 168.8 us (f32, 131,072 positions) and 165.8 vs 170.5 us (f16,
+  // 262,144), while slices of 64-960 positions lost 3-13% with four.
+  static constexpr int RLong = (D == 256 && !PAGED && G == 4) ? 4 : R;
   // Two waves per SIMD where the query, accumulator and two in-flight tiles
   // fit 256 registers without spilling (checked against the compiler's
   // resource report), else one.
   static constexpr int WPE = kSliced ? 2 : ((sizeof(KV) == 2 && D == 128 && G <= 4) ? 2 : 1);
 };
 
-template <typename KV, int G, int D, bool PAGED>
-static sk_status_t launch_variant(const SplitLaunch& s, bool launch, const void** fn, int grid[3],
-                                  int* block) {
+constexpr int kLongRowsFrom = 2048;
+
+template <typename KV, int G, int D, bool PAGED, int R>
+static sk_status_t launch_rows(const SplitLaunch& s, bool launch, const void** fn, int grid[3],
+                               int* block) {
   const sk_desc_t& d = *s.d;
   using T = Tune<KV, G, D, PAGED>;
-  auto kern = s.fused ? gqa_split_kernel<KV, G, D, PAGED, T::RL, T::R, T::HS, T::WPE, true>
-                      : gqa_split_kernel<KV, G, D, PAGED, T::RL, T::R, T::HS, T::WPE, false>;
+  auto kern = s.fused ? gqa_split_kernel<KV, G, D, PAGED, T::RL, R, T::HS, T::WPE, true>
+                      : gqa_split_kernel<KV, G, D, PAGED, T::RL, R, T::HS, T::WPE, false>;
   const dim3 gr(d.num_kv_heads, s.p->n_splits, d.batch);
   grid[0] = gr.x;
   grid[1] = gr.y;
@@ -697,9 +705,9 @@ static sk_status_t launch_variant(const SplitLaunch& s, bool launch, const void*
   }
   a.max_pages = d.max_pages_per_seq;
   {
-    using Sh = GqaShape<KV, D, T::RL, T::R, T::HS>;
+    using Sh = GqaShape<KV, D, T::RL, R, T::HS>;
     constexpr int NG = Sh::kGroups;
-    constexpr int TR = NG * T::R;
+    constexpr int TR = NG * R;
     const int P = d.page_size;
     a.paged_fast = d.layout == SK_KV_PAGED && P % NG == 0 && TR % P == 0 && s.p->chunk % P == 0;
   }
@@ -709,6 +717,16 @@ static sk_status_t launch_variant(const SplitLaunch& s, bool launch, const void*
   a.lse = s.lse;
   hipLaunchKernelGGL(kern, gr, dim3(256), 0, s.stream, a);
   return SK_OK;
+}
+
+template <typename KV, int G, int D, bool PAGED>
+static sk_status_t launch_variant(const SplitLaunch& s, bool launch, const void** fn, int grid[3],
+                                  int* block) {
+  using T = Tune<KV, G, D, PAGED>;
+  if constexpr (T::RLong != T::R) {
+    if (s.p->chunk >= kLongRowsFrom) return launch_rows<KV, G, D, PAGED, T::RLong>(s, launch, fn, grid, block);
+  }
+  return launch_rows<KV, G, D, PAGED, T::R>(s, launch, fn, grid, block);
 }
 
 template <typename KV, int G, int D>

@@ -13,7 +13,7 @@ import itertools
 import pytest
 
 import synthetic
-from harness import assert_parity, oracle_out, run_gpu
+from harness import assert_parity, oracle_out, run_gpu, run_gpu_fused
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +46,23 @@ def test_every_gqa_variant_matches_oracle(G, D, kv, layout):
     for S in (0, 7):
         out, _, call = run_gpu(case, n_splits=S)
         assert_parity(case, out, ref, label=f"G={G} D={D} {kv} {layout} q={q_dtype} plan={call.plan}")
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16", "bf16"])
+def test_long_slice_variant_of_the_four_head_layer(kv):
+    """Slices of 2,048 positions or more take the 4-head width-256 kernel with
+    four rows per tile (64-row tiles): explicit plans put the tile boundary,
+    the slice boundary and the sequence end at awkward places."""
+    case = synthetic.gqa_case(f"long-slices-{kv}", seq_lens=[9000, 4097, 2049], num_q_heads=16,
+                              num_kv_heads=4, head_dim=256, kv_dtype=kv, capacity=9010,
+                              seed=6600 + len(kv))
+    ref, _ = oracle_out(case)
+    for S in (1, 2, 4):  # chunk 9000, 4500, 2250: every one at least 2,048
+        out, _, call = run_gpu(case, n_splits=S)
+        assert call.plan.chunk >= 2048
+        assert_parity(case, out, ref, label=f"long slices {kv} plan={call.plan}")
+        out1, _, _ = run_gpu_fused(case, call=call)
+        assert_parity(case, out1, ref, label=f"long slices, one launch {kv} plan={call.plan}")
 
 
 @pytest.mark.parametrize("kv", ["f32", "f16"])
