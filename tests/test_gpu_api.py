@@ -3,7 +3,6 @@ it plans, sizes the workspace and runs ``attn_decode`` exactly as the
 ``DecodeCall`` wrapper does, so its output is the same bits, for GQA and for
 the shared latent; a short workspace is refused before any launch."""
 
-import numpy as np
 import pytest
 
 import synthetic

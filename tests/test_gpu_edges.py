@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import synthetic
-from harness import ABS_GATE, assert_parity, decode_call, oracle_out, run_gpu, run_gpu_fused
+from harness import assert_parity, oracle_out, run_gpu, run_gpu_fused
 from synthetic.torch_io import to_device
 
 pytestmark = pytest.mark.gpu
