@@ -112,9 +112,9 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int NB = 4;         // LDS tile buffers: three tiles in flight while one is consumed
   constexpr int WLH = T * CPR / 64;  // wave-loads of 64 chunks per tile half (K or V)
-  constexpr int DPW = 2 * WLH / 4;   // wave-loads per wave per tile (waves 0-1: K, 2-3: V)
+  constexpr int DPW = 2 * WLH / 4;   // wave-loads per wave per tile (half K, then half V)
   static_assert(D % 64 == 0 && KS % DS == 0 && (DS == 1 || DS == 2 || DS == 4), "head width / split");
-  static_assert(WLH % DPW == 0 && CPR >= 8, "a wave's loads stay within K or V; 8-chunk swizzle");
+  static_assert(DPW % 2 == 0 && CPR >= 8, "even split of a wave's loads; 8-chunk swizzle");
 
   // [buffer][K, V][row * D + column], rows unpadded, the 16-byte chunk index of
   // row r stored XOR-ed with r & 7 (conflict-free score and transpose reads).
@@ -221,8 +221,8 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
 
     const KT* __restrict__ kp = reinterpret_cast<const KT*>(a.k) + (int64_t)b * a.stride_seq + (int64_t)g * a.stride_head;
     const KT* __restrict__ vp = reinterpret_cast<const KT*>(a.v) + (int64_t)b * a.stride_seq + (int64_t)g * a.stride_head;
-    // Tile staging by direct global-to-LDS loads: wave-load wl of a tile
-    // (0 .. 2*WLH-1; K first, then V) fills 1 KB of the half's LDS rows; lane
+    // Tile staging by direct global-to-LDS loads: wave-load wh of a tile half
+    // (0 .. WLH-1, for K and again for V) fills 1 KB of the half's LDS rows; lane
     // slot s of it is row s / CPR, physical chunk p = s % CPR, which holds
     // logical chunk p ^ (row & 7). Rows past `stop` re-read row stop-1 (in
     // range; their scores are masked). With DS > 1 the KV group's query rows
@@ -230,26 +230,30 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
     // which stream HBM faster on MI355X. Otherwise several query tiles read
     // the same rows and the plain policy lets the later reads hit the caches.
     const uint32_t lds_kv = (uint32_t)(size_t)(const __attribute__((address_space(3))) short*)(&s_kv[0][0][0]);
-    const int wl0 = __builtin_amdgcn_readfirstlane(wave * DPW);
-    const int half = wl0 / WLH;  // 0: K, 1: V (wave-uniform)
-    const KT* __restrict__ src0 = half ? vp : kp;
+    // Every wave issues DPW/2 wave-loads of K, then the same of V: the whole
+    // K half is requested before any V row, the order the scores need it in.
+    const int wq0 = __builtin_amdgcn_readfirstlane(wave * (DPW / 2));
     auto issue = [&](int buf, int64_t tb) {
 #pragma unroll
-      for (int c = 0; c < DPW; ++c) {
-        const int wh = wl0 - half * WLH + c;  // wave-load within the half
-        const int sl = wh * 64 + lane;
-        const int row = sl / CPR, p = sl - (sl / CPR) * CPR;
-        const int64_t pos = min(tb + row, stop - 1);
-        const KT* src = src0 + pos * a.stride_pos + ((p ^ (row & 7)) * 8);
-        const uint32_t dst = lds_kv + (uint32_t)(((buf * 2 + half) * T * D + wh * 512) * 2);
-        dma16(src, __builtin_amdgcn_readfirstlane(dst), DS > 1);
+      for (int half = 0; half < 2; ++half) {
+        const KT* __restrict__ src0 = half ? vp : kp;
+#pragma unroll
+        for (int c = 0; c < DPW / 2; ++c) {
+          const int wh = wq0 + c;  // wave-load within the half
+          const int sl = wh * 64 + lane;
+          const int row = sl / CPR, p = sl - (sl / CPR) * CPR;
+          const int64_t pos = min(tb + row, stop - 1);
+          const KT* src = src0 + pos * a.stride_pos + ((p ^ (row & 7)) * 8);
+          const uint32_t dst = lds_kv + (uint32_t)(((buf * 2 + half) * T * D + wh * 512) * 2);
+          dma16(src, __builtin_amdgcn_readfirstlane(dst), DS > 1);
+        }
       }
     };
 
     // Uniform over the workgroup; said so, the loop exits on a scalar branch
     // instead of an exec-masked one (whose merged paths cost the loads' overlap).
     const int ntiles = __builtin_amdgcn_readfirstlane((int)((stop - start + T - 1) / T));
-    // Consumes tile i from LDS buffer i & 1: scores, online softmax, output.
+    // Consumes tile i from LDS buffer i % NB: scores, online softmax, output.
     auto consume = [&](int i) {
       const int64_t tb = start + (int64_t)i * T;
       const short* kb = s_kv[i % NB][0];
