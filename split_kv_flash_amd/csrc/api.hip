@@ -162,6 +162,33 @@ WsLayout ws_layout(const sk_desc_t& d, const sk_plan_t& p) {
 
 }  // namespace sk
 
+namespace {
+
+// Rounds a slice length to the planner's granule and derives the split count.
+sk_status_t finish_plan(int64_t chunk, int32_t max_seq_len, sk_plan_t* plan) {
+  if (chunk < kMinChunk) chunk = kMinChunk;
+  chunk = ceil_div(chunk, kChunkGranule) * kChunkGranule;
+  int64_t n = ceil_div(max_seq_len, chunk);
+  if (n > kMaxGridYZ) {  // unreachable for 32-bit lengths and chunk >= 64; kept as a guard
+    n = kMaxGridYZ;
+    chunk = ceil_div(max_seq_len, n);
+  }
+  plan->n_splits = (int32_t)n;
+  plan->chunk = (int32_t)chunk;
+  return ok();
+}
+
+// One round of resident query-tile workgroups over (KV head, query tile,
+// slice): [I3725] section 2's one-round rule, counted over query tiles and
+// the workgroups a compute unit holds.
+int64_t query_tile_chunk(const sk_desc_t& d, int32_t q_len, int64_t total_tokens,
+                         int32_t cu_count) {
+  const int64_t tiles = (int64_t)d.num_kv_heads * sk::query_tile_rows_tiles(d, q_len);
+  return ceil_div(tiles * total_tokens, (int64_t)sk::query_tile_resident(d) * cu_count);
+}
+
+}  // namespace
+
 extern "C" {
 
 sk_status_t attn_decode_plan(const sk_desc_t* desc, int32_t max_seq_len, int64_t total_tokens,
@@ -194,6 +221,8 @@ sk_status_t attn_decode_plan(const sk_desc_t* desc, int32_t max_seq_len, int64_t
   int64_t chunk;
   if (desc->kv_shared) {
     chunk = ceil_div(total_tokens * sk::latent_blocks_per_split(*desc), (int64_t)cu_count);
+  } else if (sk::decode_on_query_tiles(*desc)) {
+    chunk = query_tile_chunk(*desc, 1, total_tokens, cu_count);
   } else {
     const bool ragged = total_tokens < (int64_t)max_seq_len * desc->batch;
     const int64_t per_cu = (int64_t)sk::gqa_resident_blocks(*desc) * (ragged ? kRaggedBlockFactor : 1);
@@ -202,16 +231,7 @@ sk_status_t attn_decode_plan(const sk_desc_t* desc, int32_t max_seq_len, int64_t
     if (!ragged && chunk >= kLongSlice && sk::gqa_prefers_fewer_streams(*desc))
       chunk = ceil_div(4 * work, 3 * per_cu * cu_count);
   }
-  if (chunk < kMinChunk) chunk = kMinChunk;
-  chunk = ceil_div(chunk, kChunkGranule) * kChunkGranule;
-  int64_t n = ceil_div(max_seq_len, chunk);
-  if (n > kMaxGridYZ) {  // unreachable for 32-bit lengths and chunk >= 64; kept as a guard
-    n = kMaxGridYZ;
-    chunk = ceil_div(max_seq_len, n);
-  }
-  plan->n_splits = (int32_t)n;
-  plan->chunk = (int32_t)chunk;
-  return ok();
+  return finish_plan(chunk, max_seq_len, plan);
 }
 
 size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan) {
@@ -264,6 +284,30 @@ static sk_status_t prepare_split(const sk_desc_t* desc, const sk_plan_t* plan, c
   return SK_OK;
 }
 
+// The split step of two-launch decode: the shared-latent kernel, the GQA split
+// kernel, or the query-tile kernel with one query (whose partials and grid
+// have the same layout) for the descriptors it serves faster.
+static sk_status_t split_dispatch(const sk::SplitLaunch& a, bool launch, const void** fn,
+                                  int grid[3], int* block) {
+  if (a.d->kv_shared) return sk::latent_split_launch(a, launch, fn, grid, block);
+  if (sk::decode_on_query_tiles(*a.d)) {
+    sk::QueryTileLaunch t;
+    t.d = a.d;
+    t.p = a.p;
+    t.q_len = 1;
+    t.q = a.q;
+    t.k = a.k;
+    t.v = a.v;
+    t.seq_lens = a.seq_lens;
+    t.ws_acc = a.ws_acc;
+    t.ws_m = a.ws_m;
+    t.ws_l = a.ws_l;
+    t.stream = a.stream;
+    return sk::query_tile_launch(t, launch, fn, grid, block);
+  }
+  return sk::gqa_split_launch(a, launch, fn, grid, block);
+}
+
 sk_status_t attn_decode_splitk(const sk_desc_t* desc, const sk_plan_t* plan, const void* q,
                                const void* k, const void* v, const int32_t* block_table,
                                const int32_t* seq_lens, void* workspace, size_t workspace_bytes,
@@ -274,8 +318,7 @@ sk_status_t attn_decode_splitk(const sk_desc_t* desc, const sk_plan_t* plan, con
   if (s != SK_OK) return s;
   a.stream = stream;
   int grid[3], block;
-  s = desc->kv_shared ? sk::latent_split_launch(a, true, nullptr, grid, &block)
-                      : sk::gqa_split_launch(a, true, nullptr, grid, &block);
+  s = split_dispatch(a, true, nullptr, grid, &block);
   if (s != SK_OK) return fail(s, "no split kernel for this descriptor");
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
@@ -401,20 +444,7 @@ sk_status_t attn_query_tiles_plan(const sk_desc_t* desc, int32_t q_len, int32_t 
     plan->chunk = (int32_t)ceil_div(max_seq_len, n_splits_requested);
     return ok();
   }
-  // One round of one workgroup per compute unit over (KV head, query tile,
-  // slice), as for single queries ([I3725] section 2's rule on the product).
-  const int64_t tiles = (int64_t)desc->num_kv_heads * sk::query_tile_rows_tiles(*desc, q_len);
-  int64_t chunk = ceil_div(tiles * total_tokens, (int64_t)cu_count);
-  if (chunk < kMinChunk) chunk = kMinChunk;
-  chunk = ceil_div(chunk, kChunkGranule) * kChunkGranule;
-  int64_t n = ceil_div(max_seq_len, chunk);
-  if (n > kMaxGridYZ) {
-    n = kMaxGridYZ;
-    chunk = ceil_div(max_seq_len, n);
-  }
-  plan->n_splits = (int32_t)n;
-  plan->chunk = (int32_t)chunk;
-  return ok();
+  return finish_plan(query_tile_chunk(*desc, q_len, total_tokens, cu_count), max_seq_len, plan);
 }
 
 size_t attn_query_tiles_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan,
@@ -579,8 +609,7 @@ sk_status_t attn_decode_kernel_info(const sk_desc_t* desc, const sk_plan_t* plan
   if (s != SK_OK) return s;
   const void* fn = nullptr;
   int grid[3], block;
-  s = desc->kv_shared ? sk::latent_split_launch(a, false, &fn, grid, &block)
-                      : sk::gqa_split_launch(a, false, &fn, grid, &block);
+  s = split_dispatch(a, false, &fn, grid, &block);
   if (s != SK_OK) return fail(s, "no split kernel for this descriptor");
   hipFuncAttributes attr;
   hipError_t e = hipFuncGetAttributes(&attr, fn);

@@ -405,31 +405,70 @@ static int query_tile_ways(int rows, int D) {
   return 1;
 }
 
+// Workgroups one compute unit holds: the LDS tile ring with the score
+// exchange is 136, 72 and 40 KB at head width 256, 128 and 64, of 160 KB per
+// compute unit (registers allow more). A plan for fewer leaves the narrow
+// widths with too few tiles in flight: with one per compute unit, decode at
+// width 128 took 126 us where two per unit take 93 us (8 KV heads, 131,072
+// f16 positions), and width 64 took 113 us where four take 60 us.
+int query_tile_resident(const sk_desc_t& d) {
+  return d.head_dim_qk >= 256 ? 1 : (d.head_dim_qk >= 128 ? 2 : 4);
+}
+
+// Single-query decode on the query-tile kernel (q_len = 1: the rows are the
+// group's heads, and its partials have the split kernel's layout) where that
+// measured faster on MI355X: the MFMA score and output products keep wide
+// groups and narrow heads at the memory rate, while the vector split kernel
+// runs out of ALU issue with more heads per KV row (at 131,072 f16 positions,
+// 8 heads of width 256 per KV head: 355 vs 160 us; width 128, 4 heads: 100 vs
+// 93 us; width 64, one head: 75 vs 60 us). The 16-bit parts of q and the
+// weights meet the f32-arithmetic bound for f16 storage only, so bf16 stays
+// on the split kernel.
+bool decode_on_query_tiles(const sk_desc_t& d) {
+  if (!query_tile_supported(d) || d.kv_dtype != SK_F16 || d.num_kv_heads < 1) return false;
+  const int G = d.num_q_heads / d.num_kv_heads;
+  switch (d.head_dim_qk) {
+    case 64: return true;
+    case 128: return G >= 4;
+    default: return G >= 6;
+  }
+}
+
+template <typename KT, int D, int DS>
+static void qt_go(bool launch, const void** fn, dim3 grid, hipStream_t stream, const QtArgs& a) {
+  auto kern = query_tile_kernel<KT, D, DS>;
+  if (fn) *fn = reinterpret_cast<const void*>(kern);
+  if (launch) hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, a);
+}
+
 template <typename KT, int D>
-static void qt_launch(int ways, dim3 grid, hipStream_t stream, const QtArgs& a) {
+static void qt_launch(int ways, bool launch, const void** fn, dim3 grid, hipStream_t stream,
+                      const QtArgs& a) {
   if (ways == 4) {
-    if constexpr (D >= 128) hipLaunchKernelGGL((query_tile_kernel<KT, D, 4>), grid, dim3(256), 0, stream, a);
+    if constexpr (D >= 128) qt_go<KT, D, 4>(launch, fn, grid, stream, a);
   } else if (ways == 2) {
-    hipLaunchKernelGGL((query_tile_kernel<KT, D, 2>), grid, dim3(256), 0, stream, a);
+    qt_go<KT, D, 2>(launch, fn, grid, stream, a);
   } else {
-    hipLaunchKernelGGL((query_tile_kernel<KT, D, 1>), grid, dim3(256), 0, stream, a);
+    qt_go<KT, D, 1>(launch, fn, grid, stream, a);
   }
 }
 
 template <typename KT>
-static sk_status_t qt_by_dim(const QueryTileLaunch& s, const QtArgs& a, dim3 grid) {
+static sk_status_t qt_by_dim(const QueryTileLaunch& s, const QtArgs& a, dim3 grid, bool launch,
+                             const void** fn) {
   const int D = s.d->head_dim_qk;
   const int ways = query_tile_ways(a.Q * a.G, D);
   switch (D) {
-    case 64: qt_launch<KT, 64>(ways, grid, s.stream, a); break;
-    case 128: qt_launch<KT, 128>(ways, grid, s.stream, a); break;
-    case 256: qt_launch<KT, 256>(ways, grid, s.stream, a); break;
+    case 64: qt_launch<KT, 64>(ways, launch, fn, grid, s.stream, a); break;
+    case 128: qt_launch<KT, 128>(ways, launch, fn, grid, s.stream, a); break;
+    case 256: qt_launch<KT, 256>(ways, launch, fn, grid, s.stream, a); break;
     default: return SK_ERR_UNSUPPORTED;
   }
   return SK_OK;
 }
 
-sk_status_t query_tile_launch(const QueryTileLaunch& s) {
+sk_status_t query_tile_launch(const QueryTileLaunch& s, bool launch, const void** fn, int grid3[3],
+                              int* block) {
   const sk_desc_t& d = *s.d;
   if (!query_tile_supported(d)) return SK_ERR_UNSUPPORTED;
   QtArgs a;
@@ -453,8 +492,14 @@ sk_status_t query_tile_launch(const QueryTileLaunch& s) {
   a.nqt = query_tile_rows_tiles(d, s.q_len);
   a.qscale = d.scale * kLog2e;
   const dim3 grid(d.num_kv_heads * a.nqt, s.p->n_splits, d.batch);
-  if (d.kv_dtype == SK_F16) return qt_by_dim<_Float16>(s, a, grid);
-  return qt_by_dim<bf16_t>(s, a, grid);
+  if (grid3) {
+    grid3[0] = grid.x;
+    grid3[1] = grid.y;
+    grid3[2] = grid.z;
+  }
+  if (block) *block = 256;
+  if (d.kv_dtype == SK_F16) return qt_by_dim<_Float16>(s, a, grid, launch, fn);
+  return qt_by_dim<bf16_t>(s, a, grid, launch, fn);
 }
 
 }  // namespace sk

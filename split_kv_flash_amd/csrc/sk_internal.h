@@ -101,7 +101,15 @@ bool project_supported(const sk_desc_t& d, int w_dtype);
 bool query_tile_supported(const sk_desc_t& d);
 // 64-row query tiles per KV head for q_len queries.
 int query_tile_rows_tiles(const sk_desc_t& d, int q_len);
-sk_status_t query_tile_launch(const QueryTileLaunch& a);
+// Query-tile workgroups resident per compute unit (LDS-bound).
+int query_tile_resident(const sk_desc_t& d);
+// Whether single-query decode of this descriptor runs on the query-tile
+// kernel (q_len = 1) instead of the GQA split kernel.
+bool decode_on_query_tiles(const sk_desc_t& d);
+// Launches (when `launch`) the query-tile kernel; reports its function, grid
+// and block like the split launchers.
+sk_status_t query_tile_launch(const QueryTileLaunch& a, bool launch = true, const void** fn = nullptr,
+                              int grid[3] = nullptr, int* block = nullptr);
 sk_status_t combine_project_launch(const ProjectLaunch& a);
 // Zeroes n 32-bit words with a fill kernel (no memset node, so a captured
 // graph may hold it).

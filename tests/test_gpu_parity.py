@@ -281,11 +281,12 @@ def test_lds_does_not_depend_on_context_length():
         assert len(seen) == 1, seen
 
 
-def test_invalid_lengths_give_nan_for_that_sequence_only():
+@pytest.mark.parametrize("kv", ["f32", "f16"])  # f16 at width 64 runs on the query-tile kernel
+def test_invalid_lengths_give_nan_for_that_sequence_only(kv):
     import torch
 
     case = synthetic.gqa_case("bad", seq_lens=[50, 40, 30], num_q_heads=8, num_kv_heads=2,
-                              head_dim=64, capacity=64, seed=3)
+                              head_dim=64, capacity=64, seed=3, kv_dtype=kv)
     t = to_device(case)
     call = decode_call(case, t, n_splits=2)
     t["seq_lens"].copy_(torch.tensor([50, 0, 100], dtype=torch.int32))  # 0 and > capacity

@@ -188,3 +188,32 @@ def test_ragged_batch_and_invalid_length():
     o2 = call.out.double().cpu().numpy()
     assert np.all(np.isnan(o2[1]))
     assert np.array_equal(o2[0], out[0])
+
+
+@pytest.mark.parametrize("hq,hkv,D", [(24, 4, 256), (32, 4, 256), (32, 8, 128), (8, 8, 64), (48, 8, 64)])
+def test_decode_on_query_tiles_is_the_one_query_call(hq, hkv, D):
+    # f16 groups that single-query decode runs on the query-tile kernel:
+    # attn_decode's output and lse equal those of attn_query_tiles with one
+    # query bit for bit (same plan, kernel and combine), the kernel report
+    # names that kernel (its LDS holds the 4-buffer K/V ring), and the result
+    # meets the oracle with the f32-arithmetic bound. Lengths: ragged, one
+    # position, and a tail that is not a multiple of the 32-position tile.
+    import split_kv_flash_amd.binding as B
+    from harness import assert_parity, oracle_out, run_gpu
+
+    case = synthetic.gqa_case(f"routed-{hq}x{hkv}-d{D}", seq_lens=[5000, 1, 70, 4097],
+                              num_q_heads=hq, num_kv_heads=hkv, head_dim=D, kv_dtype="f16",
+                              seed=9100 + D + hq)
+    t = to_device(case)
+    out, lse, call = run_gpu(case, tensors=t)
+    info = B.attn_decode_kernel_info(call.desc, call.plan)
+    assert info.lds_bytes >= 4 * 2 * 32 * D * 2, info.lds_bytes
+    assert (info.grid_x, info.grid_y, info.grid_z) == (hkv, call.plan.n_splits, 4)
+    q1 = t["q"].unsqueeze(1).contiguous()
+    qo, ql, qcall = run_qt(case, tensors={**t, "q": q1})
+    assert (qcall.plan.n_splits, qcall.plan.chunk) == (call.plan.n_splits, call.plan.chunk)
+    assert np.array_equal(qo[:, 0], out, equal_nan=True)
+    assert np.array_equal(ql[:, 0], lse, equal_nan=True)
+    ref, rlse = oracle_out(case)
+    assert_parity(case, out, ref, label=case.name)
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-4)
