@@ -158,6 +158,10 @@ typedef struct {
  *           for the f16 6-head group of width 256, whose VALU-heavy loop needs
  *           every compute unit. The note's own S_target is about 4 per
  *           multiprocessor of its GPU.
+ *   GQA on the query-tile kernel (f16 KV: head width 64; width 128 with at least 4
+ *           query heads per KV head; width 256 with at least 6; see
+ *           attn_decode_splitk): the attn_query_tiles_plan rule with one query,
+ *           k = 1, 2 or 4 workgroups per compute unit at width 256, 128 or 64.
  *   latent: chunk = max(64, ceil(g * total_tokens / cu_count)) with g workgroups per
  *           split, each serving a slice of the query heads: for f16 caches 1 up to
  *           96 heads and 2 (of 64 heads) at 128; for f32 caches Hq/48 (Hq/32 when
@@ -200,7 +204,13 @@ size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan)
  * (kv_shared) with num_kv_heads == 1, head_dim_qk == 576, head_dim_v == 512, num_q_heads
  * in {32, 64, 96, 128}, q f32, KV f32 or f16, contiguous or indexed. Latent f16 caches run on f16
  * MFMA: q and the softmax weights are rounded to f16 there (f32 accumulation). Anything else returns
- * SK_ERR_UNSUPPORTED without launching. */
+ * SK_ERR_UNSUPPORTED without launching.
+ * Kernel: contiguous f16 caches of head width 64, of width 128 with at least 4 query
+ * heads per KV head, and of width 256 with at least 6, run on the query-tile kernel of
+ * attn_query_tiles with one query (its partials have this layout): MFMA scores and
+ * outputs with q and the weights split into two f16 parts, which keeps f32-level
+ * accuracy and holds wide groups at the memory rate where the vector split kernel
+ * runs out of ALU issue. Every other GQA descriptor runs the vector split kernel. */
 sk_status_t attn_decode_splitk(const sk_desc_t* desc, const sk_plan_t* plan,
                                const void* q, const void* k, const void* v,
                                const int32_t* block_table, const int32_t* seq_lens,
@@ -248,7 +258,8 @@ sk_status_t attn_decode(const sk_desc_t* desc, const sk_plan_t* plan, const void
  * length outside [1, min(max_seq_len, n_splits*chunk)] makes that sequence's out and lse
  * NaN. The counter section must be zero when the call starts (attn_decode_workspace_init);
  * a call that completes leaves it zero. Calls that share a workspace must not overlap in
- * time (for example on two streams).
+ * time (for example on two streams). It always runs the vector split kernel, also for
+ * the descriptors attn_decode_splitk serves with the query-tile kernel.
  * Errors: as attn_decode; SK_ERR_UNSUPPORTED for a shared latent. */
 sk_status_t attn_decode_one_launch(const sk_desc_t* desc, const sk_plan_t* plan, const void* q,
                                    const void* k, const void* v, const int32_t* block_table,
@@ -304,7 +315,10 @@ sk_status_t attn_query_tiles(const sk_desc_t* desc, const sk_plan_t* plan, int32
                              float* out, float* lse, hipStream_t stream);
 
 /* Split plan for attn_query_tiles (host only): as attn_decode_plan with the workgroup
- * budget counted over (KV head, 64-row query tile, slice); an explicit n_splits is
+ * budget counted over (KV head, 64-row query tile, slice): chunk = max(64,
+ * ceil(Hkv * tiles * total_tokens / (k * cu_count))), rounded up to a multiple of 64,
+ * with k = 1, 2 or 4 workgroups per compute unit at head width 256, 128 or 64 (the
+ * LDS tile ring bounds how many a compute unit holds); an explicit n_splits is
  * honoured with chunk = ceil(max_seq_len / n_splits). */
 sk_status_t attn_query_tiles_plan(const sk_desc_t* desc, int32_t q_len, int32_t max_seq_len,
                                   int64_t total_tokens, int32_t cu_count,
@@ -331,7 +345,8 @@ const char* attn_decode_status_string(sk_status_t status);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* attn_decode_last_error(void);
 
-/* Properties of the split kernel a (desc, plan) pair selects (needs a GPU: it asks
+/* Properties of the split kernel a (desc, plan) pair selects for attn_decode_splitk
+ * (the query-tile kernel where that entry point names it; needs a GPU: it asks
  * the HIP runtime for the kernel's attributes).
  *   lds_bytes    static LDS per workgroup (independent of the context length: Lecture 06
  *                section 2 requires shared memory of O(key width + tile), never O(n_ctx))
