@@ -158,7 +158,7 @@ typedef struct {
  *           for the f16 6-head group of width 256, whose VALU-heavy loop needs
  *           every compute unit. The note's own S_target is about 4 per
  *           multiprocessor of its GPU.
- *   GQA on the query-tile kernel (f16 KV: head width 64; width 128 with at least 4
+ *   GQA on the query-tile kernel (f16/bf16 KV: head width 64; width 128 with at least 4
  *           query heads per KV head; width 256 with at least 6; see
  *           attn_decode_splitk): the attn_query_tiles_plan rule with one query,
  *           k = 1, 2 or 4 workgroups per compute unit at width 256, 128 or 64.
@@ -205,12 +205,13 @@ size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan)
  * in {32, 64, 96, 128}, q f32, KV f32 or f16, contiguous or indexed. Latent f16 caches run on f16
  * MFMA: q and the softmax weights are rounded to f16 there (f32 accumulation). Anything else returns
  * SK_ERR_UNSUPPORTED without launching.
- * Kernel: contiguous f16 caches of head width 64, of width 128 with at least 4 query
- * heads per KV head, and of width 256 with at least 6, run on the query-tile kernel of
- * attn_query_tiles with one query (its partials have this layout): MFMA scores and
- * outputs with q and the weights split into two f16 parts, which keeps f32-level
- * accuracy and holds wide groups at the memory rate where the vector split kernel
- * runs out of ALU issue. Every other GQA descriptor runs the vector split kernel. */
+ * Kernel: contiguous f16/bf16 caches of head width 64, of width 128 with at least 4
+ * query heads per KV head, and of width 256 with at least 6, run on the query-tile
+ * kernel of attn_query_tiles with one query (its partials have this layout): MFMA
+ * scores and outputs with q and the weights split into two f16 or three bf16 parts,
+ * which keeps f32-level accuracy and holds wide groups at the memory rate where the
+ * vector split kernel runs out of ALU issue. Every other GQA descriptor runs the
+ * vector split kernel. */
 sk_status_t attn_decode_splitk(const sk_desc_t* desc, const sk_plan_t* plan,
                                const void* q, const void* k, const void* v,
                                const int32_t* block_table, const int32_t* seq_lens,

@@ -70,6 +70,7 @@ template <typename KT>
 struct QtType;
 template <>
 struct QtType<_Float16> {
+  static constexpr int kParts = 2;  // 11 + 11 significand bits
   static __device__ __forceinline__ short from(float x) { return __builtin_bit_cast(short, (_Float16)x); }
   static __device__ __forceinline__ float to(short b) { return (float)__builtin_bit_cast(_Float16, b); }
   static __device__ __forceinline__ qt_f4 mma(qt_s8 a, qt_s8 b, qt_f4 c) {
@@ -79,6 +80,7 @@ struct QtType<_Float16> {
 };
 template <>
 struct QtType<bf16_t> {
+  static constexpr int kParts = 3;  // 8 + 8 + 8 significand bits
   static __device__ __forceinline__ short from(float x) { return __builtin_bit_cast(short, (__bf16)x); }
   static __device__ __forceinline__ float to(short b) {
     return __uint_as_float(((uint32_t)(uint16_t)b) << 16);
@@ -102,6 +104,7 @@ __device__ __forceinline__ qt_s4 qt_read_tr(const short* p) {
 template <typename KT, int D, int DS>
 __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
   using TT = QtType<KT>;
+  constexpr int NP = TT::kParts;  // parts of q and of the softmax weights
   constexpr int T = 32;         // positions per K/V tile
   constexpr int KS = D / 32;    // score MFMA steps over the head width
   constexpr int CB = D / 16;    // output column blocks over the head width
@@ -158,8 +161,9 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
   if (start < stop) {
     // Query row as B operands: lane (l16, lq) holds columns 32ks + 8lq .. +7 of
     // row l16 (ks over this wave's column part), pre-scaled into base-2 units
-    // and split into high and low parts.
-    qt_s8 qh[KSW], ql[KSW];
+    // and split into NP parts, each the rounding of what the previous ones
+    // left (their sum carries 22 bits for f16 and 24 for bf16).
+    qt_s8 qp[NP][KSW];
     {
       const int64_t qbase = (((int64_t)b * a.Q + t) * a.Hq + g * a.G + hh) * D + 32 * KSW * dq;
       // Eight consecutive elements per step, widened to f32: every load is
@@ -212,10 +216,13 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
       for (int ks = 0; ks < KSW; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float x = qv[ks][e] * a.qscale;
-          const short hi = TT::from(x);
-          qh[ks][e] = hi;
-          ql[ks][e] = TT::from(x - TT::to(hi));
+          float x = qv[ks][e] * a.qscale;
+#pragma unroll
+          for (int i = 0; i < NP; ++i) {
+            const short part = TT::from(x);
+            qp[i][ks][e] = part;
+            x -= TT::to(part);
+          }
         }
     }
 
@@ -268,8 +275,8 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
           // row 16 pb + l16 (swizzle l16 & 7), logical chunk 4 (KSW dq + ks) + lq
           const qt_s8 av = *reinterpret_cast<const qt_s8*>(
               kb + (16 * pb + l16) * D + (((4 * (KSW * dq + ks) + lq) ^ (l16 & 7)) << 3));
-          sp[pb] = TT::mma(av, qh[ks], sp[pb]);
-          sp[pb] = TT::mma(av, ql[ks], sp[pb]);
+#pragma unroll
+          for (int i = 0; i < NP; ++i) sp[pb] = TT::mma(av, qp[i][ks], sp[pb]);
         }
       if constexpr (DS > 1) {
         // Partial scores of the block's DS waves: same lane layout, summed in
@@ -308,14 +315,17 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
       const float mu = (mn == -INFINITY) ? 0.0f : mn;
       const float al = fast_exp2(m - mu);
       float ls = 0.0f;
-      qt_s8 ph, pl;
+      qt_s8 pp[NP];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float p = fast_exp2(s[j] - mu);
+        float p = fast_exp2(s[j] - mu);
         ls += p;
-        const short hi = TT::from(p);
-        ph[j] = hi;
-        pl[j] = TT::from(p - TT::to(hi));
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          const short part = TT::from(p);
+          pp[i][j] = part;
+          p -= TT::to(part);
+        }
       }
       ls += xor16(ls);
       ls += xor32(ls);
@@ -343,8 +353,8 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
         const qt_s4 v0 = qt_read_tr(vrow + vch);
         const qt_s4 v1 = qt_read_tr(vrow + 16 * D + vch);
         const qt_s8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[c] = TT::mma(ph, vv, acc[c]);
-        acc[c] = TT::mma(pl, vv, acc[c]);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) acc[c] = TT::mma(pp[i], vv, acc[c]);
       }
     };
     // Ring of NB = 4 buffers: tiles i+1 .. i+3 are in flight while tile i is
@@ -421,11 +431,10 @@ int query_tile_resident(const sk_desc_t& d) {
 // groups and narrow heads at the memory rate, while the vector split kernel
 // runs out of ALU issue with more heads per KV row (at 131,072 f16 positions,
 // 8 heads of width 256 per KV head: 355 vs 160 us; width 128, 4 heads: 100 vs
-// 93 us; width 64, one head: 75 vs 60 us). The 16-bit parts of q and the
-// weights meet the f32-arithmetic bound for f16 storage only, so bf16 stays
-// on the split kernel.
+// 93 us; width 64, one head: 75 vs 60 us). q and the weights in two f16 or
+// three bf16 parts keep f32-level accuracy.
 bool decode_on_query_tiles(const sk_desc_t& d) {
-  if (!query_tile_supported(d) || d.kv_dtype != SK_F16 || d.num_kv_heads < 1) return false;
+  if (!query_tile_supported(d) || d.num_kv_heads < 1) return false;
   const int G = d.num_q_heads / d.num_kv_heads;
   switch (d.head_dim_qk) {
     case 64: return true;

@@ -4,6 +4,7 @@ sizes the workspace as documented, and rejects bad arguments before any HIP
 call."""
 
 import ctypes
+import itertools
 from fractions import Fraction
 
 import numpy as np
@@ -131,22 +132,25 @@ def test_plan_for_the_wide_f16_group_keeps_every_compute_unit():
 
 def test_plan_for_decode_on_query_tiles_counts_resident_workgroups():
     lib()
-    # f16 groups decoded by the query-tile kernel (all of width 64, width 128
+    # 16-bit groups decoded by the query-tile kernel (all of width 64, width 128
     # from 4 heads per KV head, width 256 from 6): one round of the 1, 2 or 4
     # workgroups a compute unit holds at width 256, 128 or 64, over KV heads x
     # slices; attn_query_tiles_plan with one query gives the same plan.
     for hq, hkv, D, res in [(24, 4, 256, 1), (32, 4, 256, 1), (64, 8, 256, 1), (32, 8, 128, 2),
                             (48, 8, 128, 2), (8, 8, 64, 4), (64, 8, 64, 4)]:
-        for lens in ([1000], [32768], [131072], [16384] * 8, [300, 5000, 70000]):
+        for lens, kv in itertools.product(([1000], [32768], [131072], [16384] * 8, [300, 5000, 70000]),
+                                          ("f16", "bf16")):
             for cu in (80, 256):
-                d = gqa_desc(Hq=hq, Hkv=hkv, D=D, cap=max(lens), kv="f16", batch=len(lens))
+                d = gqa_desc(Hq=hq, Hkv=hkv, D=D, cap=max(lens), kv=kv, batch=len(lens))
                 p = B.attn_decode_plan(d, max(lens), sum(lens), cu, 0)
                 want = oracle.plan_splits(lens, hkv, cu, blocks_per_cu=res)
                 assert (p.n_splits, p.chunk) == want, (hq, hkv, D, lens, cu)
                 pq = B.attn_query_tiles_plan(d, 1, max(lens), sum(lens), cu, 0)
                 assert (pq.n_splits, pq.chunk) == want
-    # bf16 storage and the narrower f16 groups keep the split kernel's rule
-    p = B.attn_decode_plan(gqa_desc(Hq=24, Hkv=4, D=256, cap=262144, kv="bf16"), 262144, 262144, 256, 0)
+    # f32 storage and the narrower 16-bit groups keep the split kernel's rule
+    p = B.attn_decode_plan(gqa_desc(Hq=24, Hkv=4, D=256, cap=262144, kv="f32"), 262144, 262144, 256, 0)
+    assert (p.n_splits, p.chunk) == (48, 5504)
+    p = B.attn_decode_plan(gqa_desc(Hq=16, Hkv=4, D=256, cap=262144, kv="bf16"), 262144, 262144, 256, 0)
     assert (p.n_splits, p.chunk) == (48, 5504)
     p = B.attn_decode_plan(gqa_desc(Hq=16, Hkv=4, D=256, cap=262144, kv="f16"), 262144, 262144, 256, 0)
     assert (p.n_splits, p.chunk) == (48, 5504)
