@@ -161,7 +161,8 @@ typedef struct {
  *   GQA on the query-tile kernel (f16/bf16 KV: head width 64; width 128 with at least 4
  *           query heads per KV head; width 256 with at least 6; see
  *           attn_decode_splitk): the attn_query_tiles_plan rule with one query,
- *           k = 1, 2 or 4 workgroups per compute unit at width 256, 128 or 64.
+ *           k = 1, 2 or 4 workgroups per compute unit at width 256, 128 or 64, and
+ *           8 for a ragged batch.
  *   latent: chunk = max(64, ceil(g * total_tokens / cu_count)) with g workgroups per
  *           split, each serving a slice of the query heads: for f16 caches 1 up to
  *           96 heads and 2 (of 64 heads) at 128; for f32 caches Hq/48 (Hq/32 when
@@ -319,7 +320,8 @@ sk_status_t attn_query_tiles(const sk_desc_t* desc, const sk_plan_t* plan, int32
  * budget counted over (KV head, 64-row query tile, slice): chunk = max(64,
  * ceil(Hkv * tiles * total_tokens / (k * cu_count))), rounded up to a multiple of 64,
  * with k = 1, 2 or 4 workgroups per compute unit at head width 256, 128 or 64 (the
- * LDS tile ring bounds how many a compute unit holds); an explicit n_splits is
+ * LDS tile ring bounds how many a compute unit holds), and k = 8 for a ragged batch
+ * (total_tokens < batch * max_seq_len), as attn_decode_plan; an explicit n_splits is
  * honoured with chunk = ceil(max_seq_len / n_splits). */
 sk_status_t attn_query_tiles_plan(const sk_desc_t* desc, int32_t q_len, int32_t max_seq_len,
                                   int64_t total_tokens, int32_t cu_count,

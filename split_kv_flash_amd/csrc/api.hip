@@ -180,11 +180,18 @@ sk_status_t finish_plan(int64_t chunk, int32_t max_seq_len, sk_plan_t* plan) {
 
 // One round of resident query-tile workgroups over (KV head, query tile,
 // slice): [I3725] section 2's one-round rule, counted over query tiles and
-// the workgroups a compute unit holds.
-int64_t query_tile_chunk(const sk_desc_t& d, int32_t q_len, int64_t total_tokens,
-                         int32_t cu_count) {
+// the workgroups a compute unit holds. A ragged batch takes the split
+// kernel's ragged budget instead (kRaggedBlockFactor per compute unit): its
+// short sequences leave long-sequence slices as the tail. On the seeded
+// ragged batch of 32 (bf16, 8 KV heads of width 128, 4 heads each, 545,012
+// positions) one round gave 4 splits and 673 us, the ragged budget 14
+// splits and 400 us.
+int64_t query_tile_chunk(const sk_desc_t& d, int32_t q_len, int32_t max_seq_len,
+                         int64_t total_tokens, int32_t cu_count) {
   const int64_t tiles = (int64_t)d.num_kv_heads * sk::query_tile_rows_tiles(d, q_len);
-  return ceil_div(tiles * total_tokens, (int64_t)sk::query_tile_resident(d) * cu_count);
+  const bool ragged = total_tokens < (int64_t)max_seq_len * d.batch;
+  const int64_t per_cu = ragged ? kRaggedBlockFactor : sk::query_tile_resident(d);
+  return ceil_div(tiles * total_tokens, per_cu * cu_count);
 }
 
 }  // namespace
@@ -222,7 +229,7 @@ sk_status_t attn_decode_plan(const sk_desc_t* desc, int32_t max_seq_len, int64_t
   if (desc->kv_shared) {
     chunk = ceil_div(total_tokens * sk::latent_blocks_per_split(*desc), (int64_t)cu_count);
   } else if (sk::decode_on_query_tiles(*desc)) {
-    chunk = query_tile_chunk(*desc, 1, total_tokens, cu_count);
+    chunk = query_tile_chunk(*desc, 1, max_seq_len, total_tokens, cu_count);
   } else {
     const bool ragged = total_tokens < (int64_t)max_seq_len * desc->batch;
     const int64_t per_cu = (int64_t)sk::gqa_resident_blocks(*desc) * (ragged ? kRaggedBlockFactor : 1);
@@ -444,7 +451,8 @@ sk_status_t attn_query_tiles_plan(const sk_desc_t* desc, int32_t q_len, int32_t 
     plan->chunk = (int32_t)ceil_div(max_seq_len, n_splits_requested);
     return ok();
   }
-  return finish_plan(query_tile_chunk(*desc, q_len, total_tokens, cu_count), max_seq_len, plan);
+  return finish_plan(query_tile_chunk(*desc, q_len, max_seq_len, total_tokens, cu_count),
+                     max_seq_len, plan);
 }
 
 size_t attn_query_tiles_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan,

@@ -135,7 +135,8 @@ def test_plan_for_decode_on_query_tiles_counts_resident_workgroups():
     # 16-bit groups decoded by the query-tile kernel (all of width 64, width 128
     # from 4 heads per KV head, width 256 from 6): one round of the 1, 2 or 4
     # workgroups a compute unit holds at width 256, 128 or 64, over KV heads x
-    # slices; attn_query_tiles_plan with one query gives the same plan.
+    # slices (a ragged batch: 8 per compute unit, as on the split kernel);
+    # attn_query_tiles_plan with one query gives the same plan.
     for hq, hkv, D, res in [(24, 4, 256, 1), (32, 4, 256, 1), (64, 8, 256, 1), (32, 8, 128, 2),
                             (48, 8, 128, 2), (8, 8, 64, 4), (64, 8, 64, 4)]:
         for lens, kv in itertools.product(([1000], [32768], [131072], [16384] * 8, [300, 5000, 70000]),
@@ -143,7 +144,8 @@ def test_plan_for_decode_on_query_tiles_counts_resident_workgroups():
             for cu in (80, 256):
                 d = gqa_desc(Hq=hq, Hkv=hkv, D=D, cap=max(lens), kv=kv, batch=len(lens))
                 p = B.attn_decode_plan(d, max(lens), sum(lens), cu, 0)
-                want = oracle.plan_splits(lens, hkv, cu, blocks_per_cu=res)
+                ragged = sum(lens) < len(lens) * max(lens)  # the ragged budget: 8 per CU
+                want = oracle.plan_splits(lens, hkv, cu, blocks_per_cu=8 if ragged else res)
                 assert (p.n_splits, p.chunk) == want, (hq, hkv, D, lens, cu)
                 pq = B.attn_query_tiles_plan(d, 1, max(lens), sum(lens), cu, 0)
                 assert (pq.n_splits, pq.chunk) == want
