@@ -219,3 +219,25 @@ def test_decode_on_query_tiles_is_the_one_query_call(hq, hkv, D, kv):
     ref, rlse = oracle_out(case)
     assert_parity(case, out, ref, label=case.name)
     np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("kv,hq,hkv,D", [("f16", 8, 8, 64), ("bf16", 24, 4, 256), ("f16", 32, 8, 128)])
+@pytest.mark.parametrize("S", [1, 3, 200])
+def test_decode_on_query_tiles_with_explicit_splits(kv, hq, hkv, D, S):
+    # Explicit split counts on routed descriptors: one slice, uneven slices,
+    # and 200 slices of 25 positions (shorter than a 32-position tile; most
+    # are empty for the short sequences and write the neutral partial).
+    from harness import assert_parity, oracle_out, run_gpu
+
+    case = synthetic.gqa_case(f"routed-S{S}-{hq}x{hkv}-d{D}-{kv}", seq_lens=[5000, 1, 333],
+                              num_q_heads=hq, num_kv_heads=hkv, head_dim=D, kv_dtype=kv,
+                              capacity=5003, seed=9300 + S + D)
+    t = to_device(case)
+    out, lse, call = run_gpu(case, n_splits=S, tensors=t)
+    assert call.plan.n_splits == S
+    qo, ql, _ = run_qt(case, n_splits=S, tensors={**t, "q": t["q"].unsqueeze(1).contiguous()})
+    assert np.array_equal(qo[:, 0], out, equal_nan=True)
+    assert np.array_equal(ql[:, 0], lse, equal_nan=True)
+    ref, rlse = oracle_out(case)
+    assert_parity(case, out, ref, label=case.name)
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-4)
