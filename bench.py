@@ -52,7 +52,7 @@ ONLY = {
 # while those sources are unchanged.
 TRAFFIC_SUMMARY = os.path.join(HERE, "profiles", "gqa_split_9b-like_f32_L131072_traffic.md")
 KERNEL_SOURCES = [os.path.join(HERE, "split_kv_flash_amd", "csrc", f)
-                  for f in ("gqa_split.hip", "sk_device.h", "sk_internal.h")]
+                  for f in ("gqa_split.hip", "sk_device.h", "sk_internal.h", "sk_merge.h")]
 
 
 def kernel_source_hash():

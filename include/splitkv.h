@@ -260,8 +260,9 @@ sk_status_t attn_decode(const sk_desc_t* desc, const sk_plan_t* plan, const void
  * length outside [1, min(max_seq_len, n_splits*chunk)] makes that sequence's out and lse
  * NaN. The counter section must be zero when the call starts (attn_decode_workspace_init);
  * a call that completes leaves it zero. Calls that share a workspace must not overlap in
- * time (for example on two streams). It always runs the vector split kernel, also for
- * the descriptors attn_decode_splitk serves with the query-tile kernel.
+ * time (for example on two streams). The descriptors attn_decode_splitk serves with the
+ * query-tile kernel run its one-launch form (the same count and merge); the others the
+ * vector split kernel's.
  * Errors: as attn_decode; SK_ERR_UNSUPPORTED for a shared latent. */
 sk_status_t attn_decode_one_launch(const sk_desc_t* desc, const sk_plan_t* plan, const void* q,
                                    const void* k, const void* v, const int32_t* block_table,

@@ -291,27 +291,36 @@ static sk_status_t prepare_split(const sk_desc_t* desc, const sk_plan_t* plan, c
   return SK_OK;
 }
 
+// Single-query decode as a query-tile launch (q_len = 1): the rows are the
+// group's heads and the partials take the split kernel's layout.
+static sk::QueryTileLaunch one_query_tiles(const sk::SplitLaunch& a) {
+  sk::QueryTileLaunch t;
+  t.d = a.d;
+  t.p = a.p;
+  t.q_len = 1;
+  t.q = a.q;
+  t.k = a.k;
+  t.v = a.v;
+  t.seq_lens = a.seq_lens;
+  t.ws_acc = a.ws_acc;
+  t.ws_m = a.ws_m;
+  t.ws_l = a.ws_l;
+  t.stream = a.stream;
+  t.fused = a.fused;
+  t.counters = a.counters;
+  t.out = a.out;
+  t.lse = a.lse;
+  return t;
+}
+
 // The split step of two-launch decode: the shared-latent kernel, the GQA split
 // kernel, or the query-tile kernel with one query (whose partials and grid
 // have the same layout) for the descriptors it serves faster.
 static sk_status_t split_dispatch(const sk::SplitLaunch& a, bool launch, const void** fn,
                                   int grid[3], int* block) {
   if (a.d->kv_shared) return sk::latent_split_launch(a, launch, fn, grid, block);
-  if (sk::decode_on_query_tiles(*a.d)) {
-    sk::QueryTileLaunch t;
-    t.d = a.d;
-    t.p = a.p;
-    t.q_len = 1;
-    t.q = a.q;
-    t.k = a.k;
-    t.v = a.v;
-    t.seq_lens = a.seq_lens;
-    t.ws_acc = a.ws_acc;
-    t.ws_m = a.ws_m;
-    t.ws_l = a.ws_l;
-    t.stream = a.stream;
-    return sk::query_tile_launch(t, launch, fn, grid, block);
-  }
+  if (sk::decode_on_query_tiles(*a.d))
+    return sk::query_tile_launch(one_query_tiles(a), launch, fn, grid, block);
   return sk::gqa_split_launch(a, launch, fn, grid, block);
 }
 
@@ -570,7 +579,8 @@ sk_status_t attn_decode_one_launch(const sk_desc_t* desc, const sk_plan_t* plan,
   a.out = out;
   a.lse = lse;
   int grid[3], block;
-  s = sk::gqa_split_launch(a, true, nullptr, grid, &block);
+  s = sk::decode_on_query_tiles(*desc) ? sk::query_tile_launch(one_query_tiles(a), true, nullptr, grid, &block)
+                                       : sk::gqa_split_launch(a, true, nullptr, grid, &block);
   if (s != SK_OK) return fail(s, "no split kernel for this descriptor");
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)

@@ -48,6 +48,7 @@
 
 #include "sk_device.h"
 #include "sk_internal.h"
+#include "sk_merge.h"
 
 namespace sk {
 
@@ -106,109 +107,6 @@ __device__ __forceinline__ void load_q_slice(float (&qr)[G][D / RL], const QT* q
 #pragma unroll
       for (int e = 0; e < VEC; ++e)
         qr[h][j * VEC + e] = to_f32(q[h * D + j * RL * VEC + li * VEC + e]) * qscale;
-}
-
-// Device-scope (all XCDs) relaxed accesses for the one-launch variant's
-// partials: the stores write through to the coherence point and the loads read
-// from it, so no cache maintenance is needed between workgroups on different
-// XCDs. The 16-byte loads are raw buffer loads with the device-scope cache
-// policy bit (sc1).
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-constexpr int kCachePolicyDevice = 16;  // sc1
-__device__ __forceinline__ float4 ld_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyDevice));
-}
-
-// Merges the n partials of query heads h0 .. h0+G-1 of sequence b into out
-// and lse (the combine step of the one-launch variant), in passes of P
-// splits: the pass's m and l values of every head are read once into LDS
-// (s_ml, 2*G*P floats), then thread t takes four consecutive columns of one
-// head, finds the pass maximum from LDS, rescales its running sums if it grew,
-// and folds the pass's accumulator rows, 16 per chunk, with the next chunk's
-// loads in flight. Rows past the pass are clamped to its last row (a written
-// partial) and weighted zero, so every read is in range.
-template <int G, int D, int NT, int P>
-__device__ __forceinline__ void merge_group(const GqaArgs& a, int b, int h0, int n, int tid,
-                                            float* s_ml) {
-  constexpr int C4 = D / 4;
-  constexpr int K = 16;
-  const int64_t row0 = ((int64_t)b * a.Hq + h0) * a.S;  // head hh's split i: row0 + hh*S + i
-  const auto racc = raw_rsrc(a.ws_acc + row0 * D, (uint32_t)((int64_t)G * a.S * D * 4));
-  // The column loop's trip count is the same for every thread (the passes
-  // below hold barriers); threads past the last column do no work in it.
-  for (int base = 0; base < G * C4; base += NT) {
-    const int idx = base + tid;
-    const bool active = idx < G * C4;
-    const int hh = active ? idx / C4 : 0;
-    const int c = active ? (idx - hh * C4) * 4 : 0;
-    const uint32_t col_off = (uint32_t)(((int64_t)hh * a.S * D + c) * 4);
-    float M = -INFINITY, ls = 0.0f;
-    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int p0 = 0; p0 < n; p0 += P) {
-      const int np = min(P, n - p0);
-      __syncthreads();  // the previous pass (or column) is done with s_ml
-      for (int j = tid; j < G * np; j += NT) {
-        const int jh = j / np, i = j - (j / np) * np;
-        const int64_t r = row0 + (int64_t)jh * a.S + p0 + i;
-        s_ml[2 * (jh * P + i)] = ld_dev(a.ws_m + r);
-        s_ml[2 * (jh * P + i) + 1] = ld_dev(a.ws_l + r);
-      }
-      __syncthreads();
-      if (!active) continue;
-      const float* ml = s_ml + 2 * hh * P;
-      float mc = M;
-      for (int i = 0; i < np; ++i) mc = fmaxf(mc, ml[2 * i]);
-      const float mu = (mc == -INFINITY) ? 0.0f : mc;  // guard: no finite maximum yet
-      const float al = fast_exp2((M - mu) * kLog2e);
-      ls *= al;
-      A.x *= al;
-      A.y *= al;
-      A.z *= al;
-      A.w *= al;
-      M = mc;
-      float4 x0[K], x1[K];
-      auto fetch = [&](float4 (&x)[K], int i0) {
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const int i = p0 + min(i0 + k, np - 1);
-          x[k] = ld_dev4(racc, col_off + (uint32_t)i * (uint32_t)(D * 4));
-        }
-      };
-      auto fold = [&](const float4 (&x)[K], int i0) {
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const int i = min(i0 + k, np - 1);
-          const float w = (i0 + k < np) ? fast_exp2((ml[2 * i] - mu) * kLog2e) : 0.0f;
-          ls = fmaf(w, ml[2 * i + 1], ls);
-          A.x = fmaf(w, x[k].x, A.x);
-          A.y = fmaf(w, x[k].y, A.y);
-          A.z = fmaf(w, x[k].z, A.z);
-          A.w = fmaf(w, x[k].w, A.w);
-        }
-      };
-      fetch(x0, 0);
-      for (int i0 = 0;;) {
-        if (i0 + K < np) fetch(x1, i0 + K);
-        fold(x0, i0);
-        i0 += K;
-        if (i0 >= np) break;
-        if (i0 + K < np) fetch(x0, i0 + K);
-        fold(x1, i0);
-        i0 += K;
-        if (i0 >= np) break;
-      }
-    }
-    if (!active) continue;
-    const float inv = 1.0f / ls;
-    float* o = a.out + ((int64_t)b * a.Hq + h0 + hh) * D + c;
-    *reinterpret_cast<float4*>(o) = make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
-    if (a.lse && c == 0) a.lse[(int64_t)b * a.Hq + h0 + hh] = M + logf(ls);
-  }
 }
 
 template <typename KV, int G, int D, bool PAGED, int RL, int R, int HS, int WPE, bool FUSED>
@@ -629,7 +527,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     __syncthreads();
     if (!s_last) return;
     // The epilogue's LDS is free again: it holds the merge's m and l values.
-    merge_group<G, D, Sh::kThreads, NW * D / 2>(a, b, h0, n, tid, &s_acc[0][0][0]);
+    merge_group<D, Sh::kThreads, NW * D / 2>(a, G, b, h0, n, tid, &s_acc[0][0][0]);
   }
 }
 

@@ -39,6 +39,7 @@
 //     close to f32 accuracy while K and V are used exactly as stored.
 #include "sk_device.h"
 #include "sk_internal.h"
+#include "sk_merge.h"
 
 namespace sk {
 
@@ -62,7 +63,15 @@ struct QtArgs {
   int32_t q_dtype;
   int32_t Q, Hq, G, S, chunk, cap, nqt;  // nqt: 64-row query tiles per KV head
   float qscale;                          // scale * log2(e)
+  // One-launch decode only (Q = 1).
+  uint32_t* counters;  // [B][Hkv], zero between calls
+  float* out;          // [B][Hq][D]
+  float* lse;          // [B][Hq] or null
 };
+
+// Splits of one merge pass of the one-launch kernel (its m and l values sit in
+// the freed K/V ring).
+constexpr int kQtMergePass = 64;
 
 // 16-bit storage types: round-to-nearest-even conversion from f32, widening,
 // and the 16x16x32 MFMA of that type.
@@ -101,7 +110,13 @@ __device__ __forceinline__ qt_s4 qt_read_tr(const short* p) {
 // fixed order (so every wave of the block derives the same softmax), and it
 // accumulates its own output columns. Few query rows (speculative verify) then
 // keep all four waves busy instead of one.
-template <typename KT, int D, int DS>
+//
+// FUSED (one query per sequence: the one-launch decode): partials are
+// written with device-scope stores, and the workgroup that completes the
+// (sequence, KV head)'s count merges them into out and lse, as the GQA split
+// kernel's one-launch variant does; empty slices take no part, and an invalid
+// length makes that sequence's outputs NaN.
+template <typename KT, int D, int DS, bool FUSED>
 __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
   using TT = QtType<KT>;
   constexpr int NP = TT::kParts;  // parts of q and of the softmax weights
@@ -138,7 +153,20 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
   const int QG = a.Q * a.G;
   const int QH = a.Q * a.Hq;
 
-  const int L = min(a.seq_lens[b], a.cap);
+  const int Lraw = a.seq_lens[b];
+  if constexpr (FUSED) {
+    const bool valid = Lraw >= 1 && Lraw <= a.cap && (int64_t)Lraw <= (int64_t)a.S * a.chunk;
+    if (!valid) {
+      if (split == 0) {
+        for (int idx = tid; idx < a.G * D; idx += 256)
+          a.out[((int64_t)b * a.Hq + g * a.G) * D + idx] = __builtin_nanf("");
+        if (a.lse && tid < a.G) a.lse[(int64_t)b * a.Hq + g * a.G + tid] = __builtin_nanf("");
+      }
+      return;
+    }
+    if ((int64_t)split * a.chunk >= Lraw) return;  // an empty slice takes no part in the merge
+  }
+  const int L = min(Lraw, a.cap);
   const int64_t start = (int64_t)split * a.chunk;
   const int64_t end = min((int64_t)L, start + a.chunk);
 
@@ -385,13 +413,51 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
       const int w = te * a.Hq + g * a.G + (re - te * a.G);
       float* dst = a.ws_acc + (((int64_t)b * QH + w) * a.S + split) * D + 16 * CBW * dq + l16;
 #pragma unroll
-      for (int c = 0; c < CBW; ++c) dst[16 * c] = acc[c][e];
+      for (int c = 0; c < CBW; ++c) {
+        if constexpr (FUSED)
+          st_dev(dst + 16 * c, acc[c][e]);
+        else
+          dst[16 * c] = acc[c][e];
+      }
     }
   }
   if (lq == 0 && rvalid && dq == 0) {
     const int64_t r = ((int64_t)b * QH + t * a.Hq + g * a.G + hh) * a.S + split;
-    a.ws_m[r] = m * kLn2;
-    a.ws_l[r] = l;
+    if constexpr (FUSED) {
+      st_dev(a.ws_m + r, m * kLn2);
+      st_dev(a.ws_l + r, l);
+    } else {
+      a.ws_m[r] = m * kLn2;
+      a.ws_l[r] = l;
+    }
+  }
+
+  if constexpr (FUSED) {
+    // Every thread waits until its device-scope stores have completed; the
+    // count then tells the last workgroup of the group that every partial is
+    // in place, and it merges them (the K/V ring is free again).
+    // The flag lives in the score exchange buffer, free by now: a separate
+    // word would take width 64 past 40 KB and four workgroups per CU.
+    int* s_last = reinterpret_cast<int*>(&s_sc[0][0][0]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int n = (int)((L + (int64_t)a.chunk - 1) / a.chunk);
+    if (tid == 0) {
+      uint32_t* cnt = a.counters + (int64_t)b * (a.Hq / a.G) + g;
+      const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = prev + 1 == (uint32_t)n;
+      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *s_last = last;
+    }
+    __syncthreads();
+    if (!*s_last) return;
+    static_assert(2 * 8 * kQtMergePass * 4 <= (int)sizeof(s_kv), "m, l of 8 heads per pass fit the ring");
+    // Sixteen accumulator rows in flight per chunk at width 256 (one
+    // workgroup per CU either way), four below it, which keeps the merge
+    // within the registers of the resident count (16 took 200 at width 64).
+    constexpr int MK = D >= 256 ? 16 : 4;
+    merge_group<D, 256, kQtMergePass, MK>(a, a.G, b, g * a.G, n, tid,
+                                          reinterpret_cast<float*>(&s_kv[0][0][0]));
   }
 }
 
@@ -443,23 +509,32 @@ bool decode_on_query_tiles(const sk_desc_t& d) {
   }
 }
 
-template <typename KT, int D, int DS>
+template <typename KT, int D, int DS, bool FUSED>
 static void qt_go(bool launch, const void** fn, dim3 grid, hipStream_t stream, const QtArgs& a) {
-  auto kern = query_tile_kernel<KT, D, DS>;
+  auto kern = query_tile_kernel<KT, D, DS, FUSED>;
   if (fn) *fn = reinterpret_cast<const void*>(kern);
   if (launch) hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, a);
 }
 
+// The one-launch kernel exists for one query per sequence, whose group of at
+// most 8 rows takes 4 ways at width 128 and 256 and 2 at width 64.
 template <typename KT, int D>
-static void qt_launch(int ways, bool launch, const void** fn, dim3 grid, hipStream_t stream,
-                      const QtArgs& a) {
-  if (ways == 4) {
-    if constexpr (D >= 128) qt_go<KT, D, 4>(launch, fn, grid, stream, a);
+static sk_status_t qt_launch(int ways, bool fused, bool launch, const void** fn, dim3 grid,
+                             hipStream_t stream, const QtArgs& a) {
+  if (fused) {
+    if (a.Q != 1 || a.G > 8 || ways != (D >= 128 ? 4 : 2)) return SK_ERR_UNSUPPORTED;
+    if constexpr (D >= 128)
+      qt_go<KT, D, 4, true>(launch, fn, grid, stream, a);
+    else
+      qt_go<KT, D, 2, true>(launch, fn, grid, stream, a);
+  } else if (ways == 4) {
+    if constexpr (D >= 128) qt_go<KT, D, 4, false>(launch, fn, grid, stream, a);
   } else if (ways == 2) {
-    qt_go<KT, D, 2>(launch, fn, grid, stream, a);
+    qt_go<KT, D, 2, false>(launch, fn, grid, stream, a);
   } else {
-    qt_go<KT, D, 1>(launch, fn, grid, stream, a);
+    qt_go<KT, D, 1, false>(launch, fn, grid, stream, a);
   }
+  return SK_OK;
 }
 
 template <typename KT>
@@ -468,12 +543,11 @@ static sk_status_t qt_by_dim(const QueryTileLaunch& s, const QtArgs& a, dim3 gri
   const int D = s.d->head_dim_qk;
   const int ways = query_tile_ways(a.Q * a.G, D);
   switch (D) {
-    case 64: qt_launch<KT, 64>(ways, launch, fn, grid, s.stream, a); break;
-    case 128: qt_launch<KT, 128>(ways, launch, fn, grid, s.stream, a); break;
-    case 256: qt_launch<KT, 256>(ways, launch, fn, grid, s.stream, a); break;
+    case 64: return qt_launch<KT, 64>(ways, s.fused, launch, fn, grid, s.stream, a);
+    case 128: return qt_launch<KT, 128>(ways, s.fused, launch, fn, grid, s.stream, a);
+    case 256: return qt_launch<KT, 256>(ways, s.fused, launch, fn, grid, s.stream, a);
     default: return SK_ERR_UNSUPPORTED;
   }
-  return SK_OK;
 }
 
 sk_status_t query_tile_launch(const QueryTileLaunch& s, bool launch, const void** fn, int grid3[3],
@@ -500,6 +574,9 @@ sk_status_t query_tile_launch(const QueryTileLaunch& s, bool launch, const void*
   a.cap = d.max_seq_len;
   a.nqt = query_tile_rows_tiles(d, s.q_len);
   a.qscale = d.scale * kLog2e;
+  a.counters = s.counters;
+  a.out = s.out;
+  a.lse = s.lse;
   const dim3 grid(d.num_kv_heads * a.nqt, s.p->n_splits, d.batch);
   if (grid3) {
     grid3[0] = grid.x;

@@ -29,7 +29,7 @@ struct SplitLaunch {
   float* ws_m;
   float* ws_l;
   hipStream_t stream;
-  // One-launch decode (GQA only): the last workgroup of each (sequence, KV
+  // One-launch decode (separate K and V): the last workgroup of each (sequence, KV
   // head) to finish merges the partials into out/lse.
   bool fused = false;
   uint32_t* counters = nullptr;
@@ -76,6 +76,11 @@ struct QueryTileLaunch {
   float* ws_m;
   float* ws_l;
   hipStream_t stream;
+  // One-launch decode (q_len = 1 only): merge in the grid into out and lse.
+  bool fused = false;
+  uint32_t* counters = nullptr;
+  float* out = nullptr;
+  float* lse = nullptr;
 };
 
 // Host-only capability checks (no HIP calls).

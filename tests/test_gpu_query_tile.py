@@ -218,7 +218,7 @@ def test_decode_on_query_tiles_is_the_one_query_call(hq, hkv, D, kv):
     assert np.array_equal(ql[:, 0], lse, equal_nan=True)
     ref, rlse = oracle_out(case)
     assert_parity(case, out, ref, label=case.name)
-    np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-4)
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=ABS_GATE[kv])  # f16 score outliers near 1e-4
 
 
 @pytest.mark.parametrize("kv,hq,hkv,D", [("f16", 8, 8, 64), ("bf16", 24, 4, 256), ("f16", 32, 8, 128)])
@@ -240,4 +240,4 @@ def test_decode_on_query_tiles_with_explicit_splits(kv, hq, hkv, D, S):
     assert np.array_equal(ql[:, 0], lse, equal_nan=True)
     ref, rlse = oracle_out(case)
     assert_parity(case, out, ref, label=case.name)
-    np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-4)
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=ABS_GATE[kv])  # f16 score outliers near 1e-4
