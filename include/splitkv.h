@@ -209,10 +209,10 @@ size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan)
  * Kernel: contiguous f16/bf16 caches of head width 64, of width 128 with at least 4
  * query heads per KV head, and of width 256 with at least 6, run on the query-tile
  * kernel of attn_query_tiles with one query (its partials have this layout): MFMA
- * scores and outputs with q and the weights split into two f16 or three bf16 parts,
- * which keeps f32-level accuracy and holds wide groups at the memory rate where the
- * vector split kernel runs out of ALU issue. Every other GQA descriptor runs the
- * vector split kernel. */
+ * scores and outputs with q and the weights split into two f16 or three bf16 parts
+ * (22 or 24 significant bits; scores within 1e-6 of exact on unit-scale data), which
+ * holds wide groups at the memory rate where the vector split kernel runs out of ALU
+ * issue. Every other GQA descriptor runs the vector split kernel. */
 sk_status_t attn_decode_splitk(const sk_desc_t* desc, const sk_plan_t* plan,
                                const void* q, const void* k, const void* v,
                                const int32_t* block_table, const int32_t* seq_lens,
@@ -308,7 +308,8 @@ sk_status_t attn_decode_combine_project(const sk_desc_t* desc, const sk_plan_t* 
  *   lse       device f32 [batch][q_len][num_q_heads], or NULL
  * Two launches (the query-tile split kernel, then the combine). A query with no visible
  * position (L_b < q_len) gets NaN. Products run on 16-bit MFMA with q and the softmax
- * weights each split into a high and a low 16-bit part, f32 accumulation.
+ * weights each split into 16-bit parts (two f16 parts, 22 bits; three bf16 parts, 24
+ * bits), f32 accumulation.
  * Supported: separate K and V, contiguous, f16/bf16 KV, head_dim 64/128/256, any group size.
  * Errors: SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE_TOO_SMALL (nothing
  * launched), SK_ERR_LAUNCH. */

@@ -33,10 +33,13 @@
 //     lane's A operand of the output product P V; the V operands come from the
 //     gfx950 transpose read ds_read_b64_tr_b16 in the same position order. P
 //     never goes through LDS.
-//   * Precision: the MFMA inputs are 16-bit, so q and P are each split into a
-//     high and a low 16-bit part (two products each): x = hi + lo carries
-//     about 22 bits (f16) or 16 bits (bf16) of x, so scores and weights keep
-//     close to f32 accuracy while K and V are used exactly as stored.
+//   * Precision: the MFMA inputs are 16-bit, so q and P are each split into
+//     16-bit parts, one product per part: two f16 parts (22 bits) or three
+//     bf16 parts (24 bits), so scores and weights keep close to f32 accuracy
+//     while K and V are used exactly as stored. f16's second part of q is
+//     taken times 2^11, which keeps it out of f16's subnormal range, and its
+//     products go to an accumulator of their own that is added back times
+//     2^-11.
 #include "sk_device.h"
 #include "sk_internal.h"
 #include "sk_merge.h"
@@ -80,6 +83,10 @@ struct QtType;
 template <>
 struct QtType<_Float16> {
   static constexpr int kParts = 2;  // 11 + 11 significand bits
+  // The second part of q is stored times 2^11: what the first part leaves is
+  // below 2^-11 of it, and for query values near 0.1 (q scale/sqrt(D) log2 e)
+  // that would be an f16 subnormal with a few significant bits.
+  static constexpr float kLoScale = 2048.0f;
   static __device__ __forceinline__ short from(float x) { return __builtin_bit_cast(short, (_Float16)x); }
   static __device__ __forceinline__ float to(short b) { return (float)__builtin_bit_cast(_Float16, b); }
   static __device__ __forceinline__ qt_f4 mma(qt_s8 a, qt_s8 b, qt_f4 c) {
@@ -90,6 +97,7 @@ struct QtType<_Float16> {
 template <>
 struct QtType<bf16_t> {
   static constexpr int kParts = 3;  // 8 + 8 + 8 significand bits
+  static constexpr float kLoScale = 1.0f;  // bf16 has f32's exponent range
   static __device__ __forceinline__ short from(float x) { return __builtin_bit_cast(short, (__bf16)x); }
   static __device__ __forceinline__ float to(short b) {
     return __uint_as_float(((uint32_t)(uint16_t)b) << 16);
@@ -99,6 +107,13 @@ struct QtType<bf16_t> {
                                                    __builtin_bit_cast(qt_bf8, b), c, 0, 0, 0);
   }
 };
+
+// The value itself, hidden from the optimiser: what is computed from it
+// starts from this rounded f32 value and cannot be fused with its producer.
+__device__ __forceinline__ float opaque_f32(float x) {
+  asm("" : "+v"(x));
+  return x;
+}
 
 __device__ __forceinline__ qt_s4 qt_read_tr(const short* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((qt_lds_s4*)(p));
@@ -240,18 +255,28 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
           }
         }
       }
+      {
+        // Each part must be the rounding of the very f32 value its residual is
+        // taken from. Left to itself the compiler rounds the exact product
+        // q*qscale straight to f16 (a mixed-precision fma) where it forms the
+        // residual, but rounds it to f32 first where it forms the MFMA
+        // operand; where the two roundings differ (about once in 2^14
+        // elements) the parts then miss x by a whole f16 step. The product is
+        // therefore made opaque, and contraction is off for the split.
+#pragma clang fp contract(off)
 #pragma unroll
-      for (int ks = 0; ks < KSW; ++ks)
+        for (int ks = 0; ks < KSW; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float x = qv[ks][e] * a.qscale;
+          for (int e = 0; e < 8; ++e) {
+            float x = opaque_f32(qv[ks][e] * a.qscale);
 #pragma unroll
-          for (int i = 0; i < NP; ++i) {
-            const short part = TT::from(x);
-            qp[i][ks][e] = part;
-            x -= TT::to(part);
+            for (int i = 0; i < NP; ++i) {
+              const short part = TT::from(i == 1 ? x * TT::kLoScale : x);
+              qp[i][ks][e] = part;
+              x -= (i == 1 ? TT::to(part) / TT::kLoScale : TT::to(part));
+            }
           }
-        }
+      }
     }
 
     const KT* __restrict__ kp = reinterpret_cast<const KT*>(a.k) + (int64_t)b * a.stride_seq + (int64_t)g * a.stride_head;
@@ -295,17 +320,31 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
       const short* vb = s_kv[i % NB][1];
 
       // ---- scores S^T: two blocks of 16 positions, this block's 16 rows ----
+      // sp: the products of q's unscaled parts; sl: those of its scaled second
+      // part (f16), added back times 2^-11.
+      constexpr bool kScaledLo = TT::kLoScale != 1.0f;
       qt_f4 sp[2] = {qt_f4{0.f, 0.f, 0.f, 0.f}, qt_f4{0.f, 0.f, 0.f, 0.f}};
+      qt_f4 sl[2] = {qt_f4{0.f, 0.f, 0.f, 0.f}, qt_f4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int pb = 0; pb < 2; ++pb)
+      for (int pb = 0; pb < 2; ++pb) {
 #pragma unroll
         for (int ks = 0; ks < KSW; ++ks) {
           // row 16 pb + l16 (swizzle l16 & 7), logical chunk 4 (KSW dq + ks) + lq
           const qt_s8 av = *reinterpret_cast<const qt_s8*>(
               kb + (16 * pb + l16) * D + (((4 * (KSW * dq + ks) + lq) ^ (l16 & 7)) << 3));
 #pragma unroll
-          for (int i = 0; i < NP; ++i) sp[pb] = TT::mma(av, qp[i][ks], sp[pb]);
+          for (int i = 0; i < NP; ++i) {
+            if (kScaledLo && i == 1)
+              sl[pb] = TT::mma(av, qp[i][ks], sl[pb]);
+            else
+              sp[pb] = TT::mma(av, qp[i][ks], sp[pb]);
+          }
         }
+        if constexpr (kScaledLo) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sp[pb][e] = fmaf(sl[pb][e], 1.0f / TT::kLoScale, sp[pb][e]);
+        }
+      }
       if constexpr (DS > 1) {
         // Partial scores of the block's DS waves: same lane layout, summed in
         // wave order. The buffer is rewritten only after the tile's closing
@@ -498,7 +537,7 @@ int query_tile_resident(const sk_desc_t& d) {
 // runs out of ALU issue with more heads per KV row (at 131,072 f16 positions,
 // 8 heads of width 256 per KV head: 355 vs 160 us; width 128, 4 heads: 100 vs
 // 93 us; width 64, one head: 75 vs 60 us). q and the weights in two f16 or
-// three bf16 parts keep f32-level accuracy.
+// three bf16 parts (22 or 24 bits) keep the scores within f32 rounding.
 bool decode_on_query_tiles(const sk_desc_t& d) {
   if (!query_tile_supported(d) || d.num_kv_heads < 1) return false;
   const int G = d.num_q_heads / d.num_kv_heads;

@@ -18,6 +18,9 @@ REL_L2_GATE = {"f32": 1e-5, "f16": 1e-3, "bf16": 1e-3}
 # Every GQA kernel computes in f32 from the exact stored values, so its error
 # is f32 rounding only; this tighter bound catches slips the gates would miss.
 REL_L2_F32_ARITH = 2e-5
+# lse of a path whose arithmetic is f32 (q and the weights used exactly, or in
+# 16-bit parts that together carry 22-24 bits): the f32 gate.
+LSE_F32_ARITH = 1e-4
 
 
 def decode_call(case, tensors, *, n_splits: int = 0, cu_count=None):

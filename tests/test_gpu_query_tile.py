@@ -18,7 +18,7 @@ import pytest
 
 import oracle
 import synthetic
-from harness import ABS_GATE, REL_L2_F32_ARITH, REL_L2_GATE, errors
+from harness import ABS_GATE, LSE_F32_ARITH, REL_L2_F32_ARITH, REL_L2_GATE, errors
 from synthetic.torch_io import to_device
 
 pytestmark = pytest.mark.gpu
@@ -192,6 +192,26 @@ def test_ragged_batch_and_invalid_length():
 
 
 @pytest.mark.parametrize("kv", ["f16", "bf16"])
+@pytest.mark.parametrize("hq,hkv,D", [(24, 4, 256), (32, 8, 128), (8, 8, 64)])
+def test_routed_decode_scores_keep_f32_accuracy(hq, hkv, D, kv):
+    # 256 one-position sequences: each lse is that head's score, so this
+    # measures the score products alone, over 2,048-8,192 scores. q in 16-bit
+    # parts (two f16, the second scaled by 2^11, or three bf16) carries 22-24
+    # bits, so the error is f32 rounding: about 1e-7, and below 1e-6 for every
+    # score (scores reach about 5 here, where an f32 step is 4.8e-7).
+    case = synthetic.gqa_case(f"scores-{hq}x{hkv}-d{D}-{kv}", seq_lens=[1] * 256,
+                              num_q_heads=hq, num_kv_heads=hkv, head_dim=D, kv_dtype=kv,
+                              capacity=1, seed=777 + D)
+    from harness import oracle_out, run_gpu
+
+    _, lse, _ = run_gpu(case)
+    _, rlse = oracle_out(case)
+    err = np.abs(lse - rlse)
+    assert err.max() <= 1e-6, f"max score error {err.max():.3e} (median {np.median(err):.2e})"
+    assert np.median(err) <= 2e-7, f"median score error {np.median(err):.3e}"
+
+
+@pytest.mark.parametrize("kv", ["f16", "bf16"])
 @pytest.mark.parametrize("hq,hkv,D", [(24, 4, 256), (32, 4, 256), (32, 8, 128), (8, 8, 64), (48, 8, 64)])
 def test_decode_on_query_tiles_is_the_one_query_call(hq, hkv, D, kv):
     # 16-bit groups that single-query decode runs on the query-tile kernel:
@@ -218,7 +238,7 @@ def test_decode_on_query_tiles_is_the_one_query_call(hq, hkv, D, kv):
     assert np.array_equal(ql[:, 0], lse, equal_nan=True)
     ref, rlse = oracle_out(case)
     assert_parity(case, out, ref, label=case.name)
-    np.testing.assert_allclose(lse, rlse, rtol=0, atol=ABS_GATE[kv])  # f16 score outliers near 1e-4
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=LSE_F32_ARITH)
 
 
 @pytest.mark.parametrize("kv,hq,hkv,D", [("f16", 8, 8, 64), ("bf16", 24, 4, 256), ("f16", 32, 8, 128)])
@@ -240,4 +260,4 @@ def test_decode_on_query_tiles_with_explicit_splits(kv, hq, hkv, D, S):
     assert np.array_equal(ql[:, 0], lse, equal_nan=True)
     ref, rlse = oracle_out(case)
     assert_parity(case, out, ref, label=case.name)
-    np.testing.assert_allclose(lse, rlse, rtol=0, atol=ABS_GATE[kv])  # f16 score outliers near 1e-4
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=LSE_F32_ARITH)
