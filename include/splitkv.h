@@ -37,6 +37,9 @@
  *                        enqueued back to back (the combine's launch overlaps
  *                        the split kernel, while the in-grid merge waits for
  *                        device-scope round trips at the end of the grid).
+ *   attn_decode_no_alloc attn_decode with the partials in a scratch array the
+ *                        library holds per device, for callers that cannot
+ *                        allocate.
  *
  * Conventions shared by every call
  *   - Pointers named "device" are device memory on the device that owns
@@ -45,7 +48,9 @@
  *     allocates nothing and keeps no global or per-device state, so calls are
  *     re-entrant and safe from several host threads and devices (Lecture 06
  *     section 2 explains why scratch must be per device, never one static
- *     pointer shared by several devices).
+ *     pointer shared by several devices). The one exception is
+ *     attn_decode_no_alloc, which keeps its partials in a fixed array of its
+ *     own on each device.
  *   - Arguments are validated before any HIP call. A failed validation
  *     returns SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED or
  *     SK_ERR_WORKSPACE_TOO_SMALL and launches nothing.
@@ -248,6 +253,29 @@ sk_status_t attn_decode(const sk_desc_t* desc, const sk_plan_t* plan, const void
                         const void* k, const void* v, const int32_t* block_table,
                         const int32_t* seq_lens, void* workspace, size_t workspace_bytes,
                         float* out, float* lse, hipStream_t stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. The whole decode call as attn_decode
+ * (the same kernels, plan, results and error behaviour), but with no workspace argument:
+ * the partials go to a scratch array the library holds on each device, of
+ * SK_NO_ALLOC_SCRATCH_BYTES bytes (64 MiB, the attn_decode_workspace_bytes layout).
+ * The array exists once per device the library runs on and is held until the process
+ * ends; its device address is looked up on the first call on a device (with that
+ * device current) and kept. The call allocates nothing and frees nothing.
+ *   stream  must belong to the current device (the scratch used is that device's)
+ * Nothing in the scratch needs to start at zero: the combine reads only the partials
+ * this call's split step wrote. Every call on a device shares that device's array, and
+ * each call overwrites what the last one left, so calls that overlap in time on one
+ * device (two streams, two threads) race and must not be made.
+ * Errors: as attn_decode; SK_ERR_WORKSPACE_TOO_SMALL, before any HIP call, when
+ * attn_decode_workspace_bytes(desc, plan) exceeds SK_NO_ALLOC_SCRATCH_BYTES (plan fewer
+ * splits, or use attn_decode with a workspace); SK_ERR_INVALID_ARG when `stream` belongs
+ * to another device; SK_ERR_HIP when the scratch address cannot be looked up. */
+#define SK_NO_ALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+sk_status_t attn_decode_no_alloc(const sk_desc_t* desc, const sk_plan_t* plan, const void* q,
+                                 const void* k, const void* v, const int32_t* block_table,
+                                 const int32_t* seq_lens, float* out, float* lse,
+                                 hipStream_t stream);
 
 /* The whole decode call in one launch (separate K and V only), same arguments and results
  * as attn_decode. Every workgroup holding positions writes its partial to the workspace

@@ -21,7 +21,8 @@ from .binding import (  # noqa: F401
     SK_BF16, SK_F16, SK_F32, SK_KV_CONTIGUOUS, SK_KV_PAGED, SkDesc, SkKernelInfo, SkPlan,
     SplitKVError, attn_decode, attn_decode_combine, attn_decode_combine_project,
     attn_decode_kernel_info,
-    attn_decode_last_error, attn_decode_one_launch, attn_decode_plan, attn_decode_splitk,
+    attn_decode_last_error, attn_decode_no_alloc, attn_decode_one_launch, attn_decode_plan,
+    attn_decode_splitk,
     attn_decode_status_string, attn_decode_workspace_bytes, attn_decode_workspace_init,
     attn_query_tiles, attn_query_tiles_plan, attn_query_tiles_workspace_bytes,
 )
@@ -30,7 +31,7 @@ __all__ = [
     "DecodeCall", "make_desc", "SkDesc", "SkPlan", "SplitKVError", "attn_decode_plan",
     "attn_decode_workspace_bytes", "attn_decode_splitk", "attn_decode_combine",
     "attn_decode_status_string", "attn_decode_last_error", "attn_decode_kernel_info",
-    "attn_decode", "attn_decode_one_launch", "attn_decode_workspace_init",
+    "attn_decode", "attn_decode_one_launch", "attn_decode_no_alloc", "attn_decode_workspace_init",
     "attn_decode_combine_project", "QueryTileCall", "attn_query_tiles", "attn_query_tiles_plan",
     "attn_query_tiles_workspace_bytes", "decode",
 ]
@@ -190,6 +191,15 @@ class DecodeCall:
         attn_decode_one_launch(self.desc, self.plan, self.q, self.k, self.v, self.block_table,
                                self.seq_lens, self.workspace, self.ws_bytes, self.out,
                                self.lse if with_lse else None, _stream_handle(stream))
+        return self.out, self.lse
+
+    def decode_no_alloc(self, stream=None, with_lse: bool = True):
+        """The whole call without this object's workspace
+        (``attn_decode_no_alloc``: the library's per-device scratch holds the
+        partials)."""
+        attn_decode_no_alloc(self.desc, self.plan, self.q, self.k, self.v, self.block_table,
+                             self.seq_lens, self.out, self.lse if with_lse else None,
+                             _stream_handle(stream))
         return self.out, self.lse
 
     def combine_project(self, w_proj, out, stream=None, with_lse: bool = True):

@@ -105,6 +105,9 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_read_probe.restype = c_int32
     L.attn_decode_one_launch.argtypes = L.attn_decode.argtypes
     L.attn_decode_one_launch.restype = c_int32
+    L.attn_decode_no_alloc.argtypes = [PD, PP, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_void_p]
+    L.attn_decode_no_alloc.restype = c_int32
     _lib = L
     return L
 
@@ -189,6 +192,18 @@ def attn_decode_one_launch(desc: SkDesc, plan: SkPlan, q, k, v, block_table, seq
                                         _ptr(v), _ptr(block_table), _ptr(seq_lens),
                                         _ptr(workspace), int(workspace_bytes), _ptr(out),
                                         _ptr(lse), stream))
+
+
+def attn_decode_no_alloc(desc: SkDesc, plan: SkPlan, q, k, v, block_table, seq_lens, out, lse,
+                         stream: int) -> None:
+    _check(lib().attn_decode_no_alloc(ctypes.byref(desc), ctypes.byref(plan), _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(block_table), _ptr(seq_lens), _ptr(out),
+                                      _ptr(lse), stream))
+
+
+# Bytes of the library's per-device scratch behind attn_decode_no_alloc
+# (SK_NO_ALLOC_SCRATCH_BYTES in include/splitkv.h).
+SK_NO_ALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def attn_decode_combine_project(desc: SkDesc, plan: SkPlan, seq_lens, workspace,

@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "sk_internal.h"
@@ -559,6 +560,86 @@ sk_status_t attn_decode(const sk_desc_t* desc, const sk_plan_t* plan, const void
                          stream);
   if (s != SK_OK) return s;
   return attn_decode_combine(desc, plan, seq_lens, workspace, workspace_bytes, out, lse, stream);
+}
+
+// Partials of attn_decode_no_alloc, for callers that cannot allocate: one
+// array per device, held by the loaded library until the process ends. Host
+// code never names it except to look up its device address: in host code the
+// name stands for a host-side shadow, not for device memory.
+static __device__ __align__(256) char scratch[SK_NO_ALLOC_SCRATCH_BYTES];
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch`, per device
+
+// The current device's scratch address, looked up with that device current on
+// its first use and kept.
+sk_status_t device_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SK_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(SK_ERR_UNSUPPORTED, "device %d is past the %d devices the scratch table covers", dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SK_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return SK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sk_status_t attn_decode_no_alloc(const sk_desc_t* desc, const sk_plan_t* plan, const void* q,
+                                 const void* k, const void* v, const int32_t* block_table,
+                                 const int32_t* seq_lens, float* out, float* lse,
+                                 hipStream_t stream) {
+  // Every argument check runs before the first HIP call: the descriptor and plan,
+  // the scratch size, then the pointers (against a stand-in, aligned workspace
+  // address, since the real one is looked up only afterwards).
+  sk_status_t s = check_desc(desc);
+  if (s != SK_OK) return s;
+  if ((s = check_plan(desc, plan)) != SK_OK) return s;
+  const size_t need = sk::ws_layout(*desc, *plan).total;
+  if (need > SK_NO_ALLOC_SCRATCH_BYTES)
+    return fail(SK_ERR_WORKSPACE_TOO_SMALL,
+                "this call needs %zu bytes of partials; the static scratch holds %zu "
+                "(plan fewer splits, or pass a workspace to attn_decode)",
+                need, (size_t)SK_NO_ALLOC_SCRATCH_BYTES);
+  sk::SplitLaunch a;
+  void* const stand_in = reinterpret_cast<void*>((uintptr_t)256);
+  s = prepare_split(desc, plan, q, k, v, block_table, seq_lens, stand_in, SK_NO_ALLOC_SCRATCH_BYTES,
+                    true, &a);
+  if (s != SK_OK) return s;
+  if (!out) return fail(SK_ERR_INVALID_ARG, "out must be non-NULL");
+  if ((uintptr_t)out % 16) return fail(SK_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  if (stream) {
+    int cur = -1, sdev = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess) e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return fail(SK_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+    if (sdev != cur)
+      return fail(SK_ERR_INVALID_ARG, "stream belongs to device %d, but device %d is current", sdev,
+                  cur);
+  }
+  void* ws = nullptr;
+  if ((s = device_scratch(&ws)) != SK_OK) return s;
+  s = attn_decode_splitk(desc, plan, q, k, v, block_table, seq_lens, ws, SK_NO_ALLOC_SCRATCH_BYTES,
+                         stream);
+  if (s != SK_OK) return s;
+  return attn_decode_combine(desc, plan, seq_lens, ws, SK_NO_ALLOC_SCRATCH_BYTES, out, lse, stream);
 }
 
 sk_status_t attn_decode_one_launch(const sk_desc_t* desc, const sk_plan_t* plan, const void* q,
