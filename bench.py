@@ -5,13 +5,18 @@ A step is one decode-attention call (the split and the combine of every
 partial) over one synthetic batch whose inputs are already resident in HBM. The
 headline workload is a 9B-like full-attention layer (16 query / 4 KV heads,
 head_dim 256, f32 KV, q f32) at 131,072 positions; other context lengths,
-storage types and workloads are reported in ``rungs``.
+storage types, split counts and workloads are the rungs.
 
-Output: one JSON line with the metric, throughput (algorithmic HBM GB/s of the
-whole call through ``attn_decode``: the split kernel, then the combine
-kernel), the split kernel's roofline (HIP-event time per launch on the launch
-stream), the one-launch variant timed beside it, and the float64 CPU oracle's
-throughput on a bounded sample.
+Every timed call is cold: a read of a 512 MB buffer (twice the Infinity Cache)
+runs before it, outside its HIP event pair. Warm figures (calls back to back)
+are reported beside the headline's, labelled as such.
+
+Output: one compact JSON line on stdout with the metric, throughput
+(algorithmic HBM GB/s of the whole call through ``attn_decode``: the split
+kernel, then the combine kernel), the split kernel's roofline (HIP-event time
+per cold launch on the launch stream), a short table of every rung, and the
+float64 CPU oracle's throughput on bounded samples. The full record of each
+rung goes to stderr.
 """
 
 from __future__ import annotations
@@ -144,14 +149,18 @@ def _pair():
 WARMUP_MIN_MS = 500.0
 
 
-def warm_up(fn, calls, min_ms=WARMUP_MIN_MS):
-    """Runs fn at least ``calls`` times and for at least ``min_ms`` of GPU time."""
+def warm_up(fn, calls, min_ms=WARMUP_MIN_MS, flush=None):
+    """Runs fn at least ``calls`` times and for at least ``min_ms`` of GPU time
+    (each call after a flush read when ``flush`` is given, as in the timed
+    calls, so that a kernel trace of the run sees only cold launches)."""
     import torch
 
     n = 0
     t0 = time.perf_counter()
     while n < calls or (time.perf_counter() - t0) * 1e3 < min_ms:
         for _ in range(max(1, calls)):
+            if flush is not None:
+                flush.sum()
             fn()
         n += max(1, calls)
         torch.cuda.synchronize()
@@ -167,7 +176,7 @@ def time_calls(fn, steps, warmup, flush=None):
     timed call. Warm-up: ``warmup`` calls and at least WARMUP_MIN_MS."""
     import torch
 
-    warm_up(fn, warmup)
+    warm_up(fn, warmup, flush=flush)
     ev = [_pair() for _ in range(steps)]
     t0 = time.perf_counter()
     for e0, e1 in ev:
@@ -189,7 +198,7 @@ def kernel_avg(fn, steps, evict=None):
     Cache is evicted before every launch and each launch is timed alone."""
     import torch
 
-    warm_up(fn, 1, min_ms=100.0)
+    warm_up(fn, 1, min_ms=100.0, flush=evict)
     if evict is None:
         e0, e1 = _pair()
         e0.record()
@@ -217,15 +226,16 @@ def pct(x, q):
     return s[min(len(s) - 1, max(0, int(round(q * (len(s) - 1)))))]
 
 
-def measure(case, steps, warmup, n_splits=0, flush=None):
+def measure(case, steps, warmup, n_splits=0, flush=None, one_launch=True, tensors=None):
     """Times one workload. The call is ``attn_decode`` (the split kernel, then
     the combine kernel); for separate K and V the one-launch variant
     (``attn_decode_one_launch``, whose last workgroups merge) is timed beside
-    it, and each kernel alone."""
+    it, and each kernel alone. With ``flush`` every timed call and launch is
+    cold (the Infinity Cache evicted before it, outside the event pair)."""
     import torch
     from synthetic.torch_io import to_device
 
-    t = to_device(case)
+    t = to_device(case) if tensors is None else tensors
     call = decode_call(case, t, n_splits)
     total, wall = time_calls(call.decode, steps, warmup, flush)
     split = kernel_avg(call.splitk, steps, flush)
@@ -241,11 +251,12 @@ def measure(case, steps, warmup, n_splits=0, flush=None):
         "GBps": round(whole_b / (us * 1e-6) / 1e9, 1),
         "frac_of_peak": round(whole_b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         "split_GBps": round(split_b / (split * 1e-3) / 1e9, 1),
+        "split_frac_of_peak": round(split_b / (split * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "bytes_call": whole_b, "bytes_split": split_b,
         "tokens_per_s_per_layer": round(case.batch * 1e6 / us, 1),
         "mall_flushed": flush is not None,
     }
-    if not case.kv_shared:
+    if one_launch and not case.kv_shared:
         one, _ = time_calls(call.decode_one_launch, steps, warmup, flush)
         fused = kernel_avg(call.decode_one_launch, steps, flush)
         us1 = median(one) * 1e3
@@ -259,7 +270,9 @@ def measure(case, steps, warmup, n_splits=0, flush=None):
         tf = flops / (split * 1e-3) / 1e12
         res.update({"split_TFLOPs": round(tf, 2), "mfma_peak_TFLOPs": peak,
                     "mfma_frac": round(tf / peak, 4), "flops_split": flops})
-    del call, t
+    del call
+    if tensors is None:
+        del t
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res, split, wall
@@ -382,18 +395,19 @@ def bandwidth_control(nbytes=1 << 30, reps=20):
     return out
 
 
-def cpu_baseline(case, heads, reps=3):
-    """Time the float64 oracle on a bounded sample (the given query heads)."""
-    import numpy as np
-
-    import oracle
-
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = None
+        return None
+
+
+def cpu_baseline(case, heads, reps=3):
+    """Time the float64 oracle on a bounded sample (the given query heads)."""
+    import oracle
+
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
@@ -405,7 +419,7 @@ def cpu_baseline(case, heads, reps=3):
     byts = kv_per_group * len(groups)
     sec = median(times)
     return {
-        "value": round(byts / sec / 1e9, 3), "unit": "GB/s", "cores": threads,
+        "value": round(byts / sec / 1e9, 3), "unit": "GB/s", "cores": _blas_threads(),
         "kind": "oracle",
         "sample": f"{case.name}: query heads {[h for _, h in heads]} (KV groups {groups}), "
                   f"median of {reps} float64 two-pass oracle calls, {sec:.2f} s each; "
@@ -414,6 +428,29 @@ def cpu_baseline(case, heads, reps=3):
         "cpu": _cpu_model(),
         "host_cores_visible": len(os.sched_getaffinity(0)),
     }
+
+
+def cpu_oracle_sample(case, heads, bytes_call, reps=1):
+    """The float64 oracle on a sample of (sequence, head) pairs of a workload,
+    scaled to the whole call by the (position, head) pairs it covers: the
+    oracle's cost is one score and one weighted row per (position, head).
+    Returns a short record: seconds for the sample, the estimated seconds of
+    the whole call, and the call's algorithmic bytes over that estimate."""
+    import oracle
+
+    v_cols = case.head_dim_v if case.kv_shared else None
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.attend_f64(case.q, case.k_rows(), case.v_rows(), case.seq_lens, case.scale,
+                          q_dtype=case.q_dtype, kv_dtype=case.kv_dtype, v_cols=v_cols, heads=heads)
+        times.append(time.perf_counter() - t0)
+    sec = median(times)
+    covered = sum(int(case.seq_lens[b]) for b, _ in heads)
+    whole = int(case.seq_lens.sum()) * case.num_q_heads
+    est = sec * whole / covered
+    return {"w": case.name, "sample_heads": len(heads), "sample_s": round(sec, 3),
+            "call_s_est": round(est, 3), "GBps_est": round(bytes_call / est / 1e9, 4)}
 
 
 def _cpu_model():
@@ -438,6 +475,7 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     import synthetic
+    from synthetic.torch_io import to_device
 
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
@@ -445,25 +483,38 @@ def main():
         f"mem={props.total_memory / 2**30:.0f} GiB")
 
     if args.only:
+        # Cold calls, as in the full run (the flush reads show up in a kernel
+        # trace as a reduction kernel of their own).
+        fl = torch.zeros(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
         fn, pos, kw = ONLY[args.only]
         c = getattr(synthetic, fn)(*pos, **kw)
         if args.only.endswith("-project"):
-            r = measure_project(c, args.steps, args.warmup, "bf16", 128)
+            r = measure_project(c, args.steps, args.warmup, "bf16", 128, fl)
         elif "q_len" in c.meta:
-            r = measure_query_tiles(c, args.steps, args.warmup)
+            r = measure_query_tiles(c, args.steps, args.warmup, fl)
         else:
-            r, _, _ = measure(c, args.steps, args.warmup, args.n_splits)
+            r, _, _ = measure(c, args.steps, args.warmup, args.n_splits, fl)
         log(f"{args.only}: {r}")
+        # A 1 GiB device-to-device copy: the kernel of known size that counter
+        # runs scale FETCH_SIZE and WRITE_SIZE by.
+        x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        torch.empty_like(x).copy_(x)
+        torch.cuda.synchronize()
         return
 
-    # Headline: A and B runs of the same workload give the A/A noise floor.
+    flush = torch.zeros(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    # Headline, cold: A and B runs of the same workload give the A/A noise
+    # floor; a warm run (calls back to back) is reported beside them.
     case = synthetic.qwen9b_like(args.seq_len, args.kv, seed=2000 + args.seq_len)
     log(f"headline workload {case.name}: K+V {case.kv_bytes() / 1e9:.3f} GB")
-    head_a, kern_a, wall_a = measure(case, args.steps, args.warmup, args.n_splits)
-    log(f"run A: {head_a}")
-    head_b, split_b, _ = measure(case, args.steps, args.warmup, args.n_splits)
-    log(f"run B: {head_b}")
+    head_a, kern_a, _ = measure(case, args.steps, args.warmup, args.n_splits, flush)
+    log(f"run A (cold): {head_a}")
+    head_b, _, _ = measure(case, args.steps, args.warmup, args.n_splits, flush, one_launch=False)
+    log(f"run B (cold): {head_b}")
     aa_spread = abs(head_a["us_per_call"] - head_b["us_per_call"]) / head_a["us_per_call"]
+    warm, warm_split, _ = measure(case, args.steps, args.warmup, args.n_splits, None, one_launch=False)
+    log(f"warm run: {warm}")
 
     split_ms = kern_a
     achieved = head_a["bytes_split"] / (split_ms * 1e-3) / 1e9
@@ -471,8 +522,9 @@ def main():
         "kernel": "gqa_split_kernel",
         "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
         "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(head_a["n_splits"]),
-        "avg_launch_us": round(split_ms * 1e3, 2),
+        "avg_launch_us": round(split_ms * 1e3, 2), "launches": "cold (Infinity Cache evicted before each)",
         "algorithmic_bytes_per_launch": head_a["bytes_split"],
+        "warm_avg_launch_us": round(warm_split * 1e3, 2),
     }
 
     control = bandwidth_control()
@@ -480,48 +532,81 @@ def main():
     roofline["frac_of_read_ceiling"] = round(achieved / control["read_kernel_GBps"], 4)
 
     rungs = []
+    oracle_samples = []
+    no_cpu = args.no_cpu_baseline
+
+    def rung(r):
+        log(f"rung {json.dumps(r)}")
+        rungs.append(r)
+
     if not args.no_rungs:
-        flush = torch.zeros(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
-        specs = []
+        rs, rw = args.rung_steps, args.rung_warmup
+        # Tiny GQA (4 query / 1 KV head, width 64, f32) at its longest length and 8 splits.
+        c = synthetic.tiny_gqa(4096, seed=1004)
+        r, _, _ = measure(c, rs, rw, 8, flush)
+        rung(r)
+        if not no_cpu:
+            oracle_samples.append(cpu_oracle_sample(c, [(0, h) for h in range(c.num_q_heads)],
+                                                    r["bytes_call"]))
+        del c
         for kv in ("f32", "f16"):
             for L in (4096, 20480, 61440, 151552, 262144):
-                specs.append(lambda kv=kv, L=L: synthetic.qwen9b_like(L, kv, seed=2000 + L))
-        specs.append(lambda: synthetic.wide_group_peaky(262144))
-        specs.append(lambda: synthetic.ragged_paged())
+                c = synthetic.qwen9b_like(L, kv, seed=2000 + L)
+                r, _, _ = measure(c, rs, rw, 0, flush)
+                rung(r)
+                del c
+        # The 27B-like peaky layer: the planned split count, then the sweep.
+        c = synthetic.wide_group_peaky(262144)
+        t = to_device(c)
+        r, _, _ = measure(c, rs, rw, 0, flush, tensors=t)
+        rung(r)
+        for S in (64, 128, 256, 512):
+            r, _, _ = measure(c, rs, rw, S, flush, one_launch=False, tensors=t)
+            r["workload"] += f" (S={S})"
+            rung(r)
+        del t
+        if not no_cpu:  # one KV group of six heads
+            oracle_samples.append(cpu_oracle_sample(c, [(0, h) for h in range(c.group)],
+                                                    r["bytes_call"]))
+        del c
+        c = synthetic.ragged_paged()
+        r, _, _ = measure(c, rs, rw, 0, flush)
+        rung(r)
+        if not no_cpu:  # every head of the first sequence
+            oracle_samples.append(cpu_oracle_sample(c, [(0, h) for h in range(c.num_q_heads)],
+                                                    r["bytes_call"]))
+        del c
         for kv in ("f32", "f16"):
             for L in (8192, 131072):
-                specs.append(lambda kv=kv, L=L: synthetic.latent_decode(L, kv, seed=3000 + L))
+                c = synthetic.latent_decode(L, kv, seed=3000 + L)
+                r, _, _ = measure(c, rs, rw, 0, flush)
+                rung(r)
+                if L == 131072:
+                    rung(measure_project(c, rs, rw, "bf16", 128, flush))
+                    if not no_cpu:  # eight of the 96 heads
+                        oracle_samples.append(cpu_oracle_sample(c, [(0, h) for h in range(8)],
+                                                                r["bytes_call"]))
+                del c
         for kv in ("f32", "f16"):  # sparse: top-2048 rows of a 131,072-row latent cache
-            specs.append(lambda kv=kv: synthetic.dsa_latent(2048, 131072, kv))
+            c = synthetic.dsa_latent(2048, 131072, kv)
+            r, _, _ = measure(c, rs, rw, 0, flush)
+            rung(r)
+            del c
         # several queries per sequence (query tiles)
-        qspecs = [lambda: synthetic.spec_verify(131072, 4, "f16"),
-                  lambda: synthetic.chunked_prefill(8192, 512, "f16"),
-                  lambda: synthetic.causal_block(2048, "f16")]
-        for mk in specs:
+        for mk in (lambda: synthetic.spec_verify(131072, 4, "f16"),
+                   lambda: synthetic.chunked_prefill(8192, 512, "f16"),
+                   lambda: synthetic.causal_block(2048, "f16")):
             c = mk()
-            small = c.kv_bytes() < MALL_FLUSH_BYTES  # could stay cached between calls
-            r, _, _ = measure(c, args.rung_steps, args.rung_warmup, 0, flush if small else None)
-            log(f"rung {r}")
-            rungs.append(r)
-            if c.kv_shared and int(c.seq_lens[0]) == 131072:
-                r = measure_project(c, args.rung_steps, args.rung_warmup, "bf16", 128, flush)
-                log(f"rung {r}")
-                rungs.append(r)
+            rung(measure_query_tiles(c, rs, rw, flush))
             del c
-        for mk in qspecs:
-            c = mk()
-            small = c.kv_bytes() < MALL_FLUSH_BYTES
-            r = measure_query_tiles(c, args.rung_steps, args.rung_warmup, flush if small else None)
-            log(f"rung {r}")
-            rungs.append(r)
-            del c
-        del flush
-        torch.cuda.empty_cache()
+    del flush
+    torch.cuda.empty_cache()
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not no_cpu:
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline(case, [(0, h) for h in range(case.num_q_heads)])
+        cpu["by_config"] = oracle_samples
         log(f"cpu baseline {cpu}")
 
     line = {
@@ -531,7 +616,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall_a, 4),
+        "ms_per_step": round(head_a["us_per_call"] / 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -542,26 +627,41 @@ def main():
                         f"head_dim 256, q f32, KV {args.kv}, context {args.seq_len}",
             "global_batch": 1, "seq_len": args.seq_len, "kv_dtype": args.kv,
             "n_splits": head_a["n_splits"], "chunk": head_a["chunk"],
-            "parallelism": "single GPU",
+            "parallelism": "single GPU", "timing": "cold calls (Infinity Cache evicted before each)",
         },
         "us_per_call": head_a["us_per_call"],
         "frac_of_peak": head_a["frac_of_peak"],
         "split_us": head_a["split_us"],
         "combine_us": head_a["combine_us"],
         "tokens_per_s_per_layer": head_a["tokens_per_s_per_layer"],
+        "warm": {"us_per_call": warm["us_per_call"], "frac_of_peak": warm["frac_of_peak"],
+                 "split_us": warm["split_us"]},
         "one_launch": {k: head_a[k] for k in ("one_launch_us_per_call", "one_launch_frac_of_peak",
                                              "one_launch_kernel_us")},
         "aa_noise_floor": round(aa_spread, 4),
         "bandwidth_control": control,
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "rungs": rungs,
+        "rungs": [brief(r) for r in rungs],
         "device": props.name,
         "cu_count": props.multi_processor_count,
     }
     if cpu:
         line["cpu_baseline_ratio"] = round(head_a["GBps"] / cpu["value"], 1)
-    print(json.dumps(line), flush=True)
+    print(json.dumps(line, separators=(",", ":")), flush=True)
+
+
+def brief(r):
+    """One rung as a short record for the final line (the full record went to stderr)."""
+    b = {"w": r["workload"], "S": r.get("n_splits"), "us": r["us_per_call"], "p10": r.get("us_p10")}
+    for src, dst in (("frac_of_peak", "frac"), ("split_us", "split_us"),
+                     ("split_frac_of_peak", "split_frac"), ("combine_us", "comb_us"),
+                     ("one_launch_us_per_call", "one_us"), ("mfma_frac", "mfma_frac"),
+                     ("TFLOPs", "TFLOPs"), ("combine_project_us", "cp_us")):
+        if src in r:
+            b[dst] = r[src]
+    b["cold"] = r.get("mall_flushed")
+    return b
 
 
 if __name__ == "__main__":

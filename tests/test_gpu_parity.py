@@ -264,21 +264,52 @@ def test_wide_group_peaky_heuristic_and_sweep():
 # ------------------------------------------------------------ contract checks
 
 
-def test_lds_does_not_depend_on_context_length():
+LDS_FAMILIES = {
+    # GQA vector split kernel
+    "9b-f32": lambda: synthetic.qwen9b_like(64, "f32", seed=1),
+    "9b-f16": lambda: synthetic.qwen9b_like(64, "f16", seed=1),
+    # decode on the query-tile kernel (wide f16 group, narrow bf16 heads)
+    "27b-f16-query-tile": lambda: synthetic.gqa_case("lds-27b", seq_lens=[64], num_q_heads=24,
+                                                     num_kv_heads=4, head_dim=256, kv_dtype="f16",
+                                                     seed=1),
+    "d64-bf16-query-tile": lambda: synthetic.gqa_case("lds-d64", seq_lens=[64], num_q_heads=8,
+                                                      num_kv_heads=8, head_dim=64, kv_dtype="bf16",
+                                                      seed=1),
+    # paged bf16 (the ragged batch's geometry)
+    "paged-bf16": lambda: synthetic.gqa_case("lds-paged", seq_lens=[64, 64], num_q_heads=32,
+                                             num_kv_heads=8, head_dim=128, q_dtype="bf16",
+                                             kv_dtype="bf16", layout="paged", seed=1),
+    # shared-latent kernels (FP32 MFMA, f16 MFMA)
+    "latent-f32": lambda: synthetic.latent_case("lds-l32", seq_len=64, kv_dtype="f32", seed=1,
+                                                scale=1.0 / 24.0),
+    "latent-f16": lambda: synthetic.latent_case("lds-l16", seq_len=64, kv_dtype="f16", seed=1,
+                                                scale=1.0 / 24.0),
+}
+
+
+@pytest.mark.parametrize("family", sorted(LDS_FAMILIES))
+def test_lds_does_not_depend_on_context_length(family):
     """Lecture 06 section 2: shared memory is O(key width + tile), never
-    O(context); the kernel a descriptor selects has one static LDS size."""
+    O(context). For each kernel family the kernel a descriptor selects, from
+    64 to 1,048,576 positions, uses at most 160 KB (one compute unit's LDS)
+    and at most two static sizes (short contexts may select a variant with
+    fewer rows or heads per workgroup), and the longest context uses exactly
+    the LDS of 131,072 positions."""
     from split_kv_flash_amd import attn_decode_kernel_info, attn_decode_plan
 
-    for kv in ("f32", "f16"):
-        case = synthetic.qwen9b_like(64, kv, seed=1)
-        call = decode_call(case, to_device(case))
-        seen = set()
-        for L in (64, 4096, 131072, 262144):
-            call.desc.max_seq_len = L
-            info = attn_decode_kernel_info(call.desc, attn_decode_plan(call.desc, L, L, 256, 0))
-            assert info.block == 256 and info.lds_bytes <= 64 * 1024
-            seen.add(info.lds_bytes)
-        assert len(seen) == 1, seen
+    case = LDS_FAMILIES[family]()
+    call = decode_call(case, to_device(case))
+    seen = {}
+    for L in (64, 4096, 131072, 262144, 1048576):
+        call.desc.max_seq_len = L
+        if call.desc.layout == 1:  # paged: the table row must cover L positions
+            call.desc.max_pages_per_seq = -(-L // call.desc.page_size)
+        plan = attn_decode_plan(call.desc, L, L * case.batch, 256, 0)
+        info = attn_decode_kernel_info(call.desc, plan)
+        assert info.block >= 64 and 0 < info.lds_bytes <= 160 * 1024, (L, info.lds_bytes)
+        seen[L] = info.lds_bytes
+    assert len(set(seen.values())) <= 2, seen
+    assert seen[1048576] == seen[131072] == seen[262144], seen
 
 
 @pytest.mark.parametrize("kv", ["f32", "f16"])  # f16 at width 64 runs on the query-tile kernel
