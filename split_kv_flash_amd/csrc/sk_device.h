@@ -158,6 +158,31 @@ __device__ __forceinline__ float xor32(float x) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(x)));
 }
 
+// The same combinations (a value with that of lane ^ 16, or of lane ^ 32)
+// through gfx950's v_permlane16_swap / v_permlane32_swap: VALU instructions,
+// where ds_swizzle and ds_bpermute take a round trip through the LDS
+// crossbar. With both operands x, permlane16_swap leaves row 2k's values in
+// rows 2k and 2k+1 of its first result and row 2k+1's in both rows of its
+// second; permlane32_swap does the same with the two 32-lane halves. Every
+// lane then combines its own value with its partner's, in one order or the
+// other (max and + are commutative, so both lanes get the same bits).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over the RL consecutive lanes that hold one KV row (RL in {16, 32, 64});
 // every lane of the group receives the total.
 template <int RL>

@@ -348,6 +348,63 @@ def test_latent_matches_oracle(kv, L):
     free()
 
 
+def _latent_batch(name, lens, cap, hq, seed):
+    """Sequences of one latent geometry stacked into a batch (f16 cache, NaN
+    rows past each length)."""
+    import dataclasses
+
+    parts = [synthetic.latent_case(f"{name}-{i}", seq_len=L, kv_dtype="f16", num_q_heads=hq,
+                                   capacity=cap, seed=seed + i, scale=1.0 / 24.0)
+             for i, L in enumerate(lens)]
+    return dataclasses.replace(parts[0], name=name, batch=len(lens),
+                               q=np.concatenate([p.q for p in parts]),
+                               k=np.concatenate([p.k for p in parts]),
+                               seq_lens=np.asarray(lens, dtype=np.int32))
+
+
+@pytest.mark.parametrize("hq", [64, 96])
+@pytest.mark.parametrize("lens,S", [((4097,), 130), ((20000,), 150), ((5000, 300), 129),
+                                    ((33, 2000), 200)])
+def test_latent_f16_register_blocked_kernel(hq, lens, S):
+    """64 and 96 f16 heads with more than 128 (split, sequence) pairs run the
+    register-blocked kernel (8 waves of 512 threads; its partial scores meet
+    in LDS in a fixed order): one-tile slices with a one-row tail (4097 at
+    S = 130), slices of 134 rows (four tiles and a 6-row tail), a batch of
+    two whose short sequence leaves empty slices, and a batch whose first
+    sequence has fewer rows than one tile. NaN rows past every length."""
+    from split_kv_flash_amd import attn_decode_kernel_info
+
+    case = _latent_batch(f"lat16r-{hq}-{'-'.join(map(str, lens))}", list(lens), max(lens) + 7, hq,
+                         seed=7700 + hq + S)
+    out, lse, call = run_gpu(case, n_splits=S)
+    info = attn_decode_kernel_info(call.desc, call.plan)
+    assert info.block == 512 and (info.grid_x, info.grid_z) == (S, 1), (info.block, info.grid_x)
+    ref, rlse = oracle_out(case)
+    assert_parity(case, out, ref, tight=False, label=f"{case.name} S={S}")
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=ABS_GATE["f16"])
+    free()
+
+
+def test_latent_f16_register_blocked_kernel_dominant_key_in_second_tile():
+    """Position 32, the first row of the first slice's second tile, holds a
+    key that dominates every head's scores: each head returns that row's
+    values, so a slip in the partial-score exchange or in the head blocks'
+    weights shows."""
+    L, S = 8300, 129  # chunk 65: slice 0 is tiles [0, 32), [32, 64), [64, 65)
+    case = synthetic.latent_case("lat16r-dom", seq_len=L, kv_dtype="f32", seed=19, scale=1 / 24)
+    q = case.q[0, 0].astype(np.float64)
+    case.q[0, :] = case.q[0, 0]
+    row = q / np.linalg.norm(q) * 24 * 30 / np.linalg.norm(q)  # score ~ 30
+    case.k[0, 32, 0] = row.astype(np.float32)
+    case.k = case.k.astype(np.float16)
+    case.kv_dtype = "f16"
+    out, _, call = run_gpu(case, n_splits=S)
+    ref, _ = oracle_out(case)
+    assert_parity(case, out, ref, tight=False, label="latent f16 dominant, register-blocked")
+    for h in (0, 17, 50, 95):
+        np.testing.assert_allclose(out[0, h], ref[0, h], rtol=0, atol=ABS_GATE["f16"])
+
+
 @pytest.mark.parametrize("kv", ["f32", "f16"])
 @pytest.mark.parametrize("L,S", [(1, 1), (1, 8), (33, 2), (1000, 3), (1000, 7)])
 def test_latent_explicit_splits_and_padding(kv, L, S):
