@@ -183,13 +183,18 @@ sk_status_t attn_decode_plan(const sk_desc_t* desc, int32_t max_seq_len, int64_t
 
 /* Bytes of workspace a call with (desc, plan) needs; 0 if the pair is invalid.
  * Layout (f32, each section starting at a multiple of 256 bytes):
- *   acc [batch][num_q_heads][n_splits][head_dim_v]   un-normalised accumulators
- *   m   [batch][num_q_heads][n_splits]               slice maximum of s_j (natural-log units)
+ *   acc [batch][num_q_heads][n_splits][head_dim_v]   sum over the slice of exp(s_j - m) V_j
+ *   m   [batch][num_q_heads][n_splits]               the slice's reference score (natural-log
+ *                                                    units), -inf for an empty slice
  *   l   [batch][num_q_heads][n_splits]               sum over the slice of exp(s_j - m)
  *   cnt [batch][num_kv_heads] uint32                 completion counters of
  *                                                    attn_decode_one_launch
  * (issue #3725 design note section 2: partials of (m, s, acc[D]) per query head and split,
- * acc left un-normalised.) */
+ * acc left un-normalised.) m is the slice maximum of s_j, except on the f16 shared-latent
+ * kernel for 64 and 96 heads at more than 128 (split, sequence) pairs, whose m can lie up to
+ * 8 ln 2 below it (it moves only when a tile's maximum exceeds it by more than that, which
+ * spares rescaling the accumulators); the combine and the result are the same for any m
+ * that l and acc are taken against. */
 size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan);
 
 /* Split kernel: writes the partial triple of every (b, h, split) into `workspace`.
