@@ -187,8 +187,10 @@ sk_status_t attn_decode_plan(const sk_desc_t* desc, int32_t max_seq_len, int64_t
  *   m   [batch][num_q_heads][n_splits]               the slice's reference score (natural-log
  *                                                    units), -inf for an empty slice
  *   l   [batch][num_q_heads][n_splits]               sum over the slice of exp(s_j - m)
- *   cnt [batch][num_kv_heads] uint32                 completion counters of
- *                                                    attn_decode_one_launch
+ *   cnt [batch][num_kv_heads][1 + ceil(n_splits/16)] uint32
+ *                                                    completion counters of
+ *                                                    attn_decode_one_launch (chunks done,
+ *                                                    then splits done per chunk of 16)
  * (issue #3725 design note section 2: partials of (m, s, acc[D]) per query head and split,
  * acc left un-normalised.) m is the slice maximum of s_j, except on the f16 shared-latent
  * kernel for 64 and 96 heads at more than 128 (split, sequence) pairs, whose m can lie up to
@@ -284,15 +286,18 @@ sk_status_t attn_decode_no_alloc(const sk_desc_t* desc, const sk_plan_t* plan, c
 
 /* The whole decode call in one launch (separate K and V only), same arguments and results
  * as attn_decode. Every workgroup holding positions writes its partial to the workspace
- * with device-scope stores, waits for them to complete and increments cnt[b][g] (a
- * device-scope atomic); the workgroup whose increment completes the ceil(L_b/chunk)
- * partials of (b, g) reads them back with device-scope loads and writes out and lse of
- * the group's query heads (Lecture 06 section 2: M = max m_i, l = sum l_i exp(m_i - M),
- * out = sum acc_i exp(m_i - M) / l), then sets cnt[b][g] back to zero. No workgroup waits
- * for another. Workgroups of empty slices exit at once and write no workspace row. A
- * length outside [1, min(max_seq_len, n_splits*chunk)] makes that sequence's out and lse
- * NaN. The counter section must be zero when the call starts (attn_decode_workspace_init);
- * a call that completes leaves it zero. Calls that share a workspace must not overlap in
+ * with device-scope stores, waits for them to complete and counts it (device-scope
+ * atomics). The merge (Lecture 06 section 2: M = max m_i, l = sum l_i exp(m_i - M),
+ * out = sum acc_i exp(m_i - M) / l) is a two-level tree over the n = ceil(L_b/chunk)
+ * non-empty splits of (b, g): the workgroup whose count completes a chunk of 16
+ * consecutive splits reads the chunk's partials back with device-scope loads and writes
+ * their merge into the chunk's first partial row; the one whose count completes the
+ * chunks merges those rows into out and lse of the group's query heads (with n <= 16 the
+ * chunk's merge goes to out directly). Each count is set back to zero by its last
+ * arrival. No workgroup waits for another. Workgroups of empty slices exit at once and
+ * write no workspace row. A length outside [1, min(max_seq_len, n_splits*chunk)] makes
+ * that sequence's out and lse NaN. The counter section must be zero when the call starts
+ * (attn_decode_workspace_init); a call that completes leaves it zero. Calls that share a workspace must not overlap in
  * time (for example on two streams). The descriptors attn_decode_splitk serves with the
  * query-tile kernel run its one-launch form (the same count and merge); the others the
  * vector split kernel's.

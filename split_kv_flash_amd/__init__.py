@@ -121,6 +121,15 @@ def _stream_handle(stream) -> int:
     return s.cuda_stream
 
 
+# Splits per chunk of the one-launch decode's merge tree (kMergeChunk in the
+# library), and the counter words it keeps per (sequence, KV head).
+MERGE_CHUNK = 16
+
+
+def merge_counter_words(n_splits: int) -> int:
+    return 1 + (n_splits + MERGE_CHUNK - 1) // MERGE_CHUNK
+
+
 class DecodeCall:
     """One decode-attention call shape: descriptor, plan, workspace, outputs.
 
@@ -211,7 +220,9 @@ class DecodeCall:
         return out, self.lse
 
     def counters(self):
-        """View of the workspace's completion counters, int32 [B][Hkv]."""
+        """View of the workspace's completion counters, int32 [B][Hkv][W]: per
+        (sequence, KV head) the one-launch merge tree's count of finished
+        chunks, then one count per chunk of MERGE_CHUNK splits."""
         import torch
 
         d, p = self.desc, self.plan
@@ -221,8 +232,9 @@ class DecodeCall:
             return (x + 255) // 256 * 256
 
         off = a256(rows * d.head_dim_v * 4) + 2 * a256(rows * 4)
-        n = d.batch * d.num_kv_heads
-        return self.workspace[off:off + 4 * n].view(torch.int32).view(d.batch, d.num_kv_heads)
+        w = merge_counter_words(p.n_splits)
+        n = d.batch * d.num_kv_heads * w
+        return self.workspace[off:off + 4 * n].view(torch.int32).view(d.batch, d.num_kv_heads, w)
 
     def partials(self):
         """Views of the workspace: acc [B][Hq][S][Dv], m and l [B][Hq][S] (f32)."""

@@ -157,7 +157,8 @@ WsLayout ws_layout(const sk_desc_t& d, const sk_plan_t& p) {
   w.m_off = align256(rows * d.head_dim_v * sizeof(float));
   w.l_off = w.m_off + align256(rows * sizeof(float));
   w.cnt_off = w.l_off + align256(rows * sizeof(float));
-  w.total = w.cnt_off + align256((size_t)d.batch * d.num_kv_heads * sizeof(uint32_t));
+  w.total = w.cnt_off + align256((size_t)d.batch * d.num_kv_heads * merge_counter_words(p.n_splits) *
+                                  sizeof(uint32_t));
   return w;
 }
 
@@ -538,7 +539,8 @@ sk_status_t attn_decode_workspace_init(const sk_desc_t* desc, const sk_plan_t* p
     return fail(SK_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes,
                 w.total);
   uint32_t* cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + w.cnt_off);
-  sk::zero_words_launch(cnt, (size_t)desc->batch * desc->num_kv_heads, stream);
+  sk::zero_words_launch(cnt, (size_t)desc->batch * desc->num_kv_heads * sk::merge_counter_words(plan->n_splits),
+                       stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return fail(SK_ERR_LAUNCH, "workspace init launch failed: %s", hipGetErrorString(e));

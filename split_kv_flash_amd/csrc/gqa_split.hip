@@ -515,19 +515,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     // every other partial was complete before its count: it reads them all.
     __shared__ int s_last;
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
     const int n = (int)((L + (int64_t)a.chunk - 1) / a.chunk);
-    if (tid == 0) {
-      uint32_t* cnt = a.counters + (int64_t)b * Hkv + g;
-      const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = prev + 1 == (uint32_t)n;
-      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = last;
-    }
-    __syncthreads();
-    if (!s_last) return;
+    uint32_t* cnt = a.counters + ((int64_t)b * Hkv + g) * merge_counter_words(a.S);
     // The epilogue's LDS is free again: it holds the merge's m and l values.
-    merge_group<D, Sh::kThreads, NW * D / 2>(a, G, b, h0, n, tid, &s_acc[0][0][0]);
+    merge_tree<D, Sh::kThreads, NW * D / 2>(a, G, b, h0, split, n, cnt, tid, &s_last, &s_acc[0][0][0]);
   }
 }
 

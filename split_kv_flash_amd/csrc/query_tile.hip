@@ -479,24 +479,15 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
     // word would take width 64 past 40 KB and four workgroups per CU.
     int* s_last = reinterpret_cast<int*>(&s_sc[0][0][0]);
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
     const int n = (int)((L + (int64_t)a.chunk - 1) / a.chunk);
-    if (tid == 0) {
-      uint32_t* cnt = a.counters + (int64_t)b * (a.Hq / a.G) + g;
-      const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = prev + 1 == (uint32_t)n;
-      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      *s_last = last;
-    }
-    __syncthreads();
-    if (!*s_last) return;
+    uint32_t* cnt = a.counters + ((int64_t)b * (a.Hq / a.G) + g) * merge_counter_words(a.S);
     static_assert(2 * 8 * kQtMergePass * 4 <= (int)sizeof(s_kv), "m, l of 8 heads per pass fit the ring");
     // Sixteen accumulator rows in flight per chunk at width 256 (one
     // workgroup per CU either way), four below it, which keeps the merge
     // within the registers of the resident count (16 took 200 at width 64).
     constexpr int MK = D >= 256 ? 16 : 4;
-    merge_group<D, 256, kQtMergePass, MK>(a, a.G, b, g * a.G, n, tid,
-                                          reinterpret_cast<float*>(&s_kv[0][0][0]));
+    merge_tree<D, 256, kQtMergePass, MK>(a, a.G, b, g * a.G, split, n, cnt, tid, s_last,
+                                         reinterpret_cast<float*>(&s_kv[0][0][0]));
   }
 }
 

@@ -8,9 +8,16 @@
 
 namespace sk {
 
+// Splits per chunk of the one-launch decode's merge tree, and the counter
+// words it keeps per (sequence, KV head): chunks done, then one per chunk.
+constexpr int kMergeChunk = 16;
+inline constexpr int merge_counter_words(int n_splits) {
+  return 1 + (n_splits + kMergeChunk - 1) / kMergeChunk;
+}
+
 // Workspace section offsets (bytes), each a multiple of 256. The counter
-// section (one uint32 per (sequence, KV head)) is used by the one-launch
-// decode only.
+// section (merge_counter_words(S) uint32 per (sequence, KV head)) is used by
+// the one-launch decode only.
 struct WsLayout {
   size_t acc_off, m_off, l_off, cnt_off, total;
 };

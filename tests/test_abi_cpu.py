@@ -183,7 +183,9 @@ def test_workspace_bytes_follow_the_documented_layout():
         p = B.SkPlan(s, 64)
         rows = bsz * hq * s
         a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-        counters = a256(bsz * d.num_kv_heads * 4)  # one uint32 per (sequence, KV head)
+        # per (sequence, KV head): the merge tree's chunk count, then one count per
+        # chunk of 16 splits
+        counters = a256(bsz * d.num_kv_heads * (1 + (s + 15) // 16) * 4)
         want = a256(rows * dv * 4) + a256(rows * 4) + a256(rows * 4) + counters
         assert B.attn_decode_workspace_bytes(d, p) == want
 
