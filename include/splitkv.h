@@ -192,11 +192,11 @@ sk_status_t attn_decode_plan(const sk_desc_t* desc, int32_t max_seq_len, int64_t
  *                                                    attn_decode_one_launch (chunks done,
  *                                                    then splits done per chunk of 16)
  * (issue #3725 design note section 2: partials of (m, s, acc[D]) per query head and split,
- * acc left un-normalised.) m is the slice maximum of s_j, except on the f16 shared-latent
- * kernel for 64 and 96 heads at more than 128 (split, sequence) pairs, whose m can lie up to
- * 8 ln 2 below it (it moves only when a tile's maximum exceeds it by more than that, which
- * spares rescaling the accumulators); the combine and the result are the same for any m
- * that l and acc are taken against. */
+ * acc left un-normalised.) m is the slice maximum of s_j, except on the shared-latent
+ * kernels of f32 caches and, for 64 and 96 heads at more than 128 (split, sequence) pairs,
+ * of f16 caches, whose m can lie up to 8 ln 2 below it (it moves only when a tile's maximum
+ * exceeds it by more than that, which spares rescaling the accumulators); the combine and
+ * the result are the same for any m that l and acc are taken against. */
 size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan);
 
 /* Split kernel: writes the partial triple of every (b, h, split) into `workspace`.

@@ -932,7 +932,10 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   // Running max (base 2) and normaliser of head head0 + l16 (replicated over
   // the four quarters); accumulators acc[4*u + e] hold heads 4*lq + i (items)
   // at column 128*dq + 64*u + 4*l16 + e.
-  float m = -INFINITY, l = 0.0f;
+  // Running max (base 2) of head head0 + l16, replicated over the four
+  // quarters; ll is this lane's share of the normaliser (its positions of
+  // every tile), summed over the quarters at the end.
+  float m = -INFINITY, ll = 0.0f;
   float4_t acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -973,93 +976,129 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   wait_vm_lgkm0<0>();  // both tiles and the query block landed
   raw_barrier();
 
-  // Software pipeline: iteration i computes the output product of tile i-1
-  // (weights pp from the previous softmax) and the partial scores of tile i;
-  // one barrier then publishes the partials (double-buffered by parity) and
-  // tile i+1; after it tile i+2 is requested into the buffer tile i-1 used and
-  // the softmax of tile i runs.
-  float pp[4] = {0.f, 0.f, 0.f, 0.f};
-  float alp = 1.0f;
-  bool movedp = false;
-  for (int i = 0;; ++i) {
-    // ---- output of tile i-1: acc = alp * acc + P[16 heads][16 positions] x V ----
-    if (i > 0) {
-      const float* prv = s_c + ((i - 1) % 3) * TSTRIDE;
-      if (__any(movedp)) {
-        // Accumulator item e is head 4*lq + e, whose factor lane 4*lq + e holds.
+  // Partial scores S^T of the tile in `cur` over this wave's 144 columns: nine
+  // steps of four MFMAs, each step's operands read from LDS one step ahead.
+  // After step t's MFMAs, stage(t) of the previous tile's softmax runs (a
+  // constant t after unrolling), so the softmax's VALU and cross-lane work
+  // issues while the matrix pipe works through the score products.
+  // Four accumulators (one per column of a 16-byte read) keep the products
+  // of a step independent, so they issue back to back; they are summed at the
+  // end in a fixed order.
+  auto scores = [&](const float* cur, auto&& stage) -> float4_t {
+    float4_t sp[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float ae = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * lq + e) << 2, __float_as_int(alp)));
-#pragma unroll
-          for (int c = 0; c < 8; ++c) acc[c][e] *= ae;
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const float4_t v4 = *reinterpret_cast<const float4_t*>(prv + vb[t] + 64 * u);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[4 * u + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(pp[t], v4[e], acc[4 * u + e], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    if (i == ntiles) break;
-    const int64_t tb = start + (int64_t)i * kT32;
-    const int rel = (int)(end - tb);  // positions of this tile before the end (> 0)
-    const float* cur = s_c + (i % 3) * TSTRIDE;
-
-    // ---- partial scores S^T over this wave's 144 columns ----
-    float4_t sp = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 4; ++u) sp[u] = float4_t{0.f, 0.f, 0.f, 0.f};
     float4_t an = *reinterpret_cast<const float4_t*>(cur + sb[0]);
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
       const float4_t av = an;
       if (t + 1 < KT) an = *reinterpret_cast<const float4_t*>(cur + sb[(t + 1) & 3] + 64 * ((t + 1) >> 2));
 #pragma unroll
-      for (int u = 0; u < 4; ++u) sp = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], qv[t][u], sp, 0, 0, 0);
+      for (int u = 0; u < 4; ++u) sp[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], qv[t][u], sp[u], 0, 0, 0);
+      stage(t);
       __builtin_amdgcn_sched_barrier(0);
     }
-    const int par = i & 1;
-    s_sx[par][wave][lane] = sp;
-    // Tile i+1 (requested one iteration ago, or in the prologue) is the only
-    // tile load still in flight: wait for it, then publish it and the partials.
-    wait_vm_lgkm0<0>();
-    raw_barrier();
-    // Every wave has finished the output product of tile i-1: its buffer takes
-    // tile i+2 now, so the load overlaps the softmax as well.
-    issue_tile((i + 2) % 3, tb + 2 * kT32);
+    return (sp[0] + sp[1]) + (sp[2] + sp[3]);
+  };
 
-    // ---- full scores (the block's four partials in a fixed order), softmax ----
+  // Software pipeline, one barrier per tile. Before iteration i the barrier
+  // has published the partial scores of tile i (double-buffered by parity)
+  // and tile i+1, and tile i+2 is in flight. Iteration i computes the partial
+  // scores of tile i+1 with the softmax of tile i interleaved, then the output
+  // product of tile i (acc = alpha * acc + P[16 heads][16 positions] x V);
+  // after the next barrier tile i+3 goes into tile i's buffer.
+  {
+    const float4_t sp0 = scores(s_c, [](int) {});
+    s_sx[0][wave][lane] = sp0;
+    raw_barrier();
+    if (start + 2 * kT32 < end) issue_tile(2, start + 2 * kT32);
+  }
+  for (int i = 0;; ++i) {
+    const int par = i & 1;
+    const bool next = i + 1 < ntiles;
+    const int rel = (int)(end - (start + (int64_t)i * kT32));  // positions of tile i before the end (> 0)
+    uint32_t badt = 0;  // rows of tile i whose index lies outside the pool
+    if constexpr (IDX) badt = (i % 3 == 0) ? bad0 : ((i % 3 == 1) ? bad1 : bad2);
+
+    // ---- softmax of tile i (the block's four partials summed in a fixed order) ----
     const float4_t x0 = s_sx[par][hb * 4 + 0][lane], x1 = s_sx[par][hb * 4 + 1][lane];
     const float4_t x2 = s_sx[par][hb * 4 + 2][lane], x3 = s_sx[par][hb * 4 + 3][lane];
-    float mx = -INFINITY;
-    uint32_t badt = 0;  // rows of this tile whose index lies outside the pool
-    if constexpr (IDX) badt = (i % 3 == 0) ? bad0 : ((i % 3 == 1) ? bad1 : bad2);
+    float pp[4], lmx = -INFINITY, mu = 0.0f, alp = 1.0f;
+    bool moved = false;
+    auto stage = [&](int t) {
+      if (t == 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pp[e] = 4 * lq + e < rel ? (x0[e] + x1[e]) + (x2[e] + x3[e]) : -INFINITY;
-      if constexpr (IDX) pp[e] = ((badt >> (4 * lq + e)) & 1) ? __builtin_nanf("") : pp[e];
-      mx = fmaxf(mx, pp[e]);
-    }
-    mx = fmaxf(mx, xor16(mx));
-    mx = fmaxf(mx, xor32(mx));
-    const float mn = fmaxf(m, mx);
-    const float mu = (mn == -INFINITY) ? 0.0f : mn;
-    alp = fast_exp2(m - mu);
-    movedp = alp != 1.0f;
-    float ls = 0.0f;
+        for (int e = 0; e < 4; ++e) {
+          pp[e] = 4 * lq + e < rel ? (x0[e] + x1[e]) + (x2[e] + x3[e]) : -INFINITY;
+          if constexpr (IDX) pp[e] = ((badt >> (4 * lq + e)) & 1) ? __builtin_nanf("") : pp[e];
+          lmx = fmaxf(lmx, pp[e]);
+        }
+      } else if (t == 1) {
+        // m moves to the tile's maximum only when that exceeds it by more than
+        // kLazyMax (base 2): the weights stay below 2^kLazyMax. Most tiles keep
+        // m, which this lane's own four scores decide without any cross-lane
+        // step; only a wave where some lane sees a larger score finds the
+        // heads' maxima and rescales.
+        if (__any(lmx > m + kLazyMax)) {
+          const float mx = max_xor32(max_xor16(lmx));
+          const float mn = mx > m + kLazyMax ? mx : m;
+          alp = fast_exp2(m - ((mn == -INFINITY) ? 0.0f : mn));
+          ll *= alp;
+          m = mn;
+          moved = true;
+        }
+        mu = (m == -INFINITY) ? 0.0f : m;
+      } else if (t == 2) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pp[e] = fast_exp2(pp[e] - mu);
-      ls += pp[e];
+        for (int e = 0; e < 4; ++e) pp[e] = fast_exp2(pp[e] - mu);
+        ll += (pp[0] + pp[1]) + (pp[2] + pp[3]);
+      }
+    };
+    if (next) {
+      const float4_t sp = scores(s_c + ((i + 1) % 3) * TSTRIDE, stage);
+      s_sx[par ^ 1][wave][lane] = sp;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 3; ++t) stage(t);
     }
-    ls += xor16(ls);
-    ls += xor32(ls);
-    l = fmaf(l, alp, ls);
-    m = mn;
+
+    // ---- output of tile i ----
+    const float* prv = s_c + (i % 3) * TSTRIDE;
+    if (moved) {
+      // Accumulator item e is head 4*lq + e, whose factor lane 4*lq + e holds.
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ae = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * lq + e) << 2, __float_as_int(alp)));
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c][e] *= ae;
+      }
+    }
+    // Value operands read one step ahead of their products.
+    float4_t vn[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) vn[u] = *reinterpret_cast<const float4_t*>(prv + vb[0] + 64 * u);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float4_t v0 = vn[0], v1 = vn[1];
+      if (t + 1 < 4) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) vn[u] = *reinterpret_cast<const float4_t*>(prv + vb[t + 1] + 64 * u);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(pp[t], v0[e], acc[e], 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(pp[t], v1[e], acc[4 + e], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (!next) break;
+    // Tile i+2 (requested after the previous barrier) is the only tile load
+    // in flight: wait for it, then publish it and the partials of tile i+1.
+    wait_vm_lgkm0<0>();
+    raw_barrier();
+    // Every wave has finished the output product of tile i: its buffer takes
+    // tile i+3.
+    const int64_t tn = start + (int64_t)(i + 3) * kT32;
+    if (tn < end) issue_tile(i % 3, tn);
   }
   // Drain the tile loads still in flight before the workgroup can retire.
   wait_vm_lgkm0<0>();
@@ -1074,6 +1113,7 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
       *reinterpret_cast<float4*>(a.ws_acc + (ws0 + (int64_t)head * a.S) * kLatDv + col) =
           make_float4(acc[4 * u + 0][i], acc[4 * u + 1][i], acc[4 * u + 2][i], acc[4 * u + 3][i]);
     }
+  const float l = sum_xor32(sum_xor16(ll));
   if (dq == 0 && lq == 0) {
     a.ws_m[ws0 + (int64_t)(head0 + l16) * a.S] = m * kLn2;
     a.ws_l[ws0 + (int64_t)(head0 + l16) * a.S] = l;

@@ -447,6 +447,9 @@ def test_latent_split_partials_match_the_oracle_schedule(kv):
         case.q, case.k_rows(), None, case.seq_lens, case.scale, call.plan.chunk,
         call.plan.n_splits, q_dtype=case.q_dtype, kv_dtype=case.kv_dtype, v_cols=512)
     tol = 2e-5 if kv == "f32" else 2e-3
-    np.testing.assert_allclose(m, rm, rtol=0, atol=tol)
-    np.testing.assert_allclose(l, rl, rtol=tol, atol=0)
+    # m is the slice maximum, or (where a kernel moves it lazily) at most 8 ln 2
+    # below it; l and acc are taken against that m, so the slice's log-sum-exp
+    # m + ln l and its normalised output acc / l are fixed whatever m is.
+    assert np.all(m <= rm + tol) and np.all(m >= rm - 8 * np.log(2) - tol)
+    np.testing.assert_allclose(m + np.log(l), rm + np.log(rl), rtol=0, atol=tol)
     assert np.abs(acc / l[..., None] - racc / rl[..., None]).max() <= tol
