@@ -228,9 +228,9 @@ def pct(x, q):
 
 def measure(case, steps, warmup, n_splits=0, flush=None, one_launch=True, tensors=None):
     """Times one workload. The call is ``attn_decode`` (the split kernel, then
-    the combine kernel); for separate K and V the one-launch variant
-    (``attn_decode_one_launch``, whose last workgroups merge) is timed beside
-    it, and each kernel alone. With ``flush`` every timed call and launch is
+    the combine kernel); the one-launch variant (``attn_decode_one_launch``:
+    the last workgroups merge, or for a shared latent every workgroup after a
+    grid barrier) is timed beside it, and each kernel alone. With ``flush`` every timed call and launch is
     cold (the Infinity Cache evicted before it, outside the event pair)."""
     import torch
     from synthetic.torch_io import to_device
@@ -256,7 +256,7 @@ def measure(case, steps, warmup, n_splits=0, flush=None, one_launch=True, tensor
         "tokens_per_s_per_layer": round(case.batch * 1e6 / us, 1),
         "mall_flushed": flush is not None,
     }
-    if one_launch and not case.kv_shared:
+    if one_launch:
         one, _ = time_calls(call.decode_one_launch, steps, warmup, flush)
         fused = kernel_avg(call.decode_one_launch, steps, flush)
         us1 = median(one) * 1e3

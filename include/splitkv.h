@@ -284,8 +284,8 @@ sk_status_t attn_decode_no_alloc(const sk_desc_t* desc, const sk_plan_t* plan, c
                                  const int32_t* seq_lens, float* out, float* lse,
                                  hipStream_t stream);
 
-/* The whole decode call in one launch (separate K and V only), same arguments and results
- * as attn_decode. Every workgroup holding positions writes its partial to the workspace
+/* The whole decode call in one launch, same arguments and results as attn_decode.
+ * Separate K and V: every workgroup holding positions writes its partial to the workspace
  * with device-scope stores, waits for them to complete and counts it (device-scope
  * atomics). The merge (Lecture 06 section 2: M = max m_i, l = sum l_i exp(m_i - M),
  * out = sum acc_i exp(m_i - M) / l) is a two-level tree over the n = ceil(L_b/chunk)
@@ -301,7 +301,18 @@ sk_status_t attn_decode_no_alloc(const sk_desc_t* desc, const sk_plan_t* plan, c
  * time (for example on two streams). The descriptors attn_decode_splitk serves with the
  * query-tile kernel run its one-launch form (the same count and merge); the others the
  * vector split kernel's.
- * Errors: as attn_decode; SK_ERR_UNSUPPORTED for a shared latent. */
+ * Shared latent (kv_shared): a split's partial row covers every head (96 x 512 floats
+ * for 96 heads), far more than one workgroup merges quickly, so the latent split kernel
+ * is started as a cooperative launch (every workgroup resident at once): each workgroup
+ * writes its partial with device-scope stores and meets the others at a grid barrier on
+ * the first two words of the counter section (arrivals, then departures: the last
+ * workgroup to depart sets both back to zero); every workgroup then merges its share of
+ * the (sequence, head, half of the value columns) rows, reading the non-empty splits
+ * back with device-scope loads. The barrier's wait is bounded (about 2^24 sleeps) so
+ * that no launch can hang on it. The same zero-counter contract holds.
+ * Errors: as attn_decode; SK_ERR_UNSUPPORTED for a shared latent whose grid (n_splits x
+ * batch x workgroups per split) does not fit on the device at once; SK_ERR_LAUNCH when
+ * the runtime refuses the cooperative launch. */
 sk_status_t attn_decode_one_launch(const sk_desc_t* desc, const sk_plan_t* plan, const void* q,
                                    const void* k, const void* v, const int32_t* block_table,
                                    const int32_t* seq_lens, void* workspace,

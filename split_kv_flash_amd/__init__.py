@@ -195,8 +195,9 @@ class DecodeCall:
         return self.out, self.lse
 
     def decode_one_launch(self, stream=None, with_lse: bool = True):
-        """The whole call in one launch (``attn_decode_one_launch``; separate K
-        and V only)."""
+        """The whole call in one launch (``attn_decode_one_launch``; a shared
+        latent runs as a cooperative launch with a grid barrier before the
+        merge)."""
         attn_decode_one_launch(self.desc, self.plan, self.q, self.k, self.v, self.block_table,
                                self.seq_lens, self.workspace, self.ws_bytes, self.out,
                                self.lse if with_lse else None, _stream_handle(stream))

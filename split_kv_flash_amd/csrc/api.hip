@@ -653,8 +653,6 @@ sk_status_t attn_decode_one_launch(const sk_desc_t* desc, const sk_plan_t* plan,
   sk_status_t s = prepare_split(desc, plan, q, k, v, block_table, seq_lens, workspace,
                                 workspace_bytes, true, &a);
   if (s != SK_OK) return s;
-  if (desc->kv_shared)
-    return fail(SK_ERR_UNSUPPORTED, "the one-launch decode serves separate K and V only");
   if (!out) return fail(SK_ERR_INVALID_ARG, "out must be non-NULL");
   if ((uintptr_t)out % 16) return fail(SK_ERR_INVALID_ARG, "out must be 16-byte aligned");
   a.stream = stream;
@@ -662,8 +660,13 @@ sk_status_t attn_decode_one_launch(const sk_desc_t* desc, const sk_plan_t* plan,
   a.out = out;
   a.lse = lse;
   int grid[3], block;
-  s = sk::decode_on_query_tiles(*desc) ? sk::query_tile_launch(one_query_tiles(a), true, nullptr, grid, &block)
-                                       : sk::gqa_split_launch(a, true, nullptr, grid, &block);
+  s = split_dispatch(a, true, nullptr, grid, &block);
+  if (s == SK_ERR_UNSUPPORTED && desc->kv_shared)
+    return fail(s, "the one-launch latent decode needs its %d x %d x %d workgroups resident at once "
+                   "(a cooperative launch): use fewer splits", grid[0], grid[1], grid[2]);
+  if (s == SK_ERR_HIP) return fail(s, "could not query the device for the cooperative launch");
+  if (s == SK_ERR_LAUNCH)
+    return fail(s, "one-launch latent decode failed to launch: %s", hipGetErrorString(hipGetLastError()));
   if (s != SK_OK) return fail(s, "no split kernel for this descriptor");
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)

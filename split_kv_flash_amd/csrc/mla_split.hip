@@ -24,6 +24,7 @@
 //     per split.
 #include "sk_device.h"
 #include "sk_internal.h"
+#include "sk_merge.h"
 
 namespace sk {
 
@@ -49,8 +50,45 @@ struct MlaArgs {
   int32_t max_idx;
   int64_t num_rows;
   int32_t nt;  // 1: this workgroup is its rows' only reader (non-temporal tile loads)
+  // One-launch decode (the FUSED kernels): partials go out with device-scope
+  // stores, then every workgroup meets at a grid barrier (arrival and
+  // departure counts in counters[0] and [1]) and merges a share of the
+  // (sequence, head) rows into out and lse.
+  uint32_t* counters;
+  float* out;
+  float* lse;
 };
 
+// A partial value: a device-scope store where workgroups on other XCDs read it
+// back after the grid barrier (the one-launch decode with more than one
+// split), a plain store otherwise.
+__device__ __forceinline__ void put_partial(float* p, float v, bool dev) {
+  if (dev)
+    st_dev(p, v);
+  else
+    *p = v;
+}
+
+// The one-launch tail of every latent split kernel; heads [h0, h0 + H) of
+// sequence blockIdx.y are this workgroup's. With one split a workgroup's own
+// partial is all its heads have: it merges them itself, with no grid barrier
+// (its plain stores have completed after the wait and the workgroup barrier). Otherwise every
+// workgroup meets the others at the grid barrier and merges a share of all
+// rows (s_lds: the kernel's tile buffers, free once the barrier has passed).
+template <int NT>
+__device__ __forceinline__ void latent_fused_tail(const MlaArgs& a, float* s_lds, int h0, int H) {
+  if (a.S == 1) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int t = ((int)blockIdx.y * a.Hq + h0) * 2;
+    latent_merge_by_wave<1, 0>(a, t, t + 2 * H, __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), NT / 64);
+    return;
+  }
+  const uint32_t n = gridDim.x * gridDim.y * gridDim.z;
+  grid_arrive_and_wait(a.counters, n);
+  latent_grid_merge<NT>(a, (int)gridDim.y, s_lds);
+  grid_depart(a.counters, a.counters + 1, n);
+}
 // Index-list tiles (IDX kernels): lane r < T of every wave holds the pool row
 // of tile row r (positions past the split's end repeat the last one), loaded
 // one tile ahead of the tile's own loads. A row outside the pool is replaced
@@ -154,7 +192,7 @@ __host__ __device__ constexpr int mla16_blocks(int Hq) { return Hq == 128 ? 4 : 
 __host__ __device__ constexpr int mla16_groups(int Hq) { return Hq / (16 * mla16_blocks(Hq)); }
 constexpr int64_t kHalveHeadsAt = 128;  // (split, sequence) pairs, half of MI355X's CUs
 
-template <int NHB, bool IDX>
+template <int NHB, bool IDX, bool FUSED>
 __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
   constexpr int H = NHB * 16;
   constexpr int NW = 2 * NHB;
@@ -190,6 +228,12 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
   const int64_t ws0 = ((int64_t)b * a.Hq + h0) * a.S + split;
 
   if (start >= end) {
+    // One-launch decode: an empty slice takes no part in the merge, but its
+    // workgroup still meets the others at the grid barrier and merges.
+    if constexpr (FUSED) {
+      latent_fused_tail<NW * 64>(a, reinterpret_cast<float*>(s_c), h0, H);
+      return;
+    }
     for (int idx = tid; idx < H * kLatDv; idx += NW * 64) {
       const int h = idx / kLatDv, e = idx - (idx / kLatDv) * kLatDv;
       a.ws_acc[(ws0 + (int64_t)h * a.S) * kLatDv + e] = 0.0f;
@@ -410,12 +454,13 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
     for (int e = 0; e < 4; ++e) {
       const int head = hb * 16 + lq * 4 + e;
       const int col = dh * 256 + cb * 16 + l16;
-      a.ws_acc[(ws0 + (int64_t)head * a.S) * kLatDv + col] = acc[cb][e];
+      put_partial(a.ws_acc + (ws0 + (int64_t)head * a.S) * kLatDv + col, acc[cb][e], FUSED && a.S > 1);
     }
   if (dh == 0 && lq == 0) {
-    a.ws_m[ws0 + (int64_t)(hb * 16 + l16) * a.S] = m * kLn2;
-    a.ws_l[ws0 + (int64_t)(hb * 16 + l16) * a.S] = l;
+    put_partial(a.ws_m + ws0 + (int64_t)(hb * 16 + l16) * a.S, m * kLn2, FUSED && a.S > 1);
+    put_partial(a.ws_l + ws0 + (int64_t)(hb * 16 + l16) * a.S, l, FUSED && a.S > 1);
   }
+  if constexpr (FUSED) latent_fused_tail<NW * 64>(a, reinterpret_cast<float*>(s_c), h0, H);
 }
 
 // ---------------------------------------------------------------------------
@@ -459,7 +504,7 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
 // are taken against before that value moves (weights stay below 2^8).
 constexpr float kLazyMax = 8.0f;
 
-template <int NB>
+template <int NB, bool FUSED>
 __global__ __launch_bounds__(512) void mla16r_split_kernel(MlaArgs a) {
   constexpr int GH = 16 * NB;                     // heads per group
   constexpr int H = 2 * GH;                       // heads per workgroup
@@ -497,6 +542,12 @@ __global__ __launch_bounds__(512) void mla16r_split_kernel(MlaArgs a) {
   const int64_t ws0 = (int64_t)b * a.Hq * a.S + split;
 
   if (start >= end) {
+    // One-launch decode: an empty slice takes no part in the merge, but its
+    // workgroup still meets the others at the grid barrier and merges.
+    if constexpr (FUSED) {
+      latent_fused_tail<NW * 64>(a, reinterpret_cast<float*>(s_c), 0, H);
+      return;
+    }
     for (int idx = tid; idx < H * kLatDv; idx += NW * 64) {
       const int h = idx / kLatDv, e = idx - (idx / kLatDv) * kLatDv;
       a.ws_acc[(ws0 + (int64_t)h * a.S) * kLatDv + e] = 0.0f;
@@ -789,13 +840,14 @@ __global__ __launch_bounds__(512) void mla16r_split_kernel(MlaArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int head = gh0 + 16 * hb + 4 * lq + e;
         const int col = 128 * c + 16 * cb + l16;
-        a.ws_acc[(ws0 + (int64_t)head * a.S) * kLatDv + col] = acc[hb][cb][e];
+        put_partial(a.ws_acc + (ws0 + (int64_t)head * a.S) * kLatDv + col, acc[hb][cb][e], FUSED && a.S > 1);
       }
   if (c < NB && lq == 0) {
     const int head = gh0 + 16 * c + l16;
-    a.ws_m[ws0 + (int64_t)head * a.S] = m * kLn2;
-    a.ws_l[ws0 + (int64_t)head * a.S] = l;
+    put_partial(a.ws_m + ws0 + (int64_t)head * a.S, m * kLn2, FUSED && a.S > 1);
+    put_partial(a.ws_l + ws0 + (int64_t)head * a.S, l, FUSED && a.S > 1);
   }
+  if constexpr (FUSED) latent_fused_tail<NW * 64>(a, reinterpret_cast<float*>(s_c), 0, H);
 }
 
 // ---------------------------------------------------------------------------
@@ -843,7 +895,7 @@ __device__ __forceinline__ uint32_t lds_addr_of(const float* p) {
 __host__ __device__ constexpr int mla32_blocks(int Hq) { return Hq % 48 == 0 ? 3 : 2; }
 __host__ __device__ constexpr int mla32_groups(int Hq) { return Hq / (16 * mla32_blocks(Hq)); }
 
-template <int NHBB, bool IDX>
+template <int NHBB, bool IDX, bool FUSED>
 __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   constexpr int NW = 4 * NHBB;
   constexpr int NT = NW * 64;
@@ -873,6 +925,10 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   const int64_t ws0 = (int64_t)b * a.Hq * a.S + split;
 
   if (start >= end) {
+    if constexpr (FUSED) {
+      latent_fused_tail<NT>(a, s_c, hg * HW, HW);
+      return;
+    }
     for (int idx = tid; idx < HW * kLatDv; idx += NT) {
       const int h = hg * HW + idx / kLatDv, e = idx - (idx / kLatDv) * kLatDv;
       a.ws_acc[(ws0 + (int64_t)h * a.S) * kLatDv + e] = 0.0f;
@@ -1110,14 +1166,19 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int head = head0 + 4 * lq + i;
       const int col = dq * 128 + 64 * u + 4 * l16;
-      *reinterpret_cast<float4*>(a.ws_acc + (ws0 + (int64_t)head * a.S) * kLatDv + col) =
-          make_float4(acc[4 * u + 0][i], acc[4 * u + 1][i], acc[4 * u + 2][i], acc[4 * u + 3][i]);
+      const float4 v = make_float4(acc[4 * u + 0][i], acc[4 * u + 1][i], acc[4 * u + 2][i], acc[4 * u + 3][i]);
+      if (FUSED && a.S > 1)  // base uniform over the workgroup, offset per lane
+        st_dev4(raw_rsrc(a.ws_acc + ws0 * kLatDv, (uint32_t)((int64_t)a.Hq * a.S * kLatDv * 4)),
+                (uint32_t)(((int64_t)head * a.S * kLatDv + col) * 4), v);
+      else
+        *reinterpret_cast<float4*>(a.ws_acc + (ws0 + (int64_t)head * a.S) * kLatDv + col) = v;
     }
   const float l = sum_xor32(sum_xor16(ll));
   if (dq == 0 && lq == 0) {
-    a.ws_m[ws0 + (int64_t)(head0 + l16) * a.S] = m * kLn2;
-    a.ws_l[ws0 + (int64_t)(head0 + l16) * a.S] = l;
+    put_partial(a.ws_m + ws0 + (int64_t)(head0 + l16) * a.S, m * kLn2, FUSED && a.S > 1);
+    put_partial(a.ws_l + ws0 + (int64_t)(head0 + l16) * a.S, l, FUSED && a.S > 1);
   }
+  if constexpr (FUSED) latent_fused_tail<NT>(a, s_c, hg * HW, HW);
 }
 
 int latent_blocks_per_split(const sk_desc_t& d) {
@@ -1146,11 +1207,13 @@ static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void*
   int threads, groups;
   const bool idx = d.layout == SK_KV_INDEXED;
   if constexpr (kF32) {
-    kern = idx ? mla32_split_kernel<mla32_blocks(H), true> : mla32_split_kernel<mla32_blocks(H), false>;
+    kern = idx ? (s.fused ? mla32_split_kernel<mla32_blocks(H), true, true> : mla32_split_kernel<mla32_blocks(H), true, false>)
+               : (s.fused ? mla32_split_kernel<mla32_blocks(H), false, true> : mla32_split_kernel<mla32_blocks(H), false, false>);
     threads = mla32_blocks(H) * 256;
     groups = mla32_groups(H);
   } else {
-    kern = idx ? mla16_split_kernel<mla16_blocks(H), true> : mla16_split_kernel<mla16_blocks(H), false>;
+    kern = idx ? (s.fused ? mla16_split_kernel<mla16_blocks(H), true, true> : mla16_split_kernel<mla16_blocks(H), true, false>)
+               : (s.fused ? mla16_split_kernel<mla16_blocks(H), false, true> : mla16_split_kernel<mla16_blocks(H), false, false>);
     threads = mla16_blocks(H) * 128;
     groups = mla16_groups(H);
     if constexpr (H == 64 || H == 96) {
@@ -1159,12 +1222,13 @@ static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void*
         // workgroup per split: up to 128 (split, sequence) pairs, the heads go
         // to two workgroups of half as many (results unchanged: each head's
         // arithmetic does not depend on its workgroup).
-        kern = idx ? mla16_split_kernel<H / 32, true> : mla16_split_kernel<H / 32, false>;
+        kern = idx ? (s.fused ? mla16_split_kernel<H / 32, true, true> : mla16_split_kernel<H / 32, true, false>)
+                   : (s.fused ? mla16_split_kernel<H / 32, false, true> : mla16_split_kernel<H / 32, false, false>);
         threads = (H / 32) * 128;
         groups = 2;
       } else if (!idx) {
         // Contiguous caches at longer contexts: the register-blocked form.
-        kern = mla16r_split_kernel<H / 32>;
+        kern = s.fused ? mla16r_split_kernel<H / 32, true> : mla16r_split_kernel<H / 32, false>;
         threads = 512;
         groups = 1;
       }
@@ -1195,7 +1259,28 @@ static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void*
   a.max_idx = d.max_pages_per_seq;
   a.num_rows = d.num_pages;
   a.nt = groups == 1;
-  hipLaunchKernelGGL(kern, gr, dim3(threads), 0, s.stream, a);
+  a.counters = s.counters;
+  a.out = s.out;
+  a.lse = s.lse;
+  if (!s.fused || s.p->n_splits == 1) {
+    hipLaunchKernelGGL(kern, gr, dim3(threads), 0, s.stream, a);
+    return SK_OK;
+  }
+  // With more than one split the one-launch form waits at a grid barrier, so
+  // every workgroup must be resident at once: a cooperative launch, which the
+  // runtime refuses rather than start a grid that does not fit; it is checked
+  // here first.
+  int per_cu = 0, cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), threads, 0) !=
+          hipSuccess)
+    return SK_ERR_HIP;
+  if ((int64_t)gr.x * gr.y * gr.z > (int64_t)per_cu * cus) return SK_ERR_UNSUPPORTED;
+  void* args[] = {&a};
+  if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), gr, dim3(threads), args, 0, s.stream) !=
+      hipSuccess)
+    return SK_ERR_LAUNCH;
   return SK_OK;
 }
 

@@ -3,7 +3,8 @@ whole-call entry point attn_decode against the float64 oracle.
 
 attn_decode_one_launch is one launch of the split kernel in which the last
 workgroup of each (sequence, KV head) to finish merges the group's partials
-(Lecture 06 section 2's combine). Every case runs with a workspace
+(Lecture 06 section 2's combine); for a shared latent it is a cooperative
+launch whose workgroups meet at a grid barrier and then all merge. Every case runs with a workspace
 whose partial rows are NaN beforehand (so the merge can only use partials
 written in this launch) and checks that the completion counters are back at
 zero afterwards, so the next call needs no preparation. Gates as for the
@@ -229,15 +230,100 @@ def test_whole_call_entry_point_equals_the_two_launches():
         assert_parity(case, two, ref, tight=(case.kv_dtype == "f32"), label=case.name)
 
 
-def test_one_launch_refuses_a_shared_latent():
-    from split_kv_flash_amd import SplitKVError
-    from split_kv_flash_amd.binding import SK_ERR_UNSUPPORTED
+# ------------------------------------------------------------ shared latent
+# One cooperative launch: each workgroup writes its partial, all meet at a grid
+# barrier, then every workgroup merges a share of the (sequence, head) rows.
 
-    case = synthetic.latent_case("lat1", seq_len=100, kv_dtype="f32", seed=53, scale=1 / 24)
-    call = decode_call(case, to_device(case))
-    with pytest.raises(SplitKVError) as e:
-        call.decode_one_launch()
-    assert e.value.status == SK_ERR_UNSUPPORTED
+
+def _latent_one_launch_twice(case, t, call):
+    """One-launch result on a poisoned workspace, then a second call on the
+    same workspace: identical bits, counters back at zero."""
+    import torch
+
+    out, lse, _ = run_gpu_fused(case, tensors=t, call=call)
+    call.out.fill_(float("nan"))
+    call.decode_one_launch()
+    torch.cuda.synchronize()
+    assert np.array_equal(call.out.double().cpu().numpy(), out, equal_nan=True)
+    assert int(call.counters().abs().sum().item()) == 0
+    return out, lse
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16"])
+@pytest.mark.parametrize("L", [64, 8192])
+def test_latent_one_launch_matches_oracle(kv, L):
+    """96 heads, heuristic plan (as the bench launches it)."""
+    case = synthetic.latent_decode(L, kv, seed=3000 + L)
+    t = to_device(case)
+    call = decode_call(case, t)
+    out, lse = _latent_one_launch_twice(case, t, call)
+    ref, rlse = oracle_out(case)
+    assert_parity(case, out, ref, tight=(kv == "f32"), label=f"latent one-launch {kv} L={L} plan={call.plan}")
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=ABS_GATE[kv])
+    two, _, _ = run_gpu(case, tensors=t, call=call)
+    assert np.abs(out - two).max() <= ABS_GATE[kv] / 10
+    del call, t
+    free()
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16"])
+def test_latent_one_launch_full_size_sampled_heads(kv):
+    """131,072 positions with the heuristic plan (256 resident workgroups):
+    three heads against the oracle, every head against the two-launch path."""
+    case = synthetic.latent_decode(131072, kv, seed=3000 + 131072)
+    t = to_device(case)
+    call = decode_call(case, t)
+    out, _ = _latent_one_launch_twice(case, t, call)
+    heads = [(0, 0), (0, 47), (0, 95)]
+    ref, _ = oracle_out(case, heads=heads)
+    assert_parity(case, out, ref, tight=(kv == "f32"), label=f"latent one-launch {kv} plan={call.plan}")
+    two, _, _ = run_gpu(case, tensors=t, call=call)
+    assert np.abs(out - two).max() <= ABS_GATE[kv] / 10
+    del call, t
+    free()
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16"])
+@pytest.mark.parametrize("hq", [32, 64, 128])
+def test_latent_one_launch_head_counts_and_empty_splits(kv, hq):
+    """Other head counts, with an explicit plan over a 3,005-row capacity for
+    a 1,500-row sequence: half the splits are empty (their workgroups write
+    nothing but still meet at the barrier and merge)."""
+    case = synthetic.latent_case(f"lat1l-{hq}-{kv}", seq_len=1500, kv_dtype=kv, num_q_heads=hq,
+                                 capacity=3005, seed=54 + hq, scale=1 / 24)
+    t = to_device(case)
+    call = decode_call(case, t, n_splits=16)
+    out, _ = _latent_one_launch_twice(case, t, call)
+    ref, _ = oracle_out(case)
+    assert_parity(case, out, ref, tight=(kv == "f32"), label=f"latent one-launch hq={hq} {kv}")
+    del call, t
+    free()
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16"])
+def test_latent_one_launch_index_lists_and_invalid_lengths(kv):
+    """Index lists (top-k rows of a pool) for a batch of three, one of them
+    with a length past n_splits*chunk: NaN for that sequence only."""
+    import torch
+
+    case = synthetic.indexed_case(f"dsa-one-{kv}", pool_rows=6000, seq_lens=[2048, 700, 1500],
+                                  num_q_heads=96, num_kv_heads=1, head_dim=576, kv_dtype=kv,
+                                  latent_value_dim=512, seed=71, scale=1.0 / 24.0)
+    t = to_device(case)
+    call = decode_call(case, t, n_splits=8)
+    out, _ = _latent_one_launch_twice(case, t, call)
+    ref, _ = oracle_out(case)
+    assert_parity(case, out, ref, tight=(kv == "f32"), label=f"indexed latent one-launch {kv}")
+    t["seq_lens"].copy_(torch.tensor([2048, 0, 1500], dtype=torch.int32))
+    call.out.fill_(0.0)
+    call.decode_one_launch()
+    torch.cuda.synchronize()
+    got, lse = call.out.double().cpu().numpy(), call.lse.double().cpu().numpy()
+    assert np.all(np.isnan(got[1])) and np.all(np.isnan(lse[1]))
+    assert np.array_equal(got[[0, 2]], out[[0, 2]])
+    assert int(call.counters().abs().sum().item()) == 0
+    del call, t
+    free()
 
 
 @pytest.mark.parametrize("kv,hq,hkv,D", [("f16", 24, 4, 256), ("bf16", 32, 4, 256),

@@ -3,7 +3,8 @@ attn_decode_one_launch).
 
 The launches allocate nothing, set no memory and never synchronise with the
 host (the one-launch path's completion counters are reset by the kernel
-itself), so a caller can capture them into a HIP graph and replay it every
+itself; the shared latent's cooperative launch resets its barrier count the
+same way), so a caller can capture them into a HIP graph and replay it every
 decode step. Each replay here runs after eager work on the same stream and a
 change of q, and must equal an eager call on the same inputs bit for bit.
 """
@@ -33,6 +34,15 @@ CASES = {
     "gqa-bf16-paged": lambda: synthetic.gqa_case(
         "graph-paged", seq_lens=[900, 2100, 33], num_q_heads=8, num_kv_heads=2, head_dim=128,
         q_dtype="bf16", kv_dtype="bf16", layout="paged", seed=8002),
+    # Contiguous 16-bit caches of wide groups or head width 64 run on the
+    # query-tile kernel with one query (its one-launch form resets its
+    # counters inside the kernel too).
+    "qtile-f16-g6-d256": lambda: synthetic.gqa_case(
+        "graph-qtile-f16", seq_lens=[3000], num_q_heads=24, num_kv_heads=4, head_dim=256,
+        q_dtype="f32", kv_dtype="f16", seed=8005, peaky_fraction=0.01),
+    "qtile-bf16-d64": lambda: synthetic.gqa_case(
+        "graph-qtile-bf16", seq_lens=[2500, 700], num_q_heads=8, num_kv_heads=2, head_dim=64,
+        q_dtype="bf16", kv_dtype="bf16", seed=8006),
     "latent-f32": lambda: synthetic.latent_case("graph-latent32", seq_len=1500, kv_dtype="f32",
                                                 seed=8003, scale=1.0 / 24.0),
     "latent-f16": lambda: synthetic.latent_case("graph-latent16", seq_len=1500, kv_dtype="f16",
@@ -45,11 +55,15 @@ CASES = {
 def test_captured_call_replays_match_eager_calls(name, mode):
     import torch
 
-    if mode == "one-launch" and name.startswith("latent"):
-        pytest.skip("the one-launch decode serves separate K and V only")
     case = CASES[name]()
     t = to_device(case)
     dc = decode_call(case, t)
+    if name.startswith("qtile"):
+        from split_kv_flash_amd import attn_decode_kernel_info
+
+        # The query-tile kernel stages K/V tiles in LDS (40 KB or more); the
+        # vector split kernel holds at most 33 KB.
+        assert attn_decode_kernel_info(dc.desc, dc.plan).lds_bytes >= 40960
     call = {"two-launch": dc, "whole-call": dc.decode, "one-launch": dc.decode_one_launch}[mode]
     q0 = t["q"].clone()
     q1 = (t["q"].float() * 0.5).to(t["q"].dtype)
