@@ -310,7 +310,8 @@ def test_argument_errors_are_reported_before_any_launch():
                   B.SK_ERR_INVALID_ARG))
     cases.append(("one launch: NULL out", _one(good, plan, out=None), B.SK_ERR_INVALID_ARG))
     cases.append(("one launch: misaligned out", _one(good, plan, out=4100), B.SK_ERR_INVALID_ARG))
-    cases.append(("one launch: shared latent", _one(latent_desc(), plan, v=None), B.SK_ERR_UNSUPPORTED))
+    cases.append(("one launch: shared latent, NULL out", _one(latent_desc(), plan, v=None, out=None),
+                  B.SK_ERR_INVALID_ARG))
     cases.append(("one launch: small workspace", _one(good, plan, wsb=64), B.SK_ERR_WORKSPACE_TOO_SMALL))
     lat = latent_desc()
     cases.append(("project: NULL weights", _proj(lat, plan, w=None), B.SK_ERR_INVALID_ARG))
