@@ -106,6 +106,9 @@ def parse():
     ap.add_argument("--rung-warmup", type=int, default=10)
     ap.add_argument("--only", choices=sorted(ONLY), default=None,
                     help="time one named workload (prints its dict, no JSON line); for profiling")
+    ap.add_argument("--no-one-launch", action="store_true",
+                    help="with --only: leave out the one-launch timing (for a shared latent a "
+                         "cooperative launch, after which rocprofv3 can crash on exit)")
     return ap.parse_args()
 
 
@@ -493,7 +496,7 @@ def main():
         elif "q_len" in c.meta:
             r = measure_query_tiles(c, args.steps, args.warmup, fl)
         else:
-            r, _, _ = measure(c, args.steps, args.warmup, args.n_splits, fl)
+            r, _, _ = measure(c, args.steps, args.warmup, args.n_splits, fl, one_launch=not args.no_one_launch)
         log(f"{args.only}: {r}")
         # A 1 GiB device-to-device copy: the kernel of known size that counter
         # runs scale FETCH_SIZE and WRITE_SIZE by.
