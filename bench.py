@@ -60,13 +60,38 @@ KERNEL_SOURCES = [os.path.join(HERE, "split_kv_flash_amd", "csrc", f)
                   for f in ("gqa_split.hip", "sk_device.h", "sk_internal.h", "sk_merge.h")]
 
 
+def _code_only(text):
+    """C++ source with comments removed and whitespace runs collapsed (string
+    literals kept), so that editing a comment does not change the hash."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"':
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash():
+    """SHA-256 of the split kernel's code (comments and layout ignored)."""
     import hashlib
 
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -14,14 +14,20 @@
 //   output  acc[h][e] += sum_j P[h][j] C[j][e] (heads x values,    K = positions)
 // with the online-softmax update between them. f16 caches use f16 MFMA (q and
 // the probabilities rounded to f16, f32 accumulation); f32 caches use
-// v_mfma_f32_16x16x4_f32 (no rounding). Two kernels live here, each described
+// v_mfma_f32_16x16x4_f32 (no rounding). Three kernels live here, each described
 // at its definition:
 //   * mla16_split_kernel (f16 caches): two waves per 16-head block, x32 MFMA,
 //     scores transposed, one barrier per tile; 32, 64 and 96 heads in one
 //     workgroup per split, 128 heads as two workgroups of 64;
+//   * mla16r_split_kernel (f16 caches, 64 and 96 heads when every compute
+//     unit gets a split): eight waves, partial scores reduced by one wave per
+//     head block, each value operand feeding every head block of a wave;
 //   * mla32_split_kernel (f32 caches): four waves per 16-head block, scores
 //     transposed so P stays in registers, heads over one or more workgroups
 //     per split.
+// Each has a FUSED instantiation for the one-launch decode: the partials go
+// out with device-scope stores and the workgroups merge them in the same
+// grid (latent_fused_tail).
 #include "sk_device.h"
 #include "sk_internal.h"
 #include "sk_merge.h"

@@ -1,5 +1,7 @@
 // Device-scope partials and the in-grid merge of the one-launch decode
-// kernels (the GQA split kernel and the query-tile kernel with one query).
+// kernels: the last-arrival tree of the GQA split kernel and the query-tile
+// kernel with one query, and the grid barrier and distributed merge of the
+// shared-latent kernels.
 //
 // Lecture 06 section 2: M = max m_i, l = sum l_i exp(m_i - M),
 // out = sum acc_i exp(m_i - M) / l, lse = M + ln l. Args is a kernel argument
