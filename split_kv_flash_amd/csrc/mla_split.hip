@@ -19,9 +19,10 @@
 //   * mla16_split_kernel (f16 caches): two waves per 16-head block, x32 MFMA,
 //     scores transposed, one barrier per tile; 32, 64 and 96 heads in one
 //     workgroup per split, 128 heads as two workgroups of 64;
-//   * mla16r_split_kernel (f16 caches, 64 and 96 heads when every compute
-//     unit gets a split): eight waves, partial scores reduced by one wave per
-//     head block, each value operand feeding every head block of a wave;
+//   * mla16w_split_kernel (f16 caches, 64 and 96 heads when every compute
+//     unit gets a split): eight waves, one wave per 16-head block computing
+//     its full scores and softmax, every wave multiplying all blocks' weights
+//     by its 64 value columns;
 //   * mla32_split_kernel (f32 caches): four waves per 16-head block, scores
 //     transposed so P stays in registers, heads over one or more workgroups
 //     per split.
@@ -469,392 +470,9 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
   if constexpr (FUSED) latent_fused_tail<NW * 64>(a, reinterpret_cast<float*>(s_c), h0, H);
 }
 
-// ---------------------------------------------------------------------------
-// f16 caches, 64 or 96 heads in one workgroup per split: the register-blocked
-// form (mla16r_split_kernel<NB>, NB = 2 or 3 head blocks of 16 per group).
-//
-// The workgroup is 8 waves in two head groups of 16*NB heads; wave w = 4*g + c
-// serves group g. What one wave holds in registers is chosen so that every
-// fragment it reads from LDS feeds NB MFMAs (one per head block of its group).
-// On MI355X a transposed LDS read (ds_read_b64_tr_b16) moves about 69 bytes
-// per clock and compute unit, against about 162 for ds_read_b128, and the
-// two-waves-per-head-block form above spends most of each tile on them; here
-// they are a third as many:
-//  * scores: wave (g, c) forms partial scores S^T of its group's 16*NB heads
-//    over latent columns 32*(c + 4t) .. +31 for t = 0..3 (x32 MFMA) and
-//    512 + 16c .. +15 (x16 MFMA; the last 64 columns are shared out by four),
-//    each cache fragment the A operand of NB MFMAs;
-//  * the four partials of a head block meet in LDS: wave c < NB reduces head
-//    block c (its own partial stays in registers, the others are read in wave
-//    order, so every run adds them in the same order), runs the online
-//    softmax of those 16 heads and publishes their weights P (f16, already in
-//    the A-operand layout of the output product) and rescale factors;
-//  * output: wave (g, c) owns value columns [128c, 128c + 128) of all its
-//    group's heads; each transposed value fragment is the B operand of NB
-//    MFMAs.
-// Iteration i: the scores of tile i; barrier A (the partials); the reduction
-// of tile i and the output product of tile i-1, group 0 reducing first and
-// group 1 multiplying first, so that on every SIMD (waves c and 4 + c) one
-// wave's softmax runs beside the other's MFMAs; barrier B (the weights, which
-// are double-buffered by tile parity, and tile i+1). Tile i+2's loads are
-// spread over the score steps of iteration i+1, into the buffer tile i-1 left
-// at barrier B, so they are issued a full iteration before they are needed.
-// Registers: q as B operands (NB * (4 half8 + 1 half4)), accumulators NB * 8
-// float4, partial scores NB * 2 float4: within two waves per SIMD at NB = 3.
-// LDS (NB = 3): 3 tile buffers (108 KB), the partials (3*NB slots of 2 KB per
-// group: a reducer does not store the block it reduces) and two tiles'
-// weights: 160,512 of 163,840 bytes.
-// ---------------------------------------------------------------------------
-
 // How far (base 2) a tile's maximum may exceed the running value the weights
 // are taken against before that value moves (weights stay below 2^8).
 constexpr float kLazyMax = 8.0f;
-
-template <int NB, bool FUSED>
-__global__ __launch_bounds__(512) void mla16r_split_kernel(MlaArgs a) {
-  constexpr int GH = 16 * NB;                     // heads per group
-  constexpr int H = 2 * GH;                       // heads per workgroup
-  constexpr int NW = 8;
-  constexpr int KSW = 4;                          // x32 score steps of one wave (columns < 512)
-  constexpr int NCB = 8;                          // 16-column blocks per wave (128 columns)
-  constexpr int TILE = kT16 * kLatDk;
-  constexpr int PSLOTS = 3 * NB;                  // partial-score slots per group
-  constexpr int kRow16 = 16 * kLatDk;
-  constexpr int WLOADS = kT16 * kCpr16 / 64;      // 36 wave-loads per tile
-  constexpr int LBASE = WLOADS / NW, LEXTRA = WLOADS % NW;
-  constexpr int DPW = LBASE + (LEXTRA > 0 ? 1 : 0);
-  static_assert(NB == 2 || NB == 3, "64 or 96 heads");
-  static_assert(DPW <= KSW + 1, "a wave's tile loads fit its score steps");
-
-  __shared__ __align__(16) _Float16 s_c[3 * TILE];
-  __shared__ __align__(16) float4_t s_part[2][PSLOTS][2][64];
-  __shared__ __align__(16) half8_t s_p[2][2][NB][64];     // [tile parity][group][block][lane]
-  __shared__ __align__(16) float s_alpha[2][2][NB][16];   // [tile parity][group][block][head]
-
-  const int split = blockIdx.x;
-  const int b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = wave >> 2;
-  const int c = wave & 3;
-  const int l16 = lane & 15;
-  const int lq = lane >> 4;
-  const int gh0 = g * GH;  // first head of this wave's group (within the workgroup)
-
-  const int L = min(a.seq_lens[b], a.cap);
-  const int64_t start = (int64_t)split * a.chunk;
-  const int64_t end = min((int64_t)L, start + a.chunk);
-  const int64_t ws0 = (int64_t)b * a.Hq * a.S + split;
-
-  if (start >= end) {
-    // One-launch decode: an empty slice takes no part in the merge, but its
-    // workgroup still meets the others at the grid barrier and merges.
-    if constexpr (FUSED) {
-      latent_fused_tail<NW * 64>(a, reinterpret_cast<float*>(s_c), 0, H);
-      return;
-    }
-    for (int idx = tid; idx < H * kLatDv; idx += NW * 64) {
-      const int h = idx / kLatDv, e = idx - (idx / kLatDv) * kLatDv;
-      a.ws_acc[(ws0 + (int64_t)h * a.S) * kLatDv + e] = 0.0f;
-    }
-    for (int h = tid; h < H; h += NW * 64) {
-      a.ws_m[ws0 + (int64_t)h * a.S] = -INFINITY;
-      a.ws_l[ws0 + (int64_t)h * a.S] = 0.0f;
-    }
-    return;
-  }
-
-  const _Float16* __restrict__ cbase = reinterpret_cast<const _Float16*>(a.c) + (int64_t)b * a.stride_seq;
-  const float* __restrict__ qb = a.q + (int64_t)b * a.Hq * kLatDk;
-
-  // Tile staging as in mla16_split_kernel: slot s of a tile holds row s/72,
-  // logical chunk (s%72) ^ (row & 7); rows past the end re-read row end-1.
-  // Every wave issues its share of a tile's 36 wave-loads (5 for waves 0-3,
-  // 4 for waves 4-7): an LDS-direct load occupies the compute unit's load
-  // path for about 16 clocks, so the loads are spread over all waves and over
-  // the score steps. A tile that reaches past the end (the last of a slice, and the
-  // look-ahead past it) has its rows clamped. The offsets are recomputed at
-  // each load (a few integer operations beside the score MFMAs) rather than
-  // held in registers.
-  const int wl0 = wave * LBASE + min(wave, LEXTRA);
-  const int nwl = LBASE + (wave < LEXTRA ? 1 : 0);
-  const uint32_t lds0 = lds_addr_of(s_c);
-  const uint32_t row_bytes = (uint32_t)(a.stride_pos * 2);
-  // A tile's base row (clamped to the last row) and how many rows follow it
-  // before the end, then its loads cc (< nwl) into buffer bi. This workgroup
-  // is its rows' only reader, so the loads take the non-temporal policy.
-  struct TileAt {
-    const _Float16* base;
-    int last;  // rows past base before the end (>= 0)
-  };
-  auto tile_at = [&](int64_t tb) {
-    const int64_t tbc = tb < end ? tb : end - 1;
-    return TileAt{cbase + tbc * a.stride_pos, (int)(end - 1 - tbc)};
-  };
-  auto issue_load = [&](int cc, int bi, const TileAt& t) {
-    const int sl = (wl0 + cc) * 64 + lane;
-    const int srow = sl / kCpr16;
-    const int scol = ((sl - srow * kCpr16) ^ (srow & 7)) * 8;
-    const uint32_t off = (uint32_t)min(srow, t.last) * row_bytes + (uint32_t)(scol * 2);
-    const uint32_t dst = lds0 + (uint32_t)((bi * TILE + (wl0 + cc) * 64 * 8) * 2);
-    dma16s(off, t.base, __builtin_amdgcn_readfirstlane(dst), true);
-  };
-
-  // Score fragments: rows l16 (+16), logical chunk 4*(c + 4t) + lq of x32 step
-  // t, i.e. ((4c + lq) ^ (l16 & 7)) + 16t (the XOR touches bits 0-2 only);
-  // the x16 step reads halves 4*(lq & 1) .. +3 of logical chunk
-  // 64 + 2c + lq/2 (columns 512 + 16c + 4*lq .. +3).
-  const int sbase = l16 * kLatDk + (((4 * c + lq) ^ (l16 & 7)) << 3);
-  const int rbase = l16 * kLatDk + (((64 + 2 * c + (lq >> 1)) ^ (l16 & 7)) << 3) + 4 * (lq & 1);
-  // Value fragments (transpose reads): rows 4*lq + l16/4 (+16), logical chunk
-  // 16c + 2cb + (l16&3)/2 of column block cb, plus 4 halves for odd l16.
-  const int r0 = 4 * lq + (l16 >> 2);
-  const int jv = (l16 & 3) >> 1;
-  const int hoff = (l16 & 1) * 4;
-  int bv[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) bv[u] = r0 * kLatDk + ((16 * c + ((2 * u + jv) ^ (r0 & 7))) << 3) + hoff;
-
-  // Partial-score slot of (writer c', head block hb): a reducer (c' < NB)
-  // keeps block c' in registers and stores the others.
-  auto slot = [](int cw, int hb) {
-    return cw < NB ? cw * (NB - 1) + (hb > cw ? hb - 1 : hb) : NB * (NB - 1) + (cw - NB) * NB + hb;
-  };
-
-  float m = -INFINITY, l = 0.0f;  // reducer: head gh0 + 16c + l16 (replicated over quarters)
-  float4_t acc[NB][NCB];
-#pragma unroll
-  for (int hb = 0; hb < NB; ++hb)
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) acc[hb][cb] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int ntiles = (int)((end - start + kT16 - 1) / kT16);
-  // Prologue: tile 0, the query rows, tile 1 (in that order, so that waiting
-  // until only tile 1's loads remain covers the first two).
-  {
-    const TileAt t0 = tile_at(start);
-#pragma unroll
-    for (int cc = 0; cc < DPW; ++cc)
-      if (LEXTRA == 0 || cc < nwl) issue_load(cc, 0, t0);
-  }
-  // Query rows as B operands, rounded to f16 once: head gh0 + 16hb + l16,
-  // columns 32*(c + 4t) + 8*lq .. +7 (x32 steps) and 512 + 16c + 4*lq .. +3
-  // (x16 step).
-  half8_t qf[NB][KSW];
-  half4_t qr[NB];
-#pragma unroll
-  for (int hb = 0; hb < NB; ++hb) {
-    const float* qrow = qb + (int64_t)(gh0 + 16 * hb + l16) * kLatDk;
-#pragma unroll
-    for (int t = 0; t < KSW; ++t) {
-      const float* qp = qrow + 32 * (c + 4 * t) + 8 * lq;
-      const float4 v0 = *reinterpret_cast<const float4*>(qp);
-      const float4 v1 = *reinterpret_cast<const float4*>(qp + 4);
-      qf[hb][t] = half8_t{(_Float16)v0.x, (_Float16)v0.y, (_Float16)v0.z, (_Float16)v0.w,
-                          (_Float16)v1.x, (_Float16)v1.y, (_Float16)v1.z, (_Float16)v1.w};
-    }
-    const float4 vr = *reinterpret_cast<const float4*>(qrow + 512 + 16 * c + 4 * lq);
-    qr[hb] = half4_t{(_Float16)vr.x, (_Float16)vr.y, (_Float16)vr.z, (_Float16)vr.w};
-  }
-  {
-    const TileAt t1 = tile_at(start + kT16);
-#pragma unroll
-    for (int cc = 0; cc < DPW; ++cc)
-      if (LEXTRA == 0 || cc < nwl) issue_load(cc, 1, t1);
-  }
-  // Tile 0 and the query rows landed; only this wave's nwl loads of tile 1
-  // may remain (loads complete in issue order).
-  if (nwl == DPW)
-    wait_vm_lgkm0<DPW>();
-  else
-    wait_vm_lgkm0<(LEXTRA == 0 ? DPW : DPW - 1)>();
-  raw_barrier();
-
-  // Output product of tile j: acc = alp * acc + P x V over this wave's 128
-  // columns, with the weights and factors the reducers published for it.
-  auto output = [&](int j) {
-    const _Float16* prv = s_c + (j % 3) * TILE;
-    const int par = j & 1;
-    float4_t alp[NB];  // factors of accumulator items (heads 4*lq + e)
-    bool moved = false;
-#pragma unroll
-    for (int hb = 0; hb < NB; ++hb) {
-      alp[hb] = *reinterpret_cast<const float4_t*>(&s_alpha[par][g][hb][4 * lq]);
-      moved = moved || alp[hb][0] != 1.0f || alp[hb][1] != 1.0f || alp[hb][2] != 1.0f ||
-              alp[hb][3] != 1.0f;
-    }
-    if (__any(moved)) {
-#pragma unroll
-      for (int hb = 0; hb < NB; ++hb)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[hb][cb][e] *= alp[hb][e];
-    }
-    half8_t pp[NB];
-#pragma unroll
-    for (int hb = 0; hb < NB; ++hb) pp[hb] = s_p[par][g][hb][lane];
-    auto vread = [&](int cb) {
-      const _Float16* vp = prv + bv[cb & 3] + 64 * (cb >> 2);
-      const half4_t v0 = lds_read_tr(vp);
-      const half4_t v1 = lds_read_tr(vp + kRow16);
-      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    half8_t vn = vread(0);
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const half8_t vv = vn;
-      if (cb + 1 < NCB) vn = vread(cb + 1);
-#pragma unroll
-      for (int hb = 0; hb < NB; ++hb) acc[hb][cb] = mfma32(pp[hb], vv, acc[hb][cb]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  for (int i = 0;; ++i) {
-    const bool more = i < ntiles;  // tile i exists (else only tile i-1's output remains)
-    const int64_t tb = start + (int64_t)i * kT16;
-    const int rel = (int)(end - tb);  // positions of tile i before the end (> 0 when more)
-    float4_t o0 = float4_t{0.f, 0.f, 0.f, 0.f}, o1 = o0;
-    if (more) {
-      // ---- partial scores of tile i over this wave's score steps; tile i+1's
-      // loads (iteration 0: already issued) go out between the steps ----
-      const _Float16* cur = s_c + (i % 3) * TILE;
-      const bool load_next = i > 0;
-      const TileAt tn = tile_at(tb + kT16);
-      float4_t sp[NB][2];
-#pragma unroll
-      for (int hb = 0; hb < NB; ++hb) sp[hb][0] = sp[hb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
-      const _Float16* sp0 = cur + sbase;
-      half8_t n0 = *reinterpret_cast<const half8_t*>(sp0);
-      half8_t n1 = *reinterpret_cast<const half8_t*>(sp0 + kRow16);
-#pragma unroll
-      for (int t = 0; t < KSW; ++t) {
-        const half8_t a0 = n0, a1 = n1;
-        if (t + 1 < KSW) {
-          n0 = *reinterpret_cast<const half8_t*>(sp0 + 128 * (t + 1));
-          n1 = *reinterpret_cast<const half8_t*>(sp0 + 128 * (t + 1) + kRow16);
-        }
-#pragma unroll
-        for (int hb = 0; hb < NB; ++hb) {
-          sp[hb][0] = mfma32(a0, qf[hb][t], sp[hb][0]);
-          sp[hb][1] = mfma32(a1, qf[hb][t], sp[hb][1]);
-        }
-        // The step's MFMAs are issued (they run on in the matrix core) before
-        // one load of tile i+1, which may wait for the load path.
-        __builtin_amdgcn_sched_barrier(0);
-        if (load_next && (LEXTRA == 0 || t < nwl)) issue_load(t, (i + 1) % 3, tn);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      {
-        const half4_t r0v = *reinterpret_cast<const half4_t*>(cur + rbase);
-        const half4_t r1v = *reinterpret_cast<const half4_t*>(cur + rbase + kRow16);
-#pragma unroll
-        for (int hb = 0; hb < NB; ++hb) {
-          sp[hb][0] = __builtin_amdgcn_mfma_f32_16x16x16f16(r0v, qr[hb], sp[hb][0], 0, 0, 0);
-          sp[hb][1] = __builtin_amdgcn_mfma_f32_16x16x16f16(r1v, qr[hb], sp[hb][1], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (load_next && KSW < nwl) issue_load(KSW, (i + 1) % 3, tn);
-      }
-#pragma unroll
-      for (int hb = 0; hb < NB; ++hb) {
-        if (c < NB && hb == c) continue;  // a reducer keeps its own block
-        s_part[g][slot(c, hb)][0][lane] = sp[hb][0];
-        s_part[g][slot(c, hb)][1][lane] = sp[hb][1];
-      }
-      // A reducer's own partial of block c (selected without indexing
-      // registers by a run-time value); the other partials are dead from here.
-      o0 = sp[0][0];
-      o1 = sp[0][1];
-#pragma unroll
-      for (int hb = 1; hb < NB; ++hb) {
-        o0 = c == hb ? sp[hb][0] : o0;
-        o1 = c == hb ? sp[hb][1] : o1;
-      }
-      wait_vm_lgkm0<DPW>();  // the partials are in LDS; tile i+1 stays in flight
-      raw_barrier();         // A: the partials of tile i
-    }
-
-    // ---- reducers: full scores of head block c, online softmax, weights ----
-    auto reduce = [&]() {
-      const int par = i & 1;
-      float4_t x0 = float4_t{0.f, 0.f, 0.f, 0.f}, x1 = x0;
-#pragma unroll
-      for (int cw = 0; cw < 4; ++cw) {  // every run adds the four partials in this order
-        if (cw == c) {
-          x0 += o0;
-          x1 += o1;
-        } else {
-          x0 += s_part[g][slot(cw, c)][0][lane];
-          x1 += s_part[g][slot(cw, c)][1][lane];
-        }
-      }
-      float v[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = 4 * lq + e < rel ? x0[e] * a.qscale : -INFINITY;
-        v[4 + e] = 16 + 4 * lq + e < rel ? x1[e] * a.qscale : -INFINITY;
-        mx = fmaxf(mx, fmaxf(v[e], v[4 + e]));
-      }
-      mx = max_xor32(max_xor16(mx));
-      // m is the value the weights are taken against. It moves to the tile's
-      // maximum only when that exceeds it by more than kLazyMax (base 2):
-      // the weights then stay below 2^kLazyMax (f16 holds them), and most
-      // tiles keep m, so their factor is exactly 1 and the accumulators are
-      // not rescaled. (m, l, acc) describe the same sums either way.
-      const float mn = mx > m + kLazyMax ? mx : m;
-      const float mu = (mn == -INFINITY) ? 0.0f : mn;
-      const float al = fast_exp2(m - mu);
-      half8_t pw;
-      float ls = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const _Float16 pj = (_Float16)fast_exp2(v[j] - mu);
-        pw[j] = pj;
-        ls += (float)pj;
-      }
-      ls = sum_xor32(sum_xor16(ls));
-      l = fmaf(l, al, ls);
-      m = mn;
-      s_p[par][g][c][lane] = pw;
-      if (lq == 0) s_alpha[par][g][c][l16] = al;
-    };
-    // Group 0 reduces first, group 1 multiplies first: waves c and 4 + c share
-    // a SIMD, so one's softmax runs beside the other's MFMAs. (The short
-    // reduction is written twice around one output product: two orders of
-    // the whole would hold two register allocations.)
-    const bool red = more && c < NB;
-    if (red && g == 0) reduce();
-    if (i > 0) output(i - 1);
-    if (red && g == 1) reduce();
-    if (!more) break;
-    wait_vm_lgkm0<0>();  // the weights are in LDS and tile i+1 has landed
-    raw_barrier();       // B: weights of tile i, tile i+1; tile i-1's buffer is free
-  }
-  // Drain the tile loads still in flight before the workgroup can retire.
-  wait_vm_lgkm0<0>();
-
-  // Partials: heads 4*lq + e of each block, columns 128c + 16cb + l16.
-#pragma unroll
-  for (int hb = 0; hb < NB; ++hb)
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int head = gh0 + 16 * hb + 4 * lq + e;
-        const int col = 128 * c + 16 * cb + l16;
-        put_partial(a.ws_acc + (ws0 + (int64_t)head * a.S) * kLatDv + col, acc[hb][cb][e], FUSED && a.S > 1);
-      }
-  if (c < NB && lq == 0) {
-    const int head = gh0 + 16 * c + l16;
-    put_partial(a.ws_m + ws0 + (int64_t)head * a.S, m * kLn2, FUSED && a.S > 1);
-    put_partial(a.ws_l + ws0 + (int64_t)head * a.S, l, FUSED && a.S > 1);
-  }
-  if constexpr (FUSED) latent_fused_tail<NW * 64>(a, reinterpret_cast<float*>(s_c), 0, H);
-}
 
 // ---------------------------------------------------------------------------
 // f32 caches: v_mfma_f32_16x16x4_f32 (exact f32 products), four waves per
