@@ -95,6 +95,40 @@ def test_plan_matches_oracle_reading(hkv):
         assert (p.n_splits, p.chunk) == want
 
 
+def test_plan_keeps_the_pages_split_properties_whatever_the_budget():
+    """What the pages fix about a plan, independent of the library's tuned
+    budget (aprender issue #3725 design note section 2; Lecture 06 sections 2
+    and 5.1): an explicit split count is honoured with chunk = ceil(L_max/S);
+    otherwise every sequence is covered (ceil(L_b/chunk) <= S), the longest
+    sequence's last split is not empty ((S-1)*chunk < L_max), a slice is at
+    least 64 positions and a whole number of 64-position tiles, and the
+    blocks (KV heads x slices over the batch) stay within a few tiles' worth of
+    one to eight per compute unit, the range the budgets span."""
+    lib()
+    rng = np.random.default_rng(11)
+    for _ in range(400):
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        batch = int(rng.integers(1, 33))
+        lens = rng.integers(1, 400000, size=batch)
+        cu = int(rng.choice([80, 132, 256, 304]))
+        req = int(rng.choice([0, 0, 0, 2, 7, 64]))
+        d = gqa_desc(Hq=4 * hkv, Hkv=hkv, D=128, cap=int(lens.max()), batch=batch)
+        p = B.attn_decode_plan(d, int(lens.max()), int(lens.sum()), cu, req)
+        l_max = int(lens.max())
+        if req:
+            assert (p.n_splits, p.chunk) == (req, -(-l_max // req))
+            continue
+        assert p.chunk >= 64 and p.chunk % 64 == 0
+        assert all(-(-int(L) // p.chunk) <= p.n_splits for L in lens)
+        assert (p.n_splits - 1) * p.chunk < l_max
+        blocks = hkv * sum(-(-int(L) // p.chunk) for L in lens)
+        if p.chunk > 64:  # not held at the minimum slice
+            # chunk is the smallest granule multiple at or above the budget's
+            # slice, so one granule less would have exceeded the budget
+            assert hkv * sum(-(-int(L) // (p.chunk - 64)) for L in lens) > 0.75 * cu
+            assert blocks <= 8 * cu + hkv * batch
+
+
 def test_plan_latent_matches_oracle_reading():
     lib()
     # f16 latents: one workgroup per split up to 96 heads, two of 64 heads at
