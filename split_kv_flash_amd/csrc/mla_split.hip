@@ -626,30 +626,64 @@ __global__ __launch_bounds__(512) void mla16w_split_kernel(MlaArgs a) {
 
   const int ntiles = (int)((end - start + kT16 - 1) / kT16);
   if (tid < 2) s_moved[tid] = -1;
-  // Prologue: tile 0, the query rows (scoring waves), tile 1.
+  // Prologue: tile 0; the query rows, rounded to f16 once and staged through
+  // the last NHB/2 tile buffers (H rows of 576 halves fill them exactly); tile
+  // 1 (before the staging when its buffer is not among them, else after). The
+  // whole workgroup reads the f32 rows as consecutive float4s, so every load
+  // instruction covers whole lines; a scoring wave's own fragments (16 rows,
+  // 32 bytes apart in each) would touch sixteen lines per instruction.
+  constexpr int QB0 = NBUF - NHB / 2;                 // first buffer of the staged rows
+  constexpr int QV = H * (kLatDk / 4) / (NW * 64);    // float4 per thread
+  static_assert(H * (kLatDk / 4) % (NW * 64) == 0, "whole float4 rounds");
+  static_assert(H * kLatDk <= (NBUF - QB0) * TILE, "the staged rows fit");
+  _Float16* const sq = s_c + QB0 * TILE;
+  auto wait_tile1 = [&]() {  // everything but this wave's loads of tile 1 has landed
+    if (nwl == DPW)
+      wait_vm_lgkm0<DPW>();
+    else
+      wait_vm_lgkm0<(LEXTRA == 0 ? DPW : DPW - 1)>();
+  };
   issue_tile(0, start);
-  half8_t qf[KS];  // head 16w + l16, columns 32t + 8lq .. +7, rounded to f16 once
-  if (scorer) {
-    const float* qrow = qb + (int64_t)(16 * wave + l16) * kLatDk + 8 * lq;
+  {
+    float4 qv[QV];
 #pragma unroll
-    for (int t = 0; t < KS; ++t) {
-      const float4 v0 = *reinterpret_cast<const float4*>(qrow + 32 * t);
-      const float4 v1 = *reinterpret_cast<const float4*>(qrow + 32 * t + 4);
-      qf[t] = half8_t{(_Float16)v0.x, (_Float16)v0.y, (_Float16)v0.z, (_Float16)v0.w,
-                      (_Float16)v1.x, (_Float16)v1.y, (_Float16)v1.z, (_Float16)v1.w};
+    for (int k = 0; k < QV; ++k) qv[k] = *reinterpret_cast<const float4*>(qb + 4 * (tid + NW * 64 * k));
+    if constexpr (QB0 >= 2) issue_tile(1, start + kT16);
+    // Row h keeps chunk c (8 halves) at chunk position c ^ (h & 7), so the 16
+    // rows a fragment read touches fall in distinct banks.
+#pragma unroll
+    for (int k = 0; k < QV; ++k) {
+      const int f = tid + NW * 64 * k;
+      const int h = f / (kLatDk / 4);
+      const int c4 = f - h * (kLatDk / 4);
+      *reinterpret_cast<half4_t*>(sq + h * kLatDk + (((c4 >> 1) ^ (h & 7)) << 3) + (c4 & 1) * 4) =
+          half4_t{(_Float16)qv[k].x, (_Float16)qv[k].y, (_Float16)qv[k].z, (_Float16)qv[k].w};
     }
+  }
+  if constexpr (QB0 >= 2)
+    wait_tile1();
+  else
+    wait_vm_lgkm0<0>();
+  raw_barrier();
+  half8_t qf[KS];  // head 16w + l16, columns 32t + 8lq .. +7
+  if (scorer) {
+    const _Float16* qrow = sq + (16 * wave + l16) * kLatDk;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) qf[t] = *reinterpret_cast<const half8_t*>(qrow + (((4 * t + lq) ^ (l16 & 7)) << 3));
   } else {
 #pragma unroll
     for (int t = 0; t < KS; ++t) qf[t] = half8_t{};
   }
-  issue_tile(1, start + kT16);
-  // Tile 0 and the query rows landed; only this wave's loads of tile 1 may
-  // remain (loads complete in issue order).
-  if (nwl == DPW)
-    wait_vm_lgkm0<DPW>();
-  else
-    wait_vm_lgkm0<(LEXTRA == 0 ? DPW : DPW - 1)>();
-  raw_barrier();
+  // The staged rows are read before any tile load may overwrite them; tile 0
+  // (and the query) landed, at most this wave's loads of tile 1 remain.
+  if constexpr (QB0 >= 2) {
+    wait_tile1();
+    raw_barrier();
+  } else {
+    wait_vm_lgkm0<0>();
+    raw_barrier();
+    issue_tile(1, start + kT16);
+  }
 
   // Output product of tile j: acc = alp * acc + P x V over this wave's 64
   // columns, for every head block.
