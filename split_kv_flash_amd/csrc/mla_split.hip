@@ -19,10 +19,10 @@
 //   * mla16_split_kernel (f16 caches): two waves per 16-head block, x32 MFMA,
 //     scores transposed, one barrier per tile; 32, 64 and 96 heads in one
 //     workgroup per split, 128 heads as two workgroups of 64;
-//   * mla16w_split_kernel (f16 caches, 64 and 96 heads when every compute
-//     unit gets a split): eight waves, one wave per 16-head block computing
-//     its full scores and softmax, every wave multiplying all blocks' weights
-//     by its 64 value columns;
+//   * mla16d_split_kernel (f16 caches, 64 and 96 heads when every compute
+//     unit gets a split): eight waves in two roles, scoring waves of 32 heads
+//     (scores and softmax in registers) and output waves that own the value
+//     columns and multiply every block's weights by them;
 //   * mla32_split_kernel (f32 caches): four waves per 16-head block, scores
 //     transposed so P stays in registers, heads over one or more workgroups
 //     per split.
@@ -509,75 +509,74 @@ constexpr int kT32 = 16;              // positions per tile
 constexpr int kCpr32 = kLatDk / 4;    // 144 chunks of 16 bytes per f32 cache row
 constexpr int kSlots32 = kT32 * kCpr32;
 
-// Wave-per-block f16 latent kernel (64 or 96 heads of a split in one
-// workgroup of eight waves). Waves w < NHB each compute the full scores of one
-// 16-head block over all 576 columns (18 x32 steps over the tile's 32 rows),
-// so a block's softmax needs no exchange of partial scores: the scoring wave
-// runs it in registers and publishes P (f16) and the rescale factors. Every
-// wave then multiplies the P of all NHB blocks by its 64 value columns, so one
-// value operand read from LDS feeds NHB products. One barrier per tile and
-// four tile buffers: iteration i scores tile i, runs the output product of
-// tile i-1 and requests tile i+2 (two tiles of look-ahead).
-template <int NHB, bool FUSED>
-__global__ __launch_bounds__(512) void mla16w_split_kernel(MlaArgs a) {
-  constexpr int H = 16 * NHB;                     // heads per workgroup
+// Dedicated-role f16 latent kernel (64 or 96 heads of a split in one
+// workgroup of eight waves). NS = NHB/2 scoring waves own 32 heads each (two
+// 16-head blocks): every K fragment read from LDS feeds both blocks, so the
+// scores take the tile out of LDS NS times rather than NHB times. A scoring
+// wave runs its two blocks' online softmax in registers and publishes P (f16)
+// and the rescale factors. The other 8 - NS output waves own the 32 16-column
+// value blocks (Mla16dRoles shares them out so every SIMD carries about the
+// same MFMA work; wave w runs on SIMD w % 4), multiply the P of all blocks by
+// them and request the tiles. One barrier per tile and four tile buffers:
+// iteration i scores tile i, runs the output product of tile i-1 and requests
+// tile i+2 (two tiles of look-ahead).
+template <int NHB>
+struct Mla16dRoles {
+  static constexpr int NS = NHB / 2;               // scoring waves
+  static constexpr int NO = 8 - NS;                // output waves
+  static constexpr int kShared = NHB == 6 ? 6 : 4; // column blocks of an output wave beside a scoring wave
+  static constexpr int kAlone = NHB == 6 ? 7 : 6;  // ... of one on a SIMD without a scoring wave
+  static constexpr bool shared(int w) { return w >= 4 && (w & 3) < NS; }
+  static constexpr int ncb(int w) { return w < NS ? 0 : (shared(w) ? kShared : kAlone); }
+  static constexpr int cb0(int w) {
+    int s = 0;
+    for (int v = NS; v < w; ++v) s += ncb(v);
+    return s;
+  }
+  static constexpr int kLoads = kT16 * kCpr16 / 64;  // 36 wave-loads per tile
+  static constexpr int LB = kLoads / NO, LX = kLoads % NO;
+  static constexpr int DPW = LB + (LX > 0 ? 1 : 0);
+};
+
+struct Mla16dShared {
+  _Float16* c;          // NBUF tile buffers
+  half8_t* p;           // [2][NHB][64]: P of a tile (f16), A-operand lane order
+  float* alpha;         // [2][NHB][16]: rescale factors of a tile
+  int* moved;           // [2]: last tile whose factors were not all 1
+};
+
+// One role of the dedicated-role kernel: NCB == 0 scores, else the output
+// product over NCB column blocks. Every role passes the same barriers.
+template <int NHB, int NCB, bool FUSED>
+__device__ __forceinline__ void mla16d_role(const MlaArgs& a, const Mla16dShared& sh, int64_t start, int64_t end,
+                                            int64_t ws0, int b) {
+  using R = Mla16dRoles<NHB>;
+  constexpr int H = 16 * NHB;
   constexpr int NW = 8;
-  constexpr int KS = kLatDk / 32;                 // 18 x32 score steps
-  constexpr int NCB = 4;                          // 16-column blocks per wave (64 columns)
+  constexpr int KS = kLatDk / 32;  // 18 x32 score steps
   constexpr int NBUF = 4;
   constexpr int TILE = kT16 * kLatDk;
   constexpr int kRow16 = 16 * kLatDk;
-  constexpr int WLOADS = kT16 * kCpr16 / 64;      // 36 wave-loads per tile
-  constexpr int LBASE = WLOADS / NW, LEXTRA = WLOADS % NW;
-  constexpr int DPW = LBASE + (LEXTRA > 0 ? 1 : 0);
-  static_assert(NHB == 4 || NHB == 6, "64 or 96 heads");
-  static_assert(NCB * 16 * NW == kLatDv, "the waves cover the value columns");
+  constexpr bool SCORER = NCB == 0;
+  static_assert(R::cb0(8) == kLatDv / 16, "the output waves cover the value columns");
 
-  __shared__ __align__(16) _Float16 s_c[NBUF * TILE];
-  __shared__ __align__(16) half8_t s_p[2][NHB][64];    // [tile parity][block][lane]
-  __shared__ __align__(16) float s_alpha[2][NHB][16];  // [tile parity][block][head]
-  __shared__ int s_moved[2];                           // tile whose factors are not all 1
-
-  const int split = blockIdx.x;
-  const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool scorer = wave < NHB;
   const int l16 = lane & 15;
   const int lq = lane >> 4;
-
-  const int L = min(a.seq_lens[b], a.cap);
-  const int64_t start = (int64_t)split * a.chunk;
-  const int64_t end = min((int64_t)L, start + a.chunk);
-  const int64_t ws0 = (int64_t)b * a.Hq * a.S + split;
-
-  if (start >= end) {
-    if constexpr (FUSED) {
-      latent_fused_tail<NW * 64>(a, reinterpret_cast<float*>(s_c), 0, H);
-      return;
-    }
-    for (int idx = tid; idx < H * kLatDv; idx += NW * 64) {
-      const int h = idx / kLatDv, e = idx - (idx / kLatDv) * kLatDv;
-      a.ws_acc[(ws0 + (int64_t)h * a.S) * kLatDv + e] = 0.0f;
-    }
-    for (int h = tid; h < H; h += NW * 64) {
-      a.ws_m[ws0 + (int64_t)h * a.S] = -INFINITY;
-      a.ws_l[ws0 + (int64_t)h * a.S] = 0.0f;
-    }
-    return;
-  }
+  _Float16* const s_c = sh.c;
 
   const _Float16* __restrict__ cbase = reinterpret_cast<const _Float16*>(a.c) + (int64_t)b * a.stride_seq;
   const float* __restrict__ qb = a.q + (int64_t)b * a.Hq * kLatDk;
 
   // Tile staging as in the other f16 kernels: slot s of a tile holds row
   // s/72, logical chunk (s%72) ^ (row & 7); rows past the end re-read row
-  // end-1. The 36 wave-loads of a tile are spread over all waves (5 for waves
-  // 0-3, 4 for waves 4-7); the workgroup is its rows' only reader
-  // (non-temporal loads).
-  const int wl0 = wave * LBASE + min(wave, LEXTRA);
-  const int nwl = LBASE + (wave < LEXTRA ? 1 : 0);
+  // end-1. The 36 wave-loads of a tile are the output waves' (the workgroup
+  // is its rows' only reader: non-temporal loads).
+  const int ow = wave - R::NS;  // output wave index (negative for a scoring wave)
+  const int wl0 = SCORER ? 0 : ow * R::LB + min(ow, R::LX);
+  const int nwl = SCORER ? 0 : R::LB + (ow < R::LX ? 1 : 0);
   const uint32_t lds0 = lds_addr_of(s_c);
   const uint32_t row_bytes = (uint32_t)(a.stride_pos * 2);
   struct TileAt {
@@ -588,61 +587,51 @@ __global__ __launch_bounds__(512) void mla16w_split_kernel(MlaArgs a) {
     const int64_t tbc = tb < end ? tb : end - 1;
     return TileAt{cbase + tbc * a.stride_pos, (int)(end - 1 - tbc)};
   };
-  auto issue_load = [&](int cc, int bi, const TileAt& t) {
-    const int sl = (wl0 + cc) * 64 + lane;
-    const int srow = sl / kCpr16;
-    const int scol = ((sl - srow * kCpr16) ^ (srow & 7)) * 8;
-    const uint32_t off = (uint32_t)min(srow, t.last) * row_bytes + (uint32_t)(scol * 2);
-    const uint32_t dst = lds0 + (uint32_t)((bi * TILE + (wl0 + cc) * 64 * 8) * 2);
-    dma16s(off, t.base, __builtin_amdgcn_readfirstlane(dst), true);
-  };
   auto issue_tile = [&](int bi, int64_t tb) {
-    const TileAt t = tile_at(tb);
+    if constexpr (!SCORER) {
+      const TileAt t = tile_at(tb);
+      // The base is wave-uniform; say so, for the scalar operand of the load.
+      const uint64_t bu = reinterpret_cast<uint64_t>(t.base);
+      const void* base = reinterpret_cast<const void*>(
+          ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32)) << 32) |
+          (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bu));
 #pragma unroll
-    for (int cc = 0; cc < DPW; ++cc)
-      if (LEXTRA == 0 || cc < nwl) issue_load(cc, bi, t);
+      for (int cc = 0; cc < R::DPW; ++cc) {
+        if (R::LX != 0 && cc >= nwl) continue;
+        const int sl = (wl0 + cc) * 64 + lane;
+        const int srow = sl / kCpr16;
+        const int scol = ((sl - srow * kCpr16) ^ (srow & 7)) * 8;
+        const uint32_t off = (uint32_t)min(srow, t.last) * row_bytes + (uint32_t)(scol * 2);
+        const uint32_t dst = lds0 + (uint32_t)((bi * TILE + (wl0 + cc) * 64 * 8) * 2);
+        dma16s(off, base, __builtin_amdgcn_readfirstlane(dst), true);
+      }
+    }
   };
-
-  // Score fragments of step t (logical chunk 4t + lq of rows l16 and l16 + 16):
-  // the XOR touches bits 0-2 only, so even and odd steps have one base each.
-  const int sb0 = l16 * kLatDk + ((lq ^ (l16 & 7)) << 3);
-  const int sb1 = l16 * kLatDk + (((4 + lq) ^ (l16 & 7)) << 3);
-  // Value fragments (transpose reads) of this wave's 64 columns: rows
-  // 4*lq + l16/4 (+16), logical chunk 8w + 2cb + (l16&3)/2, plus 4 halves for
-  // odd l16 (the position order of P's layout).
-  const int r0 = 4 * lq + (l16 >> 2);
-  const int jv = (l16 & 3) >> 1;
-  const int hoff = (l16 & 1) * 4;
-  int bv[NCB];
-#pragma unroll
-  for (int u = 0; u < NCB; ++u) bv[u] = r0 * kLatDk + ((8 * wave + ((2 * u + jv) ^ (r0 & 7))) << 3) + hoff;
-
-  float m = -INFINITY, ll = 0.0f;  // scorer: head 16w + l16 (replicated over quarters); ll this lane's share
-  float4_t acc[NHB][NCB];
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) acc[hb][cb] = float4_t{0.f, 0.f, 0.f, 0.f};
+  // Everything of this wave but its loads of the newest tile has landed.
+  auto wait_but_newest = [&]() {
+    if constexpr (SCORER) {
+      wait_vm_lgkm0<0>();
+    } else if constexpr (R::LX == 0) {
+      wait_vm_lgkm0<R::DPW>();
+    } else {
+      if (nwl == R::DPW)
+        wait_vm_lgkm0<R::DPW>();
+      else
+        wait_vm_lgkm0<R::DPW - 1>();
+    }
+  };
 
   const int ntiles = (int)((end - start + kT16 - 1) / kT16);
-  if (tid < 2) s_moved[tid] = -1;
+  if (tid < 2) sh.moved[tid] = -1;
   // Prologue: tile 0; the query rows, rounded to f16 once and staged through
-  // the last NHB/2 tile buffers (H rows of 576 halves fill them exactly); tile
-  // 1 (before the staging when its buffer is not among them, else after). The
-  // whole workgroup reads the f32 rows as consecutive float4s, so every load
-  // instruction covers whole lines; a scoring wave's own fragments (16 rows,
-  // 32 bytes apart in each) would touch sixteen lines per instruction.
-  constexpr int QB0 = NBUF - NHB / 2;                 // first buffer of the staged rows
-  constexpr int QV = H * (kLatDk / 4) / (NW * 64);    // float4 per thread
+  // the last NHB/2 tile buffers (H rows of 576 halves fill them exactly) with
+  // whole-line loads by the whole workgroup; tile 1 (before the staging when
+  // its buffer is not among them, else after).
+  constexpr int QB0 = NBUF - NHB / 2;
+  constexpr int QV = H * (kLatDk / 4) / (NW * 64);  // float4 per thread
   static_assert(H * (kLatDk / 4) % (NW * 64) == 0, "whole float4 rounds");
   static_assert(H * kLatDk <= (NBUF - QB0) * TILE, "the staged rows fit");
   _Float16* const sq = s_c + QB0 * TILE;
-  auto wait_tile1 = [&]() {  // everything but this wave's loads of tile 1 has landed
-    if (nwl == DPW)
-      wait_vm_lgkm0<DPW>();
-    else
-      wait_vm_lgkm0<(LEXTRA == 0 ? DPW : DPW - 1)>();
-  };
   issue_tile(0, start);
   {
     float4 qv[QV];
@@ -661,23 +650,25 @@ __global__ __launch_bounds__(512) void mla16w_split_kernel(MlaArgs a) {
     }
   }
   if constexpr (QB0 >= 2)
-    wait_tile1();
+    wait_but_newest();
   else
     wait_vm_lgkm0<0>();
   raw_barrier();
-  half8_t qf[KS];  // head 16w + l16, columns 32t + 8lq .. +7
-  if (scorer) {
-    const _Float16* qrow = sq + (16 * wave + l16) * kLatDk;
+  // A scoring wave's heads 32w + 16hb + l16, columns 32t + 8lq .. +7.
+  half8_t qf[SCORER ? 2 : 1][SCORER ? KS : 1];
+  if constexpr (SCORER) {
 #pragma unroll
-    for (int t = 0; t < KS; ++t) qf[t] = *reinterpret_cast<const half8_t*>(qrow + (((4 * t + lq) ^ (l16 & 7)) << 3));
-  } else {
+    for (int hb = 0; hb < 2; ++hb) {
+      const _Float16* qrow = sq + (32 * wave + 16 * hb + l16) * kLatDk;
 #pragma unroll
-    for (int t = 0; t < KS; ++t) qf[t] = half8_t{};
+      for (int t = 0; t < KS; ++t)
+        qf[hb][t] = *reinterpret_cast<const half8_t*>(qrow + (((4 * t + lq) ^ (l16 & 7)) << 3));
+    }
   }
   // The staged rows are read before any tile load may overwrite them; tile 0
   // (and the query) landed, at most this wave's loads of tile 1 remain.
   if constexpr (QB0 >= 2) {
-    wait_tile1();
+    wait_but_newest();
     raw_barrier();
   } else {
     wait_vm_lgkm0<0>();
@@ -685,149 +676,210 @@ __global__ __launch_bounds__(512) void mla16w_split_kernel(MlaArgs a) {
     issue_tile(1, start + kT16);
   }
 
-  // Output product of tile j: acc = alp * acc + P x V over this wave's 64
-  // columns, for every head block.
-  auto output = [&](int j) {
-    const _Float16* prv = s_c + (j % NBUF) * TILE;
-    const int par = j & 1;
-    if (s_moved[par] == j) {
-      // Accumulator items are heads 4*lq + e of each block.
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) {
-        const float4_t alp = *reinterpret_cast<const float4_t*>(&s_alpha[par][hb][4 * lq]);
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[hb][cb][e] *= alp[e];
-      }
-    }
-    half8_t pp[NHB];
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) pp[hb] = s_p[par][hb][lane];
-    auto vread = [&](int cb) {
-      const _Float16* vp = prv + bv[cb];
-      const half4_t v0 = lds_read_tr(vp);
-      const half4_t v1 = lds_read_tr(vp + kRow16);
-      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    half8_t vn = vread(0);
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const half8_t vv = vn;
-      if (cb + 1 < NCB) vn = vread(cb + 1);
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) acc[hb][cb] = mfma32(pp[hb], vv, acc[hb][cb]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  for (int i = 0;; ++i) {
-    const bool more = i < ntiles;  // tile i exists (else only tile i-1's output remains)
-    const int64_t tb = start + (int64_t)i * kT16;
-    // Tile i+2 goes into the buffer of tile i-2, whose output product ran
-    // before the last barrier; tiles past the end are not requested.
-    const bool load_next = more && tb + 2 * kT16 < end;
-    if (more && scorer) {
-      // ---- full scores of head block w on tile i, with tile i+2's loads
-      // issued between the steps; then the block's online softmax ----
+  if constexpr (SCORER) {
+    // Score fragments of step t (logical chunk 4t + lq of rows l16 and
+    // l16 + 16): the XOR touches bits 0-2 only, so even and odd steps have one
+    // base each.
+    const int sb0 = l16 * kLatDk + ((lq ^ (l16 & 7)) << 3);
+    const int sb1 = l16 * kLatDk + (((4 + lq) ^ (l16 & 7)) << 3);
+    auto soff = [&](int t) { return ((t & 1) ? sb1 : sb0) + 64 * (t >> 1); };
+    float m[2] = {-INFINITY, -INFINITY}, ll[2] = {0.0f, 0.0f};  // heads 32w + 16hb + l16; ll this lane's share
+    for (int i = 0; i < ntiles; ++i) {
+      const int64_t tb = start + (int64_t)i * kT16;
       const _Float16* cur = s_c + (i % NBUF) * TILE;
-      const TileAt tn = tile_at(tb + 2 * kT16);
-      float4_t se[2], so[2];  // even and odd steps, rows 0-15 and 16-31
-      se[0] = se[1] = so[0] = so[1] = float4_t{0.f, 0.f, 0.f, 0.f};
-      half8_t n0 = *reinterpret_cast<const half8_t*>(cur + sb0);
-      half8_t n1 = *reinterpret_cast<const half8_t*>(cur + sb0 + kRow16);
+      float4_t s[2][2];  // [block][rows 0-15, 16-31]
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) s[hb][0] = s[hb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+      // Operands two steps ahead.
+      half8_t k0[3], k1[3];
+      k0[0] = *reinterpret_cast<const half8_t*>(cur + soff(0));
+      k1[0] = *reinterpret_cast<const half8_t*>(cur + soff(0) + kRow16);
+      k0[1] = *reinterpret_cast<const half8_t*>(cur + soff(1));
+      k1[1] = *reinterpret_cast<const half8_t*>(cur + soff(1) + kRow16);
 #pragma unroll
       for (int t = 0; t < KS; ++t) {
-        const half8_t a0 = n0, a1 = n1;
-        if (t + 1 < KS) {
-          const int o = ((t + 1) & 1 ? sb1 : sb0) + 64 * ((t + 1) >> 1);
-          n0 = *reinterpret_cast<const half8_t*>(cur + o);
-          n1 = *reinterpret_cast<const half8_t*>(cur + o + kRow16);
+        if (t + 2 < KS) {
+          k0[(t + 2) % 3] = *reinterpret_cast<const half8_t*>(cur + soff(t + 2));
+          k1[(t + 2) % 3] = *reinterpret_cast<const half8_t*>(cur + soff(t + 2) + kRow16);
         }
-        if (t & 1) {
-          so[0] = mfma32(a0, qf[t], so[0]);
-          so[1] = mfma32(a1, qf[t], so[1]);
-        } else {
-          se[0] = mfma32(a0, qf[t], se[0]);
-          se[1] = mfma32(a1, qf[t], se[1]);
+        const half8_t a0 = k0[t % 3], a1 = k1[t % 3];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          s[hb][0] = mfma32(a0, qf[hb][t], s[hb][0]);
+          s[hb][1] = mfma32(a1, qf[hb][t], s[hb][1]);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (load_next && (t & 3) == 3 && (LEXTRA == 0 || (t >> 2) < nwl)) issue_load(t >> 2, (i + 2) % NBUF, tn);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (load_next && (LEXTRA == 0 || 4 < nwl)) issue_load(4, (i + 2) % NBUF, tn);
-      const float4_t x0 = se[0] + so[0], x1 = se[1] + so[1];
       const int rel = (int)(end - tb);  // positions of tile i before the end (> 0)
-      float v[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = 4 * lq + e < rel ? x0[e] * a.qscale : -INFINITY;
-        v[4 + e] = 16 + 4 * lq + e < rel ? x1[e] * a.qscale : -INFINITY;
-        mx = fmaxf(mx, fmaxf(v[e], v[4 + e]));
-      }
-      mx = max_xor32(max_xor16(mx));
-      // m moves to the tile's maximum only when that exceeds it by more than
-      // kLazyMax (base 2): the weights stay below 2^kLazyMax (f16 holds
-      // them), and most tiles keep m, so nothing is rescaled.
-      const float mn = mx > m + kLazyMax ? mx : m;
-      const float mu = (mn == -INFINITY) ? 0.0f : mn;
-      const float al = fast_exp2(m - mu);
-      half8_t pw;
-      float ls = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const _Float16 pj = (_Float16)fast_exp2(v[j] - mu);
-        pw[j] = pj;
-        ls += (float)pj;
-      }
-      ll = fmaf(ll, al, ls);
-      m = mn;
       const int par = i & 1;
-      s_p[par][wave][lane] = pw;
-      if (lq == 0) s_alpha[par][wave][l16] = al;
-      if (__any(al != 1.0f) && lane == 0) s_moved[par] = i;
-    } else if (load_next) {
-      const TileAt tn = tile_at(tb + 2 * kT16);
+      bool moved = false;
 #pragma unroll
-      for (int cc = 0; cc < DPW; ++cc)
-        if (LEXTRA == 0 || cc < nwl) issue_load(cc, (i + 2) % NBUF, tn);
-    }
-    if (i > 0) output(i - 1);
-    if (!more) break;
-    // Tile i+1 (requested one iteration ago, or in the prologue) must have
-    // landed; tile i+2's loads, if any, stay in flight.
-    if (load_next) {
-      if (nwl == DPW)
-        wait_vm_lgkm0<DPW>();
-      else
-        wait_vm_lgkm0<(LEXTRA == 0 ? DPW : DPW - 1)>();
-    } else {
-      wait_vm_lgkm0<0>();
-    }
-    raw_barrier();  // P and factors of tile i, tile i+1; tile i-1's buffer is free after the next output
-  }
-  // Drain the tile loads still in flight before the workgroup can retire.
-  wait_vm_lgkm0<0>();
-
-  // Partials: heads 16hb + 4*lq + e, columns 64w + 16cb + l16.
+      for (int hb = 0; hb < 2; ++hb) {
+        float v[8];
+        float mx = -INFINITY;
 #pragma unroll
-  for (int hb = 0; hb < NHB; ++hb)
+        for (int e = 0; e < 4; ++e) {
+          v[e] = 4 * lq + e < rel ? s[hb][0][e] * a.qscale : -INFINITY;
+          v[4 + e] = 16 + 4 * lq + e < rel ? s[hb][1][e] * a.qscale : -INFINITY;
+          mx = fmaxf(mx, fmaxf(v[e], v[4 + e]));
+        }
+        mx = max_xor32(max_xor16(mx));
+        // m moves to the tile's maximum only when that exceeds it by more than
+        // kLazyMax (base 2): the weights stay below 2^kLazyMax (f16 holds
+        // them), and most tiles keep m, so nothing is rescaled.
+        const float mn = mx > m[hb] + kLazyMax ? mx : m[hb];
+        const float mu = (mn == -INFINITY) ? 0.0f : mn;
+        const float al = fast_exp2(m[hb] - mu);
+        half8_t pw;
+        float ls = 0.0f;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int head = 16 * hb + 4 * lq + e;
-        const int col = 64 * wave + 16 * cb + l16;
-        put_partial(a.ws_acc + (ws0 + (int64_t)head * a.S) * kLatDv + col, acc[hb][cb][e], FUSED && a.S > 1);
+        for (int j = 0; j < 8; ++j) {
+          const _Float16 pj = (_Float16)fast_exp2(v[j] - mu);
+          pw[j] = pj;
+          ls += (float)pj;
+        }
+        ll[hb] = fmaf(ll[hb], al, ls);
+        m[hb] = mn;
+        moved = moved || al != 1.0f;
+        sh.p[(par * NHB + 2 * wave + hb) * 64 + lane] = pw;
+        if (lq == 0) sh.alpha[(par * NHB + 2 * wave + hb) * 16 + l16] = al;
       }
-  const float l = sum_xor32(sum_xor16(ll));
-  if (scorer && lq == 0) {
-    const int head = 16 * wave + l16;
-    put_partial(a.ws_m + ws0 + (int64_t)head * a.S, m * kLn2, FUSED && a.S > 1);
-    put_partial(a.ws_l + ws0 + (int64_t)head * a.S, l, FUSED && a.S > 1);
+      if (__any(moved) && lane == 0) sh.moved[par] = i;
+      wait_vm_lgkm0<0>();
+      raw_barrier();  // P and factors of tile i; tile i+1
+    }
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float l = sum_xor32(sum_xor16(ll[hb]));
+      if (lq == 0) {
+        const int head = 32 * wave + 16 * hb + l16;
+        put_partial(a.ws_m + ws0 + (int64_t)head * a.S, m[hb] * kLn2, FUSED && a.S > 1);
+        put_partial(a.ws_l + ws0 + (int64_t)head * a.S, l, FUSED && a.S > 1);
+      }
+    }
+  } else {
+    const int cb0 = R::cb0(wave);
+    // Value fragments (transpose reads): rows 4*lq + l16/4 (+16), logical
+    // chunk 2c + (l16&3)/2 of column block c, plus 4 halves for odd l16 (the
+    // position order of P's layout).
+    const int r0 = 4 * lq + (l16 >> 2);
+    const int jv = (l16 & 3) >> 1;
+    const int hoff = (l16 & 1) * 4;
+    auto voff = [&](int u) { return r0 * kLatDk + (((2 * (cb0 + u) + jv) ^ (r0 & 7)) << 3) + hoff; };
+    float4_t acc[NHB][NCB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[hb][cb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    auto output = [&](int j) {
+      const _Float16* prv = s_c + (j % NBUF) * TILE;
+      const int par = j & 1;
+      if (sh.moved[par] == j) {
+        // Accumulator items are heads 4*lq + e of each block.
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          const float4_t alp = *reinterpret_cast<const float4_t*>(&sh.alpha[(par * NHB + hb) * 16 + 4 * lq]);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[hb][cb][e] *= alp[e];
+        }
+      }
+      half8_t pp[NHB];
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) pp[hb] = sh.p[(par * NHB + hb) * 64 + lane];
+      auto vread = [&](int u) {
+        const _Float16* vp = prv + voff(u);
+        const half4_t v0 = lds_read_tr(vp);
+        const half4_t v1 = lds_read_tr(vp + kRow16);
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      half8_t vn = vread(0);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const half8_t vv = vn;
+        if (cb + 1 < NCB) vn = vread(cb + 1);
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) acc[hb][cb] = mfma32(pp[hb], vv, acc[hb][cb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    for (int i = 0;; ++i) {
+      const bool more = i < ntiles;  // tile i exists (else only tile i-1's output remains)
+      const int64_t tb = start + (int64_t)i * kT16;
+      // Tile i+2 goes into the buffer of tile i-2, whose output product ran
+      // before the last barrier; tiles past the end are not requested.
+      const bool load_next = more && tb + 2 * kT16 < end;
+      if (load_next) issue_tile((i + 2) % NBUF, tb + 2 * kT16);
+      if (i > 0) output(i - 1);
+      if (!more) break;
+      // Tile i+1 (requested one iteration ago, or in the prologue) must have
+      // landed; tile i+2's loads, if any, stay in flight.
+      if (load_next)
+        wait_but_newest();
+      else
+        wait_vm_lgkm0<0>();
+      raw_barrier();
+    }
+    // Drain the tile loads still in flight before the workgroup can retire.
+    wait_vm_lgkm0<0>();
+    // Partials: heads 16hb + 4*lq + e, columns 16(cb0 + cb) + l16.
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int head = 16 * hb + 4 * lq + e;
+          const int col = 16 * (cb0 + cb) + l16;
+          put_partial(a.ws_acc + (ws0 + (int64_t)head * a.S) * kLatDv + col, acc[hb][cb][e], FUSED && a.S > 1);
+        }
   }
-  if constexpr (FUSED) latent_fused_tail<NW * 64>(a, reinterpret_cast<float*>(s_c), 0, H);
+}
+
+template <int NHB, bool FUSED>
+__global__ __launch_bounds__(512) void mla16d_split_kernel(MlaArgs a) {
+  constexpr int H = 16 * NHB;
+  constexpr int NBUF = 4;
+  constexpr int TILE = kT16 * kLatDk;
+  using R = Mla16dRoles<NHB>;
+  static_assert(NHB == 4 || NHB == 6, "64 or 96 heads");
+  __shared__ __align__(16) _Float16 s_c[NBUF * TILE];
+  __shared__ __align__(16) half8_t s_p[2 * NHB * 64];
+  __shared__ __align__(16) float s_alpha[2 * NHB * 16];
+  __shared__ int s_moved[2];
+
+  const int split = blockIdx.x;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int L = min(a.seq_lens[b], a.cap);
+  const int64_t start = (int64_t)split * a.chunk;
+  const int64_t end = min((int64_t)L, start + a.chunk);
+  const int64_t ws0 = (int64_t)b * a.Hq * a.S + split;
+  if (start >= end) {
+    if constexpr (FUSED) {
+      latent_fused_tail<512>(a, reinterpret_cast<float*>(s_c), 0, H);
+      return;
+    }
+    for (int idx = tid; idx < H * kLatDv; idx += 512) {
+      const int h = idx / kLatDv, e = idx - (idx / kLatDv) * kLatDv;
+      a.ws_acc[(ws0 + (int64_t)h * a.S) * kLatDv + e] = 0.0f;
+    }
+    for (int h = tid; h < H; h += 512) {
+      a.ws_m[ws0 + (int64_t)h * a.S] = -INFINITY;
+      a.ws_l[ws0 + (int64_t)h * a.S] = 0.0f;
+    }
+    return;
+  }
+  const Mla16dShared sh{s_c, s_p, s_alpha, s_moved};
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave < R::NS)
+    mla16d_role<NHB, 0, FUSED>(a, sh, start, end, ws0, b);
+  else if (R::shared(wave))
+    mla16d_role<NHB, R::kShared, FUSED>(a, sh, start, end, ws0, b);
+  else
+    mla16d_role<NHB, R::kAlone, FUSED>(a, sh, start, end, ws0, b);
+  if constexpr (FUSED) latent_fused_tail<512>(a, reinterpret_cast<float*>(s_c), 0, H);
 }
 
 typedef __attribute__((address_space(3))) float lds_float_t;
@@ -1172,8 +1224,8 @@ static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void*
         threads = (H / 32) * 128;
         groups = 2;
       } else if (!idx) {
-        // Contiguous caches at longer contexts: the register-blocked form.
-        kern = s.fused ? mla16w_split_kernel<H / 16, true> : mla16w_split_kernel<H / 16, false>;
+        // Contiguous caches at longer contexts: the dedicated-role form.
+        kern = s.fused ? mla16d_split_kernel<H / 16, true> : mla16d_split_kernel<H / 16, false>;
         threads = 512;
         groups = 1;
       }

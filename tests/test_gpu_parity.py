@@ -365,17 +365,18 @@ def _latent_batch(name, lens, cap, hq, seed):
 @pytest.mark.parametrize("hq", [64, 96])
 @pytest.mark.parametrize("lens,S", [((4097,), 130), ((20000,), 150), ((5000, 300), 129),
                                     ((33, 2000), 200)])
-def test_latent_f16_wave_per_block_kernel(hq, lens, S):
+def test_latent_f16_dedicated_role_kernel(hq, lens, S):
     """64 and 96 f16 heads with more than 128 (split, sequence) pairs run the
-    wave-per-block kernel (8 waves of 512 threads; one wave scores each
-    16-head block, every wave multiplies all blocks' weights; four tile
-    buffers): one-tile slices with a one-row tail (4097 at S = 130), slices of
+    dedicated-role kernel (8 waves of 512 threads; hq/32 scoring waves of 32
+    heads, the other waves own the value columns and multiply all blocks'
+    weights; four tile buffers; the query staged through the tile buffers):
+    one-tile slices with a one-row tail (4097 at S = 130), slices of
     134 rows (four tiles and a 6-row tail), a batch of two whose short
     sequence leaves empty slices, and a batch whose first sequence has fewer
     rows than one tile. NaN rows past every length."""
     from split_kv_flash_amd import attn_decode_kernel_info
 
-    case = _latent_batch(f"lat16w-{hq}-{'-'.join(map(str, lens))}", list(lens), max(lens) + 7, hq,
+    case = _latent_batch(f"lat16d-{hq}-{'-'.join(map(str, lens))}", list(lens), max(lens) + 7, hq,
                          seed=7700 + hq + S)
     out, lse, call = run_gpu(case, n_splits=S)
     info = attn_decode_kernel_info(call.desc, call.plan)
@@ -386,13 +387,13 @@ def test_latent_f16_wave_per_block_kernel(hq, lens, S):
     free()
 
 
-def test_latent_f16_wave_per_block_kernel_dominant_key_in_second_tile():
+def test_latent_f16_dedicated_role_kernel_dominant_key_in_second_tile():
     """Position 32, the first row of the first slice's second tile, holds a
     key that dominates every head's scores: each head returns that row's
-    values, so a slip in a block's scores, in the published weights or in the
-    tile buffers' rotation shows."""
+    values, so a slip in a block's scores, in the published weights, in the
+    output waves' column blocks or in the tile buffers' rotation shows."""
     L, S = 8300, 129  # chunk 65: slice 0 is tiles [0, 32), [32, 64), [64, 65)
-    case = synthetic.latent_case("lat16w-dom", seq_len=L, kv_dtype="f32", seed=19, scale=1 / 24)
+    case = synthetic.latent_case("lat16d-dom", seq_len=L, kv_dtype="f32", seed=19, scale=1 / 24)
     q = case.q[0, 0].astype(np.float64)
     case.q[0, :] = case.q[0, 0]
     row = q / np.linalg.norm(q) * 24 * 30 / np.linalg.norm(q)  # score ~ 30
@@ -401,7 +402,7 @@ def test_latent_f16_wave_per_block_kernel_dominant_key_in_second_tile():
     case.kv_dtype = "f16"
     out, _, call = run_gpu(case, n_splits=S)
     ref, _ = oracle_out(case)
-    assert_parity(case, out, ref, tight=False, label="latent f16 dominant, wave-per-block")
+    assert_parity(case, out, ref, tight=False, label="latent f16 dominant, dedicated roles")
     for h in (0, 17, 50, 95):
         np.testing.assert_allclose(out[0, h], ref[0, h], rtol=0, atol=ABS_GATE["f16"])
 
