@@ -88,7 +88,10 @@ __device__ __forceinline__ void latent_fused_tail(const MlaArgs& a, float* s_lds
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int t = ((int)blockIdx.y * a.Hq + h0) * 2;
-    latent_merge_by_wave<1, 0>(a, t, t + 2 * H, __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), NT / 64);
+    // Inlined here: a call would put the kernel's arguments in scratch
+    // memory for the whole kernel.
+    [[clang::always_inline]] latent_merge_by_wave<1, 0>(a, t, t + 2 * H,
+                                                        __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), NT / 64);
     return;
   }
   const uint32_t n = gridDim.x * gridDim.y * gridDim.z;
