@@ -177,7 +177,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   // pre-scaled into base-2 units; loaded after the first tile is requested,
   // so the query's memory latency overlaps the first K/V loads.
   float qr[GH][DPL];
-  auto load_q = [&]() {
+  // Inlined at both paged modes' call sites: a call would put the kernel's
+  // state in scratch memory.
+  auto load_q = [&]() __attribute__((always_inline)) {
     const int64_t qbase = ((int64_t)b * a.Hq + h0 + hs * GH) * D;
     if (a.q_dtype == 0)
       load_q_slice<GH, D, RL, VEC, NL>(qr, reinterpret_cast<const float*>(a.q) + qbase, li, a.qscale);
