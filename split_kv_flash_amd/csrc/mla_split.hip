@@ -1212,8 +1212,14 @@ static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void*
     threads = mla32_blocks(H) * 256;
     groups = mla32_groups(H);
   } else {
-    kern = idx ? (s.fused ? mla16_split_kernel<mla16_blocks(H), true, true> : mla16_split_kernel<mla16_blocks(H), true, false>)
-               : (s.fused ? mla16_split_kernel<mla16_blocks(H), false, true> : mla16_split_kernel<mla16_blocks(H), false, false>);
+    if constexpr (H == 64 || H == 96) {
+      // (Contiguous caches never take the whole-head form of this kernel
+      // for these head counts, so it is not built for them.)
+      kern = s.fused ? mla16_split_kernel<mla16_blocks(H), true, true> : mla16_split_kernel<mla16_blocks(H), true, false>;
+    } else {
+      kern = idx ? (s.fused ? mla16_split_kernel<mla16_blocks(H), true, true> : mla16_split_kernel<mla16_blocks(H), true, false>)
+                 : (s.fused ? mla16_split_kernel<mla16_blocks(H), false, true> : mla16_split_kernel<mla16_blocks(H), false, false>);
+    }
     threads = mla16_blocks(H) * 128;
     groups = mla16_groups(H);
     if constexpr (H == 64 || H == 96) {

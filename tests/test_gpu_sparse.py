@@ -86,9 +86,12 @@ def test_dsa_latent_top_2048(kv):
     free()
 
 
-@pytest.mark.parametrize("kv,hq", [("f32", 32), ("f32", 64), ("f32", 128), ("f16", 32), ("f16", 64),
-                                   ("f16", 128)])
+@pytest.mark.parametrize("kv,hq", [("f32", 32), ("f32", 64), ("f32", 96), ("f32", 128), ("f16", 32),
+                                   ("f16", 64), ("f16", 96), ("f16", 128)])
 def test_latent_index_list_head_counts(kv, hq):
+    """Every head count over index lists; S = 130 takes the whole-head
+    kernels (more than 128 (split, sequence) pairs), the others the split
+    head groups."""
     for L, S in ((1000, 0), (33, 2), (1, 1), (4097, 5), (4097, 130)):
         case = synthetic.indexed_case(f"lat-idx-{kv}-{hq}-{L}", pool_rows=L + 2000, seq_lens=[L],
                                       num_q_heads=hq, num_kv_heads=1, head_dim=576, kv_dtype=kv,
