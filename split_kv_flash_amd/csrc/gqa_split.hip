@@ -109,6 +109,77 @@ __device__ __forceinline__ void load_q_slice(float (&qr)[G][D / RL], const QT* q
         qr[h][j * VEC + e] = to_f32(q[h * D + j * RL * VEC + li * VEC + e]) * qscale;
 }
 
+// Largest slices first, for a batch of 2 to 64 sequences. Workgroups start
+// in the order of their pair index k = blockIdx.y + S * blockIdx.z, so k is
+// mapped to the (split, sequence) pairs ordered by work: every full-chunk
+// slice first (sequence by sequence), then the partial last slices, longest
+// first, then the empty ones. Short slices then fill the grid's tail instead
+// of full ones starting last (list scheduling, largest job first); what each
+// pair computes and where it writes are unchanged. Wave 0 finds the pair
+// (lane t holds sequence t) and publishes it in LDS. Lengths are clamped as
+// the slices use them; in the one-launch form a rejected length counts as
+// empty, so that sequence's split-0 pair still writes its NaN result.
+__device__ __forceinline__ void work_ordered_pair(const GqaArgs& a, bool fused, int* s_pair, int& split,
+                                                  int& b) {
+  const int B = gridDim.z;
+  split = blockIdx.y;
+  b = blockIdx.z;
+  if (B == 1 || B > 64) return;
+  if (threadIdx.x < 64) {
+    const int t = threadIdx.x;
+    const int S = a.S;
+    const int64_t span = (int64_t)S * a.chunk;
+    int64_t le = 0;
+    if (t < B) {
+      const int lraw = a.seq_lens[t];
+      const bool ok = !fused || (lraw >= 1 && lraw <= a.cap && (int64_t)lraw <= span);
+      le = ok ? max((int64_t)0, min((int64_t)min(lraw, a.cap), span)) : 0;
+    }
+    const int nf = (int)(le / a.chunk);                 // full-chunk slices
+    const int r = (int)(le - (int64_t)nf * a.chunk);    // rows of the partial last slice (0: none)
+    const int n = nf + (r > 0 ? 1 : 0);
+    const int e = t < B ? S - n : 0;                    // empty slices
+    int pf = 0, pe = 0, rk = 0, F = 0, P = 0;
+    for (int u = 0; u < B; ++u) {
+      const int nfu = __builtin_amdgcn_readlane(nf, u);
+      const int ru = __builtin_amdgcn_readlane(r, u);
+      const int eu = __builtin_amdgcn_readlane(e, u);
+      pf += u < t ? nfu : 0;
+      pe += u < t ? eu : 0;
+      rk += (ru > r || (ru == r && u < t)) ? 1 : 0;  // rank among the partial slices (r > 0)
+      F += nfu;
+      P += ru > 0 ? 1 : 0;
+    }
+    const int k = (int)blockIdx.y + S * (int)blockIdx.z;
+    bool mine;
+    int sp;
+    if (k < F) {
+      mine = t < B && k >= pf && k < pf + nf;
+      sp = k - pf;
+    } else if (k < F + P) {
+      mine = t < B && r > 0 && rk == k - F;
+      sp = nf;
+    } else {
+      const int q = k - F - P;
+      mine = t < B && q >= pe && q < pe + e;
+      sp = n + (q - pe);
+    }
+    // Exactly one lane owns k (the map is a bijection); lane 0 writes the
+    // unmapped pair first, so the pair read below is always in range.
+    if (t == 0) {
+      s_pair[0] = split;
+      s_pair[1] = b;
+    }
+    if (mine && sp >= 0 && sp < S) {
+      s_pair[0] = sp;
+      s_pair[1] = t;
+    }
+  }
+  __syncthreads();
+  split = s_pair[0];
+  b = s_pair[1];
+}
+
 template <typename KV, int G, int D, bool PAGED, int RL, int R, int HS, int WPE, bool FUSED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void gqa_split_kernel(
     GqaArgs a) {
@@ -127,9 +198,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   __shared__ float s_m[NW][G];
   __shared__ float s_l[NW][G];
 
+  __shared__ int s_pair[2];
   const int g = blockIdx.x;
-  const int split = blockIdx.y;
-  const int b = blockIdx.z;
+  int split, b;
+  work_ordered_pair(a, FUSED, s_pair, split, b);
   const int Hkv = gridDim.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
