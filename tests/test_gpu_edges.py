@@ -97,6 +97,37 @@ def test_large_ragged_paged_batch_of_short_sequences():
     free()
 
 
+@pytest.mark.parametrize("B", [2, 64, 65])
+def test_work_ordered_pairs_at_the_batch_limits(B):
+    """Batches of 2 to 64 sequences start their (split, sequence) pairs in
+    order of work (full slices, partial slices longest first, empty ones);
+    65 sequences keep the grid's own order. Lengths give every kind of slice:
+    whole chunks only, a partial last slice, one position, and sequences
+    with empty slices. Both entry points, against the oracle on sampled
+    heads of every sequence."""
+    rng = np.random.default_rng(12010 + B)
+    S = 5
+    lens = rng.integers(1, 5 * 96, endpoint=True, size=B)
+    lens[0] = 5 * 96           # every slice full (chunk 96)
+    lens[1] = 1
+    if B > 2:
+        lens[2] = 96 * 2       # two full slices, three empty ones
+    case = synthetic.gqa_case(f"wo{B}", seq_lens=lens.tolist(), num_q_heads=8, num_kv_heads=2,
+                              head_dim=64, kv_dtype="f32", seed=12010 + B)
+    out, lse, call = run_gpu(case, n_splits=S)
+    assert (call.plan.n_splits, call.plan.chunk) == (S, 96)
+    heads = [(b, h) for b in range(B) for h in (0, 5)]
+    ref, rlse = oracle_out(case, heads=heads)
+    mask = np.zeros(out.shape, dtype=bool)
+    for b, h in heads:
+        mask[b, h] = True
+    assert_parity(case, np.where(mask, out, np.nan), ref, label=f"B={B}")
+    out1, lse1, _ = run_gpu_fused(case, n_splits=S)
+    assert_parity(case, np.where(mask, out1, np.nan), ref, label=f"B={B} one-launch")
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(out1))
+    free()
+
+
 @pytest.mark.parametrize("S", [257, 1000, 4096])
 def test_combine_with_many_splits(S):
     """Split counts beyond one 64-split pass and beyond the combine's four
