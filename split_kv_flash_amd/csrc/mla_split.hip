@@ -957,6 +957,7 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
     scol[c] = real ? ((sl - (sl / kCpr32) * kCpr32) ^ (sl / kCpr32)) * 4 : 0;
   }
   const uint32_t lds0 = lds_addr_of(s_c);
+  const uint32_t row_bytes32 = (uint32_t)(a.stride_pos * 4);  // a tile spans 16 rows: offsets fit 32 bits
   // Index-list layout: the next tile's rows (lane r < 16) and the bad-row
   // masks of the tiles in the three buffers. Padding slots read tile row 0.
   int32_t nidx = 0;
@@ -975,12 +976,20 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
       }
       nidx = load_tile_index(a, b, tb + kT32, end, kT32);  // the next tile's rows
     } else {
+      // One wave-uniform base per tile (rows past the end re-read row end-1;
+      // padding slots re-read the tile's first row) and 32-bit lane offsets.
+      const int64_t tbc = tb < end ? tb : end - 1;
+      const uint64_t bu = reinterpret_cast<uint64_t>(cbase + tbc * a.stride_pos);
+      const void* tbase = reinterpret_cast<const void*>(
+          ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32)) << 32) |
+          (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bu));
+      const int last = (int)(end - 1 - tbc);
 #pragma unroll
       for (int c = 0; c < DPW; ++c) {
-        int64_t pos = srow[c] < 0 ? start : tb + srow[c];
-        pos = pos < end ? pos : end - 1;
+        const int row = srow[c] < 0 ? 0 : min(srow[c], last);
+        const uint32_t off = (uint32_t)row * row_bytes32 + (uint32_t)(scol[c] * 4);
         const uint32_t dst = lds0 + (uint32_t)((bi * TSTRIDE + (wave * DPW + c) * 64 * 4) * 4);
-        dma16(cbase + pos * a.stride_pos + scol[c], __builtin_amdgcn_readfirstlane(dst), a.nt);
+        dma16s(off, tbase, __builtin_amdgcn_readfirstlane(dst), a.nt);
       }
     }
   };
