@@ -293,19 +293,26 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
     // Every wave issues DPW/2 wave-loads of K, then the same of V: the whole
     // K half is requested before any V row, the order the scores need it in.
     const int wq0 = __builtin_amdgcn_readfirstlane(wave * (DPW / 2));
+    // One wave-uniform base per tile and half, 32-bit lane offsets (the host
+    // bounds a row step to 16 MB, so 32 rows stay below 2^32 bytes).
+    const uint32_t row_bytes = (uint32_t)(a.stride_pos * (int64_t)sizeof(KT));
     auto issue = [&](int buf, int64_t tb) {
+      const int64_t tbc = min(tb, stop - 1);
+      const int last = (int)(stop - 1 - tbc);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const KT* __restrict__ src0 = half ? vp : kp;
+        const uint64_t bu = reinterpret_cast<uint64_t>((half ? vp : kp) + tbc * a.stride_pos);
+        const void* base = reinterpret_cast<const void*>(
+            ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32)) << 32) |
+            (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bu));
 #pragma unroll
         for (int c = 0; c < DPW / 2; ++c) {
           const int wh = wq0 + c;  // wave-load within the half
           const int sl = wh * 64 + lane;
           const int row = sl / CPR, p = sl - (sl / CPR) * CPR;
-          const int64_t pos = min(tb + row, stop - 1);
-          const KT* src = src0 + pos * a.stride_pos + ((p ^ (row & 7)) * 8);
+          const uint32_t off = (uint32_t)min(row, last) * row_bytes + (uint32_t)((p ^ (row & 7)) * 16);
           const uint32_t dst = lds_kv + (uint32_t)(((buf * 2 + half) * T * D + wh * 512) * 2);
-          dma16(src, __builtin_amdgcn_readfirstlane(dst), DS > 1);
+          dma16s(off, base, __builtin_amdgcn_readfirstlane(dst), DS > 1);
         }
       }
     };
