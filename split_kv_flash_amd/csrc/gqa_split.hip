@@ -164,15 +164,14 @@ __device__ __forceinline__ void work_ordered_pair(const GqaArgs& a, bool fused, 
       mine = t < B && q >= pe && q < pe + e;
       sp = n + (q - pe);
     }
-    // Exactly one lane owns k (the map is a bijection); lane 0 writes the
-    // unmapped pair first, so the pair read below is always in range.
-    if (t == 0) {
-      s_pair[0] = split;
-      s_pair[1] = b;
-    }
-    if (mine && sp >= 0 && sp < S) {
-      s_pair[0] = sp;
-      s_pair[1] = t;
+    // Exactly one lane owns k (the map is a bijection). One lane writes: the
+    // owner, or lane 0 with the unmapped pair should none match, so the pair
+    // read below is always in range.
+    const uint64_t own = __builtin_amdgcn_ballot_w64(mine && sp >= 0 && sp < S);
+    const int src = own ? (int)__builtin_ctzll(own) : 0;
+    if (t == src) {
+      s_pair[0] = own ? sp : split;
+      s_pair[1] = own ? t : b;
     }
   }
   __syncthreads();

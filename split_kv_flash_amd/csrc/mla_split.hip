@@ -747,7 +747,9 @@ __device__ __forceinline__ void mla16d_role(const MlaArgs& a, const Mla16dShared
         sh.p[(par * NHB + 2 * wave + hb) * 64 + lane] = pw;
         if (lq == 0) sh.alpha[(par * NHB + 2 * wave + hb) * 16 + l16] = al;
       }
-      if (__any(moved) && lane == 0) sh.moved[par] = i;
+      // Several scoring waves may report the same tile: an LDS atomic max
+      // (the flag only ever rises to the newest tile index).
+      if (__any(moved) && lane == 0) atomicMax(&sh.moved[par], i);
       wait_vm_lgkm0<0>();
       raw_barrier();  // P and factors of tile i; tile i+1
     }
