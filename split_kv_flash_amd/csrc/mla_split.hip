@@ -337,20 +337,53 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
     wait_vm_lgkm0<0>();
   }
   issue_tile(0, start);
-  if constexpr (IDX) wait_vm_lgkm0<0>();  // the second tile's rows
-  issue_tile(1, start + kT16);
-  // Query rows of this head block as B operands (requested after the first
-  // tiles, so their latency overlaps): lane holds head hb*16 + l16,
+  // Query rows of this head block as B operands: lane holds head hb*16 + l16,
   // columns 288*dh + 32*ks + 8*lq .. +7 (rounded to f16 once).
   half8_t qf[KS];
+  if constexpr (NHB <= 4) {
+    // Up to 64 heads: the rows are staged in f16 through tile buffers 1-2
+    // (64 rows of 576 halves fill them) with whole-line loads by the whole
+    // workgroup, then tile 1 is requested; iteration 0 waits for it only at
+    // its end. A wave's own fragments (16 rows, 32 bytes apart in each)
+    // would touch sixteen lines per load instruction.
+    constexpr int QV = H * (kLatDk / 4) / (NW * 64);  // float4 per thread
+    static_assert(H * (kLatDk / 4) % (NW * 64) == 0 && H * kLatDk <= 2 * TILE, "staged rows fit");
+    _Float16* const sq = s_c + TILE;
+    {
+      float4 qv[QV];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
+      for (int k = 0; k < QV; ++k) qv[k] = *reinterpret_cast<const float4*>(qb + 4 * (tid + NW * 64 * k));
+      // Row h keeps chunk c (8 halves) at chunk position c ^ (h & 7).
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      qf[ks][e] = (_Float16)qb[(hb * 16 + l16) * kLatDk + dh * KH + ks * 32 + lq * 8 + e];
-
-  wait_vm_lgkm0<0>();  // both tiles and the query rows landed
-  raw_barrier();
+      for (int k = 0; k < QV; ++k) {
+        const int f = tid + NW * 64 * k;
+        const int h = f / (kLatDk / 4);
+        const int c4 = f - h * (kLatDk / 4);
+        *reinterpret_cast<half4_t*>(sq + h * kLatDk + (((c4 >> 1) ^ (h & 7)) << 3) + (c4 & 1) * 4) =
+            half4_t{(_Float16)qv[k].x, (_Float16)qv[k].y, (_Float16)qv[k].z, (_Float16)qv[k].w};
+      }
+    }
+    wait_vm_lgkm0<0>();  // tile 0 (and the next tile's rows of an index list)
+    raw_barrier();
+    const _Float16* qrow = sq + (hb * 16 + l16) * kLatDk;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = *reinterpret_cast<const half8_t*>(qrow + (((dh * 36 + 4 * ks + lq) ^ (l16 & 7)) << 3));
+    wait_vm_lgkm0<0>();
+    raw_barrier();  // the staged rows are read before tile 1 overwrites them
+    issue_tile(1, start + kT16);
+  } else {
+    if constexpr (IDX) wait_vm_lgkm0<0>();  // the second tile's rows
+    issue_tile(1, start + kT16);
+    // (requested after the first tiles, so their latency overlaps)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        qf[ks][e] = (_Float16)qb[(hb * 16 + l16) * kLatDk + dh * KH + ks * 32 + lq * 8 + e];
+    wait_vm_lgkm0<0>();  // both tiles and the query rows landed
+    raw_barrier();
+  }
 
   half8_t pp = half8_t{};  // weights of the previous tile (A operand)
   float alp = 1.0f;        // its rescale factor, head hb*16 + l16
