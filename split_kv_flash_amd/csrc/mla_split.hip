@@ -1062,14 +1062,48 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   issue_tile(1, start + kT32);
   // Query block as B operands (requested after the first tiles, so their
   // latency overlaps), pre-scaled into base-2 units: qv[t][u] is
-  // column 144*dq + 16*t + 4*lq + u of head head0 + l16.
+  // column 144*dq + 16*t + 4*lq + u of head head0 + l16. The workgroup loads
+  // every block's rows as consecutive float4s (whole lines per instruction;
+  // a wave's own fragments, 16 rows 64 bytes apart, touch sixteen lines) and
+  // stages one block at a time through tile buffer 2, which one block's
+  // 16 x 576 floats fill; row h keeps float4 chunk c at position c ^ h, as
+  // the tiles do.
   float4_t qv[KT];
   {
-    const float* qrow = qb + (int64_t)(head0 + l16) * kLatDk + dq * 144 + lq * 4;
+    constexpr int QF = 16 * kLatDk / 4;      // float4 per block
+    constexpr int QV = (QF + NT - 1) / NT;    // per thread and block (the last one partial)
+    static_assert(16 * kLatDk <= TSTRIDE, "one block fits buffer 2");
+    float4 qs[NHBB][QV];
+    const float* qblk = qb + (int64_t)hg * HW * kLatDk;
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      const float4 v = *reinterpret_cast<const float4*>(qrow + 16 * t);
-      qv[t] = float4_t{v.x * a.qscale, v.y * a.qscale, v.z * a.qscale, v.w * a.qscale};
+    for (int r = 0; r < NHBB; ++r)
+#pragma unroll
+      for (int k = 0; k < QV; ++k)
+        if (QF % NT == 0 || tid + NT * k < QF)
+          qs[r][k] = *reinterpret_cast<const float4*>(qblk + (int64_t)r * 16 * kLatDk + 4 * (tid + NT * k));
+    float* const sq = s_c + 2 * TSTRIDE;
+#pragma unroll
+    for (int r = 0; r < NHBB; ++r) {
+      if (r > 0) {
+        wait_vm_lgkm0<0>();
+        raw_barrier();  // the previous block's fragments are read
+      }
+#pragma unroll
+      for (int k = 0; k < QV; ++k) {
+        const int f = tid + NT * k;
+        if (QF % NT != 0 && f >= QF) continue;
+        const int h = f / (kLatDk / 4);
+        const int c = f - h * (kLatDk / 4);
+        *reinterpret_cast<float4_t*>(sq + h * kLatDk + ((c ^ h) << 2)) =
+            float4_t{qs[r][k].x * a.qscale, qs[r][k].y * a.qscale, qs[r][k].z * a.qscale, qs[r][k].w * a.qscale};
+      }
+      wait_vm_lgkm0<0>();
+      raw_barrier();
+      if (hb == r) {
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+          qv[t] = *reinterpret_cast<const float4_t*>(sq + l16 * kLatDk + (((36 * dq + 4 * t + lq) ^ l16) << 2));
+      }
     }
   }
 
