@@ -451,19 +451,50 @@ __global__ __launch_bounds__(256) void query_tile_kernel(QtArgs a) {
   }
 
   // ---- partials of this wave's rows and columns (rows with nothing visible: neutral) ----
+  if constexpr (!FUSED) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int re = qt * RW + rb * 16 + 4 * lq + e;
-    if (re < QG) {
-      const int te = re / a.G;
-      const int w = te * a.Hq + g * a.G + (re - te * a.G);
-      float* dst = a.ws_acc + (((int64_t)b * QH + w) * a.S + split) * D + 16 * CBW * dq + l16;
+    for (int e = 0; e < 4; ++e) {
+      const int re = qt * RW + rb * 16 + 4 * lq + e;
+      if (re < QG) {
+        const int te = re / a.G;
+        const int w = te * a.Hq + g * a.G + (re - te * a.G);
+        float* dst = a.ws_acc + (((int64_t)b * QH + w) * a.S + split) * D + 16 * CBW * dq + l16;
 #pragma unroll
-      for (int c = 0; c < CBW; ++c) {
-        if constexpr (FUSED)
-          st_dev(dst + 16 * c, acc[c][e]);
-        else
-          dst[16 * c] = acc[c][e];
+        for (int c = 0; c < CBW; ++c) dst[16 * c] = acc[c][e];
+      }
+    }
+  } else {
+    // Device-scope stores in whole lines: the wave's 16 x 16*CBW block goes
+    // through its own rows of the K/V ring (free: every wave has passed the
+    // loop's last barrier; rows padded by four floats, so the writes of the
+    // four row quarters fall in distinct banks) and out as 16-byte stores,
+    // 4*CBW of them per row, from a wave-uniform base (one query per
+    // sequence: the block's rows are consecutive partial rows). Scalar
+    // device-scope stores of 64-byte row pieces cost this form about 10 us
+    // at 262,144 positions.
+    constexpr int WCOL = 16 * CBW;
+    constexpr int PITCH = WCOL + 4;
+    static_assert(4 * 16 * PITCH * (int)sizeof(float) <= (int)sizeof(s_kv), "the block fits the ring");
+    float* tw = reinterpret_cast<float*>(&s_kv[0][0][0]) + wave * 16 * PITCH;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int c = 0; c < CBW; ++c) tw[(4 * lq + e) * PITCH + 16 * c + l16] = acc[c][e];
+    wait_vm_lgkm0<0>();
+    const int re0 = qt * RW + rb * 16;  // the block's first row (a head of the group)
+    const int nrow = min(16, QG - re0);
+    if (nrow > 0) {
+      const int64_t rowstep = (int64_t)a.S * D;  // floats between consecutive heads' partial rows
+      const float* base = a.ws_acc + (((int64_t)b * QH + g * a.G + re0) * a.S + split) * D + WCOL * dq;
+      const auto rs = raw_rsrc(base, (uint32_t)((((int64_t)nrow - 1) * rowstep + WCOL) * 4));
+#pragma unroll
+      for (int k = 0; k < CBW; ++k) {
+        const int j = k * 64 + lane;
+        const int r = j / (WCOL / 4), c4 = j - (j / (WCOL / 4)) * (WCOL / 4);
+        if (r < nrow) {
+          st_dev4(rs, (uint32_t)(((int64_t)r * rowstep + 4 * c4) * 4),
+                  *reinterpret_cast<const float4*>(tw + r * PITCH + 4 * c4));
+        }
       }
     }
   }
