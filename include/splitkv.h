@@ -216,8 +216,14 @@ size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan)
  * num_q_heads/num_kv_heads in {1, 2, 4, 6, 8}, any q/KV dtype, every layout; latent
  * (kv_shared) with num_kv_heads == 1, head_dim_qk == 576, head_dim_v == 512, num_q_heads
  * in {32, 64, 96, 128}, q f32, KV f32 or f16, contiguous or indexed. Latent f16 caches run on f16
- * MFMA: q and the softmax weights are rounded to f16 there (f32 accumulation). Anything else returns
- * SK_ERR_UNSUPPORTED without launching.
+ * MFMA: q and the softmax weights are rounded to f16 there (f32 accumulation). Latent f32
+ * caches run on f16 MFMA too, with every operand (cache entries, q * scale * log2 e, the
+ * weights) split into two f16 parts, hi and (x - hi) * 2^11, and three part products per
+ * product (22 significant bits: each operand within 2^-22 |x| + 2^-36; f32 accumulation);
+ * a cache entry or scaled query value of magnitude 65,520 or more, past f16's range, makes
+ * NaN the outputs of the heads whose products it enters (every head of the sequence for a
+ * cache entry; for a query value its own head and the others its workgroup serves).
+ * Anything else returns SK_ERR_UNSUPPORTED without launching.
  * Kernel: contiguous f16/bf16 caches of head width 64, of width 128 with at least 4
  * query heads per KV head, and of width 256 with at least 6, run on the query-tile
  * kernel of attn_query_tiles with one query (its partials have this layout): MFMA

@@ -13,9 +13,10 @@
 //   scores  S[h][j] = sum_d Q[h][d] C[j][d]    (heads x positions, K = 576)
 //   output  acc[h][e] += sum_j P[h][j] C[j][e] (heads x values,    K = positions)
 // with the online-softmax update between them. f16 caches use f16 MFMA (q and
-// the probabilities rounded to f16, f32 accumulation); f32 caches use
-// v_mfma_f32_16x16x4_f32 (no rounding). Three kernels live here, each described
-// at its definition:
+// the probabilities rounded to f16, f32 accumulation); f32 caches use f16 MFMA
+// on two f16 parts of every operand (22 significant bits, three part products
+// per product, f32 accumulation). Three kernels live here, each described at
+// its definition:
 //   * mla16_split_kernel (f16 caches): two waves per 16-head block, x32 MFMA,
 //     scores transposed, one barrier per tile; 32, 64 and 96 heads in one
 //     workgroup per split, 128 heads as two workgroups of 64;
@@ -23,9 +24,9 @@
 //     unit gets a split): eight waves in two roles, scoring waves of 32 heads
 //     (scores and softmax in registers) and output waves that own the value
 //     columns and multiply every block's weights by them;
-//   * mla32_split_kernel (f32 caches): four waves per 16-head block, scores
-//     transposed so P stays in registers, heads over one or more workgroups
-//     per split.
+//   * mla32_split_kernel (f32 caches): four waves per 16-head block, tiles
+//     turned into f16 parts in LDS as they land, scores transposed so P stays
+//     in registers, heads over one or more workgroups per split.
 // Each has a FUSED instantiation for the one-launch decode: the partials go
 // out with device-scope stores and the workgroups merge them in the same
 // grid (latent_fused_tail).
@@ -511,35 +512,43 @@ __global__ __launch_bounds__(NHB * 128) void mla16_split_kernel(MlaArgs a) {
 constexpr float kLazyMax = 8.0f;
 
 // ---------------------------------------------------------------------------
-// f32 caches: v_mfma_f32_16x16x4_f32 (exact f32 products), four waves per
-// 16-head block, heads of a split spread over HG workgroups.
+// f32 caches: f16 MFMA on f16 parts, four waves per 16-head block, heads of a
+// split spread over HG workgroups.
 //
-// The f32 query block of 16 heads x 576 columns and the 16 x 512 output
+// Every f32 operand x (cache entries, q * scale * log2 e, the weights P) is
+// taken as two f16 parts, hi = round(x) and lo = round((x - hi) * 2^11), which
+// hold x within 2^-22 |x| + 2^-36, and a product of two split operands as
+// a_hi b_hi + 2^-11 (a_hi b_lo + a_lo b_hi) (the dropped a_lo b_lo is below
+// 2^-22 of it). Per flop, v_mfma_f32_16x16x32_f16 issues 16 times as fast
+// as v_mfma_f32_16x16x4_f32 (and the x16 form at least 8 times), so three
+// part products still cost well under one f32 product. f16's range ends at 65,504: an operand of magnitude 65,520 or more
+// sets a workgroup flag and the split's partials become NaN.
+//
+// The query parts of 16 heads x 576 columns and the 16 x 512 output
 // accumulators do not fit one wave's share of the register file at three waves
 // per SIMD, so each 16-head block has four waves: wave (hb, dq) computes the
 // partial scores over latent columns [144*dq, 144*dq + 144) and owns value
 // columns [128*dq, 128*dq + 128). A workgroup holds NHBB blocks (12 waves for
 // NHBB = 3) and a split's heads are spread over HG = Hq / (16*NHBB)
-// workgroups, each streaming the split's cache rows; the f32 path is bound by
-// the FP32 MFMA rate, not by HBM, so the repeated read costs little.
-//  * Scores are computed transposed, S^T[position][head] = C[position][:] .
-//    Q^T, so the MFMA result leaves lane (head l16, quarter lq) holding the
-//    scores of positions 4*lq + i: after the four partials of the block are
-//    added (through LDS, in a fixed order, so all four waves hold identical
-//    values) and the softmax runs in registers, item t of that lane is
-//    exactly the A operand P[head][4*lq + t] of output step t. P never goes
-//    through LDS.
-//  * The contraction index is ordered so every operand read is 16 bytes:
-//    score step 4*t + u takes columns 144*dq + 16*t + 4*lq + u; output step t
-//    takes positions 4*lq + t, and output column block 4*u + e of lane j is
-//    column 128*dq + 64*u + 4*j + e.
+// workgroups on one XCD, each streaming the split's cache rows (the L2 serves
+// the second reader).
 //  * Tiles of 16 cache rows go straight from HBM into LDS with
 //    global_load_lds_dwordx4, three tiles deep; each row's 144 chunks of 16
-//    bytes are stored with the chunk index XOR-ed by the row (0..15), so both
-//    the score reads (16 rows, one chunk) and the value reads (one row, 16
-//    chunks) hit distinct banks.
-//  * Two barriers per tile: one publishes the partial scores, one the next
-//    tile (each wave first waits for its own tile loads).
+//    bytes are stored with the chunk index XOR-ed by the row (0..15). Once its
+//    own loads have landed, each wave rewrites its slots in place as parts:
+//    the 16 bytes of four f32 values become four hi halves and four lo halves.
+//  * Scores are computed transposed, S^T[position][head] = C[position][:] .
+//    Q^T, with v_mfma_f32_16x16x32_f16 (chunks t and t+1 of the lane: columns
+//    4*(36*dq + lq + 4t) .. +3 and the next chunk's) and one
+//    v_mfma_f32_16x16x16_f16 step for the ninth chunk, so the result leaves
+//    lane (head l16, quarter lq) holding the scores of positions 4*lq + i:
+//    after the four partials of the block are added (through LDS, in a fixed
+//    order, so all four waves hold identical values) and the softmax runs in
+//    registers, those four weights are exactly the lane's A operand of the
+//    v_mfma_f32_16x16x16_f16 output product over the tile's 16 positions; the
+//    value parts come through the gfx950 transpose read ds_read_b64_tr_b16.
+//    P never goes through LDS.
+//  * One barrier per tile (below).
 // ---------------------------------------------------------------------------
 constexpr int kT32 = 16;              // positions per tile
 constexpr int kCpr32 = kLatDk / 4;    // 144 chunks of 16 bytes per f32 cache row
@@ -925,6 +934,54 @@ __device__ __forceinline__ uint32_t lds_addr_of(const float* p) {
   return (uint32_t)(size_t)(const lds_float_t*)(p);
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float4_t mfma16(half4_t a, half4_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Lazy-maximum threshold (base 2) of the f32-cache kernel: its weights, at
+// most 2^kLazyMax32, times 2^11 must stay finite in f16.
+constexpr float kLazyMax32 = 4.0f;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
+
+// Four f32 values as two f16 parts, packed [hi0 hi1 hi2 hi3 | lo0 lo1 lo2 lo3]:
+// hi = x rounded to f16, lo = (x - hi) * 2^11 rounded to f16. x - hi is exact
+// and at most 2^-11 |x|, so hi + lo * 2^-11 equals x within 2^-22 |x| + 2^-36
+// (the scaling keeps lo clear of f16's subnormals). The residual is one fused
+// step from the packed hi (exact: (x - hi) 2^11 is an f32 value). amax keeps
+// the largest |x| seen, to tell values that would round to infinity in f16.
+__device__ __forceinline__ u32x4_t f16_parts(float4_t x, float& amax) {
+#pragma clang fp contract(off)
+  const half2_t h0 = __builtin_convertvector(float2_t{x[0], x[1]}, half2_t);
+  const half2_t h1 = __builtin_convertvector(float2_t{x[2], x[3]}, half2_t);
+  const float r0 = __builtin_fmaf((float)h0[0], -2048.0f, x[0] * 2048.0f);
+  const float r1 = __builtin_fmaf((float)h0[1], -2048.0f, x[1] * 2048.0f);
+  const float r2 = __builtin_fmaf((float)h1[0], -2048.0f, x[2] * 2048.0f);
+  const float r3 = __builtin_fmaf((float)h1[1], -2048.0f, x[3] * 2048.0f);
+  const half2_t l0 = __builtin_convertvector(float2_t{r0, r1}, half2_t);
+  const half2_t l1 = __builtin_convertvector(float2_t{r2, r3}, half2_t);
+  amax = fmaxf(amax, fmaxf(fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])),
+                           fmaxf(__builtin_fabsf(x[2]), __builtin_fabsf(x[3]))));
+  return u32x4_t{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+                 __builtin_bit_cast(uint32_t, l0), __builtin_bit_cast(uint32_t, l1)};
+}
+
+// LDS reads at a byte address (a wave-uniform buffer base plus a lane offset;
+// the constant parts go into the instructions' offset fields).
+__device__ __forceinline__ u32x4_t lds_ld16(uint32_t addr) { return *(const lds_u32x4_t*)(size_t)addr; }
+// (volatile: two reads of one chunk must not be merged into one, whose
+// registers would then have to be moved into the operands.)
+__device__ __forceinline__ u32x2_t lds_ld8(uint32_t addr) { return *(volatile const lds_u32x2_t*)(size_t)addr; }
+__device__ __forceinline__ half4_t lds_tr16(uint32_t addr) {
+  return __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(size_t)addr));
+}
+
 // 16-head blocks per workgroup for an f32 latent with Hq heads, and the
 // workgroups that share one split.
 __host__ __device__ constexpr int mla32_blocks(int Hq) { return Hq % 48 == 0 ? 3 : 2; }
@@ -941,6 +998,7 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
 
   __shared__ __align__(16) float s_c[3 * TSTRIDE];
   __shared__ __align__(16) float4_t s_sx[2][NW][64];
+  __shared__ int s_big;  // set when some operand lies outside f16's range
 
   const int split = blockIdx.x;
   const int b = blockIdx.y;
@@ -953,6 +1011,8 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   const int l16 = lane & 15;
   const int lq = lane >> 4;
   const int head0 = hg * HW + hb * 16;
+  if (tid == 0) s_big = 0;  // ordered before every update by the prologue's barriers
+  float amax = 0.0f;  // largest |operand| this lane has split into f16 parts
 
   const int L = min(a.seq_lens[b], a.cap);
   const int64_t start = (int64_t)split * a.chunk;
@@ -1029,28 +1089,44 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
     }
   };
 
-  // Running max (base 2) and normaliser of head head0 + l16 (replicated over
-  // the four quarters); accumulators acc[4*u + e] hold heads 4*lq + i (items)
-  // at column 128*dq + 64*u + 4*l16 + e.
   // Running max (base 2) of head head0 + l16, replicated over the four
   // quarters; ll is this lane's share of the normaliser (its positions of
-  // every tile), summed over the quarters at the end.
+  // every tile), summed over the quarters at the end. Accumulator acc[cb]
+  // holds heads 4*lq + e (items) at column 128*dq + 16*cb + l16.
   float m = -INFINITY, ll = 0.0f;
   float4_t acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Per-lane LDS offsets (floats) inside a tile buffer: score reads use row
-  // l16 and logical chunk 36*dq + lq + 4*t, i.e. sb[t & 3] + 64*(t >> 2);
-  // value reads use row 4*lq + t and logical chunk 32*dq + 16*u + l16, i.e.
-  // vb[t] + 64*u.
+  // Per-lane LDS offsets (floats) inside a tile buffer. Score reads: row l16,
+  // logical chunk 36*dq + lq + 4*t (t = 0..8), i.e. soff(t). Value reads
+  // (transposed, 16 columns by 4 rows per 16 lanes): lane l16 = 4*rho + sg of
+  // quarter lq gives row 4*lq + rho, columns 4*sg .. +3 of 16-column block cb
+  // of the wave's 128, i.e. logical chunk 32*dq + 4*cb + sg, at
+  // vb[cb & 3] + 64*(cb >> 2) (the row swizzle only touches the low four bits
+  // of the chunk).
   int sb[4], vb[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     sb[v] = l16 * kLatDk + (((36 * dq + lq + 4 * v) ^ l16) << 2);
-    const int r = 4 * lq + v;
-    vb[v] = r * kLatDk + ((32 * dq + (l16 ^ r)) << 2);
+    const int r = 4 * lq + (l16 >> 2);
+    vb[v] = r * kLatDk + ((32 * dq + ((4 * v + (l16 & 3)) ^ r)) << 2);
   }
+  auto soff = [&](int t) { return sb[t & 3] + 64 * (t >> 2); };
+  // Each wave turns the slots it loaded into f16 parts in place once they have
+  // landed (16 bytes of f32 become 8 bytes of hi parts and 8 of lo parts), so
+  // every read of the tile after the barrier that publishes it takes parts.
+  // Rows of odd index keep the lo halves first: the 16 lanes of a read that
+  // meet in one 16-byte chunk position then split evenly over its two
+  // halves, which keeps the 8-byte operand reads free of bank conflicts.
+  auto split_own = [&](int bi) {
+#pragma unroll
+    for (int c = 0; c < DPW; ++c) {
+      u32x4_t* p = reinterpret_cast<u32x4_t*>(s_c + bi * TSTRIDE + ((wave * DPW + c) * 64 + lane) * 4);
+      const u32x4_t v = f16_parts(__builtin_bit_cast(float4_t, *p), amax);
+      *p = (srow[c] & 1) ? u32x4_t{v.z, v.w, v.x, v.y} : v;
+    }
+  };
 
   const int ntiles = (int)((end - start + kT32 - 1) / kT32);
   if constexpr (IDX) {
@@ -1068,7 +1144,11 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   // stages one block at a time through tile buffer 2, which one block's
   // 16 x 576 floats fill; row h keeps float4 chunk c at position c ^ h, as
   // the tiles do.
-  float4_t qv[KT];
+  // Query parts (B operands): chunk t of this wave (columns 4*(36*dq + lq + 4*t)
+  // .. +3 of head head0 + l16) as f16 parts; step s of the x32 products takes
+  // chunks 2s and 2s+1, the x16 step chunk 8.
+  half8_t qh[4], ql[4];
+  half4_t qh8, ql8;
   {
     constexpr int QF = 16 * kLatDk / 4;      // float4 per block
     constexpr int QV = (QF + NT - 1) / NT;    // per thread and block (the last one partial)
@@ -1100,39 +1180,81 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
       wait_vm_lgkm0<0>();
       raw_barrier();
       if (hb == r) {
+        u32x4_t qc[KT];
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
-          qv[t] = *reinterpret_cast<const float4_t*>(sq + l16 * kLatDk + (((36 * dq + 4 * t + lq) ^ l16) << 2));
+        for (int t = 0; t < KT; ++t) qc[t] = f16_parts(*reinterpret_cast<const float4_t*>(sq + soff(t)), amax);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          qh[u] = __builtin_bit_cast(half8_t, u32x4_t{qc[2 * u].x, qc[2 * u].y, qc[2 * u + 1].x, qc[2 * u + 1].y});
+          ql[u] = __builtin_bit_cast(half8_t, u32x4_t{qc[2 * u].z, qc[2 * u].w, qc[2 * u + 1].z, qc[2 * u + 1].w});
+        }
+        qh8 = __builtin_bit_cast(half4_t, u32x2_t{qc[8].x, qc[8].y});
+        ql8 = __builtin_bit_cast(half4_t, u32x2_t{qc[8].z, qc[8].w});
       }
     }
   }
 
   wait_vm_lgkm0<0>();  // both tiles and the query block landed
+  split_own(0);
+  split_own(1);
+  wait_vm_lgkm0<0>();
   raw_barrier();
 
-  // Partial scores S^T of the tile in `cur` over this wave's 144 columns: nine
-  // steps of four MFMAs, each step's operands read from LDS one step ahead.
-  // After step t's MFMAs, stage(t) of the previous tile's softmax runs (a
-  // constant t after unrolling), so the softmax's VALU and cross-lane work
-  // issues while the matrix pipe works through the score products.
-  // Four accumulators (one per column of a 16-byte read) keep the products
-  // of a step independent, so they issue back to back; they are summed at the
-  // end in a fixed order.
-  auto scores = [&](const float* cur, auto&& stage) -> float4_t {
-    float4_t sp[4];
+  // Partial scores S^T of the tile in `cur` over this wave's 144 columns:
+  // four x32 steps (chunks 2s, 2s+1) and one x16 step (chunk 8), three
+  // products each (C_hi q_hi, then C_hi q_lo and C_lo q_hi, whose lo parts
+  // carry 2^11, into an accumulator of their own),
+  // each step's operands read from LDS one step ahead. After steps 0-2, stage(s)
+  // of the previous tile's softmax runs (a constant after unrolling), so the
+  // softmax's VALU and cross-lane work issues while the matrix pipe works
+  // through the products. Accumulators by step parity keep consecutive
+  // products independent; they are summed at the end in a fixed order.
+  auto scores = [&](uint32_t cur, auto&& stage) -> float4_t {
+    const float4_t z = float4_t{0.f, 0.f, 0.f, 0.f};
+    float4_t sp[2] = {z, z}, sa[2] = {z, z};
+    // hi (part 0) or lo (part 1) halves of chunks t and t+1, read straight
+    // into the operand's register pairs.
+    // Lane addresses of chunks 0-3 in this buffer, made opaque so the other
+    // chunks' reads add constants in the instructions' offset fields instead
+    // of keeping an address register per read.
+    // (Row l16's hi halves sit at byte 8 * (l16 & 1) of a chunk, lo at the
+    // other: the lo address is the hi address with bit 3 flipped.)
+    uint32_t ab[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) sp[u] = float4_t{0.f, 0.f, 0.f, 0.f};
-    float4_t an = *reinterpret_cast<const float4_t*>(cur + sb[0]);
+    for (int u = 0; u < 4; ++u) {
+      ab[u] = cur + 4 * sb[u] + 8 * (l16 & 1);
+      asm volatile("" : "+v"(ab[u]));
+    }
+    auto addr = [&](int t, int part) { return (ab[t & 3] ^ (8u * part)) + 256 * (t >> 2); };
+    auto opnd = [&](int t, int part) {
+      const u32x2_t x0 = lds_ld8(addr(t, part)), x1 = lds_ld8(addr(t + 1, part));
+      return __builtin_bit_cast(half8_t, u32x4_t{x0.x, x0.y, x1.x, x1.y});
+    };
+    half8_t nh = opnd(0, 0), nl = opnd(0, 1);
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      const float4_t av = an;
-      if (t + 1 < KT) an = *reinterpret_cast<const float4_t*>(cur + sb[(t + 1) & 3] + 64 * ((t + 1) >> 2));
-#pragma unroll
-      for (int u = 0; u < 4; ++u) sp[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], qv[t][u], sp[u], 0, 0, 0);
-      stage(t);
+    for (int st = 0; st < 4; ++st) {
+      const half8_t ah = nh, al = nl;
+      if (st < 3) {
+        nh = opnd(2 * st + 2, 0);
+        nl = opnd(2 * st + 2, 1);
+      }
+      sa[st & 1] = mfma32(ah, ql[st], sa[st & 1]);
+      sp[st & 1] = mfma32(ah, qh[st], sp[st & 1]);
+      sa[st & 1] = mfma32(al, qh[st], sa[st & 1]);
+      if (st < 3) stage(st);
       __builtin_amdgcn_sched_barrier(0);
     }
-    return (sp[0] + sp[1]) + (sp[2] + sp[3]);
+    const half4_t ah = __builtin_bit_cast(half4_t, lds_ld8(addr(8, 0)));
+    const half4_t al = __builtin_bit_cast(half4_t, lds_ld8(addr(8, 1)));
+    sa[0] = mfma16(ah, ql8, sa[0]);
+    sp[0] = mfma16(ah, qh8, sp[0]);
+    sa[0] = mfma16(al, qh8, sa[0]);
+    const float4_t lo = sa[0] + sa[1];
+    const float4_t hi = sp[0] + sp[1];
+    float4_t r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = fmaf(lo[e], 1.0f / 2048.0f, hi[e]);
+    return r;
   };
 
   // Software pipeline, one barrier per tile. Before iteration i the barrier
@@ -1142,7 +1264,7 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   // product of tile i (acc = alpha * acc + P[16 heads][16 positions] x V);
   // after the next barrier tile i+3 goes into tile i's buffer.
   {
-    const float4_t sp0 = scores(s_c, [](int) {});
+    const float4_t sp0 = scores(lds0, [](int) {});
     s_sx[0][wave][lane] = sp0;
     raw_barrier();
     if (start + 2 * kT32 < end) issue_tile(2, start + 2 * kT32);
@@ -1173,9 +1295,9 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
         // m, which this lane's own four scores decide without any cross-lane
         // step; only a wave where some lane sees a larger score finds the
         // heads' maxima and rescales.
-        if (__any(lmx > m + kLazyMax)) {
+        if (__any(lmx > m + kLazyMax32)) {
           const float mx = max_xor32(max_xor16(lmx));
-          const float mn = mx > m + kLazyMax ? mx : m;
+          const float mn = mx > m + kLazyMax32 ? mx : m;
           alp = fast_exp2(m - ((mn == -INFINITY) ? 0.0f : mn));
           ll *= alp;
           m = mn;
@@ -1189,7 +1311,7 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
       }
     };
     if (next) {
-      const float4_t sp = scores(s_c + ((i + 1) % 3) * TSTRIDE, stage);
+      const float4_t sp = scores(lds0 + (uint32_t)(((i + 1) % 3) * TSTRIDE * 4), stage);
       s_sx[par ^ 1][wave][lane] = sp;
     } else {
 #pragma unroll
@@ -1197,7 +1319,6 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
     }
 
     // ---- output of tile i ----
-    const float* prv = s_c + (i % 3) * TSTRIDE;
     if (moved) {
       // Accumulator item e is head 4*lq + e, whose factor lane 4*lq + e holds.
 #pragma unroll
@@ -1207,27 +1328,57 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
         for (int c = 0; c < 8; ++c) acc[c][e] *= ae;
       }
     }
-    // Value operands read one step ahead of their products.
-    float4_t vn[2];
+    // P as f16 parts, the A operands of the x16 products over the tile's 16
+    // positions (lane: head l16, positions 4*lq + e). Each 16-column block
+    // accumulates 2^11 P V as P_hi 2^11 V_hi + P_hi V_lo + P_lo V_hi (V_lo and
+    // P_lo carry 2^11), three products into one accumulator; P_hi 2^11 is
+    // exact in f16 because the weights stay at or below 2^kLazyMax32.
+    half4_t ph, phs, pl;
+    {
+#pragma clang fp contract(off)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) vn[u] = *reinterpret_cast<const float4_t*>(prv + vb[0] + 64 * u);
+      for (int e = 0; e < 4; ++e) {
+        ph[e] = (_Float16)pp[e];
+        phs[e] = (_Float16)((float)ph[e] * 2048.0f);
+        pl[e] = (_Float16)__builtin_fmaf((float)ph[e], -2048.0f, pp[e] * 2048.0f);
+      }
+    }
+    const uint32_t prv = lds0 + (uint32_t)((i % 3) * TSTRIDE * 4);
+    // Opaque lane addresses of blocks 0-3, as for the score reads; this lane's
+    // row 4*lq + (l16 >> 2) keeps its hi halves at byte 8 * ((l16 >> 2) & 1).
+    uint32_t vab[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float4_t v0 = vn[0], v1 = vn[1];
-      if (t + 1 < 4) {
+    for (int u = 0; u < 4; ++u) {
+      vab[u] = prv + 4 * vb[u] + 8 * ((l16 >> 2) & 1);
+      asm volatile("" : "+v"(vab[u]));
+    }
+    auto vread = [&](int cb, int part) { return lds_tr16((vab[cb & 3] ^ (8u * part)) + 256 * (cb >> 2)); };
+    // Two halves of four blocks; within a half the three products of a block
+    // are four MFMAs apart.
 #pragma unroll
-        for (int u = 0; u < 2; ++u) vn[u] = *reinterpret_cast<const float4_t*>(prv + vb[t + 1] + 64 * u);
+    for (int hf = 0; hf < 2; ++hf) {
+      half4_t vh[4], vl[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        vh[c] = vread(4 * hf + c, 0);
+        vl[c] = vread(4 * hf + c, 1);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(pp[t], v0[e], acc[e], 0, 0, 0);
+      for (int c = 0; c < 4; ++c) acc[4 * hf + c] = mfma16(phs, vh[c], acc[4 * hf + c]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[4 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(pp[t], v1[e], acc[4 + e], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int c = 0; c < 4; ++c) acc[4 * hf + c] = mfma16(ph, vl[c], acc[4 * hf + c]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[4 * hf + c] = mfma16(pl, vh[c], acc[4 * hf + c]);
     }
     if (!next) break;
     // Tile i+2 (requested after the previous barrier) is the only tile load
-    // in flight: wait for it, then publish it and the partials of tile i+1.
+    // in flight: wait for it, turn this wave's slots of it into f16 parts, then
+    // publish it and the partials of tile i+1.
     wait_vm_lgkm0<0>();
+    if (i + 2 < ntiles) {
+      split_own((i + 2) % 3);
+      wait_vm_lgkm0<0>();
+    }
     raw_barrier();
     // Every wave has finished the output product of tile i: its buffer takes
     // tile i+3.
@@ -1237,24 +1388,26 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   // Drain the tile loads still in flight before the workgroup can retire.
   wait_vm_lgkm0<0>();
 
-  // Partials: four consecutive columns per lane and head as one float4.
+  // A value outside f16's range anywhere in the workgroup's operands makes
+  // its partials NaN (the parts would carry an infinity).
+  if (__any(amax >= 65520.0f) && lane == 0) atomicOr(&s_big, 1);
+  wait_vm_lgkm0<0>();
+  raw_barrier();
+  const float bad = s_big ? __builtin_nanf("") : 0.0f;
+  // Partials: lane (column l16 of block cb, quarter lq) holds heads 4*lq + i.
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int head = head0 + 4 * lq + i;
-      const int col = dq * 128 + 64 * u + 4 * l16;
-      const float4 v = make_float4(acc[4 * u + 0][i], acc[4 * u + 1][i], acc[4 * u + 2][i], acc[4 * u + 3][i]);
-      if (FUSED && a.S > 1)  // base uniform over the workgroup, offset per lane
-        st_dev4(raw_rsrc(a.ws_acc + ws0 * kLatDv, (uint32_t)((int64_t)a.Hq * a.S * kLatDv * 4)),
-                (uint32_t)(((int64_t)head * a.S * kLatDv + col) * 4), v);
-      else
-        *reinterpret_cast<float4*>(a.ws_acc + (ws0 + (int64_t)head * a.S) * kLatDv + col) = v;
+      const int col = dq * 128 + 16 * cb + l16;
+      put_partial(a.ws_acc + (ws0 + (int64_t)head * a.S) * kLatDv + col, acc[cb][i] * (1.0f / 2048.0f) + bad,
+                  FUSED && a.S > 1);
     }
   const float l = sum_xor32(sum_xor16(ll));
   if (dq == 0 && lq == 0) {
-    put_partial(a.ws_m + ws0 + (int64_t)(head0 + l16) * a.S, m * kLn2, FUSED && a.S > 1);
-    put_partial(a.ws_l + ws0 + (int64_t)(head0 + l16) * a.S, l, FUSED && a.S > 1);
+    put_partial(a.ws_m + ws0 + (int64_t)(head0 + l16) * a.S, m * kLn2 + bad, FUSED && a.S > 1);
+    put_partial(a.ws_l + ws0 + (int64_t)(head0 + l16) * a.S, l + bad, FUSED && a.S > 1);
   }
   if constexpr (FUSED) latent_fused_tail<NT>(a, s_c, hg * HW, HW);
 }
@@ -1276,7 +1429,7 @@ template <typename CT, int NHB>
 static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void** fn, int grid[3],
                                   int* block) {
   const sk_desc_t& d = *s.d;
-  // f32 caches take the FP32-MFMA kernel, f16 caches the x32 f16 kernel; each
+  // f32 caches take the f16-part kernel, f16 caches the x32 f16 kernels; each
   // spreads a split's heads over one or more workgroups (mla32_groups,
   // mla16_groups).
   constexpr int H = NHB * 16;

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import synthetic
-from harness import (ABS_GATE, assert_parity, decode_call, errors, oracle_out, run_gpu)
+from harness import (ABS_GATE, assert_parity, decode_call, errors, oracle_out, run_gpu, run_gpu_fused)
 from synthetic.torch_io import to_device
 
 pytestmark = pytest.mark.gpu
@@ -416,9 +416,43 @@ def test_latent_explicit_splits_and_padding(kv, L, S):
     ref, _ = oracle_out(case)
     assert_parity(case, out, ref, tight=(kv == "f32"), label=f"latent {kv} L={L} S={S}")
     if L == 1:
+        # One position: the output is its value row. f16 values are used as
+        # stored (exact); f32 values enter the products as two f16 parts,
+        # 22 significant bits (within 2^-22 |v| + 2^-36).
         v0 = case.k[0, 0, 0, :512].astype(np.float32)
         for h in range(case.num_q_heads):
-            assert np.array_equal(out[0, h].astype(np.float32), v0)
+            o = out[0, h].astype(np.float32)
+            if kv == "f16":
+                assert np.array_equal(o, v0)
+            else:
+                assert np.all(np.abs(o.astype(np.float64) - v0) <= 2.0**-22 * np.abs(v0) + 2.0**-36 + 2.0**-24 * np.abs(v0))
+
+
+@pytest.mark.parametrize("where", ["cache", "query"])
+def test_latent_f32_operands_beyond_f16_range_give_nan(where):
+    # An f32 latent cache enters the products as f16 parts: a cache entry or a
+    # scaled query value of magnitude 65,520 or more would carry an infinity,
+    # so the kernel makes NaN the outputs of the heads whose products it
+    # enters (every head for a cache entry; for a query value its own head,
+    # and the other heads of its workgroup), as the header says. Values just
+    # inside the range stay finite and in parity.
+    case = synthetic.latent_case("lat-f32-range", seq_len=100, kv_dtype="f32", capacity=104,
+                                 seed=77, scale=1 / 24)
+    if where == "cache":
+        case.k[0, 40, 0, 7] = 1.0e5
+    else:
+        case.q[0, 5, 100] = 1.0e7  # times 1/24 log2(e): about 6e5
+    for fused in (False, True):
+        out, _, _ = (run_gpu_fused if fused else run_gpu)(case, n_splits=2)
+        assert np.all(np.isnan(out[0] if where == "cache" else out[0, 5])), (where, fused)
+    case = synthetic.latent_case("lat-f32-edge", seq_len=100, kv_dtype="f32", capacity=104,
+                                 seed=78, scale=1 / 24)
+    case.k[0, 40, 0, 7] = 60000.0
+    out, _, _ = run_gpu(case, n_splits=2)
+    ref, _ = oracle_out(case)
+    assert np.all(np.isfinite(out))
+    _, er, _ = errors(out, ref)  # outputs near 6e4: a relative gate
+    assert er <= 1e-5, er
 
 
 @pytest.mark.parametrize("kv", ["f32", "f16"])
