@@ -1190,6 +1190,7 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
         }
         qh8 = __builtin_bit_cast(half4_t, u32x2_t{qc[8].x, qc[8].y});
         ql8 = __builtin_bit_cast(half4_t, u32x2_t{qc[8].z, qc[8].w});
+        asm volatile("" : "+v"(amax));  // formed now, not from rows kept alive to the end
       }
     }
   }
@@ -1328,11 +1329,14 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
         for (int c = 0; c < 8; ++c) acc[c][e] *= ae;
       }
     }
-    // P as f16 parts, the A operands of the x16 products over the tile's 16
-    // positions (lane: head l16, positions 4*lq + e). Each 16-column block
-    // accumulates 2^11 P V as P_hi 2^11 V_hi + P_hi V_lo + P_lo V_hi (V_lo and
-    // P_lo carry 2^11), three products into one accumulator; P_hi 2^11 is
-    // exact in f16 because the weights stay at or below 2^kLazyMax32.
+    // P as f16 parts over the tile's 16 positions (lane: head l16, positions
+    // 4*lq + e). Each 16-column block accumulates 2^11 P V as P_hi 2^11 V_hi +
+    // P_hi V_lo + P_lo V_hi (V_lo and P_lo carry 2^11) into one accumulator:
+    // the first two as one x32 product whose contraction runs over (position,
+    // part) pairs, A = [P_hi 2^11 | P_hi] against B = [V_hi | V_lo] (the
+    // lane's two transpose reads side by side), the third as an x16 product.
+    // P_hi 2^11 is exact in f16 because the weights stay at or below
+    // 2^kLazyMax32.
     half4_t ph, phs, pl;
     {
 #pragma clang fp contract(off)
@@ -1353,7 +1357,7 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
       asm volatile("" : "+v"(vab[u]));
     }
     auto vread = [&](int cb, int part) { return lds_tr16((vab[cb & 3] ^ (8u * part)) + 256 * (cb >> 2)); };
-    // Two halves of four blocks; within a half the three products of a block
+    // Two halves of four blocks; within a half the two products of a block
     // are four MFMAs apart.
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -1364,9 +1368,9 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
         vl[c] = vread(4 * hf + c, 1);
       }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[4 * hf + c] = mfma16(phs, vh[c], acc[4 * hf + c]);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[4 * hf + c] = mfma16(ph, vl[c], acc[4 * hf + c]);
+      for (int c = 0; c < 4; ++c)
+        acc[4 * hf + c] = mfma32(__builtin_shufflevector(phs, ph, 0, 1, 2, 3, 4, 5, 6, 7),
+                                 __builtin_shufflevector(vh[c], vl[c], 0, 1, 2, 3, 4, 5, 6, 7), acc[4 * hf + c]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[4 * hf + c] = mfma16(pl, vh[c], acc[4 * hf + c]);
     }
