@@ -171,7 +171,7 @@ typedef struct {
  *   latent: chunk = max(64, ceil(g * total_tokens / cu_count)) with g workgroups per
  *           split, each serving a slice of the query heads: for f16 caches 1 up to
  *           96 heads and 2 (of 64 heads) at 128; for f32 caches Hq/48 (Hq/32 when
- *           48 does not divide Hq), whose FP32-MFMA kernel holds fewer heads.
+ *           48 does not divide Hq), whose kernel holds fewer heads per workgroup.
  *           Each split costs a partial of every head, so splits stay long.
  *   chunk is rounded up to a multiple of 64 and S = ceil(max_seq_len / chunk).
  * Below SK_MIN_SPLIT_CONTEXT positions the heuristic returns S = 1 (Lecture 06

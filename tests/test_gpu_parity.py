@@ -279,7 +279,7 @@ LDS_FAMILIES = {
     "paged-bf16": lambda: synthetic.gqa_case("lds-paged", seq_lens=[64, 64], num_q_heads=32,
                                              num_kv_heads=8, head_dim=128, q_dtype="bf16",
                                              kv_dtype="bf16", layout="paged", seed=1),
-    # shared-latent kernels (FP32 MFMA, f16 MFMA)
+    # shared-latent kernels (f32 caches as f16 parts, f16 caches)
     "latent-f32": lambda: synthetic.latent_case("lds-l32", seq_len=64, kv_dtype="f32", seed=1,
                                                 scale=1.0 / 24.0),
     "latent-f16": lambda: synthetic.latent_case("lds-l16", seq_len=64, kv_dtype="f16", seed=1,
