@@ -694,7 +694,8 @@ def brief(r):
     for src, dst in (("frac_of_peak", "frac"), ("split_us", "split_us"),
                      ("split_frac_of_peak", "split_frac"), ("combine_us", "comb_us"),
                      ("one_launch_us_per_call", "one_us"), ("mfma_frac", "mfma_frac"),
-                     ("TFLOPs", "TFLOPs"), ("combine_project_us", "cp_us")):
+                     ("TFLOPs", "TFLOPs"), ("combine_project_us", "cp_us"),
+                     ("frac_of_fp32_mfma_peak", "fp32_mfma_frac")):
         if src in r:
             b[dst] = r[src]
     b["cold"] = r.get("mall_flushed")
