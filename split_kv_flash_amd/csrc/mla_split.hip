@@ -992,7 +992,7 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   constexpr int NW = 4 * NHBB;
   constexpr int NT = NW * 64;
   constexpr int HW = 16 * NHBB;                    // heads per workgroup
-  constexpr int KT = kLatDk / 4 / 16;              // 9 reads of 4 steps over 144 columns
+  constexpr int KT = kLatDk / 4 / 16;              // 9 chunks of 4 columns per lane over the wave's 144
   constexpr int DPW = (kSlots32 + NT - 1) / NT;    // tile loads per lane
   constexpr int TSTRIDE = DPW * NT * 4;            // floats per tile buffer (padded slots included)
 
@@ -1137,16 +1137,14 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   if constexpr (IDX) wait_vm_lgkm0<0>();  // the second tile's rows
   issue_tile(1, start + kT32);
   // Query block as B operands (requested after the first tiles, so their
-  // latency overlaps), pre-scaled into base-2 units: qv[t][u] is
-  // column 144*dq + 16*t + 4*lq + u of head head0 + l16. The workgroup loads
-  // every block's rows as consecutive float4s (whole lines per instruction;
-  // a wave's own fragments, 16 rows 64 bytes apart, touch sixteen lines) and
-  // stages one block at a time through tile buffer 2, which one block's
-  // 16 x 576 floats fill; row h keeps float4 chunk c at position c ^ h, as
-  // the tiles do.
-  // Query parts (B operands): chunk t of this wave (columns 4*(36*dq + lq + 4*t)
-  // .. +3 of head head0 + l16) as f16 parts; step s of the x32 products takes
-  // chunks 2s and 2s+1, the x16 step chunk 8.
+  // latency overlaps), pre-scaled into base-2 units and split into f16
+  // parts: chunk t of this wave is columns 4*(36*dq + lq + 4*t) .. +3 of head
+  // head0 + l16; step s of the x32 score products takes chunks 2s and 2s+1,
+  // the x16 step chunk 8. The workgroup loads every block's rows as
+  // consecutive float4s (whole lines per instruction; a wave's own
+  // fragments, 16 rows 64 bytes apart, touch sixteen lines) and stages one
+  // block at a time through tile buffer 2, which one block's 16 x 576 floats
+  // fill; row h keeps float4 chunk c at position c ^ h, as the tiles do.
   half8_t qh[4], ql[4];
   half4_t qh8, ql8;
   {
@@ -1201,12 +1199,12 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   wait_vm_lgkm0<0>();
   raw_barrier();
 
-  // Partial scores S^T of the tile in `cur` over this wave's 144 columns:
-  // four x32 steps (chunks 2s, 2s+1) and one x16 step (chunk 8), three
-  // products each (C_hi q_hi, then C_hi q_lo and C_lo q_hi, whose lo parts
-  // carry 2^11, into an accumulator of their own),
-  // each step's operands read from LDS one step ahead. After steps 0-2, stage(s)
-  // of the previous tile's softmax runs (a constant after unrolling), so the
+  // Partial scores S^T of the tile at LDS address `cur` over this wave's 144
+  // columns: four x32 steps (chunks 2s, 2s+1) and one x16 step (chunk 8),
+  // three products each (C_hi q_hi into one accumulator; C_hi q_lo and
+  // C_lo q_hi, whose lo parts carry 2^11, into another), each step's
+  // operands read from LDS one step ahead. After steps 0-2, stage(s) of the
+  // previous tile's softmax runs (a constant after unrolling), so the
   // softmax's VALU and cross-lane work issues while the matrix pipe works
   // through the products. Accumulators by step parity keep consecutive
   // products independent; they are summed at the end in a fixed order.
