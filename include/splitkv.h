@@ -222,7 +222,7 @@ size_t attn_decode_workspace_bytes(const sk_desc_t* desc, const sk_plan_t* plan)
  * product (22 significant bits: each operand within 2^-22 |x| + 2^-36; f32 accumulation);
  * a cache entry or scaled query value of magnitude 65,520 or more, past f16's range, makes
  * NaN the outputs of the heads whose products it enters (every head of the sequence for a
- * cache entry; for a query value its own head and the others its workgroup serves).
+ * cache entry, its own head for a query value).
  * Anything else returns SK_ERR_UNSUPPORTED without launching.
  * Kernel: contiguous f16/bf16 caches of head width 64, of width 128 with at least 4
  * query heads per KV head, and of width 256 with at least 6, run on the query-tile

@@ -521,8 +521,9 @@ constexpr float kLazyMax = 8.0f;
 // a_hi b_hi + 2^-11 (a_hi b_lo + a_lo b_hi) (the dropped a_lo b_lo is below
 // 2^-22 of it). Per flop, v_mfma_f32_16x16x32_f16 issues 16 times as fast
 // as v_mfma_f32_16x16x4_f32 (and the x16 form at least 8 times), so three
-// part products still cost well under one f32 product. f16's range ends at 65,504: an operand of magnitude 65,520 or more
-// sets a workgroup flag and the split's partials become NaN.
+// part products still cost well under one f32 product. f16's range ends at
+// 65,504: an operand of magnitude 65,520 or more makes the scores or outputs
+// it enters NaN (f16_parts).
 //
 // The query parts of 16 heads x 576 columns and the 16 x 512 output
 // accumulators do not fit one wave's share of the register file at three waves
@@ -954,9 +955,11 @@ typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
 // hi = x rounded to f16, lo = (x - hi) * 2^11 rounded to f16. x - hi is exact
 // and at most 2^-11 |x|, so hi + lo * 2^-11 equals x within 2^-22 |x| + 2^-36
 // (the scaling keeps lo clear of f16's subnormals). The residual is one fused
-// step from the packed hi (exact: (x - hi) 2^11 is an f32 value). amax keeps
-// the largest |x| seen, to tell values that would round to infinity in f16.
-__device__ __forceinline__ u32x4_t f16_parts(float4_t x, float& amax) {
+// step from the packed hi (exact: (x - hi) 2^11 is an f32 value). Past f16's
+// range (|x| >= 65,520) hi is an infinity and lo the opposite infinity (or
+// NaN): every product x enters then sums an infinity with its negation, so
+// the scores or outputs it touches come out NaN.
+__device__ __forceinline__ u32x4_t f16_parts(float4_t x) {
 #pragma clang fp contract(off)
   const half2_t h0 = __builtin_convertvector(float2_t{x[0], x[1]}, half2_t);
   const half2_t h1 = __builtin_convertvector(float2_t{x[2], x[3]}, half2_t);
@@ -966,8 +969,6 @@ __device__ __forceinline__ u32x4_t f16_parts(float4_t x, float& amax) {
   const float r3 = __builtin_fmaf((float)h1[1], -2048.0f, x[3] * 2048.0f);
   const half2_t l0 = __builtin_convertvector(float2_t{r0, r1}, half2_t);
   const half2_t l1 = __builtin_convertvector(float2_t{r2, r3}, half2_t);
-  amax = fmaxf(amax, fmaxf(fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])),
-                           fmaxf(__builtin_fabsf(x[2]), __builtin_fabsf(x[3]))));
   return u32x4_t{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
                  __builtin_bit_cast(uint32_t, l0), __builtin_bit_cast(uint32_t, l1)};
 }
@@ -998,7 +999,6 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
 
   __shared__ __align__(16) float s_c[3 * TSTRIDE];
   __shared__ __align__(16) float4_t s_sx[2][NW][64];
-  __shared__ int s_big;  // set when some operand lies outside f16's range
 
   const int split = blockIdx.x;
   const int b = blockIdx.y;
@@ -1011,8 +1011,6 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   const int l16 = lane & 15;
   const int lq = lane >> 4;
   const int head0 = hg * HW + hb * 16;
-  if (tid == 0) s_big = 0;  // ordered before every update by the prologue's barriers
-  float amax = 0.0f;  // largest |operand| this lane has split into f16 parts
 
   const int L = min(a.seq_lens[b], a.cap);
   const int64_t start = (int64_t)split * a.chunk;
@@ -1123,7 +1121,7 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
 #pragma unroll
     for (int c = 0; c < DPW; ++c) {
       u32x4_t* p = reinterpret_cast<u32x4_t*>(s_c + bi * TSTRIDE + ((wave * DPW + c) * 64 + lane) * 4);
-      const u32x4_t v = f16_parts(__builtin_bit_cast(float4_t, *p), amax);
+      const u32x4_t v = f16_parts(__builtin_bit_cast(float4_t, *p));
       *p = (srow[c] & 1) ? u32x4_t{v.z, v.w, v.x, v.y} : v;
     }
   };
@@ -1180,7 +1178,7 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
       if (hb == r) {
         u32x4_t qc[KT];
 #pragma unroll
-        for (int t = 0; t < KT; ++t) qc[t] = f16_parts(*reinterpret_cast<const float4_t*>(sq + soff(t)), amax);
+        for (int t = 0; t < KT; ++t) qc[t] = f16_parts(*reinterpret_cast<const float4_t*>(sq + soff(t)));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           qh[u] = __builtin_bit_cast(half8_t, u32x4_t{qc[2 * u].x, qc[2 * u].y, qc[2 * u + 1].x, qc[2 * u + 1].y});
@@ -1188,7 +1186,6 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
         }
         qh8 = __builtin_bit_cast(half4_t, u32x2_t{qc[8].x, qc[8].y});
         ql8 = __builtin_bit_cast(half4_t, u32x2_t{qc[8].z, qc[8].w});
-        asm volatile("" : "+v"(amax));  // formed now, not from rows kept alive to the end
       }
     }
   }
@@ -1390,12 +1387,6 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   // Drain the tile loads still in flight before the workgroup can retire.
   wait_vm_lgkm0<0>();
 
-  // A value outside f16's range anywhere in the workgroup's operands makes
-  // its partials NaN (the parts would carry an infinity).
-  if (__any(amax >= 65520.0f) && lane == 0) atomicOr(&s_big, 1);
-  wait_vm_lgkm0<0>();
-  raw_barrier();
-  const float bad = s_big ? __builtin_nanf("") : 0.0f;
   // Partials: lane (column l16 of block cb, quarter lq) holds heads 4*lq + i.
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb)
@@ -1403,13 +1394,13 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int head = head0 + 4 * lq + i;
       const int col = dq * 128 + 16 * cb + l16;
-      put_partial(a.ws_acc + (ws0 + (int64_t)head * a.S) * kLatDv + col, acc[cb][i] * (1.0f / 2048.0f) + bad,
+      put_partial(a.ws_acc + (ws0 + (int64_t)head * a.S) * kLatDv + col, acc[cb][i] * (1.0f / 2048.0f),
                   FUSED && a.S > 1);
     }
   const float l = sum_xor32(sum_xor16(ll));
   if (dq == 0 && lq == 0) {
-    put_partial(a.ws_m + ws0 + (int64_t)(head0 + l16) * a.S, m * kLn2 + bad, FUSED && a.S > 1);
-    put_partial(a.ws_l + ws0 + (int64_t)(head0 + l16) * a.S, l + bad, FUSED && a.S > 1);
+    put_partial(a.ws_m + ws0 + (int64_t)(head0 + l16) * a.S, m * kLn2, FUSED && a.S > 1);
+    put_partial(a.ws_l + ws0 + (int64_t)(head0 + l16) * a.S, l, FUSED && a.S > 1);
   }
   if constexpr (FUSED) latent_fused_tail<NT>(a, s_c, hg * HW, HW);
 }

@@ -431,11 +431,11 @@ def test_latent_explicit_splits_and_padding(kv, L, S):
 @pytest.mark.parametrize("where", ["cache", "query"])
 def test_latent_f32_operands_beyond_f16_range_give_nan(where):
     # An f32 latent cache enters the products as f16 parts: a cache entry or a
-    # scaled query value of magnitude 65,520 or more would carry an infinity,
-    # so the kernel makes NaN the outputs of the heads whose products it
-    # enters (every head for a cache entry; for a query value its own head,
-    # and the other heads of its workgroup), as the header says. Values just
-    # inside the range stay finite and in parity.
+    # scaled query value of magnitude 65,520 or more has an infinite hi part
+    # and the opposite infinity as lo part, so the outputs of the heads whose
+    # products it enters come out NaN (every head for a cache entry, its own
+    # head for a query value), as the header says. Values just inside the
+    # range stay finite and in parity.
     case = synthetic.latent_case("lat-f32-range", seq_len=100, kv_dtype="f32", capacity=104,
                                  seed=77, scale=1 / 24)
     if where == "cache":
@@ -445,6 +445,9 @@ def test_latent_f32_operands_beyond_f16_range_give_nan(where):
     for fused in (False, True):
         out, _, _ = (run_gpu_fused if fused else run_gpu)(case, n_splits=2)
         assert np.all(np.isnan(out[0] if where == "cache" else out[0, 5])), (where, fused)
+        if where == "query":
+            others = np.delete(out[0], 5, axis=0)
+            assert np.all(np.isfinite(others)), (where, fused)
     case = synthetic.latent_case("lat-f32-edge", seq_len=100, kv_dtype="f32", capacity=104,
                                  seed=78, scale=1 / 24)
     case.k[0, 40, 0, 7] = 60000.0

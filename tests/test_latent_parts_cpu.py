@@ -12,7 +12,8 @@ kernel's lazy-maximum threshold). These tests model that arithmetic in numpy
 (float64 sums of exactly widened parts) and pin:
 
 * hi + lo * 2^-11 equals x within 2^-22 |x| + 2^-36 over f16's whole range,
-  and magnitudes from 65,520 up round to infinity (the kernel's range check);
+  and magnitudes from 65,520 up give an infinite hi and the opposite
+  infinity as lo, so every product such a value enters is NaN;
 * latent scores (576 columns) from three products stay within 1e-6 of the
   exact score relative to sum |q| |c|, while hi products alone miss by far
   more;
@@ -56,9 +57,21 @@ def test_two_f16_parts_carry_22_bits_over_f16_range():
 
 
 def test_f16_range_boundary_of_the_split():
-    hi, _ = _parts(np.array([65504.0, 65519.0, 65520.0, -70000.0], dtype=np.float32))
+    hi, lo = _parts(np.array([65504.0, 65519.0, 65520.0, -70000.0], dtype=np.float32))
     assert np.isfinite(hi[:2].astype(np.float64)).all()
     assert np.isinf(hi[2:].astype(np.float64)).all()
+    # past the range, lo is the opposite infinity: a product of parts,
+    # a_hi b_hi + 2^-11 (a_hi b_lo + a_lo b_hi), then sums inf and -inf
+    assert np.all(np.sign(lo[2:].astype(np.float64)) == -np.sign(hi[2:].astype(np.float64)))
+    g = np.random.default_rng(3)
+    b = g.standard_normal(64).astype(np.float32)
+    bh, bl = _parts(b)
+    with np.errstate(invalid="ignore", over="ignore"):
+        for k in (2, 3):
+            a_hi, a_lo = np.float64(hi[k]), np.float64(lo[k])
+            mixed = a_hi * bl.astype(np.float64) + a_lo * bh.astype(np.float64)  # one accumulator
+            prod = a_hi * bh.astype(np.float64) + mixed / 2048.0
+            assert np.all(np.isnan(prod))
 
 
 def _latent(rows=512, heads=96, dk=576, seed=17, c_scale=1.0):
