@@ -1197,9 +1197,9 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   raw_barrier();
 
   // Partial scores S^T of the tile at LDS address `cur` over this wave's 144
-  // columns: four x32 steps (chunks 2s, 2s+1) and one x16 step (chunk 8),
-  // three products each (C_hi q_hi into one accumulator; C_hi q_lo and
-  // C_lo q_hi, whose lo parts carry 2^11, into another), each step's
+  // columns: four x32 steps (chunks 2s, 2s+1) and a step for chunk 8, three
+  // products each (C_hi q_hi into one accumulator; C_hi q_lo and C_lo q_hi,
+  // whose lo parts carry 2^11, into another), each step's
   // operands read from LDS one step ahead. After steps 0-2, stage(s) of the
   // previous tile's softmax runs (a constant after unrolling), so the
   // softmax's VALU and cross-lane work issues while the matrix pipe works
@@ -1242,9 +1242,11 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
     }
     const half4_t ah = __builtin_bit_cast(half4_t, lds_ld8(addr(8, 0)));
     const half4_t al = __builtin_bit_cast(half4_t, lds_ld8(addr(8, 1)));
-    sa[0] = mfma16(ah, ql8, sa[0]);
+    // The ninth chunk's two mixed products as one x32 product over
+    // (column, part) pairs: [C_hi | C_lo] against [q_lo | q_hi].
     sp[0] = mfma16(ah, qh8, sp[0]);
-    sa[0] = mfma16(al, qh8, sa[0]);
+    sa[0] = mfma32(__builtin_shufflevector(ah, al, 0, 1, 2, 3, 4, 5, 6, 7),
+                   __builtin_shufflevector(ql8, qh8, 0, 1, 2, 3, 4, 5, 6, 7), sa[0]);
     const float4_t lo = sa[0] + sa[1];
     const float4_t hi = sp[0] + sp[1];
     float4_t r;
