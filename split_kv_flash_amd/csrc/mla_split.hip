@@ -540,15 +540,16 @@ constexpr float kLazyMax = 8.0f;
 //    the 16 bytes of four f32 values become four hi halves and four lo halves.
 //  * Scores are computed transposed, S^T[position][head] = C[position][:] .
 //    Q^T, with v_mfma_f32_16x16x32_f16 (chunks t and t+1 of the lane: columns
-//    4*(36*dq + lq + 4t) .. +3 and the next chunk's) and one
-//    v_mfma_f32_16x16x16_f16 step for the ninth chunk, so the result leaves
-//    lane (head l16, quarter lq) holding the scores of positions 4*lq + i:
-//    after the four partials of the block are added (through LDS, in a fixed
-//    order, so all four waves hold identical values) and the softmax runs in
-//    registers, those four weights are exactly the lane's A operand of the
-//    v_mfma_f32_16x16x16_f16 output product over the tile's 16 positions; the
-//    value parts come through the gfx950 transpose read ds_read_b64_tr_b16.
-//    P never goes through LDS.
+//    4*(36*dq + lq + 4t) .. +3 and the next chunk's; the ninth chunk's
+//    products as one x16 and one x32 over (column, part) pairs), so the
+//    result leaves lane (head l16, quarter lq) holding the scores of
+//    positions 4*lq + i: after the four partials of the block are added
+//    (through LDS, in a fixed order, so all four waves hold identical values)
+//    and the softmax runs in registers, those four weights are exactly the
+//    lane's A operand of the output products over the tile's 16 positions
+//    (an x32 over (position, part) pairs and an x16); the value parts come
+//    through the gfx950 transpose read ds_read_b64_tr_b16. P never goes
+//    through LDS.
 //  * One barrier per tile (below).
 // ---------------------------------------------------------------------------
 constexpr int kT32 = 16;              // positions per tile
@@ -943,13 +944,13 @@ __device__ __forceinline__ float4_t mfma16(half4_t a, half4_t b, float4_t c) {
 }
 
 typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
 
 // Lazy-maximum threshold (base 2) of the f32-cache kernel: its weights, at
 // most 2^kLazyMax32, times 2^11 must stay finite in f16.
 constexpr float kLazyMax32 = 4.0f;
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
-typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
 
 // Four f32 values as two f16 parts, packed [hi0 hi1 hi2 hi3 | lo0 lo1 lo2 lo3]:
 // hi = x rounded to f16, lo = (x - hi) * 2^11 rounded to f16. x - hi is exact
@@ -1138,7 +1139,7 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   // latency overlaps), pre-scaled into base-2 units and split into f16
   // parts: chunk t of this wave is columns 4*(36*dq + lq + 4*t) .. +3 of head
   // head0 + l16; step s of the x32 score products takes chunks 2s and 2s+1,
-  // the x16 step chunk 8. The workgroup loads every block's rows as
+  // the last step chunk 8. The workgroup loads every block's rows as
   // consecutive float4s (whole lines per instruction; a wave's own
   // fragments, 16 rows 64 bytes apart, touch sixteen lines) and stages one
   // block at a time through tile buffer 2, which one block's 16 x 576 floats
@@ -1208,8 +1209,6 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   auto scores = [&](uint32_t cur, auto&& stage) -> float4_t {
     const float4_t z = float4_t{0.f, 0.f, 0.f, 0.f};
     float4_t sp[2] = {z, z}, sa[2] = {z, z};
-    // hi (part 0) or lo (part 1) halves of chunks t and t+1, read straight
-    // into the operand's register pairs.
     // Lane addresses of chunks 0-3 in this buffer, made opaque so the other
     // chunks' reads add constants in the instructions' offset fields instead
     // of keeping an address register per read.
@@ -1222,6 +1221,8 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
       asm volatile("" : "+v"(ab[u]));
     }
     auto addr = [&](int t, int part) { return (ab[t & 3] ^ (8u * part)) + 256 * (t >> 2); };
+    // hi (part 0) or lo (part 1) halves of chunks t and t+1, read straight
+    // into the operand's register pairs.
     auto opnd = [&](int t, int part) {
       const u32x2_t x0 = lds_ld8(addr(t, part)), x1 = lds_ld8(addr(t + 1, part));
       return __builtin_bit_cast(half8_t, u32x4_t{x0.x, x0.y, x1.x, x1.y});
