@@ -1408,6 +1408,398 @@ __global__ __launch_bounds__(NHBB * 256) void mla32_split_kernel(MlaArgs a) {
   if constexpr (FUSED) latent_fused_tail<NT>(a, s_c, hg * HW, HW);
 }
 
+// Dedicated-role f32 latent kernel: 48 heads of a split per workgroup of
+// eight waves (two workgroups per split, as mla32_split_kernel), on the same
+// f16 parts. Three scoring waves each own one 16-head block over all 576
+// columns (no partial-score exchange), run its online softmax in registers and
+// publish P's parts and the rescale factors. Five output waves own the 32
+// 16-column value blocks (six each beside a scoring wave on SIMDs 0-2, seven
+// each for the two on SIMD 3), multiply every block's P by them, so each
+// value block leaves LDS once per tile rather than once per head block. Every
+// wave requests its share of the tiles and splits it into parts in place as it
+// lands. Four tile buffers and
+// one barrier per tile: iteration i scores tile i, runs the output product of
+// tile i-1 and requests tile i+2.
+struct Mla32dRoles {
+  static constexpr int NS = 3;  // scoring waves (one per head block)
+  static constexpr int NO = 5;  // output waves
+  static constexpr int kShared = 6, kAlone = 7;
+  static constexpr bool shared(int w) { return w >= 4 && (w & 3) < NS; }
+  static constexpr int ncb(int w) { return w < NS ? 0 : (shared(w) ? kShared : kAlone); }
+  static constexpr int cb0(int w) {
+    int s = 0;
+    for (int v = NS; v < w; ++v) s += ncb(v);
+    return s;
+  }
+  static constexpr int kLoads = kSlots32 / 64;  // 36 wave-loads per tile, over all eight waves
+  static constexpr int LB = kLoads / 8, LX = kLoads % 8;
+  static constexpr int DPW = LB + (LX > 0 ? 1 : 0);
+};
+
+struct Mla32dShared {
+  float* c;      // four tile buffers
+  half4_t* p;    // [2][3 blocks][3 parts][64]: P_hi 2^11, P_hi, P_lo 2^11 (A-operand lane order)
+  float* alpha;  // [2][3][16]: rescale factors of a tile
+  int* moved;    // [2]: last tile whose factors were not all 1
+};
+
+// One role: NCB == 0 scores, else the output product over NCB column blocks.
+// Every role passes the same barriers.
+template <int NCB>
+__device__ __forceinline__ void mla32d_role(const MlaArgs& a, const Mla32dShared& sh, int64_t start,
+                                            int64_t end, int64_t ws0, int b, int hg) {
+  using R = Mla32dRoles;
+  constexpr int HW = 48, NW = 8, NBUF = 4;
+  constexpr int TSTR = kSlots32 * 4;  // floats per tile buffer
+  constexpr int KS = kLatDk / 32;     // 18 x32 score steps
+  constexpr bool SCORER = NCB == 0;
+  static_assert(R::cb0(8) == kLatDv / 16, "the output waves cover the value columns");
+  static_assert(R::kLoads * 64 == kSlots32, "whole wave-loads");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;
+  const int lq = lane >> 4;
+  float* const s_c = sh.c;
+
+  const float* __restrict__ cbase = reinterpret_cast<const float*>(a.c) + (int64_t)b * a.stride_seq;
+  const float* __restrict__ qb = a.q + ((int64_t)b * a.Hq + hg * HW) * kLatDk;
+
+  // Tile staging as in mla32_split_kernel (slot s: row s / 144, logical chunk
+  // (s % 144) ^ row); every wave issues and splits its share of the 36
+  // wave-loads of a tile.
+  const int wl0 = wave * R::LB + min(wave, R::LX);
+  const int nwl = R::LB + (wave < R::LX ? 1 : 0);
+  const uint32_t lds0 = lds_addr_of(s_c);
+  const uint32_t row_bytes = (uint32_t)(a.stride_pos * 4);  // 16 rows: offsets fit 32 bits
+  auto issue_tile = [&](int bi, int64_t tb) {
+    {
+      const int64_t tbc = tb < end ? tb : end - 1;
+      const uint64_t bu = reinterpret_cast<uint64_t>(cbase + tbc * a.stride_pos);
+      const void* base = reinterpret_cast<const void*>(
+          ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32)) << 32) |
+          (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bu));
+      const int last = (int)(end - 1 - tbc);
+#pragma unroll
+      for (int cc = 0; cc < R::DPW; ++cc) {
+        if (R::LX != 0 && cc >= nwl) continue;
+        const int sl = (wl0 + cc) * 64 + lane;
+        const int srow = sl / kCpr32;
+        const int scol = (sl - srow * kCpr32) ^ srow;
+        const uint32_t off = (uint32_t)min(srow, last) * row_bytes + (uint32_t)(scol * 16);
+        const uint32_t dst = lds0 + (uint32_t)((bi * TSTR + (wl0 + cc) * 256) * 4);
+        dma16s(off, base, __builtin_amdgcn_readfirstlane(dst), a.nt);
+      }
+    }
+  };
+  // The slots this wave loaded, as f16 parts in place; odd rows keep lo first.
+  auto split_own = [&](int bi) {
+    {
+#pragma unroll
+      for (int cc = 0; cc < R::DPW; ++cc) {
+        if (R::LX != 0 && cc >= nwl) continue;
+        const int sl = (wl0 + cc) * 64 + lane;
+        u32x4_t* p = reinterpret_cast<u32x4_t*>(s_c + bi * TSTR + sl * 4);
+        const u32x4_t v = f16_parts(__builtin_bit_cast(float4_t, *p));
+        *p = ((sl / kCpr32) & 1) ? u32x4_t{v.z, v.w, v.x, v.y} : v;
+      }
+    }
+  };
+  // Everything of this wave but its loads of the newest tile has landed.
+  auto wait_but_newest = [&]() {
+    if constexpr (R::LX == 0) {
+      wait_vm_lgkm0<R::DPW>();
+    } else {
+      if (nwl == R::DPW)
+        wait_vm_lgkm0<R::DPW>();
+      else
+        wait_vm_lgkm0<R::DPW - 1>();
+    }
+  };
+
+  const int ntiles = (int)((end - start + kT32 - 1) / kT32);
+  // Prologue: tile 0; the query rows (48 x 576 f32, times scale log2 e)
+  // staged through tile buffers 1-3, which they fill, with whole-line loads by
+  // the whole workgroup (row h keeps chunk c at position c ^ (h & 15)); each
+  // scoring wave splits its block's fragments into parts; then tile 1.
+  constexpr int QF = HW * kLatDk / 4;
+  constexpr int QV = (QF + NW * 64 - 1) / (NW * 64);
+  static_assert(HW * kLatDk <= 3 * TSTR, "the staged rows fit");
+  float* const sq = s_c + TSTR;
+  issue_tile(0, start);
+  {
+    float4 qv[QV];
+#pragma unroll
+    for (int k = 0; k < QV; ++k)
+      if (QF % (NW * 64) == 0 || tid + NW * 64 * k < QF)
+        qv[k] = *reinterpret_cast<const float4*>(qb + 4 * (tid + NW * 64 * k));
+#pragma unroll
+    for (int k = 0; k < QV; ++k) {
+      const int f = tid + NW * 64 * k;
+      if (QF % (NW * 64) != 0 && f >= QF) continue;
+      const int h = f / (kLatDk / 4);
+      const int c = f - h * (kLatDk / 4);
+      *reinterpret_cast<float4_t*>(sq + h * kLatDk + ((c ^ (h & 15)) << 2)) =
+          float4_t{qv[k].x * a.qscale, qv[k].y * a.qscale, qv[k].z * a.qscale, qv[k].w * a.qscale};
+    }
+  }
+  wait_vm_lgkm0<0>();  // the staged rows and tile 0
+  raw_barrier();
+  // Score chunk t of a scoring wave (t = 0..35): logical chunk lq + 4t of row
+  // (head) l16, at sb[t & 3] + 64 (t >> 2) floats; step s takes chunks 2s and
+  // 2s + 1.
+  int sb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) sb[u] = l16 * kLatDk + (((lq + 4 * u) ^ l16) << 2);
+  auto soff = [&](int t) { return sb[t & 3] + 64 * (t >> 2); };
+  half8_t qh[SCORER ? KS : 1], ql[SCORER ? KS : 1];
+  if constexpr (SCORER) {
+    const float* qrow = sq + 16 * wave * kLatDk;  // rows 16w + l16 (swizzle l16)
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const u32x4_t p0 = f16_parts(*reinterpret_cast<const float4_t*>(qrow + soff(2 * st)));
+      const u32x4_t p1 = f16_parts(*reinterpret_cast<const float4_t*>(qrow + soff(2 * st + 1)));
+      qh[st] = __builtin_bit_cast(half8_t, u32x4_t{p0.x, p0.y, p1.x, p1.y});
+      ql[st] = __builtin_bit_cast(half8_t, u32x4_t{p0.z, p0.w, p1.z, p1.w});
+    }
+  }
+  raw_barrier();  // the staged rows are read: buffers 1-3 are free
+  issue_tile(1, start + kT32);
+  split_own(0);
+  wait_but_newest();
+  raw_barrier();  // tile 0's parts
+
+  if constexpr (SCORER) {
+    float m = -INFINITY, ll = 0.0f;  // head 16w + l16 (replicated over quarters); ll: this lane's share
+    for (int i = 0; i < ntiles; ++i) {
+      const int64_t tb = start + (int64_t)i * kT32;
+      const bool load_next = tb + 2 * kT32 < end;
+      if (load_next) issue_tile((i + 2) % NBUF, tb + 2 * kT32);
+      const uint32_t cur = lds0 + (uint32_t)((i % NBUF) * TSTR * 4);
+      // Lane addresses of chunks 0-3 (hi halves: byte 8 (l16 & 1) of a
+      // chunk; lo: bit 3 flipped), opaque so the other chunks' reads use the
+      // instructions' offset fields.
+      uint32_t ab[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        ab[u] = cur + 4 * sb[u] + 8 * (l16 & 1);
+        asm volatile("" : "+v"(ab[u]));
+      }
+      auto opnd = [&](int st, int part) {
+        const u32x2_t x0 = lds_ld8((ab[(2 * st) & 3] ^ (8u * part)) + 256 * ((2 * st) >> 2));
+        const u32x2_t x1 = lds_ld8((ab[(2 * st + 1) & 3] ^ (8u * part)) + 256 * ((2 * st + 1) >> 2));
+        return __builtin_bit_cast(half8_t, u32x4_t{x0.x, x0.y, x1.x, x1.y});
+      };
+      const float4_t z = float4_t{0.f, 0.f, 0.f, 0.f};
+      float4_t sp[2] = {z, z}, sa[2] = {z, z}, sc[2] = {z, z};
+      half8_t nh = opnd(0, 0), nl = opnd(0, 1);
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        const half8_t ah = nh, al = nl;
+        if (st + 1 < KS) {
+          nh = opnd(st + 1, 0);
+          nl = opnd(st + 1, 1);
+        }
+        sa[st & 1] = mfma32(ah, ql[st], sa[st & 1]);
+        sp[st & 1] = mfma32(ah, qh[st], sp[st & 1]);
+        sc[st & 1] = mfma32(al, qh[st], sc[st & 1]);
+        if (st & 1) __builtin_amdgcn_sched_barrier(0);
+      }
+      const float4_t lo = (sa[0] + sa[1]) + (sc[0] + sc[1]);
+      const float4_t hi = sp[0] + sp[1];
+      const int rel = (int)(end - tb);  // positions of tile i before the end (> 0)
+      float v[4], lmx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = 4 * lq + e < rel ? fmaf(lo[e], 1.0f / 2048.0f, hi[e]) : -INFINITY;
+        lmx = fmaxf(lmx, v[e]);
+      }
+      // Lazy running maximum (threshold kLazyMax32, base 2), as in
+      // mla32_split_kernel.
+      float al = 1.0f;
+      bool moved = false;
+      if (__any(lmx > m + kLazyMax32)) {
+        const float mx = max_xor32(max_xor16(lmx));
+        const float mn = mx > m + kLazyMax32 ? mx : m;
+        al = fast_exp2(m - ((mn == -INFINITY) ? 0.0f : mn));
+        ll *= al;
+        m = mn;
+        moved = true;
+      }
+      const float mu = (m == -INFINITY) ? 0.0f : m;
+      half4_t phs, ph, pl;
+      {
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pe = fast_exp2(v[e] - mu);
+          ll += pe;
+          ph[e] = (_Float16)pe;
+          phs[e] = (_Float16)((float)ph[e] * 2048.0f);
+          pl[e] = (_Float16)__builtin_fmaf((float)ph[e], -2048.0f, pe * 2048.0f);
+        }
+      }
+      const int par = i & 1;
+      half4_t* pw = sh.p + (par * 3 + wave) * 3 * 64 + lane;
+      pw[0] = phs;
+      pw[64] = ph;
+      pw[128] = pl;
+      if (lq == 0) sh.alpha[(par * 3 + wave) * 16 + l16] = al;
+      // Several scoring waves may report the same tile: an LDS atomic max
+      // (the flag only ever rises to the newest tile index).
+      if (__any(moved) && lane == 0) atomicMax(&sh.moved[par], i);
+      // Tile i+1 must have landed: split this wave's slots of it.
+      if (load_next)
+        wait_but_newest();
+      else
+        wait_vm_lgkm0<0>();
+      if (i + 1 < ntiles) {
+        split_own((i + 1) % NBUF);
+        if (load_next)
+          wait_but_newest();
+        else
+          wait_vm_lgkm0<0>();
+      }
+      raw_barrier();  // P and factors of tile i; tile i+1's parts
+    }
+    wait_vm_lgkm0<0>();
+    const float l = sum_xor32(sum_xor16(ll));
+    if (lq == 0) {
+      const int head = hg * HW + 16 * wave + l16;
+      a.ws_m[ws0 + (int64_t)head * a.S] = m * kLn2;
+      a.ws_l[ws0 + (int64_t)head * a.S] = l;
+    }
+  } else {
+    const int cb0 = R::cb0(wave);
+    // Value reads (transposed, 16 columns by 4 rows per 16 lanes): lane
+    // l16 = 4 rho + sg of quarter lq takes row r = 4 lq + rho, columns
+    // 4 sg .. +3 of block cb0 + u: logical chunk 4 (cb0 + u) + sg, at
+    // (chunk ^ r); its hi halves at byte 8 (r & 1).
+    const int r = 4 * lq + (l16 >> 2);
+    uint32_t vo[NCB];
+#pragma unroll
+    for (int u = 0; u < NCB; ++u)
+      vo[u] = (uint32_t)((r * kLatDk + (((4 * (cb0 + u) + (l16 & 3)) ^ r) << 2)) * 4 + 8 * (r & 1));
+    float4_t acc[3][NCB];
+#pragma unroll
+    for (int hb = 0; hb < 3; ++hb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[hb][cb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    auto output = [&](int j) {
+      const uint32_t prv = lds0 + (uint32_t)((j % NBUF) * TSTR * 4);
+      const int par = j & 1;
+      if (sh.moved[par] == j) {
+        // Accumulator items are heads 4 lq + e of each block.
+#pragma unroll
+        for (int hb = 0; hb < 3; ++hb) {
+          const float4_t alp = *reinterpret_cast<const float4_t*>(&sh.alpha[(par * 3 + hb) * 16 + 4 * lq]);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[hb][cb][e] *= alp[e];
+        }
+      }
+      half4_t pp[3][3];
+#pragma unroll
+      for (int hb = 0; hb < 3; ++hb)
+#pragma unroll
+        for (int part = 0; part < 3; ++part) pp[hb][part] = sh.p[((par * 3 + hb) * 3 + part) * 64 + lane];
+      half4_t vh = lds_tr16(prv + vo[0]), vl = lds_tr16((prv + vo[0]) ^ 8u);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const half4_t bh = vh, bl = vl;
+        if (cb + 1 < NCB) {
+          vh = lds_tr16(prv + vo[cb + 1]);
+          vl = lds_tr16((prv + vo[cb + 1]) ^ 8u);
+        }
+        const half8_t bb = __builtin_shufflevector(bh, bl, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int hb = 0; hb < 3; ++hb)
+          acc[hb][cb] = mfma32(__builtin_shufflevector(pp[hb][0], pp[hb][1], 0, 1, 2, 3, 4, 5, 6, 7), bb, acc[hb][cb]);
+#pragma unroll
+        for (int hb = 0; hb < 3; ++hb) acc[hb][cb] = mfma16(pp[hb][2], bh, acc[hb][cb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    for (int i = 0;; ++i) {
+      const bool more = i < ntiles;  // tile i exists (else only tile i-1's output remains)
+      const int64_t tb = start + (int64_t)i * kT32;
+      // Tile i+2 goes into the buffer of tile i-2, whose output product ran
+      // before the last barrier; tiles past the end are not requested.
+      const bool load_next = more && tb + 2 * kT32 < end;
+      if (load_next) issue_tile((i + 2) % NBUF, tb + 2 * kT32);
+      if (i > 0) output(i - 1);
+      if (!more) break;
+      // Tile i+1 (requested one iteration ago, or in the prologue) must have
+      // landed: split it into parts; tile i+2's loads, if any, stay in flight.
+      if (load_next)
+        wait_but_newest();
+      else
+        wait_vm_lgkm0<0>();
+      if (i + 1 < ntiles) {
+        split_own((i + 1) % NBUF);
+        if (load_next)
+          wait_but_newest();
+        else
+          wait_vm_lgkm0<0>();
+      }
+      raw_barrier();
+    }
+    // Drain the tile loads still in flight before the workgroup can retire.
+    wait_vm_lgkm0<0>();
+    // Partials: heads 16 hb + 4 lq + e, columns 16 (cb0 + cb) + l16.
+#pragma unroll
+    for (int hb = 0; hb < 3; ++hb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int head = hg * HW + 16 * hb + 4 * lq + e;
+          const int col = 16 * (cb0 + cb) + l16;
+          a.ws_acc[(ws0 + (int64_t)head * a.S) * kLatDv + col] = acc[hb][cb][e] * (1.0f / 2048.0f);
+        }
+  }
+}
+
+__global__ __launch_bounds__(512) void mla32d_split_kernel(MlaArgs a) {
+  constexpr int HW = 48, NBUF = 4;
+  using R = Mla32dRoles;
+  __shared__ __align__(16) float s_c[NBUF * kSlots32 * 4];
+  __shared__ __align__(16) half4_t s_p[2 * 3 * 3 * 64];
+  __shared__ __align__(16) float s_alpha[2 * 3 * 16];
+  __shared__ int s_moved[2];
+
+  const int split = blockIdx.x;
+  const int b = blockIdx.y;
+  const int hg = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int L = min(a.seq_lens[b], a.cap);
+  const int64_t start = (int64_t)split * a.chunk;
+  const int64_t end = min((int64_t)L, start + a.chunk);
+  const int64_t ws0 = (int64_t)b * a.Hq * a.S + split;
+  if (start >= end) {
+    for (int idx = tid; idx < HW * kLatDv; idx += 512) {
+      const int h = hg * HW + idx / kLatDv, e = idx - (idx / kLatDv) * kLatDv;
+      a.ws_acc[(ws0 + (int64_t)h * a.S) * kLatDv + e] = 0.0f;
+    }
+    for (int h = tid; h < HW; h += 512) {
+      a.ws_m[ws0 + (int64_t)(hg * HW + h) * a.S] = -INFINITY;
+      a.ws_l[ws0 + (int64_t)(hg * HW + h) * a.S] = 0.0f;
+    }
+    return;
+  }
+  if (tid < 2) s_moved[tid] = -1;
+  const Mla32dShared sh{s_c, s_p, s_alpha, s_moved};
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave < R::NS)
+    mla32d_role<0>(a, sh, start, end, ws0, b, hg);
+  else if (R::shared(wave))
+    mla32d_role<R::kShared>(a, sh, start, end, ws0, b, hg);
+  else
+    mla32d_role<R::kAlone>(a, sh, start, end, ws0, b, hg);
+}
+
 int latent_blocks_per_split(const sk_desc_t& d) {
   return d.kv_dtype == SK_F32 ? mla32_groups(d.num_q_heads) : mla16_groups(d.num_q_heads);
 }
@@ -1438,6 +1830,13 @@ static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void*
                : (s.fused ? mla32_split_kernel<mla32_blocks(H), false, true> : mla32_split_kernel<mla32_blocks(H), false, false>);
     threads = mla32_blocks(H) * 256;
     groups = mla32_groups(H);
+    if constexpr (H == 96) {
+      if (!idx && !s.fused) {
+        // Contiguous caches, two-launch path: the dedicated-role form.
+        kern = mla32d_split_kernel;
+        threads = 512;
+      }
+    }
   } else {
     if constexpr (H == 64 || H == 96) {
       // (Contiguous caches never take the whole-head form of this kernel
