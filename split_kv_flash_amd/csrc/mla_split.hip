@@ -1831,8 +1831,11 @@ static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void*
     threads = mla32_blocks(H) * 256;
     groups = mla32_groups(H);
     if constexpr (H == 96) {
-      if (!idx && !s.fused) {
-        // Contiguous caches, two-launch path: the dedicated-role form.
+      if (!idx && !s.fused && (int64_t)s.p->n_splits * d.batch >= 64) {
+        // Contiguous caches on the two-launch path, once the grid (two
+        // workgroups per (split, sequence) pair) fills half the compute
+        // units: the dedicated-role form. Shorter grids keep the four-wave
+        // form, the one the index-list path shares tile for tile.
         kern = mla32d_split_kernel;
         threads = 512;
       }
