@@ -1445,7 +1445,7 @@ struct Mla32dShared {
 
 // One role: NCB == 0 scores, else the output product over NCB column blocks.
 // Every role passes the same barriers.
-template <int NCB>
+template <int NCB, bool FUSED>
 __device__ __forceinline__ void mla32d_role(const MlaArgs& a, const Mla32dShared& sh, int64_t start,
                                             int64_t end, int64_t ws0, int b, int hg) {
   using R = Mla32dRoles;
@@ -1667,8 +1667,8 @@ __device__ __forceinline__ void mla32d_role(const MlaArgs& a, const Mla32dShared
     const float l = sum_xor32(sum_xor16(ll));
     if (lq == 0) {
       const int head = hg * HW + 16 * wave + l16;
-      a.ws_m[ws0 + (int64_t)head * a.S] = m * kLn2;
-      a.ws_l[ws0 + (int64_t)head * a.S] = l;
+      put_partial(a.ws_m + ws0 + (int64_t)head * a.S, m * kLn2, FUSED && a.S > 1);
+      put_partial(a.ws_l + ws0 + (int64_t)head * a.S, l, FUSED && a.S > 1);
     }
   } else {
     const int cb0 = R::cb0(wave);
@@ -1757,11 +1757,13 @@ __device__ __forceinline__ void mla32d_role(const MlaArgs& a, const Mla32dShared
         for (int e = 0; e < 4; ++e) {
           const int head = hg * HW + 16 * hb + 4 * lq + e;
           const int col = 16 * (cb0 + cb) + l16;
-          a.ws_acc[(ws0 + (int64_t)head * a.S) * kLatDv + col] = acc[hb][cb][e] * (1.0f / 2048.0f);
+          put_partial(a.ws_acc + (ws0 + (int64_t)head * a.S) * kLatDv + col, acc[hb][cb][e] * (1.0f / 2048.0f),
+                      FUSED && a.S > 1);
         }
   }
 }
 
+template <bool FUSED>
 __global__ __launch_bounds__(512) void mla32d_split_kernel(MlaArgs a) {
   constexpr int HW = 48, NBUF = 4;
   using R = Mla32dRoles;
@@ -1779,6 +1781,10 @@ __global__ __launch_bounds__(512) void mla32d_split_kernel(MlaArgs a) {
   const int64_t end = min((int64_t)L, start + a.chunk);
   const int64_t ws0 = (int64_t)b * a.Hq * a.S + split;
   if (start >= end) {
+    if constexpr (FUSED) {
+      latent_fused_tail<512>(a, s_c, hg * HW, HW);
+      return;
+    }
     for (int idx = tid; idx < HW * kLatDv; idx += 512) {
       const int h = hg * HW + idx / kLatDv, e = idx - (idx / kLatDv) * kLatDv;
       a.ws_acc[(ws0 + (int64_t)h * a.S) * kLatDv + e] = 0.0f;
@@ -1793,11 +1799,12 @@ __global__ __launch_bounds__(512) void mla32d_split_kernel(MlaArgs a) {
   const Mla32dShared sh{s_c, s_p, s_alpha, s_moved};
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (wave < R::NS)
-    mla32d_role<0>(a, sh, start, end, ws0, b, hg);
+    mla32d_role<0, FUSED>(a, sh, start, end, ws0, b, hg);
   else if (R::shared(wave))
-    mla32d_role<R::kShared>(a, sh, start, end, ws0, b, hg);
+    mla32d_role<R::kShared, FUSED>(a, sh, start, end, ws0, b, hg);
   else
-    mla32d_role<R::kAlone>(a, sh, start, end, ws0, b, hg);
+    mla32d_role<R::kAlone, FUSED>(a, sh, start, end, ws0, b, hg);
+  if constexpr (FUSED) latent_fused_tail<512>(a, s_c, hg * HW, HW);
 }
 
 int latent_blocks_per_split(const sk_desc_t& d) {
@@ -1831,12 +1838,12 @@ static sk_status_t latent_variant(const SplitLaunch& s, bool launch, const void*
     threads = mla32_blocks(H) * 256;
     groups = mla32_groups(H);
     if constexpr (H == 96) {
-      if (!idx && !s.fused && (int64_t)s.p->n_splits * d.batch >= 64) {
-        // Contiguous caches on the two-launch path, once the grid (two
-        // workgroups per (split, sequence) pair) fills half the compute
-        // units: the dedicated-role form. Shorter grids keep the four-wave
-        // form, the one the index-list path shares tile for tile.
-        kern = mla32d_split_kernel;
+      if (!idx && (int64_t)s.p->n_splits * d.batch >= 64) {
+        // Contiguous caches, once the grid (two workgroups per (split,
+        // sequence) pair) fills half the compute units: the dedicated-role
+        // form. Shorter grids keep the four-wave form, the one the
+        // index-list path shares tile for tile.
+        kern = s.fused ? mla32d_split_kernel<true> : mla32d_split_kernel<false>;
         threads = 512;
       }
     }
