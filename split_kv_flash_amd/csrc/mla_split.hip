@@ -1469,8 +1469,9 @@ __device__ __forceinline__ void mla32d_role(const MlaArgs& a, const Mla32dShared
   // Tile staging as in mla32_split_kernel (slot s: row s / 144, logical chunk
   // (s % 144) ^ row); every wave issues and splits its share of the 36
   // wave-loads of a tile.
-  const int wl0 = wave * R::LB + min(wave, R::LX);
-  const int nwl = R::LB + (wave < R::LX ? 1 : 0);
+  const int wo = (wave + 5) & 7;  // output waves first: the scoring waves take the smaller shares
+  const int wl0 = wo * R::LB + min(wo, R::LX);
+  const int nwl = R::LB + (wo < R::LX ? 1 : 0);
   const uint32_t lds0 = lds_addr_of(s_c);
   const uint32_t row_bytes = (uint32_t)(a.stride_pos * 4);  // 16 rows: offsets fit 32 bits
   auto issue_tile = [&](int bi, int64_t tb) {
