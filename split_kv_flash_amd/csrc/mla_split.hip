@@ -1432,7 +1432,8 @@ struct Mla32dRoles {
     return s;
   }
   static constexpr int kLoads = kSlots32 / 64;  // 36 wave-loads per tile, over all eight waves
-  static constexpr int LB = kLoads / 8, LX = kLoads % 8;
+  static constexpr int kScoreLoads = 3;  // wave-loads per scoring wave (the output waves take the rest)
+  static constexpr int LB = (kLoads - NS * kScoreLoads) / NO, LX = (kLoads - NS * kScoreLoads) % NO;
   static constexpr int DPW = LB + (LX > 0 ? 1 : 0);
 };
 
@@ -1469,9 +1470,9 @@ __device__ __forceinline__ void mla32d_role(const MlaArgs& a, const Mla32dShared
   // Tile staging as in mla32_split_kernel (slot s: row s / 144, logical chunk
   // (s % 144) ^ row); every wave issues and splits its share of the 36
   // wave-loads of a tile.
-  const int wo = (wave + 5) & 7;  // output waves first: the scoring waves take the smaller shares
-  const int wl0 = wo * R::LB + min(wo, R::LX);
-  const int nwl = R::LB + (wo < R::LX ? 1 : 0);
+  const int ow = wave - R::NS;
+  const int wl0 = SCORER ? wave * R::kScoreLoads : R::NS * R::kScoreLoads + ow * R::LB + min(ow, R::LX);
+  const int nwl = SCORER ? R::kScoreLoads : R::LB + (ow < R::LX ? 1 : 0);
   const uint32_t lds0 = lds_addr_of(s_c);
   const uint32_t row_bytes = (uint32_t)(a.stride_pos * 4);  // 16 rows: offsets fit 32 bits
   auto issue_tile = [&](int bi, int64_t tb) {
@@ -1484,7 +1485,7 @@ __device__ __forceinline__ void mla32d_role(const MlaArgs& a, const Mla32dShared
       const int last = (int)(end - 1 - tbc);
 #pragma unroll
       for (int cc = 0; cc < R::DPW; ++cc) {
-        if (R::LX != 0 && cc >= nwl) continue;
+        if (cc >= nwl) continue;  // scoring and output waves take different shares
         const int sl = (wl0 + cc) * 64 + lane;
         const int srow = sl / kCpr32;
         const int scol = (sl - srow * kCpr32) ^ srow;
@@ -1499,7 +1500,7 @@ __device__ __forceinline__ void mla32d_role(const MlaArgs& a, const Mla32dShared
     {
 #pragma unroll
       for (int cc = 0; cc < R::DPW; ++cc) {
-        if (R::LX != 0 && cc >= nwl) continue;
+        if (cc >= nwl) continue;  // scoring and output waves take different shares
         const int sl = (wl0 + cc) * 64 + lane;
         u32x4_t* p = reinterpret_cast<u32x4_t*>(s_c + bi * TSTR + sl * 4);
         const u32x4_t v = f16_parts(__builtin_bit_cast(float4_t, *p));
@@ -1509,7 +1510,9 @@ __device__ __forceinline__ void mla32d_role(const MlaArgs& a, const Mla32dShared
   };
   // Everything of this wave but its loads of the newest tile has landed.
   auto wait_but_newest = [&]() {
-    if constexpr (R::LX == 0) {
+    if constexpr (SCORER) {
+      wait_vm_lgkm0<R::kScoreLoads>();
+    } else if constexpr (R::LX == 0) {
       wait_vm_lgkm0<R::DPW>();
     } else {
       if (nwl == R::DPW)
