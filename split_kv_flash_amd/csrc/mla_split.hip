@@ -1432,7 +1432,7 @@ struct Mla32dRoles {
     return s;
   }
   static constexpr int kLoads = kSlots32 / 64;  // 36 wave-loads per tile, over all eight waves
-  static constexpr int kScoreLoads = 3;  // wave-loads per scoring wave (the output waves take the rest)
+  static constexpr int kScoreLoads = 2;  // wave-loads per scoring wave (the output waves take the rest)
   static constexpr int LB = (kLoads - NS * kScoreLoads) / NO, LX = (kLoads - NS * kScoreLoads) % NO;
   static constexpr int DPW = LB + (LX > 0 ? 1 : 0);
 };
